@@ -1,0 +1,71 @@
+"""Layer shapes and batch recipes of the synthetic workloads.
+
+Each layer is one MoE layer's gate and up projections in spectral form:
+E experts, input width din, output width dout, spectral rank r, top-k routing.
+The shapes follow public MoE models (Qwen3-30B-A3B, Mixtral-8x7B,
+DeepSeek-MoE-16B); all values are random, seeded, and synthetic.
+"""
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Tuple
+
+WIDTH_SET = (0, 1, 2, 3, 4, 6, 8, 16)
+
+
+@dataclass(frozen=True)
+class LayerSpec:
+    name: str          # seed family: layers with the same name share factors
+    E: int
+    din: int
+    dout: int
+    r: int
+    k: int
+    decay: float       # a_{e,k} = k^-decay * LogNormal(0, ln_sigma), k from 1
+    ln_sigma: float
+    bits: object       # "uniform" or {width: percent}
+    outlier_frac: float  # fraction of input channels scaled for every token
+    outlier_scale: float
+    phi_fp16: bool     # Phi values fp16-representable (False: fp32 factors)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    layer: LayerSpec
+    T: int
+    routing: Tuple     # ("uniform",) or ("zipf", s)
+
+
+TINY = LayerSpec("tiny", E=4, din=64, dout=96, r=64, k=2, decay=0.5,
+                 ln_sigma=0.3, bits="uniform", outlier_frac=0.0,
+                 outlier_scale=1.0, phi_fp16=False)
+
+QWEN3_30B_A3B = LayerSpec(
+    "qwen3_30b_a3b", E=128, din=2048, dout=768, r=2048, k=8, decay=0.7,
+    ln_sigma=0.5, bits={0: 10, 1: 20, 2: 40, 3: 15, 4: 10, 8: 4, 16: 1},
+    outlier_frac=0.005, outlier_scale=20.0, phi_fp16=True)
+
+MIXTRAL_8X7B = LayerSpec(
+    "mixtral_8x7b", E=8, din=4096, dout=14336, r=4096, k=2, decay=0.7,
+    ln_sigma=0.5, bits={0: 5, 1: 10, 2: 40, 3: 25, 4: 15, 8: 5},
+    outlier_frac=0.005, outlier_scale=20.0, phi_fp16=True)
+
+DEEPSEEK_MOE_16B = LayerSpec(
+    "deepseek_moe_16b", E=64, din=2048, dout=1408, r=2048, k=6, decay=0.7,
+    ln_sigma=0.5, bits={1: 5, 2: 25, 3: 35, 4: 25, 6: 5, 8: 4, 16: 1},
+    outlier_frac=0.005, outlier_scale=20.0, phi_fp16=True)
+
+LAYERS: Dict[str, LayerSpec] = {l.name: l for l in
+                                (TINY, QWEN3_30B_A3B, MIXTRAL_8X7B, DEEPSEEK_MOE_16B)}
+
+WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
+    Workload("tiny_t8", TINY, 8, ("uniform",)),
+    Workload("qwen3_30b_a3b_t1", QWEN3_30B_A3B, 1, ("uniform",)),
+    Workload("qwen3_30b_a3b_t32", QWEN3_30B_A3B, 32, ("zipf", 1.1)),
+    Workload("mixtral_8x7b_t1", MIXTRAL_8X7B, 1, ("uniform",)),
+    Workload("mixtral_8x7b_t8", MIXTRAL_8X7B, 8, ("uniform",)),
+    Workload("deepseek_moe_16b_t512", DEEPSEEK_MOE_16B, 512, ("zipf", 1.0)),
+)}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]

@@ -1,0 +1,114 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case swaps one oracle function for a copy with a plausible slip (a wrong
+rounding rule, a dropped term, a transposed operand, a flipped sign, a wrong
+bit order) and checks that at least one pin test then fails.  The mistakes
+live only here, on the CPU.
+"""
+import numpy as np
+import pytest
+
+from oracle import fmt, path, quantize
+import tests.test_oracle_fmt as T_fmt
+import tests.test_oracle_path as T_path
+import tests.test_oracle_quantize as T_q
+
+
+def _q_half_up(P, b):
+    P = np.asarray(P, dtype=np.float32)
+    if b in (0, 16):
+        return _orig_qc(P, b)
+    L = np.float32(2 ** b - 1)
+    lo, hi = P.min(axis=1), P.max(axis=1)
+    s = quantize.fp16_rne((hi - lo) / L)
+    s = np.where(s == 0, np.float16(1), s).astype(np.float16)
+    m = quantize.fp16_rne(lo)
+    v = (P - m.astype(np.float32)[:, None]) / s.astype(np.float32)[:, None]
+    return np.clip(np.floor(v + np.float32(0.5)), 0, L).astype(np.uint16), s, m
+
+
+def _q_wrong_levels(P, b):
+    P = np.asarray(P, dtype=np.float32)
+    if b in (0, 16):
+        return _orig_qc(P, b)
+    L = np.float32(2 ** b)            # 2^b instead of 2^b - 1
+    lo, hi = P.min(axis=1), P.max(axis=1)
+    s = quantize.fp16_rne((hi - lo) / L)
+    m = quantize.fp16_rne(lo)
+    v = (P - m.astype(np.float32)[:, None]) / s.astype(np.float32)[:, None]
+    return np.clip(np.rint(v), 0, L - 1).astype(np.uint16), s, m
+
+
+_orig_qc = quantize.quantize_columns
+
+
+def _apply_shifted(z, a_e, phat_e, bits_e):
+    z = np.atleast_2d(np.asarray(z, dtype=np.float64))
+    y = np.zeros((z.shape[0], phat_e.shape[1]))
+    r = len(a_e)
+    for k in np.nonzero(np.asarray(bits_e) > 0)[0]:
+        y += np.outer(a_e[k] * z[:, (k + 1) % r], phat_e[k])    # wrong index
+    return y
+
+
+def _apply_no_a(z, a_e, phat_e, bits_e):
+    z = np.atleast_2d(np.asarray(z, dtype=np.float64))
+    y = np.zeros((z.shape[0], phat_e.shape[1]))
+    for k in np.nonzero(np.asarray(bits_e) > 0)[0]:
+        y += np.outer(z[:, k], phat_e[k])                        # dropped a
+    return y
+
+
+def _proj_transposed(phi, x):
+    return np.atleast_2d(np.asarray(x, dtype=np.float64)) @ np.asarray(phi, dtype=np.float64).T
+
+
+def _silu_sign(v):
+    v = np.asarray(v, dtype=np.float64)
+    return v / (1.0 + np.exp(v))
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_rounding_half_up_caught(monkeypatch):
+    monkeypatch.setattr(quantize, "quantize_columns", _q_half_up)
+    cases = T_q._cases()["cases"]
+    assert any(_fails(T_q.test_hand_derived, c) for c in cases)
+
+
+def test_wrong_level_count_caught(monkeypatch):
+    monkeypatch.setattr(quantize, "quantize_columns", _q_wrong_levels)
+    cases = T_q._cases()["cases"]
+    assert any(_fails(T_q.test_hand_derived, c) for c in cases)
+
+
+@pytest.mark.parametrize("bad", [_apply_shifted, _apply_no_a])
+def test_expert_apply_slips_caught(monkeypatch, bad):
+    monkeypatch.setattr(path, "expert_apply", bad)
+    assert _fails(T_path.test_brute_force_dense) or _fails(T_path.test_one_hot_and_linearity)
+
+
+def test_transposed_projection_caught(monkeypatch):
+    monkeypatch.setattr(path, "spectral_proj", _proj_transposed)
+    assert _fails(T_path.test_identity_and_permutation_projection)
+
+
+def test_silu_sign_caught(monkeypatch):
+    monkeypatch.setattr(path, "silu", _silu_sign)
+    assert _fails(T_path.test_silu_identities)
+
+
+def test_plane_bit_order_caught(monkeypatch):
+    orig = np.packbits
+
+    def msb_first(a, axis=None, bitorder="big"):
+        return orig(a, axis=axis, bitorder="big")
+
+    monkeypatch.setattr(fmt.np, "packbits", msb_first)
+    assert _fails(T_fmt.test_hand_built_planes)
