@@ -1,0 +1,161 @@
+/*
+ * bitsmoe.h -- C ABI of the spectral MoE gate/up decode library (gfx950).
+ *
+ * The method (BitsMoE; blog note "BitsMoE: Cost-Aware Bit Allocation In
+ * spectral Space for MoE LLM Quantization", section Methodology):
+ *   - "first split": one SVD of the stacked expert matrices of a linear type
+ *     gives a basis Phi shared by all experts, and W_e x = P_e (Phi^T x); the
+ *     bracket z = Phi^T x does not depend on the expert, so the experts a
+ *     token selects all reuse it.
+ *   - "second split": W_e = sum_k a_{e,k} p_{e,k} phi_k^T with unit columns
+ *     p_{e,k}; the magnitude a is kept, the direction p is quantized.
+ *   - "Usage": per-column widths {0,1,2,3,4,6,8,16}; 0 drops the column, 16
+ *     keeps it as FP16.
+ *   - "execution": columns of the same width are grouped and stored by bit
+ *     plane so the GPU processes the mixed widths regularly.
+ * For token t routed to expert e (slot j of its top-k list) the library
+ * computes
+ *   y_e = sum_{k: b_{e,k} > 0} a_{e,k} z_k p_hat_{e,k},   z = Phi^T x_t,
+ *   h[t, j, :] = SiLU(y_gate,e) * y_up,e,   SiLU(v) = v / (1 + exp(-v)),
+ * where p_hat is the dequantized direction: m + s*q for 1..8-bit columns
+ * (uniform asymmetric codes q, fp16 scale s and fp16 offset m per column),
+ * the fp16 value for 16-bit columns.  Routing weights are not applied.
+ *
+ * Conventions for every call below:
+ *   - Return value: BITSMOE_OK (0) or a negative status; bitsmoe_strerror()
+ *     names it and bitsmoe_last_error_detail() gives a thread-local message.
+ *   - Ownership: the caller allocates and frees every buffer.  The library
+ *     allocates no device memory and never synchronizes.
+ *   - Device pointers must be 16-byte aligned (ids: 4-byte aligned).
+ *   - Device calls enqueue work on `stream` (0 = null stream) and return at
+ *     once; inputs must stay valid until the stream reaches the work.  Host
+ *     argument checks happen before anything is enqueued; a failing check
+ *     enqueues nothing.
+ *   - Device-side faults the host cannot see (a blob whose header does not
+ *     match the dimensions passed, an expert id outside [0, E)) never cause
+ *     an out-of-bounds access: the affected output rows are written as NaN.
+ *   - Stateless and re-entrant; calls that share a workspace must not
+ *     overlap in time.
+ */
+#ifndef BITSMOE_H
+#define BITSMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* bitsmoe_stream_t; /* same type as hipStream_t */
+
+#define BITSMOE_OK        0
+#define BITSMOE_EINVAL   -1  /* null or misaligned pointer, T < 1, k < 1, k > E */
+#define BITSMOE_ESHAPE   -2  /* non-positive dims, r > 65535, din % 8 != 0, mismatch */
+#define BITSMOE_EBITS    -3  /* a width outside {0,1,2,3,4,6,8,16}, non-finite p */
+#define BITSMOE_ENOSPC   -4  /* output, blob or workspace buffer too small */
+#define BITSMOE_EFORMAT  -5  /* blob magic, version, CRC or directory invalid */
+#define BITSMOE_EHIP     -6  /* HIP runtime or launch error */
+
+#define BITSMOE_FORMAT_VERSION 1
+
+/* Library version (major*10000 + minor*100 + patch). */
+int bitsmoe_version(void);
+const char* bitsmoe_strerror(int status);
+const char* bitsmoe_last_error_detail(void);
+
+/* ---------------------------------------------------------------- packing
+ * Host-only, offline.  Quantizes and packs one linear type (gate or up) of
+ * one layer ("second split", "Usage", "execution").
+ *   p    : E*r*dout float32, column (e,k) at p[(e*r + k)*dout + i], unit norm
+ *          expected (any finite values with |p| <= 60000 are accepted)
+ *   a    : E*r float32 magnitudes a_{e,k} (stored unquantized)
+ *   bits : E*r uint8 widths in {0,1,2,3,4,6,8,16}
+ * Quantizer (1..8 bits), all in IEEE float32 without fused operations:
+ *   s = fp16_rne((max p - min p) / (2^b - 1)), s = 1 if it rounds to 0;
+ *   m = fp16_rne(min p); q_i = clamp(nearbyint((p_i - m) / s), 0, 2^b - 1)
+ *   with ties to even.  16 bits: fp16_rne(p_i).  0 bits: no entry.
+ * Blob layout (format v1, little-endian, offsets from the blob base):
+ *   header 128 B: "BMOE", u32 version, E, dout, r, dout_pad (=64*ceil(dout/64)),
+ *     n_slabs (=dout_pad/64), header_bytes(=128); u64 total_bytes at 32,
+ *     u64 dir_offset(=128) at 40, u32 CRC-32 (IEEE) of [128, total) at 48.
+ *   directory: E records of 64 B: u64 block_offset; u32 n_nz, n_q, n_16,
+ *     masks_per_slab (= sum of b over 1..8-bit columns), a_off, s_off, m_off,
+ *     planes_off, f16_off, block_bytes (offsets relative to the block);
+ *     u16 count[7] of widths 1,2,3,4,6,8,16 at 48.
+ *   expert block (256-aligned, back to back): columns ordered by width group
+ *     1,2,3,4,6,8,16 and by ascending k inside a group;
+ *     u16 kidx[n_nz] @0, f32 a[n_nz] @a_off, f16 s[n_q] @s_off,
+ *     f16 m[n_q] @m_off, u64 planes[n_slabs][masks_per_slab] @planes_off
+ *     (per 64-row slab, per 1..8-bit column, per plane j from the least
+ *     significant: bit t = bit j of q[64*slab + t], 0 for rows >= dout),
+ *     f16 values[n_16][dout_pad] @f16_off.  Padding bytes are zero.
+ * bitsmoe_pack_size: bytes the blob needs.  bitsmoe_pack: writes it into the
+ * host buffer `out` (out_bytes >= that size, else BITSMOE_ENOSPC).
+ */
+int bitsmoe_pack_size(int E, int dout, int r, const uint8_t* bits, size_t* out_bytes);
+int bitsmoe_pack(int E, int dout, int r, const float* p, const float* a,
+                 const uint8_t* bits, void* out, size_t out_bytes);
+
+/* Host-side check of a blob in host memory: magic, version, sizes, CRC and
+ * every directory record.  Fills E, dout, r when the pointers are non-null.
+ * BITSMOE_EFORMAT on any inconsistency. */
+int bitsmoe_blob_check(const void* blob, size_t bytes, int* E, int* dout, int* r);
+
+/* --------------------------------------------------------- shared projection
+ * z = Phi^T x for every token ("first split": computed once per token and
+ * shared by all routed experts).
+ *   phi_t_f16 : r_total*din fp16, basis vector n at phi_t_f16[n*din .. +din)
+ *               (Phi stored transposed: row n is phi_n).  Gate and up bases
+ *               may be stacked as r_total = 2r rows.
+ *   x_f16     : T*din fp16 activations, token t at x[t*din]
+ *   z         : T*r_total float32 output, z[t*r_total + n]
+ * din must be a multiple of 8.  fp16 products are exact in float32 and are
+ * accumulated in float32. */
+int bitsmoe_spectral_proj(const void* phi_t_f16, const void* x_f16, float* z,
+                          int T, int din, int r_total, bitsmoe_stream_t stream);
+
+/* ------------------------------------------------------------ expert apply
+ * One linear type, no epilogue: for every pair (t, j), e = ids[t*k + j],
+ *   y[(t*k + j)*dout + i] = sum_{k: b>0} a_{e,k} z[t*z_stride + k] p_hat_{e,k}[i]
+ * ("second split").  packed: device copy of a bitsmoe_pack blob of
+ * packed_bytes bytes for (E, dout, r).  z: T rows of z_stride >= r floats.
+ * ws/ws_bytes: may be NULL/0 (no workspace needed). */
+int bitsmoe_expert_apply(const void* packed, size_t packed_bytes, int E, int dout,
+                         int r, const float* z, int z_stride, const int32_t* ids,
+                         int T, int k, float* y, void* ws, size_t ws_bytes,
+                         bitsmoe_stream_t stream);
+
+/* ------------------------------------------------------------ full gate/up
+ * h[(t*k + j)*dout + i] = SiLU(y_gate)[i] * y_up[i] for e = ids[t*k + j].
+ *   packed_gate / packed_up : device blobs of gate_bytes / up_bytes
+ *   phi_t_gateup_f16        : 2r*din fp16: rows 0..r-1 = Phi_gate^T,
+ *                             rows r..2r-1 = Phi_up^T
+ *   x_f16 : T*din fp16; ids : T*k int32; h : T*k*dout float32
+ *   ws    : device workspace of at least bitsmoe_moe_gateup_workspace_size()
+ *           bytes, zero-filled before its first use (bitsmoe_workspace_init);
+ *           every call leaves its synchronization words at zero again.
+ */
+int bitsmoe_moe_gateup_workspace_size(int T, int k, int E, int din, int dout, int r,
+                                      size_t* bytes);
+int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes,
+                       const void* packed_up, size_t up_bytes,
+                       const void* phi_t_gateup_f16, const void* x_f16,
+                       const int32_t* ids, int T, int k, int E, int din, int dout,
+                       int r, float* h, void* ws, size_t ws_bytes,
+                       bitsmoe_stream_t stream);
+
+/* Zero-fills a workspace with a kernel (no memset node), on `stream`. */
+int bitsmoe_workspace_init(void* ws, size_t ws_bytes, bitsmoe_stream_t stream);
+
+/* ---------------------------------------------------------------- testing
+ * Codes of expert e as the device unpack routine decodes them, in k order:
+ * codes[k*dout + i] = q (1..8-bit columns), the fp16 bit pattern (16-bit
+ * columns), 0 (0-bit columns).  codes: device buffer of r*dout uint16. */
+int bitsmoe_dump_codes(const void* packed, size_t packed_bytes, int E, int dout,
+                       int r, int e, uint16_t* codes, bitsmoe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITSMOE_H */

@@ -1,0 +1,170 @@
+"""ctypes binding of libbitsmoe.so (declared in include/bitsmoe.h).
+
+Argument marshalling only: every device step runs in the library's gfx950
+kernels.  Device buffers are torch tensors (torch provides memory and
+streams); host buffers are numpy arrays.  There is no fallback: if the
+library is missing, importing this module raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitsmoe.so")
+
+OK, EINVAL, ESHAPE, EBITS, ENOSPC, EFORMAT, EHIP = 0, -1, -2, -3, -4, -5, -6
+
+
+class BitsMoEError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__("%s (status %d): %s" % (_strerror(status), status, detail))
+        self.status = status
+        self.detail = detail
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libbitsmoe.so is not built (%s); run "
+                          "`python -m spectral_expert_gemv_amd.build`" % LIB_PATH)
+    return ctypes.CDLL(LIB_PATH)
+
+
+_lib = _load()
+
+_vp, _sz, _i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_pi = ctypes.POINTER(ctypes.c_int)
+_psz = ctypes.POINTER(ctypes.c_size_t)
+
+_SIGS = {
+    "bitsmoe_version": ([], _i),
+    "bitsmoe_strerror": ([_i], ctypes.c_char_p),
+    "bitsmoe_last_error_detail": ([], ctypes.c_char_p),
+    "bitsmoe_pack_size": ([_i, _i, _i, _vp, _psz], _i),
+    "bitsmoe_pack": ([_i, _i, _i, _vp, _vp, _vp, _vp, _sz], _i),
+    "bitsmoe_blob_check": ([_vp, _sz, _pi, _pi, _pi], _i),
+    "bitsmoe_spectral_proj": ([_vp, _vp, _vp, _i, _i, _i, _vp], _i),
+    "bitsmoe_expert_apply": ([_vp, _sz, _i, _i, _i, _vp, _i, _vp, _i, _i, _vp, _vp, _sz, _vp], _i),
+    "bitsmoe_moe_gateup_workspace_size": ([_i, _i, _i, _i, _i, _i, _psz], _i),
+    "bitsmoe_moe_gateup": ([_vp, _sz, _vp, _sz, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                            _vp, _vp, _sz, _vp], _i),
+    "bitsmoe_workspace_init": ([_vp, _sz, _vp], _i),
+    "bitsmoe_dump_codes": ([_vp, _sz, _i, _i, _i, _i, _vp, _vp], _i),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTS = tuple(_SIGS)
+
+
+def _strerror(status):
+    return _lib.bitsmoe_strerror(int(status)).decode()
+
+
+def _check(status):
+    if status != OK:
+        raise BitsMoEError(status, _lib.bitsmoe_last_error_detail().decode())
+
+
+def version():
+    return _lib.bitsmoe_version()
+
+
+def _ptr(t):
+    """Device pointer of a torch tensor or host pointer of a numpy array."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _nbytes(t):
+    if isinstance(t, np.ndarray):
+        return t.nbytes
+    return t.numel() * t.element_size()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------- host side
+
+def pack_size(E, dout, r, bits):
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    out = ctypes.c_size_t(0)
+    _check(_lib.bitsmoe_pack_size(E, dout, r, bits.ctypes.data, ctypes.byref(out)))
+    return out.value
+
+
+def pack(p, a, bits):
+    """Quantize and pack one linear type (p: E x r x dout, a, bits: E x r)."""
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    E, r, dout = p.shape
+    if a.shape != (E, r) or bits.shape != (E, r):
+        raise ValueError("a and bits must be E x r")
+    n = pack_size(E, dout, r, bits)
+    out = np.zeros(n, dtype=np.uint8)
+    _check(_lib.bitsmoe_pack(E, dout, r, p.ctypes.data, a.ctypes.data, bits.ctypes.data,
+                             out.ctypes.data, out.nbytes))
+    return out
+
+
+def blob_check(blob):
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    E, dout, r = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(_lib.bitsmoe_blob_check(blob.ctypes.data, blob.nbytes, ctypes.byref(E),
+                                   ctypes.byref(dout), ctypes.byref(r)))
+    return E.value, dout.value, r.value
+
+
+# -------------------------------------------------------------- device side
+
+def spectral_proj(phi_t, x, z, stream=None):
+    """z[T, R] = x[T, din] @ phi_t[R, din]^T (phi_t, x fp16; z float32)."""
+    R, din = phi_t.shape
+    T = x.shape[0]
+    _check(_lib.bitsmoe_spectral_proj(_ptr(phi_t), _ptr(x), _ptr(z), T, din, R,
+                                      _stream(stream)))
+
+
+def expert_apply(packed, E, dout, r, z, ids, y, z_stride=None, ws=None, stream=None):
+    T, k = ids.shape
+    zs = z.shape[1] if z_stride is None else z_stride
+    _check(_lib.bitsmoe_expert_apply(_ptr(packed), _nbytes(packed), E, dout, r, _ptr(z), zs,
+                                     _ptr(ids), T, k, _ptr(y), _ptr(ws),
+                                     0 if ws is None else _nbytes(ws), _stream(stream)))
+
+
+def moe_gateup_workspace_size(T, k, E, din, dout, r):
+    out = ctypes.c_size_t(0)
+    _check(_lib.bitsmoe_moe_gateup_workspace_size(T, k, E, din, dout, r, ctypes.byref(out)))
+    return out.value
+
+
+def moe_gateup(packed_gate, packed_up, phi_t_gateup, x, ids, E, dout, r, h, ws, stream=None):
+    T, k = ids.shape
+    din = x.shape[1]
+    _check(_lib.bitsmoe_moe_gateup(_ptr(packed_gate), _nbytes(packed_gate), _ptr(packed_up),
+                                   _nbytes(packed_up), _ptr(phi_t_gateup), _ptr(x), _ptr(ids),
+                                   T, k, E, din, dout, r, _ptr(h), _ptr(ws), _nbytes(ws),
+                                   _stream(stream)))
+
+
+def workspace_init(ws, stream=None):
+    _check(_lib.bitsmoe_workspace_init(_ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def dump_codes(packed, E, dout, r, e, codes, stream=None):
+    _check(_lib.bitsmoe_dump_codes(_ptr(packed), _nbytes(packed), E, dout, r, e, _ptr(codes),
+                                   _stream(stream)))

@@ -1,0 +1,339 @@
+// gfx950 kernels and the device entry points of the C ABI.
+//
+// Path (BitsMoE blog note, Methodology): z = Phi^T x once per token ("first
+// split"), then for each routed expert y_e = sum_k a_{e,k} z_k p_hat_{e,k}
+// over the width-grouped bit planes ("second split", "execution"), then
+// h = SiLU(y_gate) * y_up.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "bitsmoe.h"
+#include "common.h"
+#include "device_common.h"
+#include "format.h"
+
+namespace bitsmoe {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Shared projection, small token counts: one wave per basis vector n.  Lanes
+// stride the din reduction with 16-byte loads; fp16 pairs are multiplied and
+// accumulated in float32 by v_dot2_f32_f16; a wave reduction finishes it.
+// Phi^T is read exactly once per chunk of kTokChunk tokens.
+// ---------------------------------------------------------------------------
+constexpr int kProjWaves = 4;
+constexpr int kTokChunk = 4;
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline float dot8(uint4 a, uint4 b, float acc) {
+  const half2_t* ha = reinterpret_cast<const half2_t*>(&a);
+  const half2_t* hb = reinterpret_cast<const half2_t*>(&b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(ha[i], hb[i], acc, false);
+  return acc;
+}
+
+__global__ __launch_bounds__(kProjWaves * kWave) void k_proj_gemv(
+    const uint4* __restrict__ phi_t, const uint4* __restrict__ x, float* __restrict__ z,
+    int T, int din8, int R) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int n = blockIdx.x * kProjWaves + (threadIdx.x >> 6);
+  if (n >= R) return;
+  const uint4* prow = phi_t + (size_t)n * din8;
+  for (int t0 = 0; t0 < T; t0 += kTokChunk) {
+    float acc[kTokChunk] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = lane; i < din8; i += kWave) {
+      const uint4 pv = prow[i];
+#pragma unroll
+      for (int tt = 0; tt < kTokChunk; ++tt)
+        if (t0 + tt < T) acc[tt] = dot8(pv, x[(size_t)(t0 + tt) * din8 + i], acc[tt]);
+    }
+#pragma unroll
+    for (int tt = 0; tt < kTokChunk; ++tt) {
+      const float s = wave_sum(acc[tt]);
+      if (lane == 0 && t0 + tt < T) z[(size_t)(t0 + tt) * R + n] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Expert apply over one 64-row slab, lane = row.  For every stored column
+// (width groups 1..8 then 16, ascending k inside a group):
+//   y += (a z s) q + (a z m)     for 1..8-bit columns
+//   y += (a z) p16               for 16-bit columns.
+// Returns false when the blob or the expert id cannot be used.
+// ---------------------------------------------------------------------------
+__device__ float apply_slab(const uint8_t* __restrict__ blob, uint64_t blob_bytes, int e,
+                            int E, int dout, int r, const float* __restrict__ zrow,
+                            int slab, int lane, bool& ok) {
+  DirRec d;
+  if (!load_dir(blob, blob_bytes, e, E, dout, r, d)) {
+    ok = false;
+    return 0.f;
+  }
+  const uint32_t dout_pad = reinterpret_cast<const Header*>(blob)->dout_pad;
+  const uint8_t* blk = blob + d.block_offset;
+  const uint16_t* kidx = reinterpret_cast<const uint16_t*>(blk);
+  const float* A = reinterpret_cast<const float*>(blk + d.a_off);
+  const __half* S = reinterpret_cast<const __half*>(blk + d.s_off);
+  const __half* M = reinterpret_cast<const __half*>(blk + d.m_off);
+  const uint64_t* P =
+      reinterpret_cast<const uint64_t*>(blk + d.planes_off) + (size_t)slab * d.masks_per_slab;
+  float acc = 0.f, bias = 0.f;
+  uint32_t col = 0, w = 0;
+  bool good = true;
+  for (int g = 0; g < kNumQGroups; ++g) {
+    const int b = kGroupWidth[g];
+    const uint32_t n = d.count[g];
+    for (uint32_t c = 0; c < n; ++c, ++col, w += b) {
+      uint32_t k = kidx[col];
+      good &= k < (uint32_t)r;
+      k = k < (uint32_t)r ? k : 0;
+      const float az = A[col] * zrow[k];
+      bias += az * __half2float(M[col]);
+      const uint32_t q = decode_code(P + w, b, lane);
+      acc += (az * __half2float(S[col])) * (float)q;
+    }
+  }
+  const __half* F = reinterpret_cast<const __half*>(blk + d.f16_off);
+  for (uint32_t c = 0; c < d.n_16; ++c, ++col) {
+    uint32_t k = kidx[col];
+    good &= k < (uint32_t)r;
+    k = k < (uint32_t)r ? k : 0;
+    acc += (A[col] * zrow[k]) * __half2float(F[(size_t)c * dout_pad + (size_t)slab * 64 + lane]);
+  }
+  ok = good;
+  return acc + bias;
+}
+
+// grid (T*k, n_slabs); block 64 (apply) or 128 (gate wave + up wave).
+template <bool kGateUp>
+__global__ __launch_bounds__(kGateUp ? 128 : 64) void k_expert_slab(
+    const uint8_t* __restrict__ blob_g, uint64_t bytes_g, const uint8_t* __restrict__ blob_u,
+    uint64_t bytes_u, int E, int dout, int r, const float* __restrict__ z, int z_stride,
+    int z_off_up, const int32_t* __restrict__ ids, int ktop, float* __restrict__ out) {
+  const int pair = blockIdx.x;
+  const int slab = blockIdx.y;
+  const int t = pair / ktop;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int e = ids[pair];
+  bool ok = true;
+  const uint8_t* blob = wv ? blob_u : blob_g;
+  const uint64_t bytes = wv ? bytes_u : bytes_g;
+  const float* zrow = z + (size_t)t * z_stride + (wv ? z_off_up : 0);
+  const float y = apply_slab(blob, bytes, e, E, dout, r, zrow, slab, lane, ok);
+  const int row = slab * 64 + lane;
+  if (!kGateUp) {
+    if (row < dout) out[(size_t)pair * dout + row] = ok ? y : __builtin_nanf("");
+    return;
+  }
+  __shared__ float s_y[kWave];
+  __shared__ int s_ok;
+  if (threadIdx.x == 64) s_ok = ok;
+  if (wv == 1) s_y[lane] = y;
+  __syncthreads();
+  if (wv == 0 && row < dout)
+    out[(size_t)pair * dout + row] = (ok && s_ok) ? silu_mul(y, s_y[lane]) : __builtin_nanf("");
+}
+
+// grid (n_slabs); block 64: codes of expert e in k order (0-bit columns are
+// left as the caller's zero fill).
+__global__ __launch_bounds__(64) void k_dump_codes(const uint8_t* __restrict__ blob,
+                                                   uint64_t blob_bytes, int E, int dout, int r,
+                                                   int e, uint16_t* __restrict__ codes) {
+  DirRec d;
+  const int slab = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int row = slab * 64 + lane;
+  if (!load_dir(blob, blob_bytes, e, E, dout, r, d)) {
+    if (row < dout)
+      for (int k = 0; k < r; ++k) codes[(size_t)k * dout + row] = 0xFFFFu;
+    return;
+  }
+  const uint32_t dout_pad = reinterpret_cast<const Header*>(blob)->dout_pad;
+  const uint8_t* blk = blob + d.block_offset;
+  const uint16_t* kidx = reinterpret_cast<const uint16_t*>(blk);
+  const uint64_t* P =
+      reinterpret_cast<const uint64_t*>(blk + d.planes_off) + (size_t)slab * d.masks_per_slab;
+  uint32_t col = 0, w = 0;
+  for (int g = 0; g < kNumQGroups; ++g) {
+    const int b = kGroupWidth[g];
+    for (uint32_t c = 0; c < d.count[g]; ++c, ++col, w += b) {
+      const uint32_t q = decode_code(P + w, b, lane);
+      const uint32_t k = kidx[col];
+      if (row < dout && k < (uint32_t)r) codes[(size_t)k * dout + row] = (uint16_t)q;
+    }
+  }
+  const uint16_t* F = reinterpret_cast<const uint16_t*>(blk + d.f16_off);
+  for (uint32_t c = 0; c < d.n_16; ++c, ++col) {
+    const uint32_t k = kidx[col];
+    if (row < dout && k < (uint32_t)r)
+      codes[(size_t)k * dout + row] = F[(size_t)c * dout_pad + row];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_zero_fill(uint4* __restrict__ p, size_t n16,
+                                                   uint8_t* __restrict__ tail, int ntail) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// host helpers
+// ---------------------------------------------------------------------------
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int launch_status(const char* what) {
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(BITSMOE_EHIP, "%s: %s", what, hipGetErrorString(err));
+  return BITSMOE_OK;
+}
+
+int check_blob_arg(const void* blob, size_t bytes, int E, const char* name) {
+  if (!blob) return fail(BITSMOE_EINVAL, "%s is null", name);
+  if (!aligned16(blob)) return fail(BITSMOE_EINVAL, "%s is not 16-byte aligned", name);
+  if (bytes < kHeaderBytes + (size_t)kDirRecBytes * E)
+    return fail(BITSMOE_ENOSPC, "%s: %zu bytes cannot hold header and directory", name, bytes);
+  return BITSMOE_OK;
+}
+
+int check_layer_dims(int E, int dout, int r) {
+  if (E <= 0 || dout <= 0 || r <= 0)
+    return fail(BITSMOE_ESHAPE, "E=%d dout=%d r=%d must be positive", E, dout, r);
+  if (r > 65535) return fail(BITSMOE_ESHAPE, "r=%d exceeds 65535", r);
+  if (dout > (1 << 24)) return fail(BITSMOE_ESHAPE, "dout=%d too large", dout);
+  return BITSMOE_OK;
+}
+
+int proj_args(const void* phi, const void* x, const float* z, int T, int din, int R) {
+  if (!phi || !x || !z) return fail(BITSMOE_EINVAL, "null pointer argument");
+  if (!aligned16(phi) || !aligned16(x) || !aligned16(z))
+    return fail(BITSMOE_EINVAL, "phi, x and z must be 16-byte aligned");
+  if (T < 1) return fail(BITSMOE_EINVAL, "T=%d < 1", T);
+  if (din <= 0 || R <= 0) return fail(BITSMOE_ESHAPE, "din=%d r_total=%d", din, R);
+  if (din % 8) return fail(BITSMOE_ESHAPE, "din=%d is not a multiple of 8", din);
+  return BITSMOE_OK;
+}
+
+int launch_proj(const void* phi, const void* x, float* z, int T, int din, int R,
+                hipStream_t s) {
+  const dim3 grid((R + kProjWaves - 1) / kProjWaves);
+  hipLaunchKernelGGL(k_proj_gemv, grid, dim3(kProjWaves * kWave), 0, s,
+                     (const uint4*)phi, (const uint4*)x, z, T, din / 8, R);
+  return launch_status("spectral projection launch");
+}
+
+size_t z_bytes(int T, int r) { return align_up((size_t)T * 2 * r * sizeof(float), 256); }
+
+}  // namespace
+}  // namespace bitsmoe
+
+using namespace bitsmoe;
+
+extern "C" {
+
+int bitsmoe_spectral_proj(const void* phi_t_f16, const void* x_f16, float* z, int T, int din,
+                          int r_total, bitsmoe_stream_t stream) {
+  int st = proj_args(phi_t_f16, x_f16, z, T, din, r_total);
+  if (st) return st;
+  return launch_proj(phi_t_f16, x_f16, z, T, din, r_total, (hipStream_t)stream);
+}
+
+int bitsmoe_expert_apply(const void* packed, size_t packed_bytes, int E, int dout, int r,
+                         const float* z, int z_stride, const int32_t* ids, int T, int k,
+                         float* y, void* ws, size_t ws_bytes, bitsmoe_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_layer_dims(E, dout, r);
+  if (st) return st;
+  if ((st = check_blob_arg(packed, packed_bytes, E, "packed"))) return st;
+  if (!z || !ids || !y) return fail(BITSMOE_EINVAL, "null pointer argument");
+  if (!aligned16(z) || !aligned16(y) || ((uintptr_t)ids & 3u))
+    return fail(BITSMOE_EINVAL, "misaligned z, y or ids");
+  if (T < 1 || k < 1 || k > E) return fail(BITSMOE_EINVAL, "T=%d k=%d E=%d", T, k, E);
+  if (z_stride < r) return fail(BITSMOE_ESHAPE, "z_stride=%d < r=%d", z_stride, r);
+  if ((long long)T * k > (1LL << 24))
+    return fail(BITSMOE_ESHAPE, "T*k=%lld too large", (long long)T * k);
+  const int n_slabs = (dout + 63) / 64;
+  hipLaunchKernelGGL(k_expert_slab<false>, dim3(T * k, n_slabs), dim3(64), 0,
+                     (hipStream_t)stream, (const uint8_t*)packed, (uint64_t)packed_bytes,
+                     (const uint8_t*)packed, (uint64_t)packed_bytes, E, dout, r, z, z_stride, 0,
+                     ids, k, y);
+  return launch_status("expert apply launch");
+}
+
+int bitsmoe_moe_gateup_workspace_size(int T, int k, int E, int din, int dout, int r,
+                                      size_t* bytes) {
+  if (!bytes) return fail(BITSMOE_EINVAL, "bytes is null");
+  int st = check_layer_dims(E, dout, r);
+  if (st) return st;
+  if (T < 1 || k < 1 || k > E) return fail(BITSMOE_EINVAL, "T=%d k=%d E=%d", T, k, E);
+  if (din <= 0 || din % 8) return fail(BITSMOE_ESHAPE, "din=%d", din);
+  *bytes = z_bytes(T, r);
+  return BITSMOE_OK;
+}
+
+int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* packed_up,
+                       size_t up_bytes, const void* phi_t_gateup_f16, const void* x_f16,
+                       const int32_t* ids, int T, int k, int E, int din, int dout, int r,
+                       float* h, void* ws, size_t ws_bytes, bitsmoe_stream_t stream) {
+  int st = check_layer_dims(E, dout, r);
+  if (st) return st;
+  if ((st = check_blob_arg(packed_gate, gate_bytes, E, "packed_gate"))) return st;
+  if ((st = check_blob_arg(packed_up, up_bytes, E, "packed_up"))) return st;
+  if (!ids || !h || !ws) return fail(BITSMOE_EINVAL, "null pointer argument");
+  if (!aligned16(h) || !aligned16(ws) || ((uintptr_t)ids & 3u))
+    return fail(BITSMOE_EINVAL, "misaligned h, ws or ids");
+  if (k < 1 || k > E) return fail(BITSMOE_EINVAL, "k=%d E=%d", k, E);
+  if ((st = proj_args(phi_t_gateup_f16, x_f16, (const float*)ws, T, din, 2 * r))) return st;
+  if ((long long)T * k > (1LL << 24))
+    return fail(BITSMOE_ESHAPE, "T*k=%lld too large", (long long)T * k);
+  size_t need = 0;
+  bitsmoe_moe_gateup_workspace_size(T, k, E, din, dout, r, &need);
+  if (ws_bytes < need) return fail(BITSMOE_ENOSPC, "ws_bytes=%zu < %zu", ws_bytes, need);
+  float* z = (float*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = launch_proj(phi_t_gateup_f16, x_f16, z, T, din, 2 * r, s))) return st;
+  const int n_slabs = (dout + 63) / 64;
+  hipLaunchKernelGGL(k_expert_slab<true>, dim3(T * k, n_slabs), dim3(128), 0, s,
+                     (const uint8_t*)packed_gate, (uint64_t)gate_bytes,
+                     (const uint8_t*)packed_up, (uint64_t)up_bytes, E, dout, r, z, 2 * r, r, ids,
+                     k, h);
+  return launch_status("gate/up expert launch");
+}
+
+int bitsmoe_workspace_init(void* ws, size_t ws_bytes, bitsmoe_stream_t stream) {
+  if (!ws) return fail(BITSMOE_EINVAL, "ws is null");
+  if (!aligned16(ws)) return fail(BITSMOE_EINVAL, "ws is not 16-byte aligned");
+  const size_t n16 = ws_bytes / 16;
+  const int ntail = (int)(ws_bytes % 16);
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (uint4*)ws, n16, (uint8_t*)ws + n16 * 16, ntail);
+  return launch_status("workspace fill launch");
+}
+
+int bitsmoe_dump_codes(const void* packed, size_t packed_bytes, int E, int dout, int r, int e,
+                       uint16_t* codes, bitsmoe_stream_t stream) {
+  int st = check_layer_dims(E, dout, r);
+  if (st) return st;
+  if ((st = check_blob_arg(packed, packed_bytes, E, "packed"))) return st;
+  if (!codes) return fail(BITSMOE_EINVAL, "codes is null");
+  if (!aligned16(codes)) return fail(BITSMOE_EINVAL, "codes is not 16-byte aligned");
+  if (e < 0 || e >= E) return fail(BITSMOE_EINVAL, "e=%d outside [0,%d)", e, E);
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = bitsmoe_workspace_init(codes, (size_t)r * dout * 2, stream))) return st;
+  hipLaunchKernelGGL(k_dump_codes, dim3((dout + 63) / 64), dim3(64), 0, s,
+                     (const uint8_t*)packed, (uint64_t)packed_bytes, E, dout, r, e, codes);
+  return launch_status("code dump launch");
+}
+
+}  // extern "C"

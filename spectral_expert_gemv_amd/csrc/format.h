@@ -1,0 +1,44 @@
+// Packed blob format v1: constants and the directory record shared by the
+// host packer, the host checker and the device kernels.  The layout is
+// documented in include/bitsmoe.h.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__) || defined(__HIP__)
+#define BM_HD __host__ __device__
+#else
+#define BM_HD
+#endif
+
+namespace bitsmoe {
+
+constexpr uint32_t kMagic = 0x454F4D42u;  // bytes 'B','M','O','E'
+constexpr uint32_t kVersion = 1;
+constexpr uint32_t kHeaderBytes = 128;
+constexpr uint32_t kDirRecBytes = 64;
+constexpr int kNumGroups = 7;                       // widths 1,2,3,4,6,8,16
+constexpr int kNumQGroups = 6;                      // widths 1..8
+constexpr int kGroupWidth[kNumGroups] = {1, 2, 3, 4, 6, 8, 16};
+
+struct Header {
+  uint32_t magic, version, E, dout, r, dout_pad, n_slabs, header_bytes;
+  uint64_t total_bytes, dir_offset;
+  uint32_t crc32, reserved0;
+  uint32_t pad[18];
+};
+static_assert(sizeof(Header) == 128, "header is 128 bytes");
+
+struct DirRec {
+  uint64_t block_offset;
+  uint32_t n_nz, n_q, n_16, masks_per_slab;
+  uint32_t a_off, s_off, m_off, planes_off, f16_off, block_bytes;
+  uint16_t count[kNumGroups];
+  uint16_t reserved;
+};
+static_assert(sizeof(DirRec) == 64, "directory record is 64 bytes");
+
+BM_HD constexpr inline uint64_t align_up(uint64_t x, uint64_t a) {
+  return (x + a - 1) / a * a;
+}
+
+}  // namespace bitsmoe

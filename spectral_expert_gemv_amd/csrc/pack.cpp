@@ -1,0 +1,328 @@
+// Host packer and blob checker (format v1, documented in include/bitsmoe.h).
+//
+// Quantizes each unit direction p_{e,k} at its own width and stores the
+// columns grouped by width, each 1..8-bit group as bit planes ("second
+// split", "Usage" and "execution" of the BitsMoE blog note's Methodology).
+// The quantizer runs in IEEE float32 with no contraction so that its codes
+// are reproducible bit for bit.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <thread>
+#include <vector>
+
+#include "bitsmoe.h"
+#include "common.h"
+#include "format.h"
+
+#pragma clang fp contract(off)
+
+namespace bitsmoe {
+namespace {
+
+// float32 -> binary16, round to nearest, ties to even (IEEE 754 conversion).
+uint16_t f32_to_f16(float f) {
+  uint32_t x;
+  memcpy(&x, &f, 4);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax >= 0x7F800000u) return sign | 0x7C00u | (ax > 0x7F800000u ? 0x200u : 0u);
+  if (ax >= 0x477FF000u) return sign | 0x7C00u;          // >= 65520 rounds to inf
+  if (ax < 0x38800000u) {                                 // below 2^-14: subnormal
+    if (ax < 0x33000000u) return sign;                    // below 2^-25: zero
+    const uint32_t e = ax >> 23;
+    const uint32_t mant = (ax & 0x7FFFFFu) | 0x800000u;
+    const uint32_t shift = 126u - e;                      // 14..24
+    uint32_t h = mant >> shift;
+    const uint32_t rem = mant & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1u);
+    if (rem > half || (rem == half && (h & 1u))) ++h;
+    return sign | h;
+  }
+  uint32_t h = (ax >> 13) - 0x1C000u;                     // rebias exponent 127 -> 15
+  const uint32_t rem = ax & 0x1FFFu;
+  if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) ++h;
+  return sign | h;
+}
+
+float f16_to_f32(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  const uint32_t e = (h >> 10) & 0x1Fu;
+  const uint32_t m = h & 0x3FFu;
+  uint32_t x;
+  if (e == 0) {
+    if (m == 0) {
+      x = sign;
+    } else {  // subnormal: m * 2^-24, exact in float32
+      float v = (float)m * 5.9604644775390625e-8f;
+      memcpy(&x, &v, 4);
+      x |= sign;
+    }
+  } else if (e == 31) {
+    x = sign | 0x7F800000u | (m << 13);
+  } else {
+    x = sign | ((e + 112u) << 23) | (m << 13);
+  }
+  float f;
+  memcpy(&f, &x, 4);
+  return f;
+}
+
+struct CrcTable {
+  uint32_t t[256];
+  CrcTable() {
+    for (uint32_t i = 0; i < 256; ++i) {
+      uint32_t c = i;
+      for (int k = 0; k < 8; ++k) c = (c & 1u) ? 0xEDB88320u ^ (c >> 1) : c >> 1;
+      t[i] = c;
+    }
+  }
+};
+
+// CRC-32 with the reflected IEEE polynomial (the zlib/PNG checksum).
+uint32_t crc32_ieee(const uint8_t* p, size_t n) {
+  static const CrcTable tab;  // thread-safe static initialisation
+  const uint32_t* table = tab.t;
+  uint32_t c = 0xFFFFFFFFu;
+  for (size_t i = 0; i < n; ++i) c = table[(c ^ p[i]) & 0xFFu] ^ (c >> 8);
+  return c ^ 0xFFFFFFFFu;
+}
+
+int width_group(int b) {
+  for (int g = 0; g < kNumGroups; ++g)
+    if (kGroupWidth[g] == b) return g;
+  return -1;
+}
+
+// Canonical block layout of one expert from its per-width column counts.
+DirRec block_layout(const uint16_t count[kNumGroups], uint32_t n_slabs, uint32_t dout_pad) {
+  DirRec d;
+  memset(&d, 0, sizeof(d));
+  uint32_t n_nz = 0, mps = 0;
+  for (int g = 0; g < kNumGroups; ++g) {
+    d.count[g] = count[g];
+    n_nz += count[g];
+    if (g < kNumQGroups) mps += (uint32_t)count[g] * kGroupWidth[g];
+  }
+  d.n_nz = n_nz;
+  d.n_16 = count[kNumGroups - 1];
+  d.n_q = n_nz - d.n_16;
+  d.masks_per_slab = mps;
+  d.a_off = (uint32_t)align_up(2ull * n_nz, 16);
+  d.s_off = (uint32_t)align_up(d.a_off + 4ull * n_nz, 16);
+  d.m_off = (uint32_t)align_up(d.s_off + 2ull * d.n_q, 16);
+  d.planes_off = (uint32_t)align_up(d.m_off + 2ull * d.n_q, 256);
+  d.f16_off = (uint32_t)align_up(d.planes_off + 8ull * n_slabs * mps, 256);
+  d.block_bytes = (uint32_t)align_up(d.f16_off + 2ull * d.n_16 * dout_pad, 256);
+  return d;
+}
+
+int check_dims(int E, int dout, int r) {
+  if (E <= 0 || dout <= 0 || r <= 0)
+    return fail(BITSMOE_ESHAPE, "E=%d dout=%d r=%d must be positive", E, dout, r);
+  if (r > 65535) return fail(BITSMOE_ESHAPE, "r=%d exceeds 65535", r);
+  if (dout > (1 << 24)) return fail(BITSMOE_ESHAPE, "dout=%d too large", dout);
+  return BITSMOE_OK;
+}
+
+// Per-expert directory records and the total size; validates widths.
+int plan(int E, int dout, int r, const uint8_t* bits, std::vector<DirRec>& dirs,
+         uint64_t& total) {
+  int st = check_dims(E, dout, r);
+  if (st) return st;
+  if (!bits) return fail(BITSMOE_EINVAL, "bits is null");
+  const uint32_t dout_pad = (uint32_t)align_up(dout, 64);
+  const uint32_t n_slabs = dout_pad / 64;
+  dirs.resize(E);
+  uint64_t pos = align_up(kHeaderBytes + (uint64_t)kDirRecBytes * E, 256);
+  for (int e = 0; e < E; ++e) {
+    uint16_t count[kNumGroups] = {0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < r; ++k) {
+      const int b = bits[(size_t)e * r + k];
+      if (b == 0) continue;
+      const int g = width_group(b);
+      if (g < 0) return fail(BITSMOE_EBITS, "bits[%d,%d]=%d not in {0,1,2,3,4,6,8,16}", e, k, b);
+      ++count[g];
+    }
+    dirs[e] = block_layout(count, n_slabs, dout_pad);
+    if ((uint64_t)dirs[e].f16_off + 2ull * dirs[e].n_16 * dout_pad > 0xFFFFFFFFull)
+      return fail(BITSMOE_ESHAPE, "expert %d block exceeds 4 GiB", e);
+    dirs[e].block_offset = pos;
+    pos += dirs[e].block_bytes;
+  }
+  total = pos;
+  return BITSMOE_OK;
+}
+
+void quantize_col(const float* p, int dout, int b, uint8_t* q, uint16_t* s_bits,
+                  uint16_t* m_bits) {
+  float lo = p[0], hi = p[0];
+  for (int i = 1; i < dout; ++i) {
+    lo = std::min(lo, p[i]);
+    hi = std::max(hi, p[i]);
+  }
+  const float L = (float)((1 << b) - 1);
+  const float s32 = (hi - lo) / L;
+  uint16_t sb = f32_to_f16(s32);
+  if ((sb & 0x7FFFu) == 0) sb = 0x3C00u;  // scale rounded to zero: use 1
+  const uint16_t mb = f32_to_f16(lo);
+  const float s = f16_to_f32(sb), m = f16_to_f32(mb);
+  for (int i = 0; i < dout; ++i) {
+    float v = nearbyintf((p[i] - m) / s);
+    v = v < 0.0f ? 0.0f : (v > L ? L : v);
+    q[i] = (uint8_t)v;
+  }
+  *s_bits = sb;
+  *m_bits = mb;
+}
+
+void fill_block(const DirRec& d, int e, int dout, int r, uint32_t n_slabs, uint32_t dout_pad,
+                const float* p, const float* a, const uint8_t* bits, uint8_t* blk) {
+  uint16_t* kidx = (uint16_t*)blk;
+  float* A = (float*)(blk + d.a_off);
+  uint16_t* S = (uint16_t*)(blk + d.s_off);
+  uint16_t* M = (uint16_t*)(blk + d.m_off);
+  uint64_t* P = (uint64_t*)(blk + d.planes_off);
+  uint16_t* F = (uint16_t*)(blk + d.f16_off);
+  std::vector<uint8_t> q(dout_pad, 0);
+  uint32_t col = 0, mask_base = 0;
+  for (int g = 0; g < kNumGroups; ++g) {
+    const int b = kGroupWidth[g];
+    for (int k = 0; k < r; ++k) {
+      if (bits[(size_t)e * r + k] != b) continue;
+      const float* pc = p + ((size_t)e * r + k) * dout;
+      kidx[col] = (uint16_t)k;
+      A[col] = a[(size_t)e * r + k];
+      if (b == 16) {
+        uint16_t* f = F + (size_t)(col - d.n_q) * dout_pad;
+        for (int i = 0; i < dout; ++i) f[i] = f32_to_f16(pc[i]);
+      } else {
+        quantize_col(pc, dout, b, q.data(), &S[col], &M[col]);
+        for (uint32_t sl = 0; sl < n_slabs; ++sl) {
+          for (int j = 0; j < b; ++j) {
+            uint64_t w = 0;
+            for (int t = 0; t < 64; ++t) {
+              const int row = (int)sl * 64 + t;
+              if (row < dout) w |= (uint64_t)((q[row] >> j) & 1u) << t;
+            }
+            P[(size_t)sl * d.masks_per_slab + mask_base + j] = w;
+          }
+        }
+        mask_base += b;
+      }
+      ++col;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace bitsmoe
+
+using namespace bitsmoe;
+
+extern "C" {
+
+int bitsmoe_pack_size(int E, int dout, int r, const uint8_t* bits, size_t* out_bytes) {
+  if (!out_bytes) return fail(BITSMOE_EINVAL, "out_bytes is null");
+  std::vector<DirRec> dirs;
+  uint64_t total = 0;
+  const int st = plan(E, dout, r, bits, dirs, total);
+  if (st) return st;
+  *out_bytes = (size_t)total;
+  return BITSMOE_OK;
+}
+
+int bitsmoe_pack(int E, int dout, int r, const float* p, const float* a,
+                 const uint8_t* bits, void* out, size_t out_bytes) {
+  if (!p || !a || !out) return fail(BITSMOE_EINVAL, "null pointer argument");
+  std::vector<DirRec> dirs;
+  uint64_t total = 0;
+  int st = plan(E, dout, r, bits, dirs, total);
+  if (st) return st;
+  if (out_bytes < total)
+    return fail(BITSMOE_ENOSPC, "out_bytes=%zu < %llu", out_bytes, (unsigned long long)total);
+  const size_t n = (size_t)E * r;
+  for (size_t i = 0; i < n; ++i) {
+    if (!isfinite(a[i])) return fail(BITSMOE_EBITS, "a[%zu] is not finite", i);
+    if (bits[i] == 0) continue;
+    const float* pc = p + i * dout;
+    for (int j = 0; j < dout; ++j)
+      if (!isfinite(pc[j]) || fabsf(pc[j]) > 60000.0f)
+        return fail(BITSMOE_EBITS, "p[%zu,%d] is not finite or |p| > 60000", i, j);
+  }
+  uint8_t* blob = (uint8_t*)out;
+  memset(blob, 0, total);
+  const uint32_t dout_pad = (uint32_t)align_up(dout, 64);
+  const uint32_t n_slabs = dout_pad / 64;
+  unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  nt = std::min<unsigned>(nt, (unsigned)E);
+  std::vector<std::thread> pool;
+  for (unsigned w = 0; w < nt; ++w) {
+    pool.emplace_back([&, w]() {
+      for (int e = (int)w; e < E; e += (int)nt)
+        fill_block(dirs[e], e, dout, r, n_slabs, dout_pad, p, a, bits,
+                   blob + dirs[e].block_offset);
+    });
+  }
+  for (auto& t : pool) t.join();
+  memcpy(blob + kHeaderBytes, dirs.data(), sizeof(DirRec) * dirs.size());
+  Header h;
+  memset(&h, 0, sizeof(h));
+  h.magic = kMagic;
+  h.version = kVersion;
+  h.E = (uint32_t)E;
+  h.dout = (uint32_t)dout;
+  h.r = (uint32_t)r;
+  h.dout_pad = dout_pad;
+  h.n_slabs = n_slabs;
+  h.header_bytes = kHeaderBytes;
+  h.total_bytes = total;
+  h.dir_offset = kHeaderBytes;
+  h.crc32 = crc32_ieee(blob + kHeaderBytes, total - kHeaderBytes);
+  memcpy(blob, &h, sizeof(h));
+  return BITSMOE_OK;
+}
+
+int bitsmoe_blob_check(const void* blob_v, size_t bytes, int* E_out, int* dout_out,
+                       int* r_out) {
+  if (!blob_v) return fail(BITSMOE_EINVAL, "blob is null");
+  if (bytes < kHeaderBytes) return fail(BITSMOE_EFORMAT, "blob shorter than its header");
+  const uint8_t* blob = (const uint8_t*)blob_v;
+  Header h;
+  memcpy(&h, blob, sizeof(h));
+  if (h.magic != kMagic) return fail(BITSMOE_EFORMAT, "bad magic");
+  if (h.version != kVersion) return fail(BITSMOE_EFORMAT, "unsupported version %u", h.version);
+  if (h.header_bytes != kHeaderBytes || h.dir_offset != kHeaderBytes)
+    return fail(BITSMOE_EFORMAT, "bad header size or directory offset");
+  if (check_dims((int)h.E, (int)h.dout, (int)h.r) || h.E > (1u << 20))
+    return fail(BITSMOE_EFORMAT, "bad dimensions in header");
+  if (h.dout_pad != align_up(h.dout, 64) || h.n_slabs != h.dout_pad / 64)
+    return fail(BITSMOE_EFORMAT, "bad dout_pad / n_slabs");
+  if (h.total_bytes > bytes || h.total_bytes < kHeaderBytes + (uint64_t)kDirRecBytes * h.E)
+    return fail(BITSMOE_EFORMAT, "total_bytes %llu inconsistent with buffer %zu",
+                (unsigned long long)h.total_bytes, bytes);
+  if (crc32_ieee(blob + kHeaderBytes, h.total_bytes - kHeaderBytes) != h.crc32)
+    return fail(BITSMOE_EFORMAT, "CRC mismatch");
+  uint64_t pos = align_up(kHeaderBytes + (uint64_t)kDirRecBytes * h.E, 256);
+  for (uint32_t e = 0; e < h.E; ++e) {
+    DirRec d;
+    memcpy(&d, blob + kHeaderBytes + (size_t)kDirRecBytes * e, sizeof(d));
+    DirRec c = block_layout(d.count, h.n_slabs, h.dout_pad);
+    c.block_offset = pos;
+    if (memcmp(&c, &d, sizeof(d)) != 0 || c.n_nz > h.r)
+      return fail(BITSMOE_EFORMAT, "directory record %u inconsistent", e);
+    pos += d.block_bytes;
+    if (pos > h.total_bytes) return fail(BITSMOE_EFORMAT, "block %u beyond total_bytes", e);
+    const uint16_t* kidx = (const uint16_t*)(blob + d.block_offset);
+    for (uint32_t c2 = 0; c2 < d.n_nz; ++c2)
+      if (kidx[c2] >= h.r) return fail(BITSMOE_EFORMAT, "expert %u column index out of range", e);
+  }
+  if (pos != h.total_bytes) return fail(BITSMOE_EFORMAT, "total_bytes does not match blocks");
+  if (E_out) *E_out = (int)h.E;
+  if (dout_out) *dout_out = (int)h.dout;
+  if (r_out) *r_out = (int)h.r;
+  return BITSMOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,211 @@
+"""GPU parity of the HIP path against the float64 CPU oracle (through the C ABI).
+
+Tolerances:
+* codes: bit-exact;
+* h = SiLU(y_gate) * y_up: max |dh| <= 2e-3 * max |h_oracle| per (token, slot);
+* z = Phi^T x: max |dz| <= 1e-5 * max |z_oracle| per token (fp16 products are
+  exact in float32; only the float32 sum over din rounds);
+* y (expert apply alone): max |dy| <= 5e-4 * max |y_oracle| per pair (float32
+  accumulation over up to r terms of both signs).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import fmt
+from tests.oracle_ref import max_rel_err, pairs_ref, z_ref
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+H_TOL = 2e-3
+Z_TOL = 1e-5
+Y_TOL = 5e-4
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="session")
+def bm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from spectral_expert_gemv_amd import bitsmoe
+    return bitsmoe
+
+
+_DEV = {}
+
+
+def device_layer(name):
+    from spectral_expert_gemv_amd import DeviceLayer
+    if name not in _DEV:
+        _say("building layer %s" % name)
+        L = synth.make_layer(synth.LAYERS[name])
+        _DEV[name] = (L, DeviceLayer.from_synth(L))
+    return _DEV[name]
+
+
+def _cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _run_gateup(dev, x, ids):
+    h = dev.gateup(_cuda(x), _cuda(ids))
+    torch.cuda.synchronize()
+    return h.cpu().numpy()
+
+
+# ------------------------------------------------------------------ codes
+
+@pytest.mark.parametrize("name,experts", [("tiny", None), ("qwen3_30b_a3b", [0, 17, 127])])
+def test_codes_bit_exact(bm, name, experts):
+    L, dev = device_layer(name)
+    spec = L.spec
+    for proj, blob in (("gate", dev.blob_gate), ("up", dev.blob_up)):
+        ref = fmt.unpack(dev.host_blobs[0 if proj == "gate" else 1].tobytes())["q"]
+        codes = torch.empty((spec.r, spec.dout), dtype=torch.int16, device="cuda")
+        for e in (range(spec.E) if experts is None else experts):
+            _say("codes %s %s e=%d" % (name, proj, e))
+            bm.dump_codes(blob, spec.E, spec.dout, spec.r, e, codes)
+            torch.cuda.synchronize()
+            got = codes.cpu().numpy().view(np.uint16)
+            assert np.array_equal(got, ref[e]), (proj, e)
+
+
+def test_codes_match_oracle_quantizer(bm):
+    """The device-decoded codes equal the oracle quantizer's codes."""
+    from oracle.quantize import quantize_expert
+    L, dev = device_layer("tiny")
+    spec = L.spec
+    codes = torch.empty((spec.r, spec.dout), dtype=torch.int16, device="cuda")
+    for e in range(spec.E):
+        bm.dump_codes(dev.blob_up, spec.E, spec.dout, spec.r, e, codes)
+        torch.cuda.synchronize()
+        q = quantize_expert(L.p["up"][e], L.bits["up"][e])["q"]
+        q[L.bits["up"][e] == 0] = 0
+        assert np.array_equal(codes.cpu().numpy().view(np.uint16), q)
+
+
+# ------------------------------------------------------------- projection
+
+@pytest.mark.parametrize("wl_name", ["tiny_t8", "qwen3_30b_a3b_t1", "qwen3_30b_a3b_t32"])
+def test_spectral_proj(bm, wl_name):
+    wl = synth.workload(wl_name)
+    L, dev = device_layer(wl.layer.name)
+    x, _ = synth.make_batch(wl, L)
+    T = x.shape[0]
+    z = torch.empty((T, 2 * L.spec.r), dtype=torch.float32, device="cuda")
+    bm.spectral_proj(dev.phi_t, _cuda(x), z)
+    torch.cuda.synchronize()
+    got = z.cpu().numpy()
+    ref = z_ref(L, x)
+    for t in range(T):
+        zr = np.concatenate([ref["gate"][t], ref["up"][t]])
+        assert max_rel_err(got[t], zr) <= Z_TOL, t
+
+
+# ----------------------------------------------------------- expert apply
+
+def test_expert_apply_tiny(bm):
+    wl = synth.workload("tiny_t8")
+    L, dev = device_layer("tiny")
+    x, ids = synth.make_batch(wl, L)
+    _, yg, yu = pairs_ref(L, x, ids, want_y=True)
+    zr = z_ref(L, x)
+    spec = L.spec
+    for proj, blob, yref in (("gate", dev.blob_gate, yg), ("up", dev.blob_up, yu)):
+        z = _cuda(zr[proj].astype(np.float32))
+        y = torch.empty((x.shape[0], spec.k, spec.dout), dtype=torch.float32, device="cuda")
+        bm.expert_apply(blob, spec.E, spec.dout, spec.r, z, _cuda(ids), y)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        for (t, s), ref in yref.items():
+            assert max_rel_err(got[t, s], ref) <= Y_TOL, (proj, t, s)
+
+
+# ------------------------------------------------------------------ gate/up
+
+def _check_h(got, href):
+    worst = 0.0
+    for (t, s), ref in href.items():
+        err = max_rel_err(got[t, s], ref)
+        worst = max(worst, err)
+        assert err <= H_TOL, (t, s, err)
+        assert np.all(np.isfinite(got[t, s]))
+    return worst
+
+
+@pytest.mark.parametrize("wl_name,steps", [("tiny_t8", 3), ("qwen3_30b_a3b_t1", 3),
+                                           ("qwen3_30b_a3b_t32", 1)])
+def test_gateup_full(bm, wl_name, steps):
+    wl = synth.workload(wl_name)
+    L, dev = device_layer(wl.layer.name)
+    for step in range(steps):
+        x, ids = synth.make_batch(wl, L, step=step)
+        _say("gateup %s step %d T=%d" % (wl_name, step, x.shape[0]))
+        got = _run_gateup(dev, x, ids)
+        worst = _check_h(got, pairs_ref(L, x, ids))
+        _say("  worst %.3g" % worst)
+
+
+def test_repeat_runs_bit_identical(bm):
+    wl = synth.workload("qwen3_30b_a3b_t32")
+    L, dev = device_layer(wl.layer.name)
+    x, ids = synth.make_batch(wl, L)
+    a = _run_gateup(dev, x, ids)
+    b = _run_gateup(dev, x, ids)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------------------ edge cases
+
+def test_edges_zero_expert_k1_duplicates(bm):
+    """All-0-bit expert gives h = 0; k = 1; the same expert on every token."""
+    from spectral_expert_gemv_amd import DeviceLayer
+    L = synth.make_layer(synth.LAYERS["tiny"])
+    bits_g = L.bits["gate"].copy()
+    bits_u = L.bits["up"].copy()
+    bits_g[2] = 0
+    bits_u[2] = 0
+    dev = DeviceLayer(L.phi["gate"], L.phi["up"], L.a["gate"], L.a["up"], L.p["gate"],
+                      L.p["up"], bits_g, bits_u)
+    x, _ = synth.make_batch(synth.workload("tiny_t8"), L)
+    ids = np.full((8, 1), 2, np.int32)
+    got = _run_gateup(dev, x, ids)
+    assert np.all(got == 0)
+    ids = np.array([[1], [1], [3], [1], [0], [3], [1], [1]], np.int32)
+    got = _run_gateup(dev, x, ids)
+    Lz = synth.generate.Layer(L.spec, L.phi, L.a, L.p, {"gate": bits_g, "up": bits_u},
+                              L.outlier_channels)
+    _check_h(got, pairs_ref(Lz, x, ids))
+
+
+def test_bad_expert_id_and_blob_mismatch_give_nan(bm):
+    L, dev = device_layer("tiny")
+    spec = L.spec
+    x, ids = synth.make_batch(synth.workload("tiny_t8"), L)
+    ids = ids.copy()
+    ids[3, 1] = spec.E          # out of range
+    ids[5, 0] = -1
+    got = _run_gateup(dev, x, ids)
+    assert np.all(np.isnan(got[3, 1])) and np.all(np.isnan(got[5, 0]))
+    ok = [(t, s) for t in range(8) for s in range(2) if (t, s) not in ((3, 1), (5, 0))]
+    _check_h(got, pairs_ref(L, x, ids, pairs=ok))
+    # blobs whose header says a different dout than the call: every row NaN
+    T, k = 8, 2
+    dout_call = spec.dout - 1
+    h = torch.zeros((T, k, dout_call), dtype=torch.float32, device="cuda")
+    ws = dev.workspace(T, k)
+    good_ids = _cuda(synth.make_batch(synth.workload("tiny_t8"), L)[1])
+    bm._check(bm._lib.bitsmoe_moe_gateup(
+        dev.blob_gate.data_ptr(), dev.blob_gate.numel(), dev.blob_up.data_ptr(),
+        dev.blob_up.numel(), dev.phi_t.data_ptr(), _cuda(x).data_ptr(),
+        good_ids.data_ptr(), T, k, spec.E, spec.din, dout_call, spec.r, h.data_ptr(),
+        ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert torch.isnan(h).all()
