@@ -1,0 +1,230 @@
+"""Benchmark of the spectral MoE gate/up decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one bitsmoe_moe_gateup call: z = Phi^T x for the batch, then every
+routed expert's bit-plane apply and the SiLU * mul epilogue.  Inputs are
+seeded synthetic layers (see synth/) resident in HBM before timing starts.
+To keep the 256 MB Infinity Cache from serving the data, the step rotates
+over C device copies of the layer (C * layer bytes >= 1 GiB) and over NB
+pre-generated batches.  Steps are replayed from HIP graphs (captured through
+torch) and timed with HIP events on the launch stream.
+
+Prints one JSON line (rank 0, N = 1).  The CPU baseline is the float64
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/token + % HBM roofline, spectral MoE gate/up layer, Qwen3-30B-A3B shape, batch 1"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="qwen3_30b_a3b_t1")
+    ap.add_argument("--copies", type=int, default=0, help="layer copies rotated (0: auto)")
+    ap.add_argument("--batches", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    return ap.parse_args()
+
+
+def layer_bytes_per_expert(bits, dout):
+    """Algorithmic bytes of one expert of one linear type (E vector).
+
+    bit planes (dout_pad * sum b / 8) + fp16 values of 16-bit columns +
+    10 bytes of metadata per stored column (u16 k, fp16 s, fp16 m, fp32 a).
+    """
+    dout_pad = (dout + 63) // 64 * 64
+    b = bits.astype(np.int64)
+    q = np.where((b >= 1) & (b <= 8), b, 0).sum(axis=1)
+    n16 = (b == 16).sum(axis=1)
+    nnz = (b > 0).sum(axis=1)
+    return dout_pad * q // 8 + 2 * dout_pad * n16 + 10 * nnz
+
+
+def step_bytes(spec, per_e_g, per_e_u, ids):
+    distinct = np.unique(ids)
+    T, k = ids.shape
+    phi = 2 * spec.r * spec.din * 2
+    experts = int(per_e_g[distinct].sum() + per_e_u[distinct].sum())
+    xh = T * spec.din * 2 + T * k * spec.dout * 4 + T * k * 4
+    return phi + experts + xh, phi, experts
+
+
+def cpu_baseline(layer, batches, seconds):
+    """The oracle on the host cores: tokens processed within ~`seconds`."""
+    from tests.oracle_ref import pairs_ref
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max(blas) if blas else 1
+    except Exception:  # pragma: no cover
+        cores = 1
+    tok = 0
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        x, ids = batches[i % len(batches)]
+        pairs_ref(layer, x, ids)
+        tok += x.shape[0]
+        i += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": el / tok * 1e6, "unit": "µs/token", "cores": int(cores), "kind": "oracle",
+            "tokens_per_s": tok / el,
+            "sample": "%d batch(es), %d token(s) of the same workload through the float64 "
+                      "oracle (dequantize routed experts, z = Phi^T x, ordered k sum, SiLU*mul); "
+                      "numpy, BLAS threads = %d, other work single-threaded; %.1f s"
+                      % (i, tok, cores, el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    from spectral_expert_gemv_amd import bitsmoe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = synth.workload(args.workload)
+    spec = wl.layer
+    L = synth.make_layer(spec)
+    blob_g = bitsmoe.pack(L.p["gate"], L.a["gate"], L.bits["gate"])
+    blob_u = bitsmoe.pack(L.p["up"], L.a["up"], L.bits["up"])
+    phi_t = np.ascontiguousarray(np.concatenate([np.asarray(L.phi["gate"], np.float16).T,
+                                                 np.asarray(L.phi["up"], np.float16).T]))
+    per_g = layer_bytes_per_expert(L.bits["gate"], spec.dout)
+    per_u = layer_bytes_per_expert(L.bits["up"], spec.dout)
+    host_batches = [synth.make_batch(wl, L, step=i) for i in range(args.batches)]
+    sb = [step_bytes(spec, per_g, per_u, ids) for _, ids in host_batches]
+    # enough copies that >= 1 GiB is touched between two uses of one copy
+    C = args.copies or max(2, min(64, math.ceil((1 << 30) / min(s[0] for s in sb))))
+    copies = []
+    for _ in range(C):
+        copies.append((torch.from_numpy(blob_g).to(dev), torch.from_numpy(blob_u).to(dev),
+                       torch.from_numpy(phi_t).to(dev)))
+    batches = [(torch.from_numpy(x).to(dev), torch.from_numpy(ids).to(dev))
+               for x, ids in host_batches]
+    T, k = host_batches[0][1].shape
+    ws_bytes = bitsmoe.moe_gateup_workspace_size(T, k, spec.E, spec.din, spec.dout, spec.r)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    bitsmoe.workspace_init(ws)
+    h = torch.empty((T, k, spec.dout), dtype=torch.float32, device=dev)
+
+    def step(i, stream):
+        bg, bu, ph = copies[i % C]
+        x, ids = batches[i % len(batches)]
+        bitsmoe.moe_gateup(bg, bu, ph, x, ids, spec.E, spec.dout, spec.r, h, ws, stream=stream)
+
+    stream = torch.cuda.Stream(device=dev)
+    S = C * len(batches) // math.gcd(C, len(batches))
+    S = min(S, 256)
+
+    def make_graph(n, start):
+        if n == 0:
+            return None
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for i in range(n):          # eager run once before capture
+                step(start + i, stream)
+        stream.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                step(start + i, stream.cuda_stream)
+        return g
+
+    def run(nsteps, graph_full, graph_rem):
+        if args.no_graph:
+            with torch.cuda.stream(stream):
+                for i in range(nsteps):
+                    step(i, stream)
+            return
+        for _ in range(nsteps // S):
+            graph_full.replay()
+        if nsteps % S:
+            graph_rem.replay()
+
+    K, W = args.steps, args.warmup
+    g_full = None if args.no_graph else make_graph(S, 0)
+    g_rem = None if args.no_graph else make_graph(K % S, 0)
+    g_wrem = None if args.no_graph else make_graph(W % S, 0)
+    with torch.cuda.stream(stream):
+        run(W, g_full, g_wrem)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        run(K, g_full, g_rem)
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    ms_per_step = ms / K
+    us_per_token = ms_per_step * 1000.0 / T
+
+    # algorithmic bytes averaged over the steps timed (step i uses batch i % NB)
+    avg_bytes = sum(sb[i % len(sb)][0] for i in range(K)) / K
+    achieved = avg_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # warm (single copy, MALL-resident) reference number, labelled as such
+    g_warm = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        step(0, stream)
+    stream.synchronize()
+    with torch.cuda.graph(g_warm, stream=stream):
+        for _ in range(64):
+            step(0, stream.cuda_stream)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(5):
+        g_warm.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    warm_us = ev0.elapsed_time(ev1) * 1000.0 / (5 * 64) / T
+
+    out = {
+        "metric": METRIC, "value": round(us_per_token, 4), "unit": "µs/token",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "E": spec.E, "din": spec.din, "dout": spec.dout,
+                   "r": spec.r, "top_k": spec.k, "tokens": T, "layer_copies": C,
+                   "batches": len(batches), "graph_steps": S,
+                   "inputs": "fp16 Phi and x, packed 0..16-bit directions, fp32 h"},
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "warm_mall_us_per_token": round(warm_us, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_step": round(avg_bytes),
+                     "phi_bytes": sb[0][1],
+                     "expert_bytes_avg": round(sum(s[2] for s in sb) / len(sb)),
+                     "kernel": "whole step (all launches of bitsmoe_moe_gateup)"},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(L, host_batches[:4], args.cpu_seconds)
+    print(json.dumps(out, ensure_ascii=False), flush=True)
+
+
+if __name__ == "__main__":
+    main()

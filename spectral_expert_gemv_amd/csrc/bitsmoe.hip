@@ -13,6 +13,7 @@
 #include "common.h"
 #include "device_common.h"
 #include "format.h"
+#include "kernels.h"
 
 namespace bitsmoe {
 namespace {
@@ -39,17 +40,26 @@ __device__ inline float dot8(uint4 a, uint4 b, float acc) {
 __global__ __launch_bounds__(kProjWaves * kWave) void k_proj_gemv(
     const uint4* __restrict__ phi_t, const uint4* __restrict__ x, float* __restrict__ z,
     int T, int din8, int R) {
+  constexpr int U = 4;  // 16-byte loads in flight per lane
   const int lane = threadIdx.x & (kWave - 1);
   const int n = blockIdx.x * kProjWaves + (threadIdx.x >> 6);
   if (n >= R) return;
   const uint4* prow = phi_t + (size_t)n * din8;
   for (int t0 = 0; t0 < T; t0 += kTokChunk) {
     float acc[kTokChunk] = {0.f, 0.f, 0.f, 0.f};
-    for (int i = lane; i < din8; i += kWave) {
-      const uint4 pv = prow[i];
+    for (int i0 = lane; i0 < din8; i0 += kWave * U) {
+      uint4 pv[U];
 #pragma unroll
-      for (int tt = 0; tt < kTokChunk; ++tt)
-        if (t0 + tt < T) acc[tt] = dot8(pv, x[(size_t)(t0 + tt) * din8 + i], acc[tt]);
+      for (int u = 0; u < U; ++u)
+        if (i0 + u * kWave < din8) pv[u] = prow[i0 + u * kWave];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (i0 + u * kWave >= din8) break;
+#pragma unroll
+        for (int tt = 0; tt < kTokChunk; ++tt)
+          if (t0 + tt < T)
+            acc[tt] = dot8(pv[u], x[(size_t)(t0 + tt) * din8 + i0 + u * kWave], acc[tt]);
+      }
     }
 #pragma unroll
     for (int tt = 0; tt < kTokChunk; ++tt) {
@@ -229,7 +239,6 @@ int launch_proj(const void* phi, const void* x, float* z, int T, int din, int R,
   return launch_status("spectral projection launch");
 }
 
-size_t z_bytes(int T, int r) { return align_up((size_t)T * 2 * r * sizeof(float), 256); }
 
 }  // namespace
 }  // namespace bitsmoe
@@ -275,7 +284,7 @@ int bitsmoe_moe_gateup_workspace_size(int T, int k, int E, int din, int dout, in
   if (st) return st;
   if (T < 1 || k < 1 || k > E) return fail(BITSMOE_EINVAL, "T=%d k=%d E=%d", T, k, E);
   if (din <= 0 || din % 8) return fail(BITSMOE_ESHAPE, "din=%d", din);
-  *bytes = z_bytes(T, r);
+  *bytes = gateup_plan(T, k, dout, r).total;
   return BITSMOE_OK;
 }
 
@@ -297,14 +306,28 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   size_t need = 0;
   bitsmoe_moe_gateup_workspace_size(T, k, E, din, dout, r, &need);
   if (ws_bytes < need) return fail(BITSMOE_ENOSPC, "ws_bytes=%zu < %zu", ws_bytes, need);
-  float* z = (float*)ws;
+  const GateUpPlan plan = gateup_plan(T, k, dout, r);
+  float* z = (float*)((uint8_t*)ws + plan.z_off);
   hipStream_t s = (hipStream_t)stream;
   if ((st = launch_proj(phi_t_gateup_f16, x_f16, z, T, din, 2 * r, s))) return st;
-  const int n_slabs = (dout + 63) / 64;
-  hipLaunchKernelGGL(k_expert_slab<true>, dim3(T * k, n_slabs), dim3(128), 0, s,
-                     (const uint8_t*)packed_gate, (uint64_t)gate_bytes,
-                     (const uint8_t*)packed_up, (uint64_t)up_bytes, E, dout, r, z, 2 * r, r, ids,
-                     k, h);
+  GateUpArgs a;
+  a.blob_g = (const uint8_t*)packed_gate;
+  a.blob_u = (const uint8_t*)packed_up;
+  a.bytes_g = gate_bytes;
+  a.bytes_u = up_bytes;
+  a.E = E;
+  a.dout = dout;
+  a.r = r;
+  a.z = z;
+  a.ids = ids;
+  a.ktop = k;
+  a.npairs = T * k;
+  a.h = h;
+  a.part = (float*)((uint8_t*)ws + plan.part_off);
+  a.cnt = (uint32_t*)((uint8_t*)ws + plan.cnt_off);
+  a.parts = plan.parts;
+  a.n_slabs = plan.n_slabs;
+  launch_gateup_exec(a, s);
   return launch_status("gate/up expert launch");
 }
 
