@@ -194,12 +194,13 @@ def main():
     with torch.cuda.graph(g_warm, stream=stream):
         for _ in range(64):
             step(0, stream.cuda_stream)
-    g_warm.replay()
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(5):
+    with torch.cuda.stream(stream):
         g_warm.replay()
-    ev1.record(stream)
+        stream.synchronize()
+        ev0.record(stream)
+        for _ in range(5):
+            g_warm.replay()
+        ev1.record(stream)
     torch.cuda.synchronize()
     warm_us = ev0.elapsed_time(ev1) * 1000.0 / (5 * 64) / T
 

@@ -26,6 +26,7 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kProjWaves = 4;
 constexpr int kTokChunk = 4;
+constexpr int kFusedMaxTokens = 4;  // one-launch path up to this many tokens
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -307,9 +308,7 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   bitsmoe_moe_gateup_workspace_size(T, k, E, din, dout, r, &need);
   if (ws_bytes < need) return fail(BITSMOE_ENOSPC, "ws_bytes=%zu < %zu", ws_bytes, need);
   const GateUpPlan plan = gateup_plan(T, k, dout, r);
-  float* z = (float*)((uint8_t*)ws + plan.z_off);
   hipStream_t s = (hipStream_t)stream;
-  if ((st = launch_proj(phi_t_gateup_f16, x_f16, z, T, din, 2 * r, s))) return st;
   GateUpArgs a;
   a.blob_g = (const uint8_t*)packed_gate;
   a.blob_u = (const uint8_t*)packed_up;
@@ -318,16 +317,42 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   a.E = E;
   a.dout = dout;
   a.r = r;
-  a.z = z;
   a.ids = ids;
   a.ktop = k;
   a.npairs = T * k;
   a.h = h;
   a.part = (float*)((uint8_t*)ws + plan.part_off);
   a.cnt = (uint32_t*)((uint8_t*)ws + plan.cnt_off);
-  a.parts = plan.parts;
   a.n_slabs = plan.n_slabs;
-  launch_gateup_exec(a, s);
+  // One launch when the whole grid can be resident and produces all of z;
+  // otherwise z first, then the expert kernel.
+  if (T <= kFusedMaxTokens) {
+    const long long units = (long long)T * k * plan.n_slabs * 2;
+    const int cap = fused_capacity();
+    for (int parts = plan.parts; parts >= 1; --parts) {
+      const long long blocks = units * parts;
+      if (blocks <= cap) {
+        a.parts = parts;
+        a.z = nullptr;
+        FusedArgs f;
+        f.g = a;
+        f.phi_t = (const uint4*)phi_t_gateup_f16;
+        f.x = (const uint4*)x_f16;
+        f.din8 = din / 8;
+        f.T = T;
+        f.zt = (uint64_t*)((uint8_t*)ws + plan.zt_off);
+        f.epoch = (uint32_t*)((uint8_t*)ws + plan.sync_off);
+        f.arrive = f.epoch + 1;
+        launch_gateup_fused(f, s);
+        return launch_status("fused gate/up launch");
+      }
+    }
+  }
+  float* z = (float*)((uint8_t*)ws + plan.z_off);
+  if ((st = launch_proj(phi_t_gateup_f16, x_f16, z, T, din, 2 * r, s))) return st;
+  a.z = z;
+  a.parts = plan.parts;
+  launch_gateup_swar(a, s);
   return launch_status("gate/up expert launch");
 }
 
