@@ -255,7 +255,7 @@ GateUpPlan gateup_plan(int T, int k, int dout, int r) {
   p.sync_off = align_up(p.zt_off + (size_t)T * 2 * r * sizeof(uint64_t), 256);
   p.part_off = align_up(p.sync_off + 2 * sizeof(uint32_t), 256);
   p.cnt_off = align_up(p.part_off + (size_t)units * p.parts * 64 * sizeof(float), 256);
-  p.total = align_up(p.cnt_off + (size_t)T * k * p.n_slabs * sizeof(uint32_t), 256);
+  p.total = align_up(p.cnt_off + (size_t)T * k * 2 * p.n_slabs * sizeof(uint32_t), 256);
   return p;
 }
 

@@ -89,7 +89,8 @@ const char* bitsmoe_last_error_detail(void);
  *     f16 m[n_q] @m_off, u64 planes[n_slabs][masks_per_slab] @planes_off
  *     (per 64-row slab, per 1..8-bit column, per plane j from the least
  *     significant: bit t = bit j of q[64*slab + t], 0 for rows >= dout),
- *     f16 values[n_16][dout_pad] @f16_off.  Padding bytes are zero.
+ *     f16 values[n_16][dout_pad] @f16_off = align256(planes end + 16).
+ *     Padding bytes are zero.
  * bitsmoe_pack_size: bytes the blob needs.  bitsmoe_pack: writes it into the
  * host buffer `out` (out_bytes >= that size, else BITSMOE_ENOSPC).
  */

@@ -30,7 +30,7 @@ Expert block (first at align256(128 + 64 E), blocks back to back)
          per 64-row slab, for each 1..8-bit column in order and each plane
          j = 0..b-1 (j = 0 is the least significant code bit): one u64 whose
          bit t is bit j of q[64*slab + t] (0 for rows >= dout)
-  f16    f16[n_16][dout_pad]       at f16_off = align256(planes_off + 8 n_slabs mps)
+  f16    f16[n_16][dout_pad]       at f16_off = align256(planes_off + 8 n_slabs mps + 16)
          fp16 values of the 16-bit columns (rows >= dout are 0)
   block_bytes = align256(f16_off + 2 n_16 dout_pad)
 All padding bytes are zero.
@@ -63,7 +63,7 @@ def _block_layout(bits_e: np.ndarray, n_slabs: int, dout_pad: int):
     s_off = _al(a_off + 4 * n_nz, 16)
     m_off = _al(s_off + 2 * n_q, 16)
     p_off = _al(m_off + 2 * n_q, 256)
-    f_off = _al(p_off + 8 * n_slabs * mps, 256)
+    f_off = _al(p_off + 8 * n_slabs * mps + 16, 256)
     nbytes = _al(f_off + 2 * n_16 * dout_pad, 256)
     return dict(cnt=cnt, n_nz=n_nz, n_q=n_q, n_16=n_16, mps=mps, a_off=a_off,
                 s_off=s_off, m_off=m_off, p_off=p_off, f_off=f_off, nbytes=nbytes)

@@ -285,7 +285,7 @@ int bitsmoe_moe_gateup_workspace_size(int T, int k, int E, int din, int dout, in
   if (st) return st;
   if (T < 1 || k < 1 || k > E) return fail(BITSMOE_EINVAL, "T=%d k=%d E=%d", T, k, E);
   if (din <= 0 || din % 8) return fail(BITSMOE_ESHAPE, "din=%d", din);
-  *bytes = gateup_plan(T, k, dout, r).total;
+  *bytes = gateup_plan(T, r).total;
   return BITSMOE_OK;
 }
 
@@ -307,9 +307,10 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   size_t need = 0;
   bitsmoe_moe_gateup_workspace_size(T, k, E, din, dout, r, &need);
   if (ws_bytes < need) return fail(BITSMOE_ENOSPC, "ws_bytes=%zu < %zu", ws_bytes, need);
-  const GateUpPlan plan = gateup_plan(T, k, dout, r);
+  const GateUpPlan plan = gateup_plan(T, r);
   hipStream_t s = (hipStream_t)stream;
-  GateUpArgs a;
+  StagedArgs sa;
+  GateUpArgs& a = sa.g;
   a.blob_g = (const uint8_t*)packed_gate;
   a.blob_u = (const uint8_t*)packed_up;
   a.bytes_g = gate_bytes;
@@ -321,38 +322,24 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   a.ktop = k;
   a.npairs = T * k;
   a.h = h;
-  a.part = (float*)((uint8_t*)ws + plan.part_off);
-  a.cnt = (uint32_t*)((uint8_t*)ws + plan.cnt_off);
-  a.n_slabs = plan.n_slabs;
-  // One launch when the whole grid can be resident and produces all of z;
-  // otherwise z first, then the expert kernel.
-  if (T <= kFusedMaxTokens) {
-    const long long units = (long long)T * k * plan.n_slabs * 2;
-    const int cap = fused_capacity();
-    for (int parts = plan.parts; parts >= 1; --parts) {
-      const long long blocks = units * parts;
-      if (blocks <= cap) {
-        a.parts = parts;
-        a.z = nullptr;
-        FusedArgs f;
-        f.g = a;
-        f.phi_t = (const uint4*)phi_t_gateup_f16;
-        f.x = (const uint4*)x_f16;
-        f.din8 = din / 8;
-        f.T = T;
-        f.zt = (uint64_t*)((uint8_t*)ws + plan.zt_off);
-        f.epoch = (uint32_t*)((uint8_t*)ws + plan.sync_off);
-        f.arrive = f.epoch + 1;
-        launch_gateup_fused(f, s);
-        return launch_status("fused gate/up launch");
-      }
-    }
+  a.n_slabs = (dout + 63) / 64;
+  sa.phi_t = (const uint4*)phi_t_gateup_f16;
+  sa.x = (const uint4*)x_f16;
+  sa.din8 = din / 8;
+  sa.T = T;
+  sa.zt = (uint64_t*)((uint8_t*)ws + plan.zt_off);
+  sa.z = (const float*)((uint8_t*)ws + plan.z_off);
+  sa.epoch = (uint32_t*)((uint8_t*)ws + plan.sync_off);
+  sa.arrive = sa.epoch + 1;
+  // One launch when every work-group can be resident at once (the groups
+  // wait for each other's z); otherwise z first, then the expert kernel.
+  const long long blocks = staged_blocks(T, k, dout);
+  if (T <= kFusedMaxTokens && blocks <= staged_capacity()) {
+    launch_gateup_staged(sa, true, s);
+    return launch_status("one-launch gate/up");
   }
-  float* z = (float*)((uint8_t*)ws + plan.z_off);
-  if ((st = launch_proj(phi_t_gateup_f16, x_f16, z, T, din, 2 * r, s))) return st;
-  a.z = z;
-  a.parts = plan.parts;
-  launch_gateup_swar(a, s);
+  if ((st = launch_proj(phi_t_gateup_f16, x_f16, (float*)sa.z, T, din, 2 * r, s))) return st;
+  launch_gateup_staged(sa, false, s);
   return launch_status("gate/up expert launch");
 }
 

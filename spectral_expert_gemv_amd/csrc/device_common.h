@@ -12,18 +12,24 @@ namespace bitsmoe {
 constexpr int kWave = 64;
 
 // Directory record of expert e of a device blob, validated against the
-// dimensions the host passed and against the blob size.  Returns false (and
-// leaves `d` unusable) when the blob cannot be read safely.
+// dimensions the host passed and against the blob size.  The header and the
+// record are loaded together (the record address uses e clamped into
+// [0, E), always inside the directory the host size check guarantees), and
+// then validated.  Returns false when the blob cannot be read safely.
 __device__ inline bool load_dir(const uint8_t* __restrict__ blob, uint64_t blob_bytes,
                                 int e, int E, int dout, int r, DirRec& d) {
   const Header* h = reinterpret_cast<const Header*>(blob);
-  if (h->magic != kMagic || h->version != kVersion || h->E != (uint32_t)E ||
-      h->dout != (uint32_t)dout || h->r != (uint32_t)r)
+  const int ec = e < 0 ? 0 : (e >= E ? E - 1 : e);
+  d = reinterpret_cast<const DirRec*>(blob + kHeaderBytes)[ec];
+  const uint32_t magic = h->magic, version = h->version, hE = h->E, hdout = h->dout,
+                 hr = h->r, n_slabs32 = h->n_slabs;
+  if (magic != kMagic || version != kVersion || hE != (uint32_t)E ||
+      hdout != (uint32_t)dout || hr != (uint32_t)r)
     return false;
   if (e < 0 || e >= E) return false;
-  d = reinterpret_cast<const DirRec*>(blob + kHeaderBytes)[e];
-  const uint64_t n_slabs = h->n_slabs;
+  const uint64_t n_slabs = n_slabs32;
   const uint64_t dout_pad = n_slabs * 64;
+  if (n_slabs != (uint64_t)((dout + 63) / 64)) return false;
   if (d.block_offset + d.block_bytes > blob_bytes) return false;
   uint32_t n_nz = 0, mps = 0;
 #pragma unroll
@@ -37,10 +43,10 @@ __device__ inline bool load_dir(const uint8_t* __restrict__ blob, uint64_t blob_
   if ((uint64_t)d.a_off + 4ull * n_nz > d.block_bytes || 2ull * n_nz > d.a_off ||
       (uint64_t)d.s_off + 2ull * d.n_q > d.block_bytes ||
       (uint64_t)d.m_off + 2ull * d.n_q > d.block_bytes ||
-      (uint64_t)d.planes_off + 8ull * n_slabs * mps > d.block_bytes ||
+      (uint64_t)d.planes_off + 8ull * n_slabs * mps + 16 > d.f16_off ||
       (uint64_t)d.f16_off + 2ull * d.n_16 * dout_pad > d.block_bytes ||
       (d.a_off & 3u) || (d.s_off & 1u) || (d.m_off & 1u) || (d.planes_off & 7u) ||
-      (d.f16_off & 1u))
+      (d.f16_off & 15u))
     return false;
   return true;
 }

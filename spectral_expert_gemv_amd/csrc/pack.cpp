@@ -113,7 +113,9 @@ DirRec block_layout(const uint16_t count[kNumGroups], uint32_t n_slabs, uint32_t
   d.s_off = (uint32_t)align_up(d.a_off + 4ull * n_nz, 16);
   d.m_off = (uint32_t)align_up(d.s_off + 2ull * d.n_q, 16);
   d.planes_off = (uint32_t)align_up(d.m_off + 2ull * d.n_q, 256);
-  d.f16_off = (uint32_t)align_up(d.planes_off + 8ull * n_slabs * mps, 256);
+  // at least 16 zero bytes follow the planes, so 16-byte reads of the last
+  // masks stay inside the block
+  d.f16_off = (uint32_t)align_up(d.planes_off + 8ull * n_slabs * mps + 16, 256);
   d.block_bytes = (uint32_t)align_up(d.f16_off + 2ull * d.n_16 * dout_pad, 256);
   return d;
 }
