@@ -27,6 +27,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/token + % HBM roofline, spectral MoE gate/up layer, Qwen3-30B-A3B shape, batch 1"
 HBM_PEAK_GBS = 8000.0
+KERNEL_ONE_LAUNCH = "k_gateup_staged<true> (z, expert apply and SiLU*mul in one launch)"
+KERNEL_TWO_LAUNCHES = "k_proj_gemv + k_gateup_staged<false> (timed together)"
+# HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counter runs, scaled by
+# the same counters on a plain copy of known size; None until measured for
+# the current kernel.
+TRAFFIC = {"qwen3_30b_a3b_t1": 35013405}
 
 
 def parse():
@@ -40,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after the bench, copy a tensor of this many MiB 4 times "
+                         "(reference dispatches for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -186,23 +195,31 @@ def main():
     avg_bytes = sum(sb[i % len(sb)][0] for i in range(K)) / K
     achieved = avg_bytes / (ms_per_step * 1e-3) / 1e9
 
+    # The timed region is back-to-back launches of the step's kernel(s) on
+    # `stream`: its per-launch average is the event time over K steps.
+    kern_us = ms_per_step * 1000.0
+    kern_bytes = avg_bytes
+    kern_gbs = achieved
+
     # warm (single copy, MALL-resident) reference number, labelled as such
-    g_warm = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        step(0, stream)
-    stream.synchronize()
-    with torch.cuda.graph(g_warm, stream=stream):
-        for _ in range(64):
-            step(0, stream.cuda_stream)
-    with torch.cuda.stream(stream):
-        g_warm.replay()
+    warm_us = None
+    if not args.no_graph:
+        g_warm = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            step(0, stream)
         stream.synchronize()
-        ev0.record(stream)
-        for _ in range(5):
+        with torch.cuda.graph(g_warm, stream=stream):
+            for _ in range(64):
+                step(0, stream.cuda_stream)
+        with torch.cuda.stream(stream):
             g_warm.replay()
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    warm_us = ev0.elapsed_time(ev1) * 1000.0 / (5 * 64) / T
+            stream.synchronize()
+            ev0.record(stream)
+            for _ in range(5):
+                g_warm.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        warm_us = ev0.elapsed_time(ev1) * 1000.0 / (5 * 64) / T
 
     out = {
         "metric": METRIC, "value": round(us_per_token, 4), "unit": "µs/token",
@@ -214,17 +231,27 @@ def main():
                    "batches": len(batches), "graph_steps": S,
                    "inputs": "fp16 Phi and x, packed 0..16-bit directions, fp32 h"},
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
-        "warm_mall_us_per_token": round(warm_us, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_step": round(avg_bytes),
+        "warm_mall_us_per_token": None if warm_us is None else round(warm_us, 4),
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": TRAFFIC.get(wl.name), "bytes_per_launch": round(kern_bytes),
                      "phi_bytes": sb[0][1],
                      "expert_bytes_avg": round(sum(s[2] for s in sb) / len(sb)),
-                     "kernel": "whole step (all launches of bitsmoe_moe_gateup)"},
+                     "launch_us_avg": round(kern_us, 3),
+                     "kernel": KERNEL_ONE_LAUNCH if T <= 4 else KERNEL_TWO_LAUNCHES},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(L, host_batches[:4], args.cpu_seconds)
     print(json.dumps(out, ensure_ascii=False), flush=True)
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(4):          # elementwise kernel: reads n bytes, writes n bytes
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print("copy calibration: 4 copies of %d MiB" % args.copy_calib_mib, file=sys.stderr)
 
 
 if __name__ == "__main__":
