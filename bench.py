@@ -27,12 +27,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/token + % HBM roofline, spectral MoE gate/up layer, Qwen3-30B-A3B shape, batch 1"
 HBM_PEAK_GBS = 8000.0
-KERNEL_ONE_LAUNCH = "k_gateup_staged<true> (z, expert apply and SiLU*mul in one launch)"
-KERNEL_TWO_LAUNCHES = "k_proj_gemv + k_gateup_staged<false> (timed together)"
+KERNEL_ONE_LAUNCH = "k_gateup_half (z, expert apply and SiLU*mul in one launch)"
+KERNEL_TWO_LAUNCHES = "k_proj_gemv + k_gateup_staged (timed together)"
 # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counter runs, scaled by
 # the same counters on a plain copy of known size; None until measured for
 # the current kernel.
-TRAFFIC = {"qwen3_30b_a3b_t1": 35013405}
+TRAFFIC = {"qwen3_30b_a3b_t1": 25332783}
 
 
 def parse():

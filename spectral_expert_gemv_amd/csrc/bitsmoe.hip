@@ -26,7 +26,6 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kProjWaves = 4;
 constexpr int kTokChunk = 4;
-constexpr int kFusedMaxTokens = 4;  // one-launch path up to this many tokens
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -242,6 +241,16 @@ int launch_proj(const void* phi, const void* x, float* z, int T, int din, int R,
 
 
 }  // namespace
+
+GateUpPlan gateup_plan(int T, int r) {
+  GateUpPlan p;
+  p.z_off = 0;
+  p.zt_off = align_up((size_t)T * 2 * r * sizeof(float), 256);
+  p.sync_off = align_up(p.zt_off + (size_t)T * 2 * r * sizeof(uint64_t), 256);
+  p.total = align_up(p.sync_off + 2 * sizeof(uint32_t), 256);
+  return p;
+}
+
 }  // namespace bitsmoe
 
 using namespace bitsmoe;
@@ -323,23 +332,27 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   a.npairs = T * k;
   a.h = h;
   a.n_slabs = (dout + 63) / 64;
-  sa.phi_t = (const uint4*)phi_t_gateup_f16;
-  sa.x = (const uint4*)x_f16;
-  sa.din8 = din / 8;
   sa.T = T;
-  sa.zt = (uint64_t*)((uint8_t*)ws + plan.zt_off);
   sa.z = (const float*)((uint8_t*)ws + plan.z_off);
-  sa.epoch = (uint32_t*)((uint8_t*)ws + plan.sync_off);
-  sa.arrive = sa.epoch + 1;
   // One launch when every work-group can be resident at once (the groups
   // wait for each other's z); otherwise z first, then the expert kernel.
-  const long long blocks = staged_blocks(T, k, dout);
-  if (T <= kFusedMaxTokens && blocks <= staged_capacity()) {
-    launch_gateup_staged(sa, true, s);
+  const int hgrid = half_grid();
+  if (T <= kHalfMaxTokens && r <= kHalfMaxR && hgrid > 0) {
+    HalfArgs ha;
+    ha.g = a;
+    ha.phi_t = (const uint4*)phi_t_gateup_f16;
+    ha.x = (const uint4*)x_f16;
+    ha.din8 = din / 8;
+    ha.T = T;
+    ha.zt = (uint64_t*)((uint8_t*)ws + plan.zt_off);
+    ha.epoch = (uint32_t*)((uint8_t*)ws + plan.sync_off);
+    ha.arrive = ha.epoch + 1;
+    ha.grid = hgrid;
+    launch_gateup_half(ha, s);
     return launch_status("one-launch gate/up");
   }
   if ((st = launch_proj(phi_t_gateup_f16, x_f16, (float*)sa.z, T, din, 2 * r, s))) return st;
-  launch_gateup_staged(sa, false, s);
+  launch_gateup_staged(sa, s);
   return launch_status("gate/up expert launch");
 }
 

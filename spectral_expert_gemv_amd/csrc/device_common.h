@@ -11,23 +11,42 @@ namespace bitsmoe {
 
 constexpr int kWave = 64;
 
-// Directory record of expert e of a device blob, validated against the
-// dimensions the host passed and against the blob size.  The header and the
-// record are loaded together (the record address uses e clamped into
-// [0, E), always inside the directory the host size check guarantees), and
-// then validated.  Returns false when the blob cannot be read safely.
-__device__ inline bool load_dir(const uint8_t* __restrict__ blob, uint64_t blob_bytes,
-                                int e, int E, int dout, int r, DirRec& d) {
-  const Header* h = reinterpret_cast<const Header*>(blob);
+// Header fields a directory record is checked against.
+struct HdrF {
+  uint32_t magic, version, E, dout, r, n_slabs;
+};
+
+// Scalar loads (constant address space): the header is the same for all lanes.
+__device__ inline HdrF load_hdr(const uint8_t* __restrict__ blob) {
+  typedef __attribute__((address_space(4))) const Header CHeader;
+  CHeader* h = (CHeader*)(blob);
+  HdrF f;
+  f.magic = h->magic;
+  f.version = h->version;
+  f.E = h->E;
+  f.dout = h->dout;
+  f.r = h->r;
+  f.n_slabs = h->n_slabs;
+  return f;
+}
+
+// Directory record of expert e, loaded from e clamped into [0, E) (always
+// inside the directory the host size check guarantees); check_dir decides
+// whether it may be used.
+__device__ inline DirRec load_rec(const uint8_t* __restrict__ blob, int e, int E) {
   const int ec = e < 0 ? 0 : (e >= E ? E - 1 : e);
-  d = reinterpret_cast<const DirRec*>(blob + kHeaderBytes)[ec];
-  const uint32_t magic = h->magic, version = h->version, hE = h->E, hdout = h->dout,
-                 hr = h->r, n_slabs32 = h->n_slabs;
-  if (magic != kMagic || version != kVersion || hE != (uint32_t)E ||
-      hdout != (uint32_t)dout || hr != (uint32_t)r)
+  return reinterpret_cast<const DirRec*>(blob + kHeaderBytes)[ec];
+}
+
+// Validates a record against the dimensions the host passed and against the
+// blob size.  Returns false when the blob cannot be read safely.
+__device__ inline bool check_dir(const HdrF& h, const DirRec& d, uint64_t blob_bytes, int e,
+                                 int E, int dout, int r) {
+  if (h.magic != kMagic || h.version != kVersion || h.E != (uint32_t)E ||
+      h.dout != (uint32_t)dout || h.r != (uint32_t)r)
     return false;
   if (e < 0 || e >= E) return false;
-  const uint64_t n_slabs = n_slabs32;
+  const uint64_t n_slabs = h.n_slabs;
   const uint64_t dout_pad = n_slabs * 64;
   if (n_slabs != (uint64_t)((dout + 63) / 64)) return false;
   if (d.block_offset + d.block_bytes > blob_bytes) return false;
@@ -49,6 +68,13 @@ __device__ inline bool load_dir(const uint8_t* __restrict__ blob, uint64_t blob_
       (d.f16_off & 15u))
     return false;
   return true;
+}
+
+// Directory record of expert e of a device blob, loaded and validated.
+__device__ inline bool load_dir(const uint8_t* __restrict__ blob, uint64_t blob_bytes,
+                                int e, int E, int dout, int r, DirRec& d) {
+  d = load_rec(blob, e, E);
+  return check_dir(load_hdr(blob), d, blob_bytes, e, E, dout, r);
 }
 
 // Code of row `lane` of one 1..8-bit column in a 64-row slab: bit j comes

@@ -6,6 +6,9 @@
 
 namespace bitsmoe {
 
+constexpr int kHalfMaxTokens = 4;   // one-launch path: T <= this
+constexpr int kHalfMaxR = 4096;      //   and r <= this (z of a token fits LDS)
+
 // Workspace layout of one gate/up call (offsets in bytes from ws).
 struct GateUpPlan {
   size_t z_off;       // T x 2r float32 (two-launch path)
@@ -28,20 +31,28 @@ struct GateUpArgs {
 
 struct StagedArgs {
   GateUpArgs g;
-  const uint4* phi_t;  // 2r x din fp16 (one-launch path)
-  const uint4* x;      // T x din fp16 (one-launch path)
+  int T;
+  const float* z;      // T x 2r z computed by the projection launch
+};
+// Staged gate/up kernel (second launch of the two-launch path): one
+// work-group per (token, slot, 32-row half-slab).
+size_t staged_lds_bytes();
+long long staged_blocks(int T, int k, int dout);
+int launch_gateup_staged(const StagedArgs& s, hipStream_t st);
+
+// One-launch gate/up kernel, one work-group per (pair, half-slab) unit.
+struct HalfArgs {
+  GateUpArgs g;
+  const uint4* phi_t;  // 2r x din fp16
+  const uint4* x;      // T x din fp16
   int din8, T;
-  uint64_t* zt;        // T x 2r tagged z (one-launch path)
-  const float* z;      // T x 2r z (two-launch path)
+  uint64_t* zt;        // T x 2r tagged z
   uint32_t* epoch;
   uint32_t* arrive;
+  int grid;            // multiple of 8
 };
-// Staged gate/up kernel: one work-group per (token, slot, 32-row half-slab).
-// staged_capacity(): work-groups resident at once on the current device
-// (0: unknown); the one-launch variant needs staged_blocks() <= capacity.
-size_t staged_lds_bytes();
-int staged_capacity();
-long long staged_blocks(int T, int k, int dout);
-void launch_gateup_staged(const StagedArgs& s, bool fused, hipStream_t st);
+size_t half_lds_bytes();
+int half_grid();  // work-groups of the half-slab kernel on this device (0: unavailable)
+void launch_gateup_half(const HalfArgs& s, hipStream_t st);
 
 }  // namespace bitsmoe

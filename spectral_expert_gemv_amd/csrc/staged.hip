@@ -1,4 +1,4 @@
-// Gate/up expert kernel with LDS staging, and its one-launch variant.
+// Gate/up expert kernel with LDS staging (z computed by a previous launch).
 //
 // BitsMoE blog note, Methodology: "first split" (z = Phi^T x once per token,
 // shared by the routed experts), "second split" (expert output = sum over
@@ -21,14 +21,6 @@
 //     adds coef * code to 32 row registers.  Row sums go through LDS.
 // Columns are processed in chunks that fit the LDS budget.
 //
-// One-launch variant (kFused): every wave also computes a share of the 2r
-// rows of z (Phi^T rows, v_dot2_f32_f16, wave reduction) and publishes each
-// value as a 64-bit word (float bits | epoch tag << 32) with one
-// agent-coherent store; step 2 then waits for the tag.  No fence is needed:
-// a reader that sees the tag sees the value in the same word.  Groups wait
-// for other groups, so the host uses this variant only when every group is
-// resident at once; waits are bounded (time-out gives NaN rows and the
-// kernel still exits).  The last group of the grid advances the epoch.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -47,11 +39,8 @@ constexpr int kPitchS = kRowsS + 1;
 constexpr int kMaxM = 6144;                 // staged plane masks (u64) per projection
 constexpr int kMaxC = 2048;                 // staged columns per projection
 constexpr int kZIt = kMaxC / kGL;           // z gathers per lane per chunk
-constexpr int kRowsPreload = 3;             // Phi^T rows a wave loads up front
-constexpr uint32_t kSpin = 1u << 20;
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 // LDS layout (dynamic), per projection:
 //   masks u64[kMaxM + 2] | kidx u16[kMaxC + 16] | a f32[kMaxC + 8] (later coef)
@@ -97,14 +86,6 @@ __device__ __forceinline__ void stage16(void* dst, const void* src, int n, int l
                                      (lds_void*)(d + 16 * (size_t)(i - lane)), 16, 0, 0);
 }
 
-__device__ __forceinline__ float dot8(uint4 a, uint4 b, float acc) {
-  const half2_t* ha = reinterpret_cast<const half2_t*>(&a);
-  const half2_t* hb = reinterpret_cast<const half2_t*>(&b);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(ha[i], hb[i], acc, false);
-  return acc;
-}
-
 // Widths of the 1..8-bit groups without a memory table (g in 0..5).
 __device__ __forceinline__ int width_of(int g) { return g < 4 ? g + 1 : (g == 4 ? 6 : 8); }
 
@@ -144,71 +125,6 @@ __device__ __forceinline__ void column(const uint32_t* words, int b, float coef,
   }
 }
 
-// Spins (bounded) until the tagged word at p carries `tag`, starting from
-// the word w already read; whole wave.  NaN after the bound.
-__device__ __forceinline__ float settle_tagged(const uint64_t* p, uint64_t w, uint32_t tag,
-                                               bool active) {
-  bool ready = !active || (uint32_t)(w >> 32) == tag;
-  uint32_t spins = 0;
-  while (!__all(ready) && spins < kSpin) {
-    __builtin_amdgcn_s_sleep(1);
-    if (!ready) {
-      w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ready = (uint32_t)(w >> 32) == tag;
-    }
-    ++spins;
-  }
-  if (!active) return 0.f;
-  return ready ? __uint_as_float((uint32_t)w) : __builtin_nanf("");
-}
-
-__device__ void produce_z(const StagedArgs& s, int gw, int nw, int lane, uint32_t tag,
-                          uint4 (&pv)[kRowsPreload][4], uint4 (&xv)[4]) {
-  const int R = 2 * s.g.r;
-  for (int q = 0; gw + q * nw < R; ++q) {
-    const int n = gw + q * nw;
-    const uint4* prow = s.phi_t + (size_t)n * s.din8;
-    uint4 p0[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + u * kWave;
-      if (q == 0) p0[u] = pv[0][u];
-      else if (q == 1) p0[u] = pv[1][u];
-      else if (q == 2) p0[u] = pv[2][u];
-      else p0[u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
-    }
-    for (int tt = 0; tt < s.T; ++tt) {
-      const uint4* xt = s.x + (size_t)tt * s.din8;
-      float acc = 0.f;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = lane + u * kWave;
-        if (i < s.din8) acc = dot8(p0[u], tt == 0 ? xv[u] : xt[i], acc);
-      }
-      for (int i0 = 4 * kWave; i0 < s.din8; i0 += 4 * kWave) {  // din > 2048
-        uint4 q4[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + lane + u * kWave;
-          q4[u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + lane + u * kWave;
-          if (i < s.din8) acc = dot8(q4[u], xt[i], acc);
-        }
-      }
-      acc = wave_sum(acc);
-      if (lane == 0) {
-        const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(acc);
-        __hip_atomic_store(&s.zt[(size_t)tt * R + n], w, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-}
-
-template <bool kFused>
 __global__ __launch_bounds__(kSThreads) void k_gateup_staged(StagedArgs s) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   const GateUpArgs& a = s.g;
@@ -223,31 +139,7 @@ __global__ __launch_bounds__(kSThreads) void k_gateup_staged(StagedArgs s) {
   const int t = pair / a.ktop;
   const int R = 2 * a.r;
 
-  // ---- loads that need nothing else ----
   const int e = a.ids[pair];
-  uint32_t tag = 0;
-  uint4 pv[kRowsPreload][4];
-  uint4 xv[4];
-  const int gw = blockIdx.x * kSWaves + wv;
-  const int nw = gridDim.x * kSWaves;
-  if (kFused) {
-    tag = __hip_atomic_load(s.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-#pragma unroll
-    for (int q = 0; q < kRowsPreload; ++q) {
-      const int n = gw + q * nw;
-      const uint4* prow = s.phi_t + (size_t)(n < R ? n : 0) * s.din8;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = lane + u * kWave;
-        pv[q][u] = (n < R && i < s.din8) ? prow[i] : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + u * kWave;
-      xv[u] = i < s.din8 ? s.x[i] : make_uint4(0, 0, 0, 0);
-    }
-  }
 
   // ---- this projection's expert block ----
   const uint8_t* blob = proj ? a.blob_u : a.blob_g;
@@ -272,7 +164,6 @@ __global__ __launch_bounds__(kSThreads) void k_gateup_staged(StagedArgs s) {
   }
   const int n_q = ok ? (int)d.n_q : 0;
   const int n16 = ok ? (int)d.n_16 : 0;
-  const uint64_t* zt_tok = s.zt + (size_t)t * R + (proj ? a.r : 0);
   const float* z_tok = s.z + (size_t)t * R + (proj ? a.r : 0);
   const Lds L = lds_of(lds_raw, proj);
   auto mask_of = [&](int c) -> uint32_t {  // first mask of column c (uniform c)
@@ -340,15 +231,12 @@ __global__ __launch_bounds__(kSThreads) void k_gateup_staged(StagedArgs s) {
       stage16(L.m, g_m + cu0, nu, lp, lane);
       stage16(L.a, g_a + cf0, nf, lp, lane);
     }
-    // ---- one-launch variant: this wave's share of z, meanwhile ----
-    if (kFused && ch == 0) produce_z(s, gw, nw, lane, tag, pv, xv);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // ---- 2. z gather (all loads first), coef = a * s * z_k into LDS ----
     const int n_it = (nc + kGL - 1) / kGL;
     {
       uint32_t kc[kZIt];
-      uint64_t zw[kZIt];
       float zf[kZIt];
 #pragma unroll
       for (int it = 0; it < kZIt; ++it) {
@@ -357,20 +245,14 @@ __global__ __launch_bounds__(kSThreads) void k_gateup_staged(StagedArgs s) {
         const uint32_t kk = live ? L.kidx[c0 - cu0 + i] : 0u;
         good &= kk < (uint32_t)a.r;
         kc[it] = kk < (uint32_t)a.r ? kk : 0u;
-        if (kFused) {
-          zw[it] = live ? __hip_atomic_load(zt_tok + kc[it], __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT)
-                        : 0ull;
-        } else {
-          zf[it] = live ? z_tok[kc[it]] : 0.f;
-        }
+        zf[it] = live ? z_tok[kc[it]] : 0.f;
       }
 #pragma unroll
       for (int it = 0; it < kZIt; ++it) {
         if (it >= n_it) break;
         const int i = it * kGL + lp;
         const bool live = i < nc;
-        const float z = kFused ? settle_tagged(zt_tok + kc[it], zw[it], tag, live) : zf[it];
+        const float z = zf[it];
         if (live) {
           const float az = L.a[c0 - cf0 + i] * z;
           L.a[c0 - cf0 + i] = az * __half2float(__ushort_as_half(L.s[c0 - cu0 + i]));
@@ -413,7 +295,6 @@ __global__ __launch_bounds__(kSThreads) void k_gateup_staged(StagedArgs s) {
     __syncthreads();  // LDS is restaged by the next chunk
     c0 = c1;
   }
-  if (kFused && nch_all == 0) produce_z(s, gw, nw, lane, tag, pv, xv);
 
   // ---- 16-bit columns: fp16 values (loads issued at the start) ----
   for (int it = 0; it < n_it16; ++it) {
@@ -421,14 +302,7 @@ __global__ __launch_bounds__(kSThreads) void k_gateup_staged(StagedArgs s) {
     const bool live = it * kGL + lp < n16;
     good &= fk < (uint32_t)a.r;
     const uint32_t kc = fk < (uint32_t)a.r ? fk : 0u;
-    float z;
-    if (kFused) {
-      const uint64_t w0 =
-          live ? __hip_atomic_load(zt_tok + kc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-      z = settle_tagged(zt_tok + kc, w0, tag, live);
-    } else {
-      z = live ? z_tok[kc] : 0.f;
-    }
+    const float z = live ? z_tok[kc] : 0.f;
     const float az = fa * z;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -478,14 +352,6 @@ __global__ __launch_bounds__(kSThreads) void k_gateup_staged(StagedArgs s) {
     if (row < a.dout)
       a.h[(size_t)pair * a.dout + row] = all_ok ? silu_mul(g, u) : __builtin_nanf("");
   }
-  if (kFused && threadIdx.x == 0) {
-    const uint32_t n =
-        __hip_atomic_fetch_add(s.arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (n == gridDim.x - 1) {
-      __hip_atomic_store(s.arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(s.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
 }
 
 static_assert(kLdsBytes >= (size_t)kSThreads * kPitchS * 4, "reduction fits the staging area");
@@ -494,50 +360,23 @@ static_assert(kLdsBytes >= (size_t)kSThreads * kPitchS * 4, "reduction fits the 
 
 size_t staged_lds_bytes() { return kLdsBytes; }
 
-GateUpPlan gateup_plan(int T, int r) {
-  GateUpPlan p;
-  p.z_off = 0;
-  p.zt_off = align_up((size_t)T * 2 * r * sizeof(float), 256);
-  p.sync_off = align_up(p.zt_off + (size_t)T * 2 * r * sizeof(uint64_t), 256);
-  p.total = align_up(p.sync_off + 2 * sizeof(uint32_t), 256);
-  return p;
-}
-
-int staged_capacity() {
-  static int cap[64];
-  static bool done[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (!done[dev]) {
-    int cus = 0, nb = 0;
-    // allow the dynamic LDS size (a no-op where it is already permitted)
-    (void)hipFuncSetAttribute((const void*)k_gateup_staged<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    (void)hipFuncSetAttribute((const void*)k_gateup_staged<false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    (void)hipGetLastError();
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_gateup_staged<true>, kSThreads,
-                                                     kLdsBytes) != hipSuccess)
-      return 0;
-    cap[dev] = cus * nb;
-    done[dev] = true;
-  }
-  return cap[dev];
-}
-
 long long staged_blocks(int T, int k, int dout) {
   return (long long)T * k * 2 * ((dout + 63) / 64);
 }
 
-void launch_gateup_staged(const StagedArgs& s, bool fused, hipStream_t st) {
+int launch_gateup_staged(const StagedArgs& s, hipStream_t st) {
+  static bool attr_done[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr_done[dev]) {
+    // allow the dynamic LDS size (a no-op where it is already permitted)
+    (void)hipFuncSetAttribute((const void*)k_gateup_staged,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    (void)hipGetLastError();
+    attr_done[dev] = true;
+  }
   const long long blocks = staged_blocks(s.T, s.g.ktop, s.g.dout);
-  if (fused)
-    hipLaunchKernelGGL(k_gateup_staged<true>, dim3((unsigned)blocks), dim3(kSThreads), kLdsBytes,
-                       st, s);
-  else
-    hipLaunchKernelGGL(k_gateup_staged<false>, dim3((unsigned)blocks), dim3(kSThreads), kLdsBytes,
-                       st, s);
+  hipLaunchKernelGGL(k_gateup_staged, dim3((unsigned)blocks), dim3(kSThreads), kLdsBytes, st, s);
+  return 0;
 }
 
 }  // namespace bitsmoe

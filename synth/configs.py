@@ -54,11 +54,21 @@ DEEPSEEK_MOE_16B = LayerSpec(
     ln_sigma=0.5, bits={1: 5, 2: 25, 3: 35, 4: 25, 6: 5, 8: 4, 16: 1},
     outlier_frac=0.005, outlier_scale=20.0, phi_fp16=True)
 
+# Test-only shape: wide columns (mostly 6- and 8-bit, many fp16) and a ragged
+# dout, so that one 64-row slab of one expert holds more plane masks and
+# fp16 columns than a work-group stages at once.
+WIDE = LayerSpec("wide", E=4, din=3072, dout=4133, r=3072, k=2, decay=0.5,
+                 ln_sigma=0.3, bits={4: 10, 6: 30, 8: 50, 16: 10}, outlier_frac=0.0,
+                 outlier_scale=1.0, phi_fp16=True)
+
 LAYERS: Dict[str, LayerSpec] = {l.name: l for l in
-                                (TINY, QWEN3_30B_A3B, MIXTRAL_8X7B, DEEPSEEK_MOE_16B)}
+                                (TINY, QWEN3_30B_A3B, MIXTRAL_8X7B, DEEPSEEK_MOE_16B, WIDE)}
 
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     Workload("tiny_t8", TINY, 8, ("uniform",)),
+    Workload("tiny_t1", TINY, 1, ("uniform",)),
+    Workload("tiny_t4", TINY, 4, ("uniform",)),
+    Workload("wide_t2", WIDE, 2, ("uniform",)),
     Workload("qwen3_30b_a3b_t1", QWEN3_30B_A3B, 1, ("uniform",)),
     Workload("qwen3_30b_a3b_t32", QWEN3_30B_A3B, 32, ("zipf", 1.1)),
     Workload("mixtral_8x7b_t1", MIXTRAL_8X7B, 1, ("uniform",)),

@@ -140,8 +140,9 @@ def _check_h(got, href):
     return worst
 
 
-@pytest.mark.parametrize("wl_name,steps", [("tiny_t8", 3), ("qwen3_30b_a3b_t1", 3),
-                                           ("qwen3_30b_a3b_t32", 1)])
+@pytest.mark.parametrize("wl_name,steps", [("tiny_t1", 3), ("tiny_t4", 3), ("tiny_t8", 3),
+                                           ("qwen3_30b_a3b_t1", 3), ("qwen3_30b_a3b_t32", 1),
+                                           ("wide_t2", 2)])
 def test_gateup_full(bm, wl_name, steps):
     wl = synth.workload(wl_name)
     L, dev = device_layer(wl.layer.name)
@@ -153,8 +154,9 @@ def test_gateup_full(bm, wl_name, steps):
         _say("  worst %.3g" % worst)
 
 
-def test_repeat_runs_bit_identical(bm):
-    wl = synth.workload("qwen3_30b_a3b_t32")
+@pytest.mark.parametrize("wl_name", ["qwen3_30b_a3b_t1", "qwen3_30b_a3b_t32"])
+def test_repeat_runs_bit_identical(bm, wl_name):
+    wl = synth.workload(wl_name)
     L, dev = device_layer(wl.layer.name)
     x, ids = synth.make_batch(wl, L)
     a = _run_gateup(dev, x, ids)
@@ -164,8 +166,11 @@ def test_repeat_runs_bit_identical(bm):
 
 # ------------------------------------------------------------ edge cases
 
-def test_edges_zero_expert_k1_duplicates(bm):
-    """All-0-bit expert gives h = 0; k = 1; the same expert on every token."""
+@pytest.mark.parametrize("T", [4, 8])
+def test_edges_zero_expert_k1_duplicates(bm, T):
+    """All-0-bit expert gives h = 0; k = 1; the same expert on every token.
+
+    T = 4 runs the one-launch kernel, T = 8 the two-launch path."""
     from spectral_expert_gemv_amd import DeviceLayer
     L = synth.make_layer(synth.LAYERS["tiny"])
     bits_g = L.bits["gate"].copy()
@@ -175,33 +180,36 @@ def test_edges_zero_expert_k1_duplicates(bm):
     dev = DeviceLayer(L.phi["gate"], L.phi["up"], L.a["gate"], L.a["up"], L.p["gate"],
                       L.p["up"], bits_g, bits_u)
     x, _ = synth.make_batch(synth.workload("tiny_t8"), L)
-    ids = np.full((8, 1), 2, np.int32)
+    x = x[:T]
+    ids = np.full((T, 1), 2, np.int32)
     got = _run_gateup(dev, x, ids)
     assert np.all(got == 0)
-    ids = np.array([[1], [1], [3], [1], [0], [3], [1], [1]], np.int32)
+    ids = np.array([[1], [1], [3], [1], [0], [3], [1], [1]], np.int32)[:T]
     got = _run_gateup(dev, x, ids)
     Lz = synth.generate.Layer(L.spec, L.phi, L.a, L.p, {"gate": bits_g, "up": bits_u},
                               L.outlier_channels)
     _check_h(got, pairs_ref(Lz, x, ids))
 
 
-def test_bad_expert_id_and_blob_mismatch_give_nan(bm):
+@pytest.mark.parametrize("T", [4, 8])
+def test_bad_expert_id_and_blob_mismatch_give_nan(bm, T):
     L, dev = device_layer("tiny")
     spec = L.spec
     x, ids = synth.make_batch(synth.workload("tiny_t8"), L)
-    ids = ids.copy()
+    x, ids = x[:T], ids[:T].copy()
     ids[3, 1] = spec.E          # out of range
-    ids[5, 0] = -1
+    ids[T - 3, 0] = -1
+    bad = ((3, 1), (T - 3, 0))
     got = _run_gateup(dev, x, ids)
-    assert np.all(np.isnan(got[3, 1])) and np.all(np.isnan(got[5, 0]))
-    ok = [(t, s) for t in range(8) for s in range(2) if (t, s) not in ((3, 1), (5, 0))]
+    assert all(np.all(np.isnan(got[t, j])) for t, j in bad)
+    ok = [(t, s) for t in range(T) for s in range(2) if (t, s) not in bad]
     _check_h(got, pairs_ref(L, x, ids, pairs=ok))
     # blobs whose header says a different dout than the call: every row NaN
-    T, k = 8, 2
+    k = 2
     dout_call = spec.dout - 1
     h = torch.zeros((T, k, dout_call), dtype=torch.float32, device="cuda")
     ws = dev.workspace(T, k)
-    good_ids = _cuda(synth.make_batch(synth.workload("tiny_t8"), L)[1])
+    good_ids = _cuda(synth.make_batch(synth.workload("tiny_t8"), L)[1][:T])
     bm._check(bm._lib.bitsmoe_moe_gateup(
         dev.blob_gate.data_ptr(), dev.blob_gate.numel(), dev.blob_up.data_ptr(),
         dev.blob_up.numel(), dev.phi_t.data_ptr(), _cuda(x).data_ptr(),
