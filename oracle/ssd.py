@@ -8,7 +8,7 @@ SVD W_cat = U Sigma Phi^T is taken, and P = U Sigma so that W_e = P_e Phi^T
 with P_e the e-th block of dout rows.  "second split": the columns of P_e are
 normalised, W_e = sum_k a_{e,k} p_{e,k} phi_k^T with ||p_{e,k}||_2 = 1.
 
-Pinned by tests/test_oracle_ssd.py: reconstruction of random dense W_e (which
+Pinned by tests/test_oracle_path.py (test_ssd_reconstruction_and_structure): reconstruction of random dense W_e (which
 is independent input, not built from factors) to 1e-5 relative in fp32
 factors; orthonormality of Phi; unit columns; the singular values match
 numpy's ``svdvals`` of the stacked matrix.
