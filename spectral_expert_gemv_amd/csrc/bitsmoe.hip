@@ -19,10 +19,10 @@ namespace bitsmoe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Shared projection, small token counts: one wave per basis vector n.  Lanes
+// Shared projection for din > 4096: one wave per basis vector n.  Lanes
 // stride the din reduction with 16-byte loads; fp16 pairs are multiplied and
 // accumulated in float32 by v_dot2_f32_f16; a wave reduction finishes it.
-// Phi^T is read exactly once per chunk of kTokChunk tokens.
+// Phi^T is read once per chunk of kTokChunk tokens.
 // ---------------------------------------------------------------------------
 constexpr int kProjWaves = 4;
 constexpr int kTokChunk = 4;
@@ -65,6 +65,88 @@ __global__ __launch_bounds__(kProjWaves * kWave) void k_proj_gemv(
     for (int tt = 0; tt < kTokChunk; ++tt) {
       const float s = wave_sum(acc[tt]);
       if (lane == 0 && t0 + tt < T) z[(size_t)(t0 + tt) * R + n] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared projection, token batches: a work-group of 4 waves owns 16 Phi^T
+// rows (4 per wave, held in registers, read once) and walks the tokens 4 at a
+// time; each batch of x is copied into LDS once with 16-byte
+// global_load_lds and read by all 16 rows.  A wave's 16 dot products (4
+// rows x 4 tokens) are finished with a transpose reduction (17 lane
+// exchanges) and lanes 0-15 store them.  U: 16-byte x units per lane (din <=
+// 512 U).
+// ---------------------------------------------------------------------------
+constexpr int kPRW = 4;     // Phi^T rows per wave
+constexpr int kPT = 4;      // tokens per batch
+constexpr int kPMaxU = 8;   // din <= 4096
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int O>
+__device__ __forceinline__ void pstep(float (&v)[kPRW * kPT], bool up) {
+#pragma unroll
+  for (int i = 0; i < O; ++i) {
+    const float send = up ? v[i] : v[i + O];
+    const float keep = up ? v[i + O] : v[i];
+    v[i] = keep + __shfl_xor(send, O, kWave);
+  }
+}
+
+template <int U>
+__global__ __launch_bounds__(kProjWaves * kWave) void k_proj_rows(
+    const uint4* __restrict__ phi_t, const uint4* __restrict__ x, float* __restrict__ z,
+    int T, int din8, int R) {
+  __shared__ __align__(16) uint4 xs[kPT][kPMaxU * kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * kProjWaves + wv) * kPRW;
+  uint4 ph[kPRW][U];
+#pragma unroll
+  for (int i = 0; i < kPRW; ++i) {
+    const int n = n0 + i;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = lane + kWave * u;
+      ph[i][u] = (n < R && idx < din8) ? phi_t[(size_t)n * din8 + idx] : make_uint4(0, 0, 0, 0);
+    }
+  }
+  for (int t0 = 0; t0 < T; t0 += kPT) {
+    __syncthreads();  // the previous batch has been read
+    for (int tt = 0; tt < kPT && t0 + tt < T; ++tt) {
+      const uint4* src = x + (size_t)(t0 + tt) * din8;
+      uint8_t* dst = reinterpret_cast<uint8_t*>(&xs[tt][0]);
+      for (int i = threadIdx.x; i < din8; i += kProjWaves * kWave)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + i),
+                                         (lds_void_t*)(dst + 16 * (size_t)(i - lane)), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    float v[kPRW * kPT];
+#pragma unroll
+    for (int i = 0; i < kPRW * kPT; ++i) v[i] = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = lane + kWave * u;
+      if (idx < din8) {
+#pragma unroll
+        for (int tt = 0; tt < kPT; ++tt) {
+          const uint4 xv = xs[tt][idx];
+#pragma unroll
+          for (int i = 0; i < kPRW; ++i) v[i * kPT + tt] = dot8(ph[i][u], xv, v[i * kPT + tt]);
+        }
+      }
+    }
+    pstep<8>(v, (lane & 8) != 0);
+    pstep<4>(v, (lane & 4) != 0);
+    pstep<2>(v, (lane & 2) != 0);
+    pstep<1>(v, (lane & 1) != 0);
+    float sum = v[0] + __shfl_xor(v[0], 16, kWave);
+    sum += __shfl_xor(sum, 32, kWave);
+    if (lane < kPRW * kPT) {
+      const int i = lane / kPT, tt = lane % kPT;
+      if (n0 + i < R && t0 + tt < T) z[(size_t)(t0 + tt) * R + n0 + i] = sum;
     }
   }
 }
@@ -233,21 +315,37 @@ int proj_args(const void* phi, const void* x, const float* z, int T, int din, in
 
 int launch_proj(const void* phi, const void* x, float* z, int T, int din, int R,
                 hipStream_t s) {
-  const dim3 grid((R + kProjWaves - 1) / kProjWaves);
-  hipLaunchKernelGGL(k_proj_gemv, grid, dim3(kProjWaves * kWave), 0, s,
-                     (const uint4*)phi, (const uint4*)x, z, T, din / 8, R);
+  const int din8 = din / 8;
+  const dim3 grid_rows((R + kProjWaves * kPRW - 1) / (kProjWaves * kPRW));
+  const dim3 block(kProjWaves * kWave);
+  const uint4* p4 = (const uint4*)phi;
+  const uint4* x4 = (const uint4*)x;
+  if (din8 <= kWave)
+    hipLaunchKernelGGL(k_proj_rows<1>, grid_rows, block, 0, s, p4, x4, z, T, din8, R);
+  else if (din8 <= 2 * kWave)
+    hipLaunchKernelGGL(k_proj_rows<2>, grid_rows, block, 0, s, p4, x4, z, T, din8, R);
+  else if (din8 <= 4 * kWave)
+    hipLaunchKernelGGL(k_proj_rows<4>, grid_rows, block, 0, s, p4, x4, z, T, din8, R);
+  else if (din8 <= kPMaxU * kWave)
+    hipLaunchKernelGGL(k_proj_rows<8>, grid_rows, block, 0, s, p4, x4, z, T, din8, R);
+  else
+    hipLaunchKernelGGL(k_proj_gemv, dim3((R + kProjWaves - 1) / kProjWaves), block, 0, s, p4,
+                       x4, z, T, din8, R);
   return launch_status("spectral projection launch");
 }
 
 
 }  // namespace
 
-GateUpPlan gateup_plan(int T, int r) {
+GateUpPlan gateup_plan(int T, int k, int E, int r) {
   GateUpPlan p;
+  const size_t P = (size_t)T * k;
+  const size_t gmax = P < (size_t)E ? P : (size_t)E;
   p.z_off = 0;
   p.zt_off = align_up((size_t)T * 2 * r * sizeof(float), 256);
   p.sync_off = align_up(p.zt_off + (size_t)T * 2 * r * sizeof(uint64_t), 256);
-  p.total = align_up(p.sync_off + 2 * sizeof(uint32_t), 256);
+  p.route_off = align_up(p.sync_off + 2 * sizeof(uint32_t), 256);
+  p.total = align_up(p.route_off + (1 + gmax + gmax + 1 + P) * sizeof(int), 256);
   return p;
 }
 
@@ -294,7 +392,7 @@ int bitsmoe_moe_gateup_workspace_size(int T, int k, int E, int din, int dout, in
   if (st) return st;
   if (T < 1 || k < 1 || k > E) return fail(BITSMOE_EINVAL, "T=%d k=%d E=%d", T, k, E);
   if (din <= 0 || din % 8) return fail(BITSMOE_ESHAPE, "din=%d", din);
-  *bytes = gateup_plan(T, r).total;
+  *bytes = gateup_plan(T, k, E, r).total;
   return BITSMOE_OK;
 }
 
@@ -316,7 +414,7 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   size_t need = 0;
   bitsmoe_moe_gateup_workspace_size(T, k, E, din, dout, r, &need);
   if (ws_bytes < need) return fail(BITSMOE_ENOSPC, "ws_bytes=%zu < %zu", ws_bytes, need);
-  const GateUpPlan plan = gateup_plan(T, r);
+  const GateUpPlan plan = gateup_plan(T, k, E, r);
   hipStream_t s = (hipStream_t)stream;
   StagedArgs sa;
   GateUpArgs& a = sa.g;
@@ -352,6 +450,23 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     return launch_status("one-launch gate/up");
   }
   if ((st = launch_proj(phi_t_gateup_f16, x_f16, (float*)sa.z, T, din, 2 * r, s))) return st;
+  if (r <= kGroupMaxR && r % 2 == 0 && E <= kGroupMaxE && grouped_tokens_per_batch(r) > 0) {
+    // batched tokens: pairs grouped by expert, each expert's planes read once
+    GroupArgs gs;
+    gs.g = a;
+    gs.z = sa.z;
+    const long long P = (long long)T * k;
+    gs.gmax = (int)(P < E ? P : E);
+    int* rb = (int*)((uint8_t*)ws + plan.route_off);
+    gs.rl.ngroups = rb;
+    gs.rl.gexp = rb + 1;
+    gs.rl.goff = rb + 1 + gs.gmax;
+    gs.rl.pairs = rb + 1 + 2 * gs.gmax + 1;
+    launch_route_group(ids, (int)P, E, dout, h, gs.rl, s);
+    if ((st = launch_status("route grouping launch"))) return st;
+    launch_gateup_grouped(gs, s);
+    return launch_status("grouped gate/up launch");
+  }
   launch_gateup_staged(sa, s);
   return launch_status("gate/up expert launch");
 }

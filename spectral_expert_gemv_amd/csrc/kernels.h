@@ -8,15 +8,18 @@ namespace bitsmoe {
 
 constexpr int kHalfMaxTokens = 4;   // one-launch path: T <= this
 constexpr int kHalfMaxR = 4096;      //   and r <= this (z of a token fits LDS)
+constexpr int kGroupMaxR = 4096;     // grouped path: r <= this
+constexpr int kGroupMaxE = 16384;    //   and E <= this (route histogram in LDS)
 
 // Workspace layout of one gate/up call (offsets in bytes from ws).
 struct GateUpPlan {
-  size_t z_off;       // T x 2r float32 (two-launch path)
+  size_t z_off;       // T x 2r float32 (projection launch of the batched paths)
   size_t zt_off;      // T x 2r uint64 tagged z (one-launch path)
   size_t sync_off;    // uint32 epoch, uint32 grid arrival counter (left at 0)
+  size_t route_off;   // route lists: ngroups, gexp[gmax], goff[gmax + 1], pairs[T k]
   size_t total;
 };
-GateUpPlan gateup_plan(int T, int r);
+GateUpPlan gateup_plan(int T, int k, int E, int r);
 
 struct GateUpArgs {
   const uint8_t* blob_g;
@@ -54,5 +57,24 @@ struct HalfArgs {
 size_t half_lds_bytes();
 int half_grid();  // work-groups of the half-slab kernel on this device (0: unavailable)
 void launch_gateup_half(const HalfArgs& s, hipStream_t st);
+
+// Pairs grouped by expert (written by the route-grouping launch).
+struct RouteLists {
+  int* ngroups;  // [1]
+  int* gexp;     // expert of group g, ascending
+  int* goff;     // pairs of group g: pairs[goff[g] .. goff[g + 1])
+  int* pairs;    // pair indices t * k + slot
+};
+struct GroupArgs {
+  GateUpArgs g;
+  const float* z;  // T x 2r
+  RouteLists rl;
+  int gmax;        // min(E, T * k): groups the grid is sized for
+};
+size_t grouped_lds_bytes();
+int grouped_tokens_per_batch(int r);  // 0: r too large for the grouped kernel
+int launch_route_group(const int32_t* ids, int P, int E, int dout, float* h,
+                       const RouteLists& rl, hipStream_t st);
+int launch_gateup_grouped(const GroupArgs& s, hipStream_t st);
 
 }  // namespace bitsmoe
