@@ -27,12 +27,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/token + % HBM roofline, spectral MoE gate/up layer, Qwen3-30B-A3B shape, batch 1"
 HBM_PEAK_GBS = 8000.0
-KERNEL_ONE_LAUNCH = "k_gateup_half (z, expert apply and SiLU*mul in one launch)"
-KERNEL_TWO_LAUNCHES = "k_proj_gemv + k_gateup_staged (timed together)"
+KERNEL_ONE_LAUNCH = "k_gateup_fused (z, expert apply and SiLU*mul in one launch)"
+KERNEL_TWO_LAUNCHES = "k_proj_rows + k_route_group + k_gateup_grouped (timed together)"
 # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counter runs, scaled by
 # the same counters on a plain copy of known size; None until measured for
 # the current kernel.
-TRAFFIC = {"qwen3_30b_a3b_t1": 25332783}
+TRAFFIC = {}
 
 
 def parse():
@@ -56,9 +56,11 @@ def layer_bytes_per_expert(bits, dout):
     """Algorithmic bytes of one expert of one linear type (E vector).
 
     bit planes (dout_pad * sum b / 8) + fp16 values of 16-bit columns +
-    10 bytes of metadata per stored column (u16 k, fp16 s, fp16 m, fp32 a).
+    10 bytes of metadata per stored column (u16 k, fp16 s, fp16 m, fp32 a);
+    dout_pad = dout rounded up to the 32-row segment.  Padding slots of the
+    packed format are not counted.
     """
-    dout_pad = (dout + 63) // 64 * 64
+    dout_pad = (dout + 31) // 32 * 32
     b = bits.astype(np.int64)
     q = np.where((b >= 1) & (b <= 8), b, 0).sum(axis=1)
     n16 = (b == 16).sum(axis=1)

@@ -1,4 +1,7 @@
-"""Independent writer and reader of the packed spectral-expert blob (format v1).
+"""Independent writer and reader of the packed spectral-expert blob (format v2).
+
+Test infrastructure: only the tests, the smoke check and the benchmark's CPU
+baseline use this module; the HIP library never imports it.
 
 Source: BitsMoE blog note, "Methodology / execution": components of the same
 width are placed together and then packed by bit plane so that a GPU can
@@ -9,30 +12,39 @@ bytes from its own C++ code, and the tests compare the two.
 Layout (little-endian; offsets in bytes from the blob base):
 
 Header, 128 bytes
-  0 'BMOE' | 4 u32 version=1 | 8 u32 E | 12 u32 dout | 16 u32 r
-  20 u32 dout_pad = 64*ceil(dout/64) | 24 u32 n_slabs = dout_pad/64
+  0 'BMOE' | 4 u32 version=2 | 8 u32 E | 12 u32 dout | 16 u32 r
+  20 u32 dout_pad = 32*ceil(dout/32) | 24 u32 n_seg = dout_pad/32
   28 u32 header_bytes=128 | 32 u64 total_bytes | 40 u64 dir_offset=128
   48 u32 CRC-32 (IEEE, as zlib) of bytes [128, total_bytes) | rest zero
 Directory, E records of 64 bytes at dir_offset
   0 u64 block_offset | 8 u32 n_nz | 12 u32 n_q | 16 u32 n_16
-  20 u32 masks_per_slab = sum of b over the 1..8-bit columns
+  20 u32 seg_words (u32 words of one 32-row segment record)
   24 u32 a_off | 28 u32 s_off | 32 u32 m_off | 36 u32 planes_off
-  40 u32 f16_off | 44 u32 block_bytes (offsets relative to block_offset)
+  40 f32 cmax | 44 u32 block_bytes (offsets relative to block_offset)
   48 u16 count of columns of width 1,2,3,4,6,8,16 (7 values) | 62 u16 0
+  cmax = max over the expert's stored columns of |a_k| * s_k (1..8 bits,
+  float32 product) or |a_k| (16 bits); 0 when the expert stores none.
 Expert block (first at align256(128 + 64 E), blocks back to back)
-  column order: width groups 1,2,3,4,6,8,16, ascending k inside a group;
-  0-bit columns have no entry at all
-  kidx   u16[n_nz]                 at 0
-  a      f32[n_nz]                 at a_off      = align16(2 n_nz)
-  s      f16[n_q]                  at s_off      = align16(a_off + 4 n_nz)
-  m      f16[n_q]                  at m_off      = align16(s_off + 2 n_q)
-  planes u64[n_slabs][masks_per_slab] at planes_off = align256(m_off + 2 n_q)
-         per 64-row slab, for each 1..8-bit column in order and each plane
-         j = 0..b-1 (j = 0 is the least significant code bit): one u64 whose
-         bit t is bit j of q[64*slab + t] (0 for rows >= dout)
-  f16    f16[n_16][dout_pad]       at f16_off = align256(planes_off + 8 n_slabs mps + 16)
-         fp16 values of the 16-bit columns (rows >= dout are 0)
-  block_bytes = align256(f16_off + 2 n_16 dout_pad)
+  slot order: width groups 1,2,3,4,6,8,16; inside a group the columns in
+  ascending k, then zero slots up to a multiple of 32 (nb_w = 8 ceil(n_w /
+  32) blocks of 4 slots per group, so that a 32-slot step never mixes
+  widths); 0-bit columns have no slot at all.
+  n_slot = 4 * sum nb_w, n_qslot = 4 * sum of nb_w over widths 1..8.
+  kidx   u16[n_slot]  at 0                   (0 in padding slots)
+  a      f32[n_slot]  at a_off  = align16(2 n_slot)          (0 in padding)
+  s      f16[n_qslot] at s_off  = align16(a_off + 4 n_slot)  (0 in padding)
+  m      f16[n_qslot] at m_off  = align16(s_off + 2 n_qslot) (0 in padding)
+  planes u32[n_seg][seg_words] at planes_off = align256(m_off + 2 n_qslot)
+         one record per 32-row segment; inside it, block after block in slot
+         order, 4*w words per block of width w: for row octet i = 0..3
+         (segment rows 8i..8i+7) w words.
+         w <= 8: word (i, j), j = 0..w-1 is plane j; its bit 4*rho + u is
+         bit j (j = 0 least significant) of the code of segment row 8i + rho
+         in slot 4*beta + u.
+         w = 16: word (i, 2*rho + h) holds the fp16 values of segment row
+         8i + rho in slots 4*beta + 2h (low half) and 4*beta + 2h + 1.
+         seg_words = 4 * sum over blocks of w.  Rows >= dout are 0.
+  block_bytes = align256(planes_off + 4 n_seg seg_words + 16)
 All padding bytes are zero.
 """
 import struct
@@ -43,9 +55,10 @@ import numpy as np
 from .quantize import quantize_expert
 
 MAGIC = b"BMOE"
-VERSION = 1
+VERSION = 2
 HEADER_BYTES = 128
 DIR_REC = 64
+SEG_ROWS = 32
 GROUP_WIDTHS = (1, 2, 3, 4, 6, 8, 16)
 
 
@@ -53,24 +66,65 @@ def _al(x: int, a: int) -> int:
     return (x + a - 1) // a * a
 
 
-def _block_layout(bits_e: np.ndarray, n_slabs: int, dout_pad: int):
-    cnt = [int(np.count_nonzero(bits_e == w)) for w in GROUP_WIDTHS]
+def nibble_shift(rho, u):
+    """Bit position of (row rho of an octet, slot u of a block) in a plane word."""
+    return 4 * rho + u
+
+
+GROUP_SLOTS = 32   # each width group is padded to a multiple of this
+
+
+def _block_layout(cnt, n_seg: int):
+    nb = [(c + GROUP_SLOTS - 1) // GROUP_SLOTS * (GROUP_SLOTS // 4) for c in cnt]
     n_nz = sum(cnt)
     n_16 = cnt[-1]
     n_q = n_nz - n_16
-    mps = sum(w * c for w, c in zip(GROUP_WIDTHS[:-1], cnt[:-1]))
-    a_off = _al(2 * n_nz, 16)
-    s_off = _al(a_off + 4 * n_nz, 16)
-    m_off = _al(s_off + 2 * n_q, 16)
-    p_off = _al(m_off + 2 * n_q, 256)
-    f_off = _al(p_off + 8 * n_slabs * mps + 16, 256)
-    nbytes = _al(f_off + 2 * n_16 * dout_pad, 256)
-    return dict(cnt=cnt, n_nz=n_nz, n_q=n_q, n_16=n_16, mps=mps, a_off=a_off,
-                s_off=s_off, m_off=m_off, p_off=p_off, f_off=f_off, nbytes=nbytes)
+    n_slot = 4 * sum(nb)
+    n_qslot = 4 * sum(nb[:-1])
+    seg_words = 4 * sum(n * w for n, w in zip(nb, GROUP_WIDTHS))
+    a_off = _al(2 * n_slot, 16)
+    s_off = _al(a_off + 4 * n_slot, 16)
+    m_off = _al(s_off + 2 * n_qslot, 16)
+    p_off = _al(m_off + 2 * n_qslot, 256)
+    nbytes = _al(p_off + 4 * n_seg * seg_words + 16, 256)
+    return dict(cnt=list(cnt), nb=nb, n_nz=n_nz, n_q=n_q, n_16=n_16, n_slot=n_slot,
+                n_qslot=n_qslot, seg_words=seg_words, a_off=a_off, s_off=s_off,
+                m_off=m_off, p_off=p_off, nbytes=nbytes)
 
 
-def _column_order(bits_e: np.ndarray):
-    return np.concatenate([np.nonzero(bits_e == w)[0] for w in GROUP_WIDTHS]).astype(np.int64)
+def _slots(bits_e: np.ndarray):
+    """Column index per slot (-1 for padding), group after group."""
+    out = []
+    for w in GROUP_WIDTHS:
+        cols = np.nonzero(bits_e == w)[0]
+        pad = (-cols.size) % GROUP_SLOTS
+        out.append(np.concatenate([cols, np.full(pad, -1)]))
+    return np.concatenate(out).astype(np.int64)
+
+
+def _plane_words(Q: np.ndarray, w: int, n_seg: int) -> np.ndarray:
+    """Segment records of one width group: n_seg x (nb * 4 * w) uint32.
+
+    Q: (4 nb) x dout_pad codes (w <= 8) or fp16 bit patterns (w = 16),
+    one row per slot of the group.
+    """
+    nb = Q.shape[0] // 4
+    if w == 16:
+        # [beta][pair h][low/high][seg][octet i][rho]
+        F = Q.astype(np.uint32).reshape(nb, 2, 2, n_seg, 4, 8)
+        word = F[:, :, 0] | (F[:, :, 1] << 16)            # beta, h, seg, i, rho
+        return np.ascontiguousarray(word.transpose(2, 0, 3, 4, 1)).reshape(n_seg, nb * 64)
+    # [beta][u][seg][octet i][rho]
+    V = Q.astype(np.uint32).reshape(nb, 4, n_seg, 4, 8)
+    rho = np.arange(8).reshape(1, 1, 1, 1, 8)
+    u = np.arange(4).reshape(1, 4, 1, 1, 1)
+    sh = nibble_shift(rho, u).astype(np.uint32)
+    planes = []
+    for j in range(w):
+        bit = (V >> j) & 1
+        planes.append(np.bitwise_or.reduce(bit << sh, axis=(1, 4)))  # beta, seg, i
+    P = np.stack(planes, axis=-1)                          # beta, seg, i, j
+    return np.ascontiguousarray(P.transpose(1, 0, 2, 3)).reshape(n_seg, nb * 4 * w)
 
 
 def pack(p: np.ndarray, a: np.ndarray, bits: np.ndarray) -> bytes:
@@ -79,9 +133,12 @@ def pack(p: np.ndarray, a: np.ndarray, bits: np.ndarray) -> bytes:
     p: E x r x dout float32 unit columns, a: E x r float32, bits: E x r.
     """
     E, r, dout = p.shape
-    dout_pad = _al(dout, 64)
-    n_slabs = dout_pad // 64
-    lays = [_block_layout(bits[e], n_slabs, dout_pad) for e in range(E)]
+    dout_pad = _al(dout, SEG_ROWS)
+    n_seg = dout_pad // SEG_ROWS
+    lays = []
+    for e in range(E):
+        cnt = [int(np.count_nonzero(bits[e] == w)) for w in GROUP_WIDTHS]
+        lays.append(_block_layout(cnt, n_seg))
     first = _al(HEADER_BYTES + DIR_REC * E, 256)
     offs = []
     pos = first
@@ -93,44 +150,47 @@ def pack(p: np.ndarray, a: np.ndarray, bits: np.ndarray) -> bytes:
     for e in range(E):
         L = lays[e]
         base = offs[e]
-        order = _column_order(bits[e])
+        slots = _slots(bits[e])
+        real = slots >= 0
+        ks = np.where(real, slots, 0)
         qe = quantize_expert(p[e], bits[e])
-        struct.pack_into("<QIIIIIIIIII", buf, HEADER_BYTES + DIR_REC * e,
-                         base, L["n_nz"], L["n_q"], L["n_16"], L["mps"],
+        a_s = np.where(real, a[e][ks], np.float32(0)).astype("<f4")
+        qs = L["n_qslot"]
+        s_s = np.where(real[:qs], qe["s"][ks[:qs]], np.float16(0)).astype("<f2")
+        m_s = np.where(real[:qs], qe["m"][ks[:qs]], np.float16(0)).astype("<f2")
+        # coefficient bound: |a| * s (float32 product) or |a| for 16-bit columns
+        cmax = np.float32(0)
+        if real[:qs].any():
+            cmax = max(cmax, np.max(np.abs(a_s[:qs][real[:qs]]) *
+                                    s_s[real[:qs]].astype(np.float32)))
+        if real[qs:].any():
+            cmax = max(cmax, np.max(np.abs(a_s[qs:][real[qs:]])))
+        struct.pack_into("<QIIIIIIIIfI", buf, HEADER_BYTES + DIR_REC * e,
+                         base, L["n_nz"], L["n_q"], L["n_16"], L["seg_words"],
                          L["a_off"], L["s_off"], L["m_off"], L["p_off"],
-                         L["f_off"], L["nbytes"])
+                         float(cmax), L["nbytes"])
         struct.pack_into("<7H", buf, HEADER_BYTES + DIR_REC * e + 48, *L["cnt"])
-        n_nz, n_q = L["n_nz"], L["n_q"]
-        buf[base:base + 2 * n_nz] = order.astype("<u2").tobytes()
-        buf[base + L["a_off"]:base + L["a_off"] + 4 * n_nz] = \
-            a[e][order].astype("<f4").tobytes()
-        qorder = order[:n_q]
-        buf[base + L["s_off"]:base + L["s_off"] + 2 * n_q] = qe["s"][qorder].astype("<f2").tobytes()
-        buf[base + L["m_off"]:base + L["m_off"] + 2 * n_q] = qe["m"][qorder].astype("<f2").tobytes()
-        # bit planes: codes padded to dout_pad rows
-        planes = np.zeros((n_slabs, L["mps"]), dtype="<u8")
-        col = 0
-        for w in GROUP_WIDTHS[:-1]:
-            g = np.nonzero(bits[e] == w)[0]
-            if g.size == 0:
+        n_slot = L["n_slot"]
+        buf[base:base + 2 * n_slot] = ks.astype("<u2").tobytes()
+        buf[base + L["a_off"]:base + L["a_off"] + 4 * n_slot] = a_s.tobytes()
+        buf[base + L["s_off"]:base + L["s_off"] + 2 * qs] = s_s.tobytes()
+        buf[base + L["m_off"]:base + L["m_off"] + 2 * qs] = m_s.tobytes()
+        planes = np.zeros((n_seg, L["seg_words"]), dtype="<u4")
+        col = 0   # word offset inside a segment record
+        sl = 0    # first slot of the group
+        for w, nb in zip(GROUP_WIDTHS, L["nb"]):
+            if nb == 0:
                 continue
-            Q = np.zeros((g.size, dout_pad), dtype=np.uint16)
-            Q[:, :dout] = qe["q"][g]
-            for j in range(w):
-                bj = ((Q >> j) & 1).astype(np.uint8).reshape(g.size, n_slabs, 64)
-                packed = np.packbits(bj, axis=2, bitorder="little")  # g x slabs x 8
-                words = packed.reshape(g.size, n_slabs * 8).view("<u8").reshape(g.size, n_slabs)
-                planes[:, col + j:col + w * g.size:w] = words.T
-            col += w * g.size
-        assert col == L["mps"]
+            gs = slots[sl:sl + 4 * nb]
+            Q = np.zeros((4 * nb, dout_pad), dtype=np.uint16)
+            Q[gs >= 0, :dout] = qe["q"][gs[gs >= 0]]
+            planes[:, col:col + 4 * w * nb] = _plane_words(Q, w, n_seg)
+            col += 4 * w * nb
+            sl += 4 * nb
+        assert col == L["seg_words"]
         buf[base + L["p_off"]:base + L["p_off"] + planes.nbytes] = planes.tobytes()
-        g16 = np.nonzero(bits[e] == 16)[0]
-        if g16.size:
-            F = np.zeros((g16.size, dout_pad), dtype="<u2")
-            F[:, :dout] = qe["q"][g16]
-            buf[base + L["f_off"]:base + L["f_off"] + F.nbytes] = F.tobytes()
     struct.pack_into("<4sIIIIIII", buf, 0, MAGIC, VERSION, E, dout, r,
-                     dout_pad, n_slabs, HEADER_BYTES)
+                     dout_pad, n_seg, HEADER_BYTES)
     struct.pack_into("<QQ", buf, 32, total, HEADER_BYTES)
     struct.pack_into("<I", buf, 48, zlib.crc32(memoryview(buf)[HEADER_BYTES:]) & 0xFFFFFFFF)
     return bytes(buf)
@@ -138,61 +198,89 @@ def pack(p: np.ndarray, a: np.ndarray, bits: np.ndarray) -> bytes:
 
 def read_header(blob) -> dict:
     mv = memoryview(blob)
-    magic, ver, E, dout, r, dout_pad, n_slabs, hb = struct.unpack_from("<4sIIIIIII", mv, 0)
+    magic, ver, E, dout, r, dout_pad, n_seg, hb = struct.unpack_from("<4sIIIIIII", mv, 0)
     total, dir_off = struct.unpack_from("<QQ", mv, 32)
     crc, = struct.unpack_from("<I", mv, 48)
     return dict(magic=magic, version=ver, E=E, dout=dout, r=r, dout_pad=dout_pad,
-                n_slabs=n_slabs, header_bytes=hb, total_bytes=total,
+                n_seg=n_seg, header_bytes=hb, total_bytes=total,
                 dir_offset=dir_off, crc32=crc)
+
+
+def read_dir(blob, e: int) -> dict:
+    H = read_header(blob)
+    off = H["dir_offset"] + DIR_REC * e
+    (base, n_nz, n_q, n_16, seg_words, a_off, s_off, m_off, p_off, cmax,
+     nbytes) = struct.unpack_from("<QIIIIIIIIfI", blob, off)
+    cnt = struct.unpack_from("<7H", blob, off + 48)
+    return dict(block_offset=base, n_nz=n_nz, n_q=n_q, n_16=n_16, seg_words=seg_words,
+                a_off=a_off, s_off=s_off, m_off=m_off, p_off=p_off, cmax=cmax,
+                block_bytes=nbytes, count=cnt)
+
+
+def _plane_codes(words: np.ndarray, w: int, nb: int, n_seg: int) -> np.ndarray:
+    """Inverse of _plane_words: (4 nb) x dout_pad codes / fp16 bit patterns."""
+    if w == 16:
+        Wd = words.reshape(n_seg, nb, 4, 8, 2)             # seg, beta, i, rho, h
+        lo = (Wd & 0xFFFF).astype(np.uint16)
+        hi = (Wd >> 16).astype(np.uint16)
+        F = np.stack([lo, hi], axis=-1)                    # seg, beta, i, rho, h, lh
+        return np.ascontiguousarray(F.transpose(1, 4, 5, 0, 2, 3)).reshape(4 * nb, n_seg * 32)
+    Wd = words.reshape(n_seg, nb, 4, w)                    # seg, beta, i, j
+    Q = np.zeros((nb, 4, n_seg, 4, 8), dtype=np.uint16)    # beta, u, seg, i, rho
+    for j in range(w):
+        pj = Wd[:, :, :, j].transpose(1, 0, 2)             # beta, seg, i
+        for u in range(4):
+            for rho in range(8):
+                bit = (pj >> nibble_shift(rho, u)) & 1
+                Q[:, u, :, :, rho] |= (bit.astype(np.uint16) << j)
+    return Q.reshape(4 * nb, n_seg * 32)
 
 
 def unpack(blob) -> dict:
     """Read codes back: returns dict with per-expert arrays in k order.
 
     'q'   E x r x dout uint16 (codes; fp16 bit patterns for b = 16; 0 for b = 0)
-    's','m' E x r float16, 'a' E x r float32 (0 for b = 0), 'bits' E x r uint8
+    's','m' E x r float16, 'a' E x r float32 (0 for b = 0), 'bits' E x r uint8,
+    'cmax' E float32 (the directory's coefficient bound)
     """
     H = read_header(blob)
     if H["magic"] != MAGIC or H["version"] != VERSION:
-        raise ValueError("not a v1 BMOE blob")
+        raise ValueError("not a v2 BMOE blob")
     if zlib.crc32(memoryview(blob)[HEADER_BYTES:H["total_bytes"]]) & 0xFFFFFFFF != H["crc32"]:
         raise ValueError("CRC mismatch")
-    E, r, dout, dp, ns = H["E"], H["r"], H["dout"], H["dout_pad"], H["n_slabs"]
+    E, r, dout, dp, ns = H["E"], H["r"], H["dout"], H["dout_pad"], H["n_seg"]
     q = np.zeros((E, r, dout), dtype=np.uint16)
     s = np.ones((E, r), dtype=np.float16)
     m = np.zeros((E, r), dtype=np.float16)
     a = np.zeros((E, r), dtype=np.float32)
     bits = np.zeros((E, r), dtype=np.uint8)
+    cmax = np.zeros(E, dtype=np.float32)
     buf = np.frombuffer(blob, dtype=np.uint8)
     for e in range(E):
-        (base, n_nz, n_q, n_16, mps, a_off, s_off, m_off, p_off, f_off,
-         nbytes) = struct.unpack_from("<QIIIIIIIIII", blob, H["dir_offset"] + DIR_REC * e)
-        cnt = struct.unpack_from("<7H", blob, H["dir_offset"] + DIR_REC * e + 48)
-        order = buf[base:base + 2 * n_nz].view("<u2").astype(np.int64)
-        a[e, order] = buf[base + a_off:base + a_off + 4 * n_nz].view("<f4")
-        qo = order[:n_q]
-        s[e, qo] = buf[base + s_off:base + s_off + 2 * n_q].view("<f2")
-        m[e, qo] = buf[base + m_off:base + m_off + 2 * n_q].view("<f2")
-        planes = buf[base + p_off:base + p_off + 8 * ns * mps].view("<u8").reshape(ns, mps)
+        D = read_dir(blob, e)
+        cmax[e] = D["cmax"]
+        L = _block_layout(list(D["count"]), ns)
+        base = D["block_offset"]
+        n_slot, qs = L["n_slot"], L["n_qslot"]
+        kidx = buf[base:base + 2 * n_slot].view("<u2").astype(np.int64)
+        a_s = buf[base + D["a_off"]:base + D["a_off"] + 4 * n_slot].view("<f4")
+        s_s = buf[base + D["s_off"]:base + D["s_off"] + 2 * qs].view("<f2")
+        m_s = buf[base + D["m_off"]:base + D["m_off"] + 2 * qs].view("<f2")
+        planes = buf[base + D["p_off"]:base + D["p_off"] + 4 * ns * L["seg_words"]]
+        planes = planes.view("<u4").reshape(ns, L["seg_words"])
         col = 0
-        ci = 0
-        for w, c in zip(GROUP_WIDTHS, cnt):
-            ks = order[ci:ci + c]
-            ci += c
-            if c == 0:
+        sl = 0
+        for w, c, nb in zip(GROUP_WIDTHS, D["count"], L["nb"]):
+            if nb == 0:
                 continue
+            ks = kidx[sl:sl + c]
             bits[e, ks] = w
-            if w == 16:
-                continue
-            Q = np.zeros((c, dp), dtype=np.uint16)
-            for j in range(w):
-                words = np.ascontiguousarray(planes[:, col + j:col + w * c:w].T)  # c x ns
-                bj = np.unpackbits(words.view(np.uint8).reshape(c, ns, 8), axis=2,
-                                   bitorder="little").reshape(c, dp)
-                Q |= (bj.astype(np.uint16) << j)
-            q[e, ks] = Q[:, :dout]
-            col += w * c
-        if n_16:
-            F = buf[base + f_off:base + f_off + 2 * n_16 * dp].view("<u2").reshape(n_16, dp)
-            q[e, order[n_q:]] = F[:, :dout]
-    return dict(header=H, q=q, s=s, m=m, a=a, bits=bits)
+            a[e, ks] = a_s[sl:sl + c]
+            if w != 16:
+                s[e, ks] = s_s[sl:sl + c]
+                m[e, ks] = m_s[sl:sl + c]
+            Q = _plane_codes(planes[:, col:col + 4 * w * nb], w, nb, ns)
+            q[e, ks] = Q[:c, :dout]
+            col += 4 * w * nb
+            sl += 4 * nb
+    return dict(header=H, q=q, s=s, m=m, a=a, bits=bits, cmax=cmax)

@@ -27,6 +27,13 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libbitsmoe.so is not built (%s); run "
                           "`python -m spectral_expert_gemv_amd.build`" % LIB_PATH)
+    # One HIP runtime per process: torch ships its own libamdhip64 under the
+    # same soname as ROCm's, and the library's launches must run in the
+    # runtime that owns torch's device memory and streams.  Importing torch
+    # first makes the library's libamdhip64.so.7 dependency resolve to
+    # torch's copy (loaded the other way round, the library's first launch
+    # finds no device).
+    import torch  # noqa: F401
     return ctypes.CDLL(LIB_PATH)
 
 

@@ -75,8 +75,10 @@ __global__ __launch_bounds__(kProjWaves * kWave) void k_proj_gemv(
 // time; each batch of x is copied into LDS once with 16-byte
 // global_load_lds and read by all 16 rows.  A wave's 16 dot products (4
 // rows x 4 tokens) are finished with a transpose reduction (17 lane
-// exchanges) and lanes 0-15 store them.  U: 16-byte x units per lane (din <=
-// 512 U).
+// exchanges) and lanes 0-15 store them.  When zpart is given, the
+// work-group also writes max |z| over its 16 rows per token (zpart[t * nzp
+// + group]), from which the grouped kernel sizes its fp16 coefficient
+// scale.  U: 16-byte x units per lane (din <= 512 U).
 // ---------------------------------------------------------------------------
 constexpr int kPRW = 4;     // Phi^T rows per wave
 constexpr int kPT = 4;      // tokens per batch
@@ -97,8 +99,9 @@ __device__ __forceinline__ void pstep(float (&v)[kPRW * kPT], bool up) {
 template <int U>
 __global__ __launch_bounds__(kProjWaves * kWave) void k_proj_rows(
     const uint4* __restrict__ phi_t, const uint4* __restrict__ x, float* __restrict__ z,
-    int T, int din8, int R) {
+    float* __restrict__ zpart, int T, int din8, int R) {
   __shared__ __align__(16) uint4 xs[kPT][kPMaxU * kWave];
+  __shared__ float wmx[kProjWaves][kPT];
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * kProjWaves + wv) * kPRW;
@@ -148,123 +151,137 @@ __global__ __launch_bounds__(kProjWaves * kWave) void k_proj_rows(
       const int i = lane / kPT, tt = lane % kPT;
       if (n0 + i < R && t0 + tt < T) z[(size_t)(t0 + tt) * R + n0 + i] = sum;
     }
+    if (zpart) {
+      float m = lane < kPRW * kPT ? fabsf(sum) : 0.f;
+      m = fmaxf(m, __shfl_xor(m, 4, kWave));
+      m = fmaxf(m, __shfl_xor(m, 8, kWave));
+      if (lane < kPT) wmx[wv][lane] = m;
+      __syncthreads();
+      const int tt = threadIdx.x;
+      if (tt < kPT && t0 + tt < T) {
+        const float mm = fmaxf(fmaxf(wmx[0][tt], wmx[1][tt]), fmaxf(wmx[2][tt], wmx[3][tt]));
+        zpart[(size_t)(t0 + tt) * gridDim.x + blockIdx.x] = mm;
+      }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Expert apply over one 64-row slab, lane = row.  For every stored column
-// (width groups 1..8 then 16, ascending k inside a group):
+// Expert apply over one 32-row segment, lane = row (a wave covers two
+// segments).  For every slot (width groups 1..8 then 16, ascending k inside
+// a group, zero padding slots contribute nothing):
 //   y += (a z s) q + (a z m)     for 1..8-bit columns
 //   y += (a z) p16               for 16-bit columns.
 // Returns false when the blob or the expert id cannot be used.
 // ---------------------------------------------------------------------------
-__device__ float apply_slab(const uint8_t* __restrict__ blob, uint64_t blob_bytes, int e,
-                            int E, int dout, int r, const float* __restrict__ zrow,
-                            int slab, int lane, bool& ok) {
+__device__ float apply_seg(const uint8_t* __restrict__ blob, uint64_t blob_bytes, int e, int E,
+                           int dout, int r, const float* __restrict__ zrow, int seg, int row,
+                           bool& ok) {
   DirRec d;
   if (!load_dir(blob, blob_bytes, e, E, dout, r, d)) {
     ok = false;
     return 0.f;
   }
-  const uint32_t dout_pad = reinterpret_cast<const Header*>(blob)->dout_pad;
   const uint8_t* blk = blob + d.block_offset;
   const uint16_t* kidx = reinterpret_cast<const uint16_t*>(blk);
   const float* A = reinterpret_cast<const float*>(blk + d.a_off);
   const __half* S = reinterpret_cast<const __half*>(blk + d.s_off);
   const __half* M = reinterpret_cast<const __half*>(blk + d.m_off);
-  const uint64_t* P =
-      reinterpret_cast<const uint64_t*>(blk + d.planes_off) + (size_t)slab * d.masks_per_slab;
+  const uint32_t* rec =
+      reinterpret_cast<const uint32_t*>(blk + d.planes_off) + (size_t)seg * d.seg_words;
+  const SlotGeo geo = slot_geo(d.count);
   float acc = 0.f, bias = 0.f;
-  uint32_t col = 0, w = 0;
+  uint32_t slot = 0, word = 0;
   bool good = true;
-  for (int g = 0; g < kNumQGroups; ++g) {
-    const int b = kGroupWidth[g];
-    const uint32_t n = d.count[g];
-    for (uint32_t c = 0; c < n; ++c, ++col, w += b) {
-      uint32_t k = kidx[col];
-      good &= k < (uint32_t)r;
-      k = k < (uint32_t)r ? k : 0;
-      const float az = A[col] * zrow[k];
-      bias += az * __half2float(M[col]);
-      const uint32_t q = decode_code(P + w, b, lane);
-      acc += (az * __half2float(S[col])) * (float)q;
+  for (int g = 0; g < kNumGroups; ++g) {
+    const int w = kGroupWidth[g];
+    for (uint32_t b = 0; b < geo.nb[g]; ++b, slot += 4, word += 4u * w) {
+      for (int u = 0; u < 4; ++u) {
+        uint32_t k = kidx[slot + u];
+        good &= k < (uint32_t)r;
+        k = k < (uint32_t)r ? k : 0;
+        const float az = A[slot + u] * zrow[k];
+        if (w == 16) {
+          acc += az * __half2float(__ushort_as_half((unsigned short)decode_f16(rec + word, row, u)));
+        } else {
+          bias += az * __half2float(M[slot + u]);
+          acc += (az * __half2float(S[slot + u])) * (float)decode_code(rec + word, w, row, u);
+        }
+      }
     }
-  }
-  const __half* F = reinterpret_cast<const __half*>(blk + d.f16_off);
-  for (uint32_t c = 0; c < d.n_16; ++c, ++col) {
-    uint32_t k = kidx[col];
-    good &= k < (uint32_t)r;
-    k = k < (uint32_t)r ? k : 0;
-    acc += (A[col] * zrow[k]) * __half2float(F[(size_t)c * dout_pad + (size_t)slab * 64 + lane]);
   }
   ok = good;
   return acc + bias;
 }
 
-// grid (T*k, n_slabs); block 64 (apply) or 128 (gate wave + up wave).
+// grid (T*k, ceil(n_seg / 2)); block 64 (apply) or 128 (gate wave + up wave).
 template <bool kGateUp>
-__global__ __launch_bounds__(kGateUp ? 128 : 64) void k_expert_slab(
+__global__ __launch_bounds__(kGateUp ? 128 : 64) void k_expert_seg(
     const uint8_t* __restrict__ blob_g, uint64_t bytes_g, const uint8_t* __restrict__ blob_u,
     uint64_t bytes_u, int E, int dout, int r, const float* __restrict__ z, int z_stride,
     int z_off_up, const int32_t* __restrict__ ids, int ktop, float* __restrict__ out) {
   const int pair = blockIdx.x;
-  const int slab = blockIdx.y;
-  const int t = pair / ktop;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
+  const int seg = 2 * (int)blockIdx.y + (lane >> 5);
+  const int row = lane & 31;
+  const int orow = seg * kSegRows + row;
+  const int t = pair / ktop;
   const int e = ids[pair];
   bool ok = true;
   const uint8_t* blob = wv ? blob_u : blob_g;
   const uint64_t bytes = wv ? bytes_u : bytes_g;
   const float* zrow = z + (size_t)t * z_stride + (wv ? z_off_up : 0);
-  const float y = apply_slab(blob, bytes, e, E, dout, r, zrow, slab, lane, ok);
-  const int row = slab * 64 + lane;
+  const bool live = orow < dout;
+  const float y = live ? apply_seg(blob, bytes, e, E, dout, r, zrow, seg, row, ok) : 0.f;
   if (!kGateUp) {
-    if (row < dout) out[(size_t)pair * dout + row] = ok ? y : __builtin_nanf("");
+    if (live) out[(size_t)pair * dout + orow] = ok ? y : __builtin_nanf("");
     return;
   }
   __shared__ float s_y[kWave];
-  __shared__ int s_ok;
-  if (threadIdx.x == 64) s_ok = ok;
-  if (wv == 1) s_y[lane] = y;
+  __shared__ int s_ok[kWave];
+  if (wv == 1) {
+    s_y[lane] = y;
+    s_ok[lane] = ok;
+  }
   __syncthreads();
-  if (wv == 0 && row < dout)
-    out[(size_t)pair * dout + row] = (ok && s_ok) ? silu_mul(y, s_y[lane]) : __builtin_nanf("");
+  if (wv == 0 && live)
+    out[(size_t)pair * dout + orow] =
+        (ok && s_ok[lane]) ? silu_mul(y, s_y[lane]) : __builtin_nanf("");
 }
 
-// grid (n_slabs); block 64: codes of expert e in k order (0-bit columns are
-// left as the caller's zero fill).
+// grid (ceil(n_seg / 2)); block 64: codes of expert e in k order (0-bit
+// columns are left as the caller's zero fill; padding slots are skipped).
 __global__ __launch_bounds__(64) void k_dump_codes(const uint8_t* __restrict__ blob,
                                                    uint64_t blob_bytes, int E, int dout, int r,
                                                    int e, uint16_t* __restrict__ codes) {
   DirRec d;
-  const int slab = blockIdx.x;
   const int lane = threadIdx.x;
-  const int row = slab * 64 + lane;
+  const int seg = 2 * (int)blockIdx.x + (lane >> 5);
+  const int row = lane & 31;
+  const int orow = seg * kSegRows + row;
+  if (orow >= dout) return;
   if (!load_dir(blob, blob_bytes, e, E, dout, r, d)) {
-    if (row < dout)
-      for (int k = 0; k < r; ++k) codes[(size_t)k * dout + row] = 0xFFFFu;
+    for (int k = 0; k < r; ++k) codes[(size_t)k * dout + orow] = 0xFFFFu;
     return;
   }
-  const uint32_t dout_pad = reinterpret_cast<const Header*>(blob)->dout_pad;
   const uint8_t* blk = blob + d.block_offset;
   const uint16_t* kidx = reinterpret_cast<const uint16_t*>(blk);
-  const uint64_t* P =
-      reinterpret_cast<const uint64_t*>(blk + d.planes_off) + (size_t)slab * d.masks_per_slab;
-  uint32_t col = 0, w = 0;
-  for (int g = 0; g < kNumQGroups; ++g) {
-    const int b = kGroupWidth[g];
-    for (uint32_t c = 0; c < d.count[g]; ++c, ++col, w += b) {
-      const uint32_t q = decode_code(P + w, b, lane);
-      const uint32_t k = kidx[col];
-      if (row < dout && k < (uint32_t)r) codes[(size_t)k * dout + row] = (uint16_t)q;
+  const uint32_t* rec =
+      reinterpret_cast<const uint32_t*>(blk + d.planes_off) + (size_t)seg * d.seg_words;
+  const SlotGeo geo = slot_geo(d.count);
+  uint32_t slot = 0, word = 0;
+  for (int g = 0; g < kNumGroups; ++g) {
+    const int w = kGroupWidth[g];
+    for (uint32_t b = 0; b < geo.nb[g]; ++b, slot += 4, word += 4u * w) {
+      for (int u = 0; u < 4; ++u) {
+        if (4 * b + u >= d.count[g]) continue;  // padding slot
+        const uint32_t k = kidx[slot + u];
+        const uint32_t q = w == 16 ? decode_f16(rec + word, row, u)
+                                   : decode_code(rec + word, w, row, u);
+        if (k < (uint32_t)r) codes[(size_t)k * dout + orow] = (uint16_t)q;
+      }
     }
-  }
-  const uint16_t* F = reinterpret_cast<const uint16_t*>(blk + d.f16_off);
-  for (uint32_t c = 0; c < d.n_16; ++c, ++col) {
-    const uint32_t k = kidx[col];
-    if (row < dout && k < (uint32_t)r)
-      codes[(size_t)k * dout + row] = F[(size_t)c * dout_pad + row];
   }
 }
 
@@ -313,7 +330,9 @@ int proj_args(const void* phi, const void* x, const float* z, int T, int din, in
   return BITSMOE_OK;
 }
 
-int launch_proj(const void* phi, const void* x, float* z, int T, int din, int R,
+// z = Phi^T x; zpart (may be null; din <= 4096 only) gets max |z| per
+// 16-row work-group and token.
+int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, int din, int R,
                 hipStream_t s) {
   const int din8 = din / 8;
   const dim3 grid_rows((R + kProjWaves * kPRW - 1) / (kProjWaves * kPRW));
@@ -321,13 +340,13 @@ int launch_proj(const void* phi, const void* x, float* z, int T, int din, int R,
   const uint4* p4 = (const uint4*)phi;
   const uint4* x4 = (const uint4*)x;
   if (din8 <= kWave)
-    hipLaunchKernelGGL(k_proj_rows<1>, grid_rows, block, 0, s, p4, x4, z, T, din8, R);
+    hipLaunchKernelGGL(k_proj_rows<1>, grid_rows, block, 0, s, p4, x4, z, zpart, T, din8, R);
   else if (din8 <= 2 * kWave)
-    hipLaunchKernelGGL(k_proj_rows<2>, grid_rows, block, 0, s, p4, x4, z, T, din8, R);
+    hipLaunchKernelGGL(k_proj_rows<2>, grid_rows, block, 0, s, p4, x4, z, zpart, T, din8, R);
   else if (din8 <= 4 * kWave)
-    hipLaunchKernelGGL(k_proj_rows<4>, grid_rows, block, 0, s, p4, x4, z, T, din8, R);
+    hipLaunchKernelGGL(k_proj_rows<4>, grid_rows, block, 0, s, p4, x4, z, zpart, T, din8, R);
   else if (din8 <= kPMaxU * kWave)
-    hipLaunchKernelGGL(k_proj_rows<8>, grid_rows, block, 0, s, p4, x4, z, T, din8, R);
+    hipLaunchKernelGGL(k_proj_rows<8>, grid_rows, block, 0, s, p4, x4, z, zpart, T, din8, R);
   else
     hipLaunchKernelGGL(k_proj_gemv, dim3((R + kProjWaves - 1) / kProjWaves), block, 0, s, p4,
                        x4, z, T, din8, R);
@@ -337,15 +356,23 @@ int launch_proj(const void* phi, const void* x, float* z, int T, int din, int R,
 
 }  // namespace
 
+int tile_cap(int T, int k, int E) {
+  const long long P = (long long)T * k;
+  const long long g = P < E ? P : E;
+  const long long cap = g + (P + kTile - 1) / kTile;
+  return (int)((cap + 7) / 8 * 8);
+}
+
 GateUpPlan gateup_plan(int T, int k, int E, int r) {
   GateUpPlan p;
   const size_t P = (size_t)T * k;
-  const size_t gmax = P < (size_t)E ? P : (size_t)E;
+  const size_t nzp = ((size_t)2 * r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
   p.z_off = 0;
-  p.zt_off = align_up((size_t)T * 2 * r * sizeof(float), 256);
+  p.zpart_off = align_up((size_t)T * 2 * r * sizeof(float), 256);
+  p.zt_off = align_up(p.zpart_off + (size_t)T * nzp * sizeof(float), 256);
   p.sync_off = align_up(p.zt_off + (size_t)T * 2 * r * sizeof(uint64_t), 256);
   p.route_off = align_up(p.sync_off + 2 * sizeof(uint32_t), 256);
-  p.total = align_up(p.route_off + (1 + gmax + gmax + 1 + P) * sizeof(int), 256);
+  p.total = align_up(p.route_off + (1 + 3 * (size_t)tile_cap(T, k, E) + P) * sizeof(int), 256);
   return p;
 }
 
@@ -359,7 +386,7 @@ int bitsmoe_spectral_proj(const void* phi_t_f16, const void* x_f16, float* z, in
                           int r_total, bitsmoe_stream_t stream) {
   int st = proj_args(phi_t_f16, x_f16, z, T, din, r_total);
   if (st) return st;
-  return launch_proj(phi_t_f16, x_f16, z, T, din, r_total, (hipStream_t)stream);
+  return launch_proj(phi_t_f16, x_f16, z, nullptr, T, din, r_total, (hipStream_t)stream);
 }
 
 int bitsmoe_expert_apply(const void* packed, size_t packed_bytes, int E, int dout, int r,
@@ -377,8 +404,8 @@ int bitsmoe_expert_apply(const void* packed, size_t packed_bytes, int E, int dou
   if (z_stride < r) return fail(BITSMOE_ESHAPE, "z_stride=%d < r=%d", z_stride, r);
   if ((long long)T * k > (1LL << 24))
     return fail(BITSMOE_ESHAPE, "T*k=%lld too large", (long long)T * k);
-  const int n_slabs = (dout + 63) / 64;
-  hipLaunchKernelGGL(k_expert_slab<false>, dim3(T * k, n_slabs), dim3(64), 0,
+  const int n_pairs_seg = (dout + 2 * kSegRows - 1) / (2 * kSegRows);
+  hipLaunchKernelGGL(k_expert_seg<false>, dim3(T * k, n_pairs_seg), dim3(64), 0,
                      (hipStream_t)stream, (const uint8_t*)packed, (uint64_t)packed_bytes,
                      (const uint8_t*)packed, (uint64_t)packed_bytes, E, dout, r, z, z_stride, 0,
                      ids, k, y);
@@ -416,8 +443,8 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   if (ws_bytes < need) return fail(BITSMOE_ENOSPC, "ws_bytes=%zu < %zu", ws_bytes, need);
   const GateUpPlan plan = gateup_plan(T, k, E, r);
   hipStream_t s = (hipStream_t)stream;
-  StagedArgs sa;
-  GateUpArgs& a = sa.g;
+  uint8_t* wsb = (uint8_t*)ws;
+  GateUpArgs a;
   a.blob_g = (const uint8_t*)packed_gate;
   a.blob_u = (const uint8_t*)packed_up;
   a.bytes_g = gate_bytes;
@@ -429,45 +456,49 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   a.ktop = k;
   a.npairs = T * k;
   a.h = h;
-  a.n_slabs = (dout + 63) / 64;
-  sa.T = T;
-  sa.z = (const float*)((uint8_t*)ws + plan.z_off);
+  a.n_seg = (dout + kSegRows - 1) / kSegRows;
+  float* z = (float*)(wsb + plan.z_off);
   // One launch when every work-group can be resident at once (the groups
-  // wait for each other's z); otherwise z first, then the expert kernel.
-  const int hgrid = half_grid();
-  if (T <= kHalfMaxTokens && r <= kHalfMaxR && hgrid > 0) {
-    HalfArgs ha;
-    ha.g = a;
-    ha.phi_t = (const uint4*)phi_t_gateup_f16;
-    ha.x = (const uint4*)x_f16;
-    ha.din8 = din / 8;
-    ha.T = T;
-    ha.zt = (uint64_t*)((uint8_t*)ws + plan.zt_off);
-    ha.epoch = (uint32_t*)((uint8_t*)ws + plan.sync_off);
-    ha.arrive = ha.epoch + 1;
-    ha.grid = hgrid;
-    launch_gateup_half(ha, s);
+  // wait for each other's z); otherwise z first, then the expert kernels.
+  const int fgrid = fused_grid();
+  if (T <= kFusedMaxTokens && r <= kFusedMaxR && fgrid > 0) {
+    FusedArgs fa;
+    fa.g = a;
+    fa.phi_t = (const uint4*)phi_t_gateup_f16;
+    fa.x = (const uint4*)x_f16;
+    fa.din8 = din / 8;
+    fa.T = T;
+    fa.zt = (uint64_t*)(wsb + plan.zt_off);
+    fa.epoch = (uint32_t*)(wsb + plan.sync_off);
+    fa.arrive = fa.epoch + 1;
+    fa.grid = fgrid;
+    launch_gateup_fused(fa, s);
     return launch_status("one-launch gate/up");
   }
-  if ((st = launch_proj(phi_t_gateup_f16, x_f16, (float*)sa.z, T, din, 2 * r, s))) return st;
-  if (r <= kGroupMaxR && r % 2 == 0 && E <= kGroupMaxE && grouped_tokens_per_batch(r) > 0) {
-    // batched tokens: pairs grouped by expert, each expert's planes read once
+  const bool grouped = r <= kGroupMaxR && E <= kGroupMaxE && din <= kGroupMaxDin;
+  float* zpart = grouped ? (float*)(wsb + plan.zpart_off) : nullptr;
+  if ((st = launch_proj(phi_t_gateup_f16, x_f16, z, zpart, T, din, 2 * r, s))) return st;
+  if (grouped) {
+    // batched tokens: pairs grouped by expert, each expert's planes read and
+    // unpacked once per tile of up to 16 tokens
     GroupArgs gs;
     gs.g = a;
-    gs.z = sa.z;
-    const long long P = (long long)T * k;
-    gs.gmax = (int)(P < E ? P : E);
-    int* rb = (int*)((uint8_t*)ws + plan.route_off);
-    gs.rl.ngroups = rb;
-    gs.rl.gexp = rb + 1;
-    gs.rl.goff = rb + 1 + gs.gmax;
-    gs.rl.pairs = rb + 1 + 2 * gs.gmax + 1;
-    launch_route_group(ids, (int)P, E, dout, h, gs.rl, s);
+    gs.z = z;
+    gs.zpart = zpart;
+    gs.nzp = (2 * r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
+    gs.tcap = tile_cap(T, k, E);
+    int* rb = (int*)(wsb + plan.route_off);
+    gs.rl.ntiles = rb;
+    gs.rl.tile = rb + 1;
+    gs.rl.pairs = rb + 1 + 3 * gs.tcap;
+    launch_route_group(ids, T * k, E, dout, h, gs.rl, s);
     if ((st = launch_status("route grouping launch"))) return st;
     launch_gateup_grouped(gs, s);
     return launch_status("grouped gate/up launch");
   }
-  launch_gateup_staged(sa, s);
+  hipLaunchKernelGGL(k_expert_seg<true>,
+                     dim3(T * k, (a.n_seg + 1) / 2), dim3(128), 0, s, a.blob_g, a.bytes_g,
+                     a.blob_u, a.bytes_u, E, dout, r, (const float*)z, 2 * r, r, ids, k, h);
   return launch_status("gate/up expert launch");
 }
 
@@ -494,7 +525,7 @@ int bitsmoe_dump_codes(const void* packed, size_t packed_bytes, int E, int dout,
   if (e < 0 || e >= E) return fail(BITSMOE_EINVAL, "e=%d outside [0,%d)", e, E);
   hipStream_t s = (hipStream_t)stream;
   if ((st = bitsmoe_workspace_init(codes, (size_t)r * dout * 2, stream))) return st;
-  hipLaunchKernelGGL(k_dump_codes, dim3((dout + 63) / 64), dim3(64), 0, s,
+  hipLaunchKernelGGL(k_dump_codes, dim3((dout + 2 * kSegRows - 1) / (2 * kSegRows)), dim3(64), 0, s,
                      (const uint8_t*)packed, (uint64_t)packed_bytes, E, dout, r, e, codes);
   return launch_status("code dump launch");
 }

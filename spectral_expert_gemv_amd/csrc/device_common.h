@@ -1,5 +1,5 @@
 // Device-side helpers shared by the gfx950 kernels: blob directory access
-// with bounds checks, the bit-plane code decoder, wave reductions.
+// with bounds checks, the lane-per-row code decoder, wave reductions.
 #pragma once
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
@@ -13,7 +13,7 @@ constexpr int kWave = 64;
 
 // Header fields a directory record is checked against.
 struct HdrF {
-  uint32_t magic, version, E, dout, r, n_slabs;
+  uint32_t magic, version, E, dout, r, n_seg;
 };
 
 // Scalar loads (constant address space): the header is the same for all lanes.
@@ -26,7 +26,7 @@ __device__ inline HdrF load_hdr(const uint8_t* __restrict__ blob) {
   f.E = h->E;
   f.dout = h->dout;
   f.r = h->r;
-  f.n_slabs = h->n_slabs;
+  f.n_seg = h->n_seg;
   return f;
 }
 
@@ -46,26 +46,22 @@ __device__ inline bool check_dir(const HdrF& h, const DirRec& d, uint64_t blob_b
       h.dout != (uint32_t)dout || h.r != (uint32_t)r)
     return false;
   if (e < 0 || e >= E) return false;
-  const uint64_t n_slabs = h.n_slabs;
-  const uint64_t dout_pad = n_slabs * 64;
-  if (n_slabs != (uint64_t)((dout + 63) / 64)) return false;
+  const uint64_t n_seg = h.n_seg;
+  if (n_seg != (uint64_t)((dout + kSegRows - 1) / kSegRows)) return false;
   if (d.block_offset + d.block_bytes > blob_bytes) return false;
-  uint32_t n_nz = 0, mps = 0;
+  const SlotGeo g = slot_geo(d.count);
+  uint32_t n_nz = 0;
 #pragma unroll
-  for (int g = 0; g < kNumGroups; ++g) {
-    n_nz += d.count[g];
-    if (g < kNumQGroups) mps += (uint32_t)d.count[g] * kGroupWidth[g];
-  }
+  for (int i = 0; i < kNumGroups; ++i) n_nz += d.count[i];
   if (n_nz != d.n_nz || d.n_16 != d.count[kNumGroups - 1] || d.n_q + d.n_16 != n_nz ||
-      mps != d.masks_per_slab || n_nz > (uint32_t)r)
+      g.seg_words != d.seg_words || n_nz > (uint32_t)r)
     return false;
-  if ((uint64_t)d.a_off + 4ull * n_nz > d.block_bytes || 2ull * n_nz > d.a_off ||
-      (uint64_t)d.s_off + 2ull * d.n_q > d.block_bytes ||
-      (uint64_t)d.m_off + 2ull * d.n_q > d.block_bytes ||
-      (uint64_t)d.planes_off + 8ull * n_slabs * mps + 16 > d.f16_off ||
-      (uint64_t)d.f16_off + 2ull * d.n_16 * dout_pad > d.block_bytes ||
-      (d.a_off & 3u) || (d.s_off & 1u) || (d.m_off & 1u) || (d.planes_off & 7u) ||
-      (d.f16_off & 15u))
+  if (2ull * g.n_slot > d.a_off || (uint64_t)d.a_off + 4ull * g.n_slot > d.s_off ||
+      (uint64_t)d.s_off + 2ull * g.n_qslot > d.m_off ||
+      (uint64_t)d.m_off + 2ull * g.n_qslot > d.planes_off ||
+      (uint64_t)d.planes_off + 4ull * n_seg * g.seg_words + 16 > d.block_bytes ||
+      (d.a_off & 15u) || (d.s_off & 15u) || (d.m_off & 15u) || (d.planes_off & 15u) ||
+      (d.block_offset & 15u))
     return false;
   return true;
 }
@@ -77,13 +73,21 @@ __device__ inline bool load_dir(const uint8_t* __restrict__ blob, uint64_t blob_
   return check_dir(load_hdr(blob), d, blob_bytes, e, E, dout, r);
 }
 
-// Code of row `lane` of one 1..8-bit column in a 64-row slab: bit j comes
-// from plane j's 64-bit mask (bit `lane`).  Every kernel decodes codes with
-// this routine, including the code dump used by the bit-exact tests.
-__device__ inline uint32_t decode_code(const uint64_t* __restrict__ masks, int b, int lane) {
+// Code of segment row `row` (0..31) in slot u (0..3) of a block of width
+// w <= 8 whose record starts at `rec`: bit j from word (row / 8, j), bit
+// 4 (row % 8) + u.  Used by the lane-per-row kernels and the code dump.
+__device__ inline uint32_t decode_code(const uint32_t* __restrict__ rec, int w, int row, int u) {
+  const uint32_t* oct = rec + (row >> 3) * w;
+  const int sh = 4 * (row & 7) + u;
   uint32_t q = 0;
-  for (int j = 0; j < b; ++j) q |= (uint32_t)((masks[j] >> lane) & 1ull) << j;
+  for (int j = 0; j < w; ++j) q |= ((oct[j] >> sh) & 1u) << j;
   return q;
+}
+
+// fp16 bit pattern of segment row `row` in slot u of a 16-bit block.
+__device__ inline uint32_t decode_f16(const uint32_t* __restrict__ rec, int row, int u) {
+  const uint32_t wv = rec[(row >> 3) * 16 + 2 * (row & 7) + (u >> 1)];
+  return (u & 1) ? (wv >> 16) : (wv & 0xFFFFu);
 }
 
 __device__ inline float wave_sum(float v) {

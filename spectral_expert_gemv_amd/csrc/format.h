@@ -1,4 +1,4 @@
-// Packed blob format v1: constants and the directory record shared by the
+// Packed blob format v2: constants and the directory record shared by the
 // host packer, the host checker and the device kernels.  The layout is
 // documented in include/bitsmoe.h.
 #pragma once
@@ -13,7 +13,8 @@
 namespace bitsmoe {
 
 constexpr uint32_t kMagic = 0x454F4D42u;  // bytes 'B','M','O','E'
-constexpr uint32_t kVersion = 1;
+constexpr uint32_t kVersion = 2;
+constexpr int kSegRows = 32;                        // rows of one segment record
 constexpr uint32_t kHeaderBytes = 128;
 constexpr uint32_t kDirRecBytes = 64;
 constexpr int kNumGroups = 7;                       // widths 1,2,3,4,6,8,16
@@ -21,7 +22,7 @@ constexpr int kNumQGroups = 6;                      // widths 1..8
 constexpr int kGroupWidth[kNumGroups] = {1, 2, 3, 4, 6, 8, 16};
 
 struct Header {
-  uint32_t magic, version, E, dout, r, dout_pad, n_slabs, header_bytes;
+  uint32_t magic, version, E, dout, r, dout_pad, n_seg, header_bytes;
   uint64_t total_bytes, dir_offset;
   uint32_t crc32, reserved0;
   uint32_t pad[18];
@@ -30,8 +31,10 @@ static_assert(sizeof(Header) == 128, "header is 128 bytes");
 
 struct DirRec {
   uint64_t block_offset;
-  uint32_t n_nz, n_q, n_16, masks_per_slab;
-  uint32_t a_off, s_off, m_off, planes_off, f16_off, block_bytes;
+  uint32_t n_nz, n_q, n_16, seg_words;
+  uint32_t a_off, s_off, m_off, planes_off;
+  float cmax;  // max |a_k| s_k (1..8 bits) or |a_k| (16 bits) over stored columns
+  uint32_t block_bytes;
   uint16_t count[kNumGroups];
   uint16_t reserved;
 };
@@ -39,6 +42,27 @@ static_assert(sizeof(DirRec) == 64, "directory record is 64 bytes");
 
 BM_HD constexpr inline uint64_t align_up(uint64_t x, uint64_t a) {
   return (x + a - 1) / a * a;
+}
+
+constexpr uint32_t kGroupSlots = 32;  // width groups are padded to a multiple of this
+
+// Slot geometry of one expert, derived from its per-width column counts:
+// each width group is padded to a multiple of 32 slots (8 blocks of 4), so
+// that a 32-slot step never mixes two widths.
+struct SlotGeo {
+  uint32_t nb[kNumGroups];  // blocks per group
+  uint32_t n_slot, n_qslot, seg_words;
+};
+BM_HD inline SlotGeo slot_geo(const uint16_t count[kNumGroups]) {
+  SlotGeo g;
+  g.n_slot = g.n_qslot = g.seg_words = 0;
+  for (int i = 0; i < kNumGroups; ++i) {
+    g.nb[i] = ((uint32_t)count[i] + kGroupSlots - 1u) / kGroupSlots * (kGroupSlots / 4u);
+    g.n_slot += 4u * g.nb[i];
+    if (i < kNumQGroups) g.n_qslot += 4u * g.nb[i];
+    g.seg_words += 4u * g.nb[i] * (uint32_t)kGroupWidth[i];
+  }
+  return g;
 }
 
 }  // namespace bitsmoe

@@ -1,0 +1,427 @@
+// One-launch gate/up kernel for a few tokens: z = Phi^T x is produced inside
+// the launch, then one 512-lane work-group per (token, slot, 32-row segment)
+// unit applies both projections with MFMA and writes SiLU(gate) * up.
+//
+// BitsMoE blog note, Methodology: "first split" (z = Phi^T x once per token,
+// reused by every routed expert), "second split" (an expert's output is the
+// sum over components of magnitude * z_k * quantized unit direction) and
+// "execution" (components of one width stored together, plane by plane).
+//
+// gfx950 mapping.
+//  * Units u = segment * pairs + pair go to XCD u % 8 (work-group b runs on
+//    XCD b % 8 and takes units b, b + G, ...); with 8 or more pairs every
+//    segment of a pair sits on one XCD, whose L2 then serves the pair's
+//    column metadata to all of them.
+//  * Waves 0-3 of every work-group issue the loads of their contiguous run
+//    of Phi^T rows first (the rows do not depend on anything), compute z for
+//    them once the loads are in (v_dot2_f32_f16, wave reduction) and publish
+//    each value as one 64-bit word (float bits | epoch tag << 32,
+//    device-coherent store): a consumer can tell a fresh value from a stale
+//    one without any fence or shared counter.  Waves 4-7 meanwhile read the
+//    routed id and the two directory records and copy the unit's gate and up
+//    segment records into LDS (16-byte global_load_lds).
+//  * Coefficients: lane l of projection p owns slots l, l + 256, ...; all its
+//    metadata loads and tagged z gathers go out together; the gathers whose
+//    tag is not there yet are re-issued together until all are, then it forms
+//    c = a s z (a z for 16-bit slots) and a m z, and after a block-wide max
+//    writes the fp16 pair hi + lo of c 2^S into LDS.
+//  * Apply: each wave of a projection takes every 4th 32-slot K step; the
+//    codes of its 16-row tiles are unpacked from the plane nibbles straight
+//    into fp16 A operands and multiplied with the coefficient column (B,
+//    token column 0) by v_mfma_f32_16x16x32_f16, hi and lo parts.
+//  * The 4 waves' row sums meet in LDS; wave 0 scales back by 2^-S, adds the
+//    offset sums and writes SiLU(gate) * up for the 32 rows.
+// Segments whose record exceeds the LDS arena are applied in chunks of K
+// steps.  Work-groups wait for other groups' z, so the host launches at most
+// as many groups as can be resident at once; all waits are bounded (a
+// time-out gives NaN rows, the kernel still exits).  The last group of the
+// grid advances the epoch.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "format.h"
+#include "kernels.h"
+#include "seg_common.h"
+
+namespace bitsmoe {
+namespace {
+
+using namespace seg;
+
+constexpr int kFWaves = 8;
+constexpr int kFThreads = kFWaves * kWave;  // 512
+constexpr int kFProj = 256;                 // lanes per projection (waves 0-3 gate, 4-7 up)
+constexpr int kFPW = kFWaves / 2;           // waves per projection
+constexpr int kFMaxW = 12288;               // plane words per projection per chunk
+constexpr int kFMaxS = 4320;                // slots per projection (r <= 4096, padded)
+// slots per lane of the coefficient pass: 9 covers r <= 2048, 17 r <= 4096
+constexpr int kFPre = 4;                    // Phi^T rows a wave loads up front
+constexpr uint32_t kFSpin = 1u << 20;
+
+struct __align__(16) FusedLds {
+  uint32_t W[2][kFMaxW + 64];
+  _Float16 Chi[2][kFMaxS];
+  _Float16 Clo[2][kFMaxS];
+  float red[2][kFPW][kSegRows];
+  float pmax[2][kFPW];
+  float pbias[2][kFPW];
+  uint32_t pok[2][kFPW];
+  int nch[2];
+};
+
+__device__ __forceinline__ float fdot8(uint4 a, uint4 b, float acc) {
+  const h2* ha = reinterpret_cast<const h2*>(&a);
+  const h2* hb = reinterpret_cast<const h2*>(&b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(ha[i], hb[i], acc, false);
+  return acc;
+}
+
+// Dot product of one Phi^T row (p: this lane's 4 16-byte units of the first
+// 2048 inputs) with token tt's x, over all din inputs.
+__device__ __forceinline__ float zdot(const FusedArgs& s, const uint4* prow, const uint4 (&p)[4],
+                                      const uint4 (&xv)[4], int tt, int lane) {
+  const uint4* xt = s.x + (size_t)tt * s.din8;
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = lane + u * kWave;
+    if (i < s.din8) acc = fdot8(p[u], tt == 0 ? xv[u] : xt[i], acc);
+  }
+  for (int i0 = 4 * kWave; i0 < s.din8; i0 += 4 * kWave) {  // din > 2048
+    uint4 q4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + lane + u * kWave;
+      q4[u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + lane + u * kWave;
+      if (i < s.din8) acc = fdot8(q4[u], xt[i], acc);
+    }
+  }
+  return wave_sum(acc);
+}
+
+__device__ __forceinline__ void publish_z(const FusedArgs& s, int tt, int n, float v, uint32_t tag,
+                                          int lane) {
+  if (lane == 0) {
+    const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
+    __hip_atomic_store(&s.zt[(size_t)tt * 2 * s.g.r + n], w, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Waves 0-3 of work-group b: z rows [n0, n0 + nrw) of every token, published
+// tagged.  The loads of the first kFPre rows and of x are all issued before
+// the first is used, in straight-line code (so that they stay together).
+__device__ __forceinline__ void produce_z(const FusedArgs& s, int n0, int nrw, int lane,
+                                          uint32_t tag) {
+  const int R = 2 * s.g.r;
+  uint4 pv[kFPre][4];
+  uint4 xv[4];
+#pragma unroll
+  for (int q = 0; q < kFPre; ++q) {
+    const int n = (q < nrw && n0 + q < R) ? n0 + q : 0;
+    const uint4* prow = s.phi_t + (size_t)n * s.din8;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + u * kWave;
+      pv[q][u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = lane + u * kWave;
+    xv[u] = i < s.din8 ? s.x[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < kFPre; ++q) {
+    const int n = n0 + q;
+    if (q < nrw && n < R)
+      for (int tt = 0; tt < s.T; ++tt)
+        publish_z(s, tt, n, zdot(s, s.phi_t + (size_t)n * s.din8, pv[q], xv, tt, lane), tag,
+                  lane);
+  }
+  for (int q = kFPre; q < nrw && n0 + q < R; ++q) {  // rows beyond the first kFPre
+    const int n = n0 + q;
+    const uint4* prow = s.phi_t + (size_t)n * s.din8;
+    uint4 p0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + u * kWave;
+      p0[u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
+    }
+    for (int tt = 0; tt < s.T; ++tt)
+      publish_z(s, tt, n, zdot(s, prow, p0, xv, tt, lane), tag, lane);
+  }
+}
+
+// Stage chunk [b0, b1) of segment sg of projection p into arena (nl lanes).
+__device__ __forceinline__ void stage_chunk(uint32_t* arena, const SegProj& p, int sg,
+                                            uint32_t b0, uint32_t b1, int lp, int lane, int nl) {
+  if (b1 <= b0) return;
+  const uint32_t w0 = block_word(p, b0), w1 = block_word(p, b1);
+  stage16(arena, p.planes + (size_t)sg * p.seg_words + w0, (w1 - w0) / 4u, lp, lane, nl);
+}
+
+template <int kFSper>
+__global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
+  extern __shared__ __align__(16) uint8_t lds_raw[];
+  FusedLds& L = *reinterpret_cast<FusedLds*>(lds_raw);
+  const GateUpArgs& a = s.g;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The epoch changes only between launches (the previous launch's last
+  // group wrote it), so a scalar load sees it; unlike a vector load it does
+  // not hold up the Phi^T loads behind it.
+  typedef __attribute__((address_space(4))) const uint32_t CU32;
+  const uint32_t tag = *(CU32*)s.epoch + 1u;
+  const int pj = wv >= kFPW ? 1 : 0;           // waves 0-3 gate, 4-7 up
+  const int wp = wv & (kFPW - 1);
+  const int lp = (int)threadIdx.x & (kFProj - 1);
+  const int R = 2 * a.r;
+  const int G = s.grid;
+  const int np = a.npairs;
+  const int U = np * a.n_seg;
+
+  // ---- waves 0-3: z for their contiguous run of Phi^T rows, first ----
+  const int nzw = G * kFPW;              // producing waves
+  const int nrw = (R + nzw - 1) / nzw;   // rows per producing wave
+  if (pj == 0) produce_z(s, ((int)blockIdx.x * kFPW + wp) * nrw, nrw, lane, tag);
+
+  bool first = true;
+  for (int u = (int)blockIdx.x; u < U || first; u += G) {
+    const bool have = u < U;
+    const int pair = have ? u % np : 0;
+    const int sg = have ? u / np : 0;
+    const int t = pair / a.ktop;
+    const int e = have ? __builtin_amdgcn_readfirstlane(a.ids[pair]) : 0;
+    // projection of this wave; on the first unit waves 4-7 stage both
+    // (4-5 gate, 6-7 up) while waves 0-3 produce z
+    const int sp = first ? (wv >> 1) & 1 : pj;
+    const uint8_t* sblob = sp ? a.blob_u : a.blob_g;
+    const SegProj SP = uniform_seg(make_seg(sblob, sp ? a.bytes_u : a.bytes_g, e,
+                                            load_rec_s(sblob, e, a.E), load_hdr(sblob), a.E,
+                                            a.dout, a.r));
+    const uint32_t c1s = chunk_end(SP, 0, kFMaxW);
+    if (have) {
+      if (first) {
+        if (pj == 1) stage_chunk(&L.W[sp][0], SP, sg, 0, c1s, (int)threadIdx.x & 127, lane, 128);
+      } else {
+        stage_chunk(&L.W[pj][0], SP, sg, 0, c1s, lp, lane, kFProj);
+      }
+    }
+    if (!have) break;
+    const uint8_t* blob = pj ? a.blob_u : a.blob_g;
+    const SegProj P = (sp == pj) ? SP
+                                 : uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
+                                                        load_rec_s(blob, e, a.E), load_hdr(blob),
+                                                        a.E, a.dout, a.r));
+    // ---- coefficients of this projection's slots: every metadata load and
+    // tagged z gather is in flight before the first is used; gathers whose tag
+    // is not there yet are re-issued together ----
+    bool good = P.ok;
+    float cv[kFSper];  // coefficients of this lane's slots
+    float bias = 0.f, cmx = 0.f;
+    bool zready;
+    {
+      const uint64_t* zrow = s.zt + (size_t)t * R + (pj ? a.r : 0);
+      uint32_t kv[kFSper];
+      float av[kFSper];
+      uint32_t sm[kFSper];  // fp16 s | fp16 m << 16
+      uint64_t zw[kFSper];
+#pragma unroll
+      for (int i = 0; i < kFSper; ++i) {
+        const uint32_t sl = (uint32_t)lp + kFProj * i;
+        kv[i] = sl < P.n_slot ? P.kidx[sl] : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < kFSper; ++i) {
+        const uint32_t sl = (uint32_t)lp + kFProj * i;
+        good &= kv[i] < (uint32_t)a.r;
+        kv[i] = kv[i] < (uint32_t)a.r ? kv[i] : 0u;
+        zw[i] = sl < P.n_slot
+                    ? __hip_atomic_load(zrow + kv[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : ((uint64_t)tag << 32);
+      }
+      // a, s and m: loaded with the gathers when registers allow (r <= 2048),
+      // else after them
+      auto load_asm = [&]() {
+#pragma unroll
+        for (int i = 0; i < kFSper; ++i) {
+          const uint32_t sl = (uint32_t)lp + kFProj * i;
+          const bool q = sl < P.n_qslot;
+          av[i] = sl < P.n_slot ? P.A[sl] : 0.f;
+          sm[i] = q ? ((uint32_t)P.S[sl] | ((uint32_t)P.M[sl] << 16)) : 0x3C00u;
+        }
+      };
+      if constexpr (kFSper <= 9) load_asm();
+      uint32_t spins = 0;
+      while (true) {
+        bool ready = true;
+#pragma unroll
+        for (int i = 0; i < kFSper; ++i) ready &= (uint32_t)(zw[i] >> 32) == tag;
+        if (__all(ready) || spins >= kFSpin) break;
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int i = 0; i < kFSper; ++i)
+          if ((uint32_t)(zw[i] >> 32) != tag)
+            zw[i] = __hip_atomic_load(zrow + kv[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ++spins;
+      }
+      zready = spins < kFSpin;
+      if constexpr (kFSper > 9) load_asm();
+#pragma unroll
+      for (int i = 0; i < kFSper; ++i) {
+        const float z = __uint_as_float((uint32_t)zw[i]);
+        const float az = av[i] * z;
+        const float sv = __half2float(__ushort_as_half((unsigned short)(sm[i] & 0xFFFFu)));
+        const float mv = __half2float(__ushort_as_half((unsigned short)(sm[i] >> 16)));
+        bias += az * mv;          // m = 0 for 16-bit and padding slots
+        const float c = az * sv;  // s = 1 for 16-bit slots
+        cv[i] = c;
+        cmx = fmaxf(cmx, fabsf(c));
+      }
+    }
+    good = good && zready;
+    {
+      float m = cmx;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+      const float bw = wave_sum(bias);
+      const bool wok = __all(good);
+      if (lane == 0) {
+        L.pmax[pj][wp] = m;
+        L.pbias[pj][wp] = bw;
+        L.pok[pj][wp] = wok;
+      }
+    }
+    __syncthreads();
+    const float pmx = fmaxf(fmaxf(L.pmax[pj][0], L.pmax[pj][1]), fmaxf(L.pmax[pj][2], L.pmax[pj][3]));
+    const int S = coef_shift(pmx, 1.0f);
+#pragma unroll
+    for (int i = 0; i < kFSper; ++i) {
+      const uint32_t sl = (uint32_t)lp + kFProj * i;
+      // slots up to the next multiple of 32 are written (zeros past n_slot)
+      if (sl < (P.n_slot + 31u) / 32u * 32u) {
+        _Float16 hi, lo;
+        split_coef(cv[i], S, hi, lo);
+        L.Chi[pj][sl] = hi;
+        L.Clo[pj][sl] = lo;
+      }
+    }
+    // chunk counts of both projections (they advance together)
+    {
+      int nc = 0;
+      for (uint32_t b = 0; b < P.n_blk; b = chunk_end(P, b, kFMaxW)) ++nc;
+      if (threadIdx.x == (unsigned)(pj * kFProj)) L.nch[pj] = nc;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int nch = __builtin_amdgcn_readfirstlane(max(L.nch[0], L.nch[1]));  // uniform
+    // ---- apply ----
+    f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    uint32_t b0 = 0;
+    for (int ch = 0; ch < max(nch, 1); ++ch) {
+      const uint32_t b1 = chunk_end(P, b0, kFMaxW);
+      if (ch > 0) {
+        __syncthreads();  // every wave is done with the previous chunk
+        stage_chunk(&L.W[pj][0], P, sg, b0, b1, lp, lane, kFProj);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      if (b1 > b0) {
+        const uint32_t* base = &L.W[pj][0] - block_word(P, b0);
+        mfma_ksteps(P, base, &L.Chi[pj][0], &L.Clo[pj][0], 0, 0u, 1,
+                    b0 / kBlkPerK, (b1 + kBlkPerK - 1) / kBlkPerK, wp, lane, acc0, acc1);
+      }
+      b0 = b1;
+    }
+    // ---- row sums of the 4 waves, SiLU * mul ----
+    if ((lane & 15) == 0) {
+      const int kg = lane >> 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        L.red[pj][wp][4 * kg + i] = acc0[i];
+        L.red[pj][wp][16 + 4 * kg + i] = acc1[i];
+      }
+    }
+    __syncthreads();
+    if (wv == 0 && lane < kSegRows) {
+      float ys[2];
+      bool ok = true;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float mx = fmaxf(fmaxf(L.pmax[q][0], L.pmax[q][1]), fmaxf(L.pmax[q][2], L.pmax[q][3]));
+        const int Sq = coef_shift(mx, 1.0f);
+        float sum = 0.f, bsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kFPW; ++w) {
+          sum += L.red[q][w][lane];
+          bsum += L.pbias[q][w];
+          ok = ok && L.pok[q][w];
+        }
+        ys[q] = ldexpf(sum, -Sq) + bsum;
+      }
+      const int row = sg * kSegRows + lane;
+      if (row < a.dout)
+        a.h[(size_t)pair * a.dout + row] = ok ? silu_mul(ys[0], ys[1]) : __builtin_nanf("");
+    }
+    __syncthreads();  // LDS is reused by the next unit
+    first = false;
+  }
+
+  // ---- grid arrival: the last group advances the epoch ----
+  if (threadIdx.x == 0) {
+    const uint32_t n =
+        __hip_atomic_fetch_add(s.arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (n == (uint32_t)G - 1) {
+      __hip_atomic_store(s.arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(s.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+}  // namespace
+
+size_t fused_lds_bytes() { return sizeof(FusedLds); }
+
+int fused_grid() {
+  static int grid[64];
+  static bool done[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!done[dev]) {
+    int cus = 0, nb9 = 0, nb17 = 0;
+    (void)hipFuncSetAttribute((const void*)k_gateup_fused<9>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FusedLds));
+    (void)hipFuncSetAttribute((const void*)k_gateup_fused<17>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(FusedLds));
+    (void)hipGetLastError();
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb9, k_gateup_fused<9>, kFThreads,
+                                                     sizeof(FusedLds)) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb17, k_gateup_fused<17>, kFThreads,
+                                                     sizeof(FusedLds)) != hipSuccess)
+      return 0;
+    // one group per compute unit, all resident at once, a multiple of 8
+    grid[dev] = (nb9 >= 1 && nb17 >= 1 && cus >= 8) ? (cus & ~7) : 0;
+    done[dev] = true;
+  }
+  return grid[dev];
+}
+
+void launch_gateup_fused(const FusedArgs& s, hipStream_t st) {
+  // slots per lane: n_slot <= r + 7 * 31 (each width group padded to 32 slots)
+  if (s.g.r + 7 * 31 <= 9 * kFProj)
+    hipLaunchKernelGGL(k_gateup_fused<9>, dim3((unsigned)s.grid), dim3(kFThreads),
+                       sizeof(FusedLds), st, s);
+  else
+    hipLaunchKernelGGL(k_gateup_fused<17>, dim3((unsigned)s.grid), dim3(kFThreads),
+                       sizeof(FusedLds), st, s);
+}
+
+}  // namespace bitsmoe

@@ -6,36 +6,56 @@
 // unit direction) and "execution" (components of one width stored together,
 // plane by plane).  Grouping the batch's (token, slot) pairs by expert
 // extends the first split's reuse across tokens: an expert's planes are read
-// from HBM and decoded once per batch instead of once per routed token.
+// from HBM and unpacked once per tile of up to 16 routed tokens instead of
+// once per token, and the tokens become the N columns of the MFMA.
 //
 // k_route_group (one work-group): counting sort of the T*k pairs by expert
 // id -- LDS histogram, block scan, scatter -- into per-expert pair lists
-// (groups in ascending expert id; the order of pairs inside a group does not
-// affect any result).  Pairs whose id lies outside [0, E) get NaN rows.
+// (experts ascending; the order of pairs inside a list does not affect any
+// result), cut into tiles of at most 16 pairs.  Pairs whose id lies outside
+// [0, E) get NaN rows.
 //
-// k_gateup_grouped: one 512-lane work-group per (group, 64-row slab, 32-row
-// half), both projections (waves 0-3 gate, 4-7 up), placed XCD-aware like
-// the one-launch kernel.  The slab's plane masks and metadata are staged in
-// LDS once (column chunks if they do not fit); the group's pairs are then
-// taken NT (up to 2) at a time: their z rows (from the projection launch) go to LDS,
-// and each lane spreads a column's plane bits into byte codes once and adds
-// coef_t * code for all NT tokens.  A transpose reduction per token, the 4
-// waves of a projection through LDS, and SiLU * mul finish each pair.
+// k_gateup_grouped: one 512-lane work-group per (tile, 32-row segment) unit,
+// both projections (waves 0-3 gate, 4-7 up); unit u = segment * tcap + tile
+// runs on XCD u % 8, so every segment of a tile shares one L2.  The segment
+// records are staged in LDS once; the tile's coefficients are formed 256
+// slots at a time: c = a s z_t[k] (a z for 16-bit slots) gathered from the
+// projection's z rows, as fp16 hi + lo parts of c 2^S_t, where S_t follows
+// from the expert's bound max |a s| (directory) and the token's max |z|
+// (partial maxima written by the projection launch).  The apply is the same
+// MFMA K-step loop as the one-launch kernel with up to 16 token columns.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
 #include "format.h"
 #include "kernels.h"
-#include "slab_common.h"
+#include "seg_common.h"
 
 namespace bitsmoe {
 namespace {
 
-using namespace slab;
+using namespace seg;
 
 // ------------------------------------------------------------ route groups
 constexpr int kRThreads = 1024;
+
+// Exclusive block scan of one value per thread; total gets the sum.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* buf, uint32_t& total) {
+  const int tid = threadIdx.x;
+  buf[tid] = v;
+  __syncthreads();
+  for (int d = 1; d < kRThreads; d <<= 1) {
+    const uint32_t a = tid >= d ? buf[tid - d] : 0u;
+    __syncthreads();
+    buf[tid] += a;
+    __syncthreads();
+  }
+  total = buf[kRThreads - 1];
+  const uint32_t incl = buf[tid];
+  __syncthreads();
+  return incl - v;
+}
 
 __global__ __launch_bounds__(kRThreads) void k_route_group(const int32_t* __restrict__ ids,
                                                            int P, int E, int dout,
@@ -43,7 +63,7 @@ __global__ __launch_bounds__(kRThreads) void k_route_group(const int32_t* __rest
                                                            RouteLists rl) {
   extern __shared__ uint32_t cnt[];  // E counters, then E cursors
   uint32_t* cur = cnt + E;
-  __shared__ uint32_t part[kRThreads], dpart[kRThreads];
+  __shared__ uint32_t buf[kRThreads];
   const int tid = threadIdx.x;
   for (int i = tid; i < E; i += kRThreads) cnt[i] = 0;
   __syncthreads();
@@ -52,41 +72,28 @@ __global__ __launch_bounds__(kRThreads) void k_route_group(const int32_t* __rest
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1u);
   }
   __syncthreads();
-  // block scan over E: each thread owns a contiguous run of counters
+  // each thread owns a contiguous run of experts
   const int per = (E + kRThreads - 1) / kRThreads;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-  uint32_t sum = 0, nd = 0;
+  uint32_t sum = 0, nt = 0;
   for (int e = e0; e < e1; ++e) {
     sum += cnt[e];
-    nd += cnt[e] > 0 ? 1u : 0u;
+    nt += (cnt[e] + kTile - 1) / kTile;
   }
-  part[tid] = sum;
-  dpart[tid] = nd;
-  __syncthreads();
-  for (int d = 1; d < kRThreads; d <<= 1) {
-    const uint32_t a = tid >= d ? part[tid - d] : 0u;
-    const uint32_t b = tid >= d ? dpart[tid - d] : 0u;
-    __syncthreads();
-    part[tid] += a;
-    dpart[tid] += b;
-    __syncthreads();
-  }
-  uint32_t off = part[tid] - sum, g = dpart[tid] - nd;
+  uint32_t total_pairs, total_tiles;
+  uint32_t off = block_scan(sum, buf, total_pairs);
+  uint32_t ti = block_scan(nt, buf, total_tiles);
   for (int e = e0; e < e1; ++e) {
     const uint32_t c = cnt[e];
     cur[e] = off;
-    if (c > 0) {
-      rl.gexp[g] = e;
-      rl.goff[g] = (int)off;
-      ++g;
+    for (uint32_t i = 0; i < c; i += kTile, ++ti) {
+      rl.tile[3 * ti] = e;
+      rl.tile[3 * ti + 1] = (int)(off + i);
+      rl.tile[3 * ti + 2] = (int)min((uint32_t)kTile, c - i);
     }
     off += c;
   }
-  if (tid == kRThreads - 1) {
-    const uint32_t ng = dpart[tid];
-    rl.goff[ng] = (int)part[tid];
-    rl.ngroups[0] = (int)ng;
-  }
+  if (tid == 0) rl.ntiles[0] = (int)total_tiles;
   __syncthreads();
   for (int p = tid; p < P; p += kRThreads) {
     const int e = ids[p];
@@ -103,50 +110,34 @@ constexpr int kGWaves = 8;
 constexpr int kGThreads = kGWaves * kWave;  // 512
 constexpr int kGProj = 256;                 // lanes per projection
 constexpr int kGPW = kGWaves / 2;           // waves per projection
-constexpr int kGMaxM = 5120;                // u64 per projection per chunk
-constexpr int kGMaxC = 2048;                // columns per projection per chunk
-constexpr int kGZ = 8192;                   // z floats staged per token batch
-constexpr int kGMaxNT = 2;
+constexpr int kGMaxW = 12288;               // plane words per projection per chunk
+constexpr int kGCS = kGProj;                // slots per coefficient chunk (one per lane)
+constexpr int kGCStride = kGCS + 8;         // fp16 per token row (bank spread)
+constexpr int kGZP = 16;                    // lanes per token for the partial maxima
 
 struct __align__(16) GroupLds {
-  uint64_t M[2][kGMaxM + 2];
-  float A[2][kGMaxC + 8];
-  uint16_t K[2][kGMaxC + 16];
-  uint16_t S[2][kGMaxC + 16];
-  uint16_t Mo[2][kGMaxC + 16];
-  float Z[kGZ];
-  float red[2][kGPW][kGMaxNT][kSlabRows];
-  float bias[2][kGPW][kGMaxNT];
-  uint32_t ok[2][kGPW];
+  uint32_t W[2][kGMaxW + 64];
+  union {
+    struct {
+      _Float16 hi[2][kTile * kGCStride];
+      _Float16 lo[2][kTile * kGCStride];
+    } c;
+    float red[2][kGPW][kTile][kSegRows];
+  } u;
+  float pbias[2][kGPW][kTile];
+  int S[2][kTile];
+  int pair[kTile];
+  uint32_t pok[2][kGPW];
   int nch[2];
 };
 
-// One column of width b <= B over 32 rows for NT tokens: the codes are
-// spread once and converted once; coef[t] * code is added for every token.
-template <int B, int NT>
-__device__ __forceinline__ void column32n(const uint32_t* words, int b, const float (&coef)[NT],
-                                          float (&acc)[NT][kSlabRows]) {
-  uint32_t w[B];
-#pragma unroll
-  for (int j = 0; j < B; ++j) w[j] = j < b ? words[2 * j] : 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const uint32_t x = __builtin_amdgcn_ubfe(w[j], 4 * i, 4);
-      c |= ((x * 0x00204081u) & 0x01010101u) << j;
-    }
-    const float f[4] = {(float)(c & 0xFFu), (float)((c >> 8) & 0xFFu),
-                        (float)((c >> 16) & 0xFFu), (float)(c >> 24)};
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[t][4 * i + r] = fmaf(coef[t], f[r], acc[t][4 * i + r]);
-  }
+__device__ __forceinline__ void stage_chunk(uint32_t* arena, const SegProj& p, int sg,
+                                            uint32_t b0, uint32_t b1, int lp, int lane, int nl) {
+  if (b1 <= b0) return;
+  const uint32_t w0 = block_word(p, b0), w1 = block_word(p, b1);
+  stage16(arena, p.planes + (size_t)sg * p.seg_words + w0, (w1 - w0) / 4u, lp, lane, nl);
 }
 
-template <int NT>
 __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   GroupLds& L = *reinterpret_cast<GroupLds*>(lds_raw);
@@ -154,210 +145,156 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pj = wv >= kGPW ? 1 : 0;  // waves 0-3 gate, 4-7 up
+  const int wp = wv & (kGPW - 1);
   const int lp = (int)threadIdx.x & (kGProj - 1);
   const int R = 2 * a.r;
-  const uint32_t dout_pad = (uint32_t)a.n_slabs * 64u;
 
-  // unit (group, slab, half); XCD q % 8 shared by both halves of a slab
-  const int Q = s.gmax * a.n_slabs;
-  const int b = blockIdx.x;
-  const int j = b >> 3;
-  const int q = 8 * (j >> 1) + (b & 7);
-  if (q >= Q) return;
-  const int hh = j & 1;
-  const int gi = q % s.gmax, slab = q / s.gmax;
-  if (gi >= s.rl.ngroups[0]) return;
-  const int e = __builtin_amdgcn_readfirstlane(s.rl.gexp[gi]);
-  const int p0 = __builtin_amdgcn_readfirstlane(s.rl.goff[gi]);
-  const int p1 = __builtin_amdgcn_readfirstlane(s.rl.goff[gi + 1]);
+  const int u = blockIdx.x;
+  const int ti = u % s.tcap, sg = u / s.tcap;
+  if (sg >= a.n_seg || ti >= s.rl.ntiles[0]) return;
+  const int e = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti]);
+  const int p0 = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti + 1]);
+  const int nt = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti + 2]);
 
   const uint8_t* blob = pj ? a.blob_u : a.blob_g;
-  const Proj P = make_proj(blob, pj ? a.bytes_u : a.bytes_g, e, load_rec_s(blob, e, a.E),
-                           load_hdr(blob), a);
-  const HGeo Gm = hgeo(P);
-  const uint32_t ncol = P.nq + P.n16;
+  const SegProj P = uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
+                                         load_rec_s(blob, e, a.E), load_hdr(blob), a.E, a.dout,
+                                         a.r));
+  uint32_t b1 = chunk_end(P, 0, kGMaxW);
+  stage_chunk(&L.W[pj][0], P, sg, 0, b1, lp, lane, kGProj);
+
+  // tokens of the tile and their coefficient scales: lanes (n, j) of the
+  // projection take partial maxima j, j + 16, ... of token n
+  if (threadIdx.x < (unsigned)nt) L.pair[threadIdx.x] = s.rl.pairs[p0 + threadIdx.x];
+  {
+    const int n = lp / kGZP, j = lp % kGZP;
+    const int pz0 = pj ? a.r / kProjRowsPerBlock : 0;
+    const int pz1 = pj ? s.nzp : (a.r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
+    float zm = 0.f;
+    if (n < nt) {
+      const int t = s.rl.pairs[p0 + n] / a.ktop;
+      const float* zp = s.zpart + (size_t)t * s.nzp;
+      for (int i = pz0 + j; i < pz1; i += kGZP) zm = fmaxf(zm, zp[i]);
+    }
+#pragma unroll
+    for (int off = kGZP / 2; off > 0; off >>= 1) zm = fmaxf(zm, __shfl_xor(zm, off, kWave));
+    if (j == 0 && n < nt) L.S[pj][n] = coef_shift(P.cmax, zm);
+  }
   {
     int nc = 0;
-    for (uint32_t c = 0; c < ncol; c = hchunk_end<kGMaxM, kGMaxC>(P, Gm, c)) ++nc;
+    for (uint32_t b = 0; b < P.n_blk; b = chunk_end(P, b, kGMaxW)) ++nc;
     if (threadIdx.x == (unsigned)(pj * kGProj)) L.nch[pj] = nc;
   }
   __syncthreads();
-  const int nch = max(L.nch[0], L.nch[1]);
-  const Arena ar = {&L.M[pj][0], &L.K[pj][0], &L.A[pj][0], &L.S[pj][0], &L.Mo[pj][0]};
-  const uint32_t* Mw = reinterpret_cast<const uint32_t*>(&L.M[pj][0]);
-  const float* Asrc = &L.A[pj][0];
+  const int nch = __builtin_amdgcn_readfirstlane(max(L.nch[0], L.nch[1]));  // uniform
+  int Sn[kTile];
+  int zoff[kTile];  // z row of token n, this projection
+#pragma unroll
+  for (int n = 0; n < kTile; ++n) {
+    Sn[n] = n < nt ? L.S[pj][n] : 0;
+    zoff[n] = n < nt ? (L.pair[n] / a.ktop) * R + (pj ? a.r : 0) : 0;
+  }
 
-  for (int t0 = p0; t0 < p1; t0 += NT) {
-    const int nt = min(NT, p1 - t0);
-    float acc[NT][kSlabRows];
+  bool good = P.ok;
+  float bias[kTile];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < kSlabRows; ++i) acc[t][i] = 0.f;
-    float biasv[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) biasv[t] = 0.f;
-    bool good = P.ok;
-    // z rows of this batch's tokens: Z[t][0, 2r) -- 16-byte loads, all
-    // issued before the first is used
-    {
-      const float4* zsrc[NT];
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int pair = __builtin_amdgcn_readfirstlane(s.rl.pairs[t0 + (t < nt ? t : 0)]);
-        zsrc[t] = reinterpret_cast<const float4*>(s.z + (size_t)(pair / a.ktop) * R);
-      }
-      constexpr int kPer = kGZ / 4 / kGThreads;  // float4 per lane at most
-      const int n4 = R / 4;                     // float4 per token (R = 2r, r % 4 == 0)
-      float4 v[kPer];
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int i = (int)threadIdx.x + kGThreads * u;
-        const int t = i >= n4 ? 1 : 0;
-        v[u] = (i < nt * n4 && t < NT) ? zsrc[t < NT ? t : 0][i - t * n4]
-                                        : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int i = (int)threadIdx.x + kGThreads * u;
-        if (i < nt * n4) reinterpret_cast<float4*>(L.Z)[i] = v[u];
-      }
+  for (int n = 0; n < kTile; ++n) bias[n] = 0.f;
+  f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  uint32_t b0 = 0;
+  for (int ch = 0; ch < max(nch, 1); ++ch) {
+    if (ch > 0) {
+      __syncthreads();  // every wave is done with the previous chunk
+      b1 = chunk_end(P, b0, kGMaxW);
+      stage_chunk(&L.W[pj][0], P, sg, b0, b1, lp, lane, kGProj);
     }
-    uint32_t c0 = 0;
-    for (int ch = 0; ch < max(nch, 1); ++ch) {
-      const uint32_t c1 = c0 < ncol ? hchunk_end<kGMaxM, kGMaxC>(P, Gm, c0) : c0;
-      // the slab is staged once when it fits one chunk
-      const bool restage = nch > 1 || t0 == p0;
-      if (restage && c1 > c0) hstage_chunk(ar, P, c0, c1, slab, hh, dout_pad, lp, lane, kGProj);
+    // coefficient chunks of 256 slots (64 blocks) inside the plane chunk
+    const uint32_t kbe = (b1 + kBlkPerK - 1) / kBlkPerK;
+    const int ncc = max((int)((b1 - b0 + 63u) / 64u), 1);
+    for (int cc = 0; cc < ncc; ++cc) {
+      const uint32_t cb0 = b0 + 64u * cc;
+      const uint32_t s0 = 4u * cb0;
+      const uint32_t sl = s0 + (uint32_t)lp;
+      const bool live = sl < 4u * b1;  // padding slots have a = 0
+      if (cc > 0) __syncthreads();     // the previous coefficient chunk is read
+      uint32_t k = live ? P.kidx[sl] : 0u;
+      good &= k < (uint32_t)a.r;
+      k = k < (uint32_t)a.r ? k : 0u;
+      const float av = live ? P.A[sl] : 0.f;
+      const bool isq = sl < P.n_qslot;
+      const float sv = (live && isq) ? __half2float(__ushort_as_half(P.S[sl])) : 1.f;
+      const float mv = (live && isq) ? __half2float(__ushort_as_half(P.M[sl])) : 0.f;
+      float zv[kTile];
+#pragma unroll
+      for (int n = 0; n < kTile; ++n) zv[n] = (live && n < nt) ? s.z[zoff[n] + k] : 0.f;
+#pragma unroll
+      for (int n = 0; n < kTile; ++n) {
+        const float az = av * zv[n];
+        bias[n] += az * mv;
+        _Float16 hi, lo;
+        split_coef(az * sv, Sn[n], hi, lo);
+        L.u.c.hi[pj][n * kGCStride + lp] = hi;
+        L.u.c.lo[pj][n * kGCStride + lp] = lo;
+      }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      const uint32_t q0 = min(c0, P.nq), q1 = min(c1, P.nq);
-      const uint32_t ma0 = ((uint32_t)slab * P.mps + hmask_of(Gm, q0)) & ~1u;
-      const uint32_t mu =
-          q1 > q0 ? hunits(ma0, (uint32_t)slab * P.mps + hmask_of(Gm, q1), 2) : 0u;
-      const int n_items = (int)(c1 - c0);
-      const int nqi = (int)(q1 - q0);
-      const float* zrow = &L.Z[pj ? a.r : 0];
-#pragma unroll 1
-      for (int r0 = 0; r0 < n_items; r0 += kGProj) {
-        const int it = r0 + (((r0 / kGProj) & 1) ? kGProj - 1 - lp : lp);
-        const bool live = it < n_items;
-        const uint32_t c = c0 + (uint32_t)(live ? it : 0);
-        const uint32_t kk = live ? L.K[pj][c - (c0 & ~7u)] : 0u;
-        good &= kk < (uint32_t)a.r;
-        const uint32_t kc = kk < (uint32_t)a.r ? kk : 0u;
-        const float av = live ? Asrc[c - (c0 & ~3u)] : 0.f;
-        float az[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) az[t] = (live && t < nt) ? av * zrow[t * R + kc] : 0.f;
-        const bool isq = live && it < nqi;
-        if (__any(isq)) {
-          int grp = 0;
-#pragma unroll
-          for (int gg = 1; gg < kNumQGroups; ++gg) grp += c >= Gm.gcol[gg] ? 1 : 0;
-          uint32_t gc = Gm.gcol[0], gm = Gm.gmask[0];
-#pragma unroll
-          for (int gg = 1; gg < kNumQGroups; ++gg) {
-            if (grp == gg) {
-              gc = Gm.gcol[gg];
-              gm = Gm.gmask[gg];
-            }
-          }
-          const int bw = isq ? hwidth(grp) : 0;
-          float coef[NT];
-          uint32_t mi = 0;
-          if (isq) {
-            const uint32_t si = c - (q0 & ~7u);
-            const float sv = __half2float(__ushort_as_half(L.S[pj][si]));
-            const float mv = __half2float(__ushort_as_half(L.Mo[pj][si]));
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              coef[t] = az[t] * sv;
-              biasv[t] += az[t] * mv;
-            }
-            mi = (uint32_t)slab * P.mps + gm + (c - gc) * (uint32_t)bw - ma0;
-          } else {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) coef[t] = 0.f;
-          }
-          const uint32_t* wp = Mw + 2 * mi + hh;
-          switch (hwave_bmax(bw)) {
-            case 1: column32n<1, NT>(wp, bw, coef, acc); break;
-            case 2: column32n<2, NT>(wp, bw, coef, acc); break;
-            case 3: column32n<3, NT>(wp, bw, coef, acc); break;
-            case 4: column32n<4, NT>(wp, bw, coef, acc); break;
-            case 6: column32n<6, NT>(wp, bw, coef, acc); break;
-            case 8: column32n<8, NT>(wp, bw, coef, acc); break;
-            default: break;
-          }
-        }
-        const bool isf = live && it >= nqi;
-        if (__any(isf)) {
-          const uint4* fv =
-              reinterpret_cast<const uint4*>(&L.M[pj][2 * mu + 8 * (isf ? it - nqi : 0)]);
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const uint4 v4 = fv[qq];
-            const __half2* h2 = reinterpret_cast<const __half2*>(&v4);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float2 f2 = __half22float2(h2[u]);
-#pragma unroll
-              for (int t = 0; t < NT; ++t) {
-                const float cf = isf ? az[t] : 0.f;
-                acc[t][8 * qq + 2 * u] = fmaf(cf, f2.x, acc[t][8 * qq + 2 * u]);
-                acc[t][8 * qq + 2 * u + 1] = fmaf(cf, f2.y, acc[t][8 * qq + 2 * u + 1]);
-              }
-            }
-          }
-        }
+      const uint32_t kb0 = cb0 / kBlkPerK;
+      const uint32_t kb1 = min(kb0 + 8u, kbe);
+      if (b1 > cb0) {
+        const uint32_t* base = &L.W[pj][0] - block_word(P, b0);
+        mfma_ksteps(P, base, &L.u.c.hi[pj][0], &L.u.c.lo[pj][0], kGCStride, s0,
+                    nt, kb0, kb1, wp, lane, acc0, acc1);
       }
-      __syncthreads();  // arenas are restaged by the next chunk or batch
-      c0 = c1;
     }
-    // row sums of each token, SiLU * mul
-    const int wp = wv & (kGPW - 1);
+    b0 = b1;
+  }
+  __syncthreads();  // coefficient tables are reused as row-sum buffers
+  // ---- row sums of the 4 waves per token, SiLU * mul ----
+  {
+    const int n = lane & 15, kg = lane >> 4;
+    if (n < nt) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float v = htranspose_sum(acc[t], lane);
-      const float bw = wave_sum(biasv[t]);
-      if (lane < kSlabRows) L.red[pj][wp][t][lane] = v;
-      if (lane == 0) L.bias[pj][wp][t] = bw;
+      for (int i = 0; i < 4; ++i) {
+        L.u.red[pj][wp][n][4 * kg + i] = acc0[i];
+        L.u.red[pj][wp][n][16 + 4 * kg + i] = acc1[i];
+      }
     }
-    {
-      const bool wok = __all(good);
-      if (lane == 0) L.ok[pj][wp] = wok;
+#pragma unroll
+    for (int n2 = 0; n2 < kTile; ++n2) {
+      if (n2 < nt) {
+        const float bw = wave_sum(bias[n2]);
+        if (lane == 0) L.pbias[pj][wp][n2] = bw;
+      }
     }
-    __syncthreads();
-    if (wv == 0 && lane < kSlabRows) {
+    const bool wok = __all(good);
+    if (lane == 0) L.pok[pj][wp] = wok;
+  }
+  __syncthreads();
+  {
+    const int n = threadIdx.x >> 5, row = threadIdx.x & 31;
+    if (n < nt) {
+      float ys[2];
       bool ok = true;
 #pragma unroll
-      for (int w = 0; w < kGPW; ++w) ok = ok && L.ok[0][w] && L.ok[1][w];
-      const int row = slab * 64 + hh * kSlabRows + lane;
-      for (int t = 0; t < nt; ++t) {
-        float gsum = 0.f, usum = 0.f;
+      for (int q = 0; q < 2; ++q) {
+        float sum = 0.f, bsum = 0.f;
 #pragma unroll
         for (int w = 0; w < kGPW; ++w) {
-          gsum += L.red[0][w][t][lane] + L.bias[0][w][t];
-          usum += L.red[1][w][t][lane] + L.bias[1][w][t];
+          sum += L.u.red[q][w][n][row];
+          bsum += L.pbias[q][w][n];
+          ok = ok && L.pok[q][w];
         }
-        const int pair = s.rl.pairs[t0 + t];
-        if (row < a.dout)
-          a.h[(size_t)pair * a.dout + row] = ok ? silu_mul(gsum, usum) : __builtin_nanf("");
+        ys[q] = ldexpf(sum, -L.S[q][n]) + bsum;
       }
+      const int orow = sg * kSegRows + row;
+      if (orow < a.dout)
+        a.h[(size_t)L.pair[n] * a.dout + orow] = ok ? silu_mul(ys[0], ys[1]) : __builtin_nanf("");
     }
-    __syncthreads();  // red, Z are reused by the next batch
   }
 }
 
 }  // namespace
 
 size_t grouped_lds_bytes() { return sizeof(GroupLds); }
-
-int grouped_tokens_per_batch(int r) {
-  const int nt = kGZ / (2 * r);
-  return nt >= kGMaxNT ? kGMaxNT : (nt >= 1 ? 1 : 0);
-}
 
 int launch_route_group(const int32_t* ids, int P, int E, int dout, float* h,
                        const RouteLists& rl, hipStream_t st) {
@@ -370,22 +307,14 @@ int launch_gateup_grouped(const GroupArgs& s, hipStream_t st) {
   static bool attr_done[64];
   int dev = 0;
   if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr_done[dev]) {
-    (void)hipFuncSetAttribute((const void*)k_gateup_grouped<1>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GroupLds));
-    (void)hipFuncSetAttribute((const void*)k_gateup_grouped<2>,
+    (void)hipFuncSetAttribute((const void*)k_gateup_grouped,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(GroupLds));
     (void)hipGetLastError();
     attr_done[dev] = true;
   }
-  // units rounded up so that both halves of every slab exist: 2 * 8 * ceil(Q / 8)
-  const long long Q = (long long)s.gmax * s.g.n_slabs;
-  const long long blocks = 16 * ((Q + 7) / 8);
-  const dim3 grid((unsigned)blocks);
-  switch (grouped_tokens_per_batch(s.g.r)) {
-    case 2: hipLaunchKernelGGL(k_gateup_grouped<2>, grid, dim3(kGThreads), sizeof(GroupLds), st, s); break;
-    case 1: hipLaunchKernelGGL(k_gateup_grouped<1>, grid, dim3(kGThreads), sizeof(GroupLds), st, s); break;
-    default: return -1;
-  }
+  const long long blocks = (long long)s.tcap * s.g.n_seg;
+  hipLaunchKernelGGL(k_gateup_grouped, dim3((unsigned)blocks), dim3(kGThreads), sizeof(GroupLds),
+                     st, s);
   return 0;
 }
 

@@ -6,20 +6,25 @@
 
 namespace bitsmoe {
 
-constexpr int kHalfMaxTokens = 4;   // one-launch path: T <= this
-constexpr int kHalfMaxR = 4096;      //   and r <= this (z of a token fits LDS)
+constexpr int kFusedMaxTokens = 4;   // one-launch path: T <= this
+constexpr int kFusedMaxR = 4096;     //   and r <= this
 constexpr int kGroupMaxR = 4096;     // grouped path: r <= this
 constexpr int kGroupMaxE = 16384;    //   and E <= this (route histogram in LDS)
+constexpr int kGroupMaxDin = 4096;   //   and din <= this (row-blocked projection)
+constexpr int kProjRowsPerBlock = 16;  // Phi^T rows per work-group of the projection
+constexpr int kTile = 16;            // tokens per grouped work unit (MFMA N)
 
 // Workspace layout of one gate/up call (offsets in bytes from ws).
 struct GateUpPlan {
-  size_t z_off;       // T x 2r float32 (projection launch of the batched paths)
+  size_t z_off;       // T x 2r float32 (projection launch of the batched path)
+  size_t zpart_off;   // T x ceil(2r / 16) float32: max |z| per projection work-group
   size_t zt_off;      // T x 2r uint64 tagged z (one-launch path)
   size_t sync_off;    // uint32 epoch, uint32 grid arrival counter (left at 0)
-  size_t route_off;   // route lists: ngroups, gexp[gmax], goff[gmax + 1], pairs[T k]
+  size_t route_off;   // route lists (see RouteLists)
   size_t total;
 };
 GateUpPlan gateup_plan(int T, int k, int E, int r);
+int tile_cap(int T, int k, int E);  // tiles the grouped grid is sized for
 
 struct GateUpArgs {
   const uint8_t* blob_g;
@@ -29,50 +34,42 @@ struct GateUpArgs {
   const int32_t* ids;
   int ktop, npairs;
   float* h;           // npairs x dout
-  int n_slabs;
+  int n_seg;          // ceil(dout / 32)
 };
 
-struct StagedArgs {
-  GateUpArgs g;
-  int T;
-  const float* z;      // T x 2r z computed by the projection launch
-};
-// Staged gate/up kernel (second launch of the two-launch path): one
-// work-group per (token, slot, 32-row half-slab).
-size_t staged_lds_bytes();
-long long staged_blocks(int T, int k, int dout);
-int launch_gateup_staged(const StagedArgs& s, hipStream_t st);
-
-// One-launch gate/up kernel, one work-group per (pair, half-slab) unit.
-struct HalfArgs {
+// One-launch gate/up kernel (T <= kFusedMaxTokens): z = Phi^T x produced by
+// every work-group and exchanged through tagged words, then one work-group
+// per (pair, 32-row segment) unit.
+struct FusedArgs {
   GateUpArgs g;
   const uint4* phi_t;  // 2r x din fp16
   const uint4* x;      // T x din fp16
   int din8, T;
   uint64_t* zt;        // T x 2r tagged z
-  uint32_t* epoch;
-  uint32_t* arrive;
-  int grid;            // multiple of 8
+  uint32_t* epoch;     // tag of the previous launch
+  uint32_t* arrive;    // work-groups done (0 between launches)
+  int grid;            // multiple of 8, all work-groups resident
 };
-size_t half_lds_bytes();
-int half_grid();  // work-groups of the half-slab kernel on this device (0: unavailable)
-void launch_gateup_half(const HalfArgs& s, hipStream_t st);
+size_t fused_lds_bytes();
+int fused_grid();  // work-groups of the fused kernel on this device (0: unavailable)
+void launch_gateup_fused(const FusedArgs& s, hipStream_t st);
 
-// Pairs grouped by expert (written by the route-grouping launch).
+// Pairs grouped by expert and cut into tiles of <= kTile pairs (written by
+// the route-grouping launch).
 struct RouteLists {
-  int* ngroups;  // [1]
-  int* gexp;     // expert of group g, ascending
-  int* goff;     // pairs of group g: pairs[goff[g] .. goff[g + 1])
-  int* pairs;    // pair indices t * k + slot
+  int* ntiles;   // [1]
+  int* tile;     // per tile: expert id, first pair index into pairs, pair count (3 ints)
+  int* pairs;    // pair indices t * k + slot, grouped by expert
 };
 struct GroupArgs {
   GateUpArgs g;
-  const float* z;  // T x 2r
+  const float* z;      // T x 2r
+  const float* zpart;  // T x nzp: max |z| per projection work-group
+  int nzp;             // projection work-groups (ceil(2r / 16))
   RouteLists rl;
-  int gmax;        // min(E, T * k): groups the grid is sized for
+  int tcap;            // tiles the grid is sized for
 };
 size_t grouped_lds_bytes();
-int grouped_tokens_per_batch(int r);  // 0: r too large for the grouped kernel
 int launch_route_group(const int32_t* ids, int P, int E, int dout, float* h,
                        const RouteLists& rl, hipStream_t st);
 int launch_gateup_grouped(const GroupArgs& s, hipStream_t st);

@@ -1,10 +1,12 @@
-// Host packer and blob checker (format v1, documented in include/bitsmoe.h).
+// Host packer and blob checker (format v2, documented in include/bitsmoe.h).
 //
 // Quantizes each unit direction p_{e,k} at its own width and stores the
 // columns grouped by width, each 1..8-bit group as bit planes ("second
 // split", "Usage" and "execution" of the BitsMoE blog note's Methodology).
-// The quantizer runs in IEEE float32 with no contraction so that its codes
-// are reproducible bit for bit.
+// Plane words hold one 4-bit nibble per row (the row's bits of 4 adjacent
+// slots), so a lane that owns a row reads a contiguous run of words per
+// block.  The quantizer runs in IEEE float32 with no contraction so that its
+// codes are reproducible bit for bit.
 #include <math.h>
 #include <string.h>
 
@@ -95,28 +97,28 @@ int width_group(int b) {
   return -1;
 }
 
-// Canonical block layout of one expert from its per-width column counts.
-DirRec block_layout(const uint16_t count[kNumGroups], uint32_t n_slabs, uint32_t dout_pad) {
+// Canonical block layout of one expert from its per-width column counts
+// (cmax and block_offset are filled in by the caller).
+DirRec block_layout(const uint16_t count[kNumGroups], uint32_t n_seg) {
   DirRec d;
   memset(&d, 0, sizeof(d));
-  uint32_t n_nz = 0, mps = 0;
-  for (int g = 0; g < kNumGroups; ++g) {
-    d.count[g] = count[g];
-    n_nz += count[g];
-    if (g < kNumQGroups) mps += (uint32_t)count[g] * kGroupWidth[g];
+  const SlotGeo g = slot_geo(count);
+  uint32_t n_nz = 0;
+  for (int i = 0; i < kNumGroups; ++i) {
+    d.count[i] = count[i];
+    n_nz += count[i];
   }
   d.n_nz = n_nz;
   d.n_16 = count[kNumGroups - 1];
   d.n_q = n_nz - d.n_16;
-  d.masks_per_slab = mps;
-  d.a_off = (uint32_t)align_up(2ull * n_nz, 16);
-  d.s_off = (uint32_t)align_up(d.a_off + 4ull * n_nz, 16);
-  d.m_off = (uint32_t)align_up(d.s_off + 2ull * d.n_q, 16);
-  d.planes_off = (uint32_t)align_up(d.m_off + 2ull * d.n_q, 256);
+  d.seg_words = g.seg_words;
+  d.a_off = (uint32_t)align_up(2ull * g.n_slot, 16);
+  d.s_off = (uint32_t)align_up(d.a_off + 4ull * g.n_slot, 16);
+  d.m_off = (uint32_t)align_up(d.s_off + 2ull * g.n_qslot, 16);
+  d.planes_off = (uint32_t)align_up(d.m_off + 2ull * g.n_qslot, 256);
   // at least 16 zero bytes follow the planes, so 16-byte reads of the last
-  // masks stay inside the block
-  d.f16_off = (uint32_t)align_up(d.planes_off + 8ull * n_slabs * mps + 16, 256);
-  d.block_bytes = (uint32_t)align_up(d.f16_off + 2ull * d.n_16 * dout_pad, 256);
+  // words stay inside the block
+  d.block_bytes = (uint32_t)align_up(d.planes_off + 4ull * n_seg * g.seg_words + 16, 256);
   return d;
 }
 
@@ -134,8 +136,7 @@ int plan(int E, int dout, int r, const uint8_t* bits, std::vector<DirRec>& dirs,
   int st = check_dims(E, dout, r);
   if (st) return st;
   if (!bits) return fail(BITSMOE_EINVAL, "bits is null");
-  const uint32_t dout_pad = (uint32_t)align_up(dout, 64);
-  const uint32_t n_slabs = dout_pad / 64;
+  const uint32_t n_seg = (uint32_t)(align_up(dout, kSegRows) / kSegRows);
   dirs.resize(E);
   uint64_t pos = align_up(kHeaderBytes + (uint64_t)kDirRecBytes * E, 256);
   for (int e = 0; e < E; ++e) {
@@ -147,9 +148,11 @@ int plan(int E, int dout, int r, const uint8_t* bits, std::vector<DirRec>& dirs,
       if (g < 0) return fail(BITSMOE_EBITS, "bits[%d,%d]=%d not in {0,1,2,3,4,6,8,16}", e, k, b);
       ++count[g];
     }
-    dirs[e] = block_layout(count, n_slabs, dout_pad);
-    if ((uint64_t)dirs[e].f16_off + 2ull * dirs[e].n_16 * dout_pad > 0xFFFFFFFFull)
+    const SlotGeo g = slot_geo(count);
+    if (align_up(2ull * g.n_slot + 8ull * g.n_slot, 256) + 4ull * n_seg * g.seg_words + 512 >
+        0xFFFFFFFFull)
       return fail(BITSMOE_ESHAPE, "expert %d block exceeds 4 GiB", e);
+    dirs[e] = block_layout(count, n_seg);
     dirs[e].block_offset = pos;
     pos += dirs[e].block_bytes;
   }
@@ -179,43 +182,80 @@ void quantize_col(const float* p, int dout, int b, uint8_t* q, uint16_t* s_bits,
   *m_bits = mb;
 }
 
-void fill_block(const DirRec& d, int e, int dout, int r, uint32_t n_slabs, uint32_t dout_pad,
-                const float* p, const float* a, const uint8_t* bits, uint8_t* blk) {
+// Slot -> column list of one expert: groups of width 1,2,3,4,6,8,16, columns
+// in ascending k, each group padded with -1 to a multiple of 32.
+std::vector<int> slot_columns(const uint8_t* bits_e, int r) {
+  std::vector<int> cols;
+  for (int g = 0; g < kNumGroups; ++g) {
+    for (int k = 0; k < r; ++k)
+      if (bits_e[k] == kGroupWidth[g]) cols.push_back(k);
+    while (cols.size() % kGroupSlots) cols.push_back(-1);
+  }
+  return cols;
+}
+
+void fill_block(DirRec& d, int e, int dout, int r, uint32_t n_seg, const float* p,
+                const float* a, const uint8_t* bits, uint8_t* blk) {
+  const SlotGeo geo = slot_geo(d.count);
+  const std::vector<int> cols = slot_columns(bits + (size_t)e * r, r);
   uint16_t* kidx = (uint16_t*)blk;
   float* A = (float*)(blk + d.a_off);
   uint16_t* S = (uint16_t*)(blk + d.s_off);
   uint16_t* M = (uint16_t*)(blk + d.m_off);
-  uint64_t* P = (uint64_t*)(blk + d.planes_off);
-  uint16_t* F = (uint16_t*)(blk + d.f16_off);
-  std::vector<uint8_t> q(dout_pad, 0);
-  uint32_t col = 0, mask_base = 0;
+  uint32_t* P = (uint32_t*)(blk + d.planes_off);
+  const uint32_t dout_pad = n_seg * kSegRows;
+  // codes (1..8 bits) or fp16 bit patterns (16 bits) of the 4 slots of a block
+  std::vector<uint16_t> q4(4 * (size_t)dout_pad);
+  std::vector<uint8_t> q(dout_pad);
+  float cmax = 0.0f;
+  uint32_t slot = 0, word = 0;  // word: offset of the block inside a segment record
   for (int g = 0; g < kNumGroups; ++g) {
-    const int b = kGroupWidth[g];
-    for (int k = 0; k < r; ++k) {
-      if (bits[(size_t)e * r + k] != b) continue;
-      const float* pc = p + ((size_t)e * r + k) * dout;
-      kidx[col] = (uint16_t)k;
-      A[col] = a[(size_t)e * r + k];
-      if (b == 16) {
-        uint16_t* f = F + (size_t)(col - d.n_q) * dout_pad;
-        for (int i = 0; i < dout; ++i) f[i] = f32_to_f16(pc[i]);
-      } else {
-        quantize_col(pc, dout, b, q.data(), &S[col], &M[col]);
-        for (uint32_t sl = 0; sl < n_slabs; ++sl) {
-          for (int j = 0; j < b; ++j) {
-            uint64_t w = 0;
-            for (int t = 0; t < 64; ++t) {
-              const int row = (int)sl * 64 + t;
-              if (row < dout) w |= (uint64_t)((q[row] >> j) & 1u) << t;
-            }
-            P[(size_t)sl * d.masks_per_slab + mask_base + j] = w;
+    const int w = kGroupWidth[g];
+    for (uint32_t blkno = 0; blkno < geo.nb[g]; ++blkno, slot += 4, word += 4u * w) {
+      std::fill(q4.begin(), q4.end(), 0);
+      for (int u = 0; u < 4; ++u) {
+        const int k = cols[slot + u];
+        if (k < 0) continue;  // padding slot: everything stays 0
+        const float* pc = p + ((size_t)e * r + k) * dout;
+        const float ak = a[(size_t)e * r + k];
+        kidx[slot + u] = (uint16_t)k;
+        A[slot + u] = ak;
+        uint16_t* qs = &q4[(size_t)u * dout_pad];
+        if (w == 16) {
+          for (int i = 0; i < dout; ++i) qs[i] = f32_to_f16(pc[i]);
+          cmax = std::max(cmax, fabsf(ak));
+        } else {
+          quantize_col(pc, dout, w, q.data(), &S[slot + u], &M[slot + u]);
+          for (int i = 0; i < dout; ++i) qs[i] = q[i];
+          const float bound = fabsf(ak) * f16_to_f32(S[slot + u]);
+          cmax = std::max(cmax, bound);
+        }
+      }
+      for (uint32_t sg = 0; sg < n_seg; ++sg) {
+        uint32_t* rec = P + (size_t)sg * d.seg_words + word;
+        for (int oct = 0; oct < 4; ++oct) {
+          const uint32_t row0 = sg * kSegRows + 8u * oct;
+          if (w == 16) {
+            for (int rho = 0; rho < 8; ++rho)
+              for (int h = 0; h < 2; ++h)
+                rec[oct * 16 + 2 * rho + h] =
+                    (uint32_t)q4[(size_t)(2 * h) * dout_pad + row0 + rho] |
+                    ((uint32_t)q4[(size_t)(2 * h + 1) * dout_pad + row0 + rho] << 16);
+            continue;
+          }
+          for (int j = 0; j < w; ++j) {
+            uint32_t v = 0;
+            for (int rho = 0; rho < 8; ++rho)
+              for (int u = 0; u < 4; ++u)
+                v |= (uint32_t)((q4[(size_t)u * dout_pad + row0 + rho] >> j) & 1u)
+                     << (4 * rho + u);
+            rec[oct * w + j] = v;
           }
         }
-        mask_base += b;
       }
-      ++col;
     }
   }
+  d.cmax = cmax;
 }
 
 }  // namespace
@@ -255,16 +295,14 @@ int bitsmoe_pack(int E, int dout, int r, const float* p, const float* a,
   }
   uint8_t* blob = (uint8_t*)out;
   memset(blob, 0, total);
-  const uint32_t dout_pad = (uint32_t)align_up(dout, 64);
-  const uint32_t n_slabs = dout_pad / 64;
+  const uint32_t n_seg = (uint32_t)(align_up(dout, kSegRows) / kSegRows);
   unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
   nt = std::min<unsigned>(nt, (unsigned)E);
   std::vector<std::thread> pool;
   for (unsigned w = 0; w < nt; ++w) {
     pool.emplace_back([&, w]() {
       for (int e = (int)w; e < E; e += (int)nt)
-        fill_block(dirs[e], e, dout, r, n_slabs, dout_pad, p, a, bits,
-                   blob + dirs[e].block_offset);
+        fill_block(dirs[e], e, dout, r, n_seg, p, a, bits, blob + dirs[e].block_offset);
     });
   }
   for (auto& t : pool) t.join();
@@ -276,8 +314,8 @@ int bitsmoe_pack(int E, int dout, int r, const float* p, const float* a,
   h.E = (uint32_t)E;
   h.dout = (uint32_t)dout;
   h.r = (uint32_t)r;
-  h.dout_pad = dout_pad;
-  h.n_slabs = n_slabs;
+  h.dout_pad = n_seg * kSegRows;
+  h.n_seg = n_seg;
   h.header_bytes = kHeaderBytes;
   h.total_bytes = total;
   h.dir_offset = kHeaderBytes;
@@ -299,8 +337,8 @@ int bitsmoe_blob_check(const void* blob_v, size_t bytes, int* E_out, int* dout_o
     return fail(BITSMOE_EFORMAT, "bad header size or directory offset");
   if (check_dims((int)h.E, (int)h.dout, (int)h.r) || h.E > (1u << 20))
     return fail(BITSMOE_EFORMAT, "bad dimensions in header");
-  if (h.dout_pad != align_up(h.dout, 64) || h.n_slabs != h.dout_pad / 64)
-    return fail(BITSMOE_EFORMAT, "bad dout_pad / n_slabs");
+  if (h.dout_pad != align_up(h.dout, kSegRows) || h.n_seg != h.dout_pad / kSegRows)
+    return fail(BITSMOE_EFORMAT, "bad dout_pad / n_seg");
   if (h.total_bytes > bytes || h.total_bytes < kHeaderBytes + (uint64_t)kDirRecBytes * h.E)
     return fail(BITSMOE_EFORMAT, "total_bytes %llu inconsistent with buffer %zu",
                 (unsigned long long)h.total_bytes, bytes);
@@ -310,14 +348,18 @@ int bitsmoe_blob_check(const void* blob_v, size_t bytes, int* E_out, int* dout_o
   for (uint32_t e = 0; e < h.E; ++e) {
     DirRec d;
     memcpy(&d, blob + kHeaderBytes + (size_t)kDirRecBytes * e, sizeof(d));
-    DirRec c = block_layout(d.count, h.n_slabs, h.dout_pad);
+    DirRec c = block_layout(d.count, h.n_seg);
     c.block_offset = pos;
+    c.cmax = d.cmax;
+    if (!(d.cmax >= 0.0f) || !isfinite(d.cmax))
+      return fail(BITSMOE_EFORMAT, "directory record %u: bad coefficient bound", e);
     if (memcmp(&c, &d, sizeof(d)) != 0 || c.n_nz > h.r)
       return fail(BITSMOE_EFORMAT, "directory record %u inconsistent", e);
     pos += d.block_bytes;
     if (pos > h.total_bytes) return fail(BITSMOE_EFORMAT, "block %u beyond total_bytes", e);
     const uint16_t* kidx = (const uint16_t*)(blob + d.block_offset);
-    for (uint32_t c2 = 0; c2 < d.n_nz; ++c2)
+    const uint32_t n_slot = slot_geo(d.count).n_slot;
+    for (uint32_t c2 = 0; c2 < n_slot; ++c2)
       if (kidx[c2] >= h.r) return fail(BITSMOE_EFORMAT, "expert %u column index out of range", e);
   }
   if (pos != h.total_bytes) return fail(BITSMOE_EFORMAT, "total_bytes does not match blocks");

@@ -69,6 +69,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     Workload("tiny_t1", TINY, 1, ("uniform",)),
     Workload("tiny_t4", TINY, 4, ("uniform",)),
     Workload("wide_t2", WIDE, 2, ("uniform",)),
+    Workload("wide_t8", WIDE, 8, ("uniform",)),
+    Workload("tiny_t64", TINY, 64, ("zipf", 1.1)),
     Workload("qwen3_30b_a3b_t1", QWEN3_30B_A3B, 1, ("uniform",)),
     Workload("qwen3_30b_a3b_t32", QWEN3_30B_A3B, 32, ("zipf", 1.1)),
     Workload("mixtral_8x7b_t1", MIXTRAL_8X7B, 1, ("uniform",)),

@@ -116,7 +116,7 @@ def test_blob_check_rejects_corruption():
     blob = bm.pack(p, a, bits)
     assert bm.blob_check(blob) == (3, 96, 16)
     for mutate in (lambda b: b.__setitem__(0, 0),                 # magic
-                   lambda b: b.__setitem__(4, 2),                 # version
+                   lambda b: b.__setitem__(4, 1),                 # version
                    lambda b: b.__setitem__(len(b) - 300, b[len(b) - 300] ^ 1)):  # CRC
         bb = blob.copy()
         mutate(bb)

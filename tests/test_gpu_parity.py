@@ -141,8 +141,9 @@ def _check_h(got, href):
 
 
 @pytest.mark.parametrize("wl_name,steps", [("tiny_t1", 3), ("tiny_t4", 3), ("tiny_t8", 3),
-                                           ("qwen3_30b_a3b_t1", 3), ("qwen3_30b_a3b_t32", 1),
-                                           ("wide_t2", 2)])
+                                           ("tiny_t64", 2), ("qwen3_30b_a3b_t1", 3),
+                                           ("qwen3_30b_a3b_t32", 1), ("wide_t2", 2),
+                                           ("wide_t8", 1)])
 def test_gateup_full(bm, wl_name, steps):
     wl = synth.workload(wl_name)
     L, dev = device_layer(wl.layer.name)

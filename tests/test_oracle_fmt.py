@@ -25,20 +25,61 @@ def test_hand_built_planes():
     bits = np.array([[2, 0, 1]], np.uint8)
     blob = fmt.pack(p, a, bits)
     H = fmt.read_header(blob)
-    assert H["magic"] == b"BMOE" and H["dout_pad"] == 64 and H["n_slabs"] == 1
-    base, n_nz, n_q, n_16, mps = struct.unpack_from("<QIIII", blob, 128)
-    assert (n_nz, n_q, n_16, mps) == (2, 2, 0, 3)
+    assert H["magic"] == b"BMOE" and H["version"] == 2
+    assert H["dout_pad"] == 32 and H["n_seg"] == 1
+    base, n_nz, n_q, n_16, seg_words = struct.unpack_from("<QIIII", blob, 128)
+    # each used group padded to 32 slots = 8 blocks: 4 * 8 * (1 + 2) words
+    assert (n_nz, n_q, n_16, seg_words) == (2, 2, 0, 96)
     assert base == 256  # align256(128 + 64)
     cnt = struct.unpack_from("<7H", blob, 128 + 48)
     assert cnt == (1, 1, 0, 0, 0, 0, 0)
-    # width group 1 first (column 2), then width 2 (column 0)
-    assert struct.unpack_from("<2H", blob, base) == (2, 0)
+    # width group 1 first (column 2 + 31 padding slots), then width 2 (column 0)
+    kidx = struct.unpack_from("<64H", blob, base)
+    assert kidx[0] == 2 and kidx[32] == 0 and not any(kidx[1:32]) and not any(kidx[33:])
     a_off, s_off, m_off, p_off = struct.unpack_from("<IIII", blob, 128 + 24)
-    assert struct.unpack_from("<2f", blob, base + a_off) == (0.5, 2.0)
-    words = struct.unpack_from("<3Q", blob, base + p_off)
-    # column 2, plane 0: codes [0,1,0,0] -> bit 1 -> 0b0010
-    # column 0, plane 0: codes&1 = [0,1,0,1] -> 0b1010; plane 1: [0,0,1,1] -> 0b1100
-    assert words == (0b0010, 0b1010, 0b1100)
+    a_s = struct.unpack_from("<64f", blob, base + a_off)
+    assert (a_s[0], a_s[32]) == (0.5, 2.0) and sum(map(abs, a_s)) == 2.5
+    # s of column 0 is fp16(1/3) = 0.333251953125; of column 2, 0.25
+    s = struct.unpack_from("<64e", blob, base + s_off)
+    assert (s[0], s[32]) == (0.25, 0.333251953125) and sum(s) == 0.25 + 0.333251953125
+    cmax, = struct.unpack_from("<f", blob, 128 + 40)
+    assert cmax == np.float32(2.0) * np.float32(0.333251953125)
+    words = struct.unpack_from("<96I", blob, base + p_off)
+    # group 1 (width 1), block 0, octet 0: slot 0 (column 2) has code 1 in
+    #   row 1 -> bit 4*1 + 0; octets 1-3 are rows 8..31 (padding) -> 0;
+    #   blocks 1-7 of the group are padding (4 words each)
+    # group 2 (width 2) starts at word 4 * 8 * 1 = 32; its block 0, octet 0:
+    #   slot 32 (column 0) codes [0,1,2,3] in rows 0..3
+    #   plane 0: rows 1, 3 -> bits 4, 12; plane 1: rows 2, 3 -> bits 8, 12
+    expect = [0] * 96
+    expect[0] = 0x10
+    expect[32], expect[33] = 0x1010, 0x1100
+    assert words == tuple(expect)
+
+
+def test_hand_built_fp16_block():
+    # one 16-bit column among 5: its block holds row-major fp16 pairs
+    dout = 40
+    p = np.zeros((1, 5, dout), np.float32)
+    for k in range(5):
+        p[0, k, :] = (np.arange(dout) + 100 * k) / 1024.0   # exact in fp16
+    a = np.ones((1, 5), np.float32)
+    bits = np.array([[0, 16, 16, 0, 16]], np.uint8)
+    blob = fmt.pack(p, a, bits)
+    H = fmt.read_header(blob)
+    assert (H["dout_pad"], H["n_seg"]) == (64, 2)
+    base, n_nz, n_q, n_16, seg_words = struct.unpack_from("<QIIII", blob, 128)
+    assert (n_nz, n_q, n_16, seg_words) == (3, 0, 3, 4 * 8 * 16)
+    p_off, = struct.unpack_from("<I", blob, 128 + 36)
+    W = np.frombuffer(blob, "<u4", count=2 * 512, offset=base + p_off).reshape(2, 512)
+    f16 = lambda v: int(np.float16(v).view(np.uint16))
+    # segment 1, octet 0, rho 2 = row 34; word 2*rho + h, h = 1 -> slots 2, 3
+    # slot 2 is column 4, slot 3 is padding
+    assert W[1, 0 * 16 + 2 * 2 + 1] == f16((34 + 400) / 1024.0)
+    # h = 0 -> slots 0 (column 1) and 1 (column 2)
+    assert W[1, 2 * 2] == f16((34 + 100) / 1024.0) | (f16((34 + 200) / 1024.0) << 16)
+    # rows >= dout (segment 1, octet 1, rows 40..47) are 0
+    assert np.all(W[1, 16:32] == 0)
 
 
 def _random_layer(E, r, dout, bits, seed):
@@ -48,7 +89,7 @@ def _random_layer(E, r, dout, bits, seed):
     return p, a, bits.astype(np.uint8)
 
 
-@pytest.mark.parametrize("dout", [96, 64, 130])
+@pytest.mark.parametrize("dout", [96, 64, 130, 33])
 def test_round_trip_all_widths(dout):
     E, r = 4, 24
     rng = np.random.default_rng(dout)
@@ -81,8 +122,9 @@ def test_header_alignment_and_crc():
     for e in range(3):
         base, = struct.unpack_from("<Q", blob, 128 + 64 * e)
         assert base % 256 == 0
-        offs = struct.unpack_from("<6I", blob, 128 + 64 * e + 24)
-        assert offs[3] % 256 == 0 and offs[4] % 256 == 0 and offs[5] % 256 == 0
+        offs = struct.unpack_from("<4I", blob, 128 + 64 * e + 24)
+        nbytes, = struct.unpack_from("<I", blob, 128 + 64 * e + 44)
+        assert offs[3] % 256 == 0 and nbytes % 256 == 0
     bad = bytearray(blob)
     bad[-300] ^= 1
     with pytest.raises(ValueError):

@@ -105,10 +105,6 @@ def test_silu_sign_caught(monkeypatch):
 
 
 def test_plane_bit_order_caught(monkeypatch):
-    orig = np.packbits
-
-    def msb_first(a, axis=None, bitorder="big"):
-        return orig(a, axis=axis, bitorder="big")
-
-    monkeypatch.setattr(fmt.np, "packbits", msb_first)
+    # rows and slots swapped inside a plane word
+    monkeypatch.setattr(fmt, "nibble_shift", lambda rho, u: 8 * u + rho)
     assert _fails(T_fmt.test_hand_built_planes)
