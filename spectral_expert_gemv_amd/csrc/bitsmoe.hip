@@ -371,7 +371,7 @@ GateUpPlan gateup_plan(int T, int k, int E, int r) {
   p.zpart_off = align_up((size_t)T * 2 * r * sizeof(float), 256);
   p.zt_off = align_up(p.zpart_off + (size_t)T * nzp * sizeof(float), 256);
   p.sync_off = align_up(p.zt_off + (size_t)T * 2 * r * sizeof(uint64_t), 256);
-  p.route_off = align_up(p.sync_off + 2 * sizeof(uint32_t), 256);
+  p.route_off = align_up(p.sync_off + 128 + 64 * 128, 256);
   p.total = align_up(p.route_off + (1 + 3 * (size_t)tile_cap(T, k, E) + P) * sizeof(int), 256);
   return p;
 }
@@ -471,6 +471,7 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     fa.zt = (uint64_t*)(wsb + plan.zt_off);
     fa.epoch = (uint32_t*)(wsb + plan.sync_off);
     fa.arrive = fa.epoch + 1;
+    fa.hint = fa.epoch + 32;
     fa.grid = fgrid;
     launch_gateup_fused(fa, s);
     return launch_status("one-launch gate/up");

@@ -53,14 +53,20 @@ constexpr int kFWaves = 8;
 constexpr int kFThreads = kFWaves * kWave;  // 512
 constexpr int kFProj = 256;                 // lanes per projection (waves 0-3 gate, 4-7 up)
 constexpr int kFPW = kFWaves / 2;           // waves per projection
-constexpr int kFMaxW = 12288;               // plane words per projection per chunk
+constexpr int kFMaxW = 10240;               // plane words per projection per chunk
 constexpr int kFMaxS = 4320;                // slots per projection (r <= 4096, padded)
 // slots per lane of the coefficient pass: 9 covers r <= 2048, 17 r <= 4096
 constexpr int kFPre = 4;                    // Phi^T rows a wave loads up front
 constexpr uint32_t kFSpin = 1u << 20;
+constexpr int kFHint = 64;         // hint counters (one per 64th of the producing waves)
+constexpr int kFHintStride = 32;   // u32 between counters (one 128-byte line each)
+
+constexpr int kFZ = 2 * kFusedMaxR;         // z values of one token (gate, up)
+constexpr int kFZPer = kFZ / kFThreads;     // tagged z words per lane
 
 struct __align__(16) FusedLds {
   uint32_t W[2][kFMaxW + 64];
+  float Z[kFZ];
   _Float16 Chi[2][kFMaxS];
   _Float16 Clo[2][kFMaxS];
   float red[2][kFPW][kSegRows];
@@ -78,10 +84,10 @@ __device__ __forceinline__ float fdot8(uint4 a, uint4 b, float acc) {
   return acc;
 }
 
-// Dot product of one Phi^T row (p: this lane's 4 16-byte units of the first
-// 2048 inputs) with token tt's x, over all din inputs.
-__device__ __forceinline__ float zdot(const FusedArgs& s, const uint4* prow, const uint4 (&p)[4],
-                                      const uint4 (&xv)[4], int tt, int lane) {
+// This lane's partial dot product of one Phi^T row (p: this lane's 4 16-byte
+// units of the first 2048 inputs) with token tt's x, over all din inputs.
+__device__ __forceinline__ float zpart(const FusedArgs& s, const uint4* prow, const uint4 (&p)[4],
+                                       const uint4 (&xv)[4], int tt, int lane) {
   const uint4* xt = s.x + (size_t)tt * s.din8;
   float acc = 0.f;
 #pragma unroll
@@ -102,23 +108,35 @@ __device__ __forceinline__ float zdot(const FusedArgs& s, const uint4* prow, con
       if (i < s.din8) acc = fdot8(q4[u], xt[i], acc);
     }
   }
-  return wave_sum(acc);
+  return acc;
 }
 
-__device__ __forceinline__ void publish_z(const FusedArgs& s, int tt, int n, float v, uint32_t tag,
-                                          int lane) {
-  if (lane == 0) {
-    const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
-    __hip_atomic_store(&s.zt[(size_t)tt * 2 * s.g.r + n], w, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void publish_z(const FusedArgs& s, int tt, int n, float v, uint32_t tag) {
+  const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
+  __hip_atomic_store(&s.zt[(size_t)tt * 2 * s.g.r + n], w, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One transposing exchange of a kFPre-value reduction: lanes with bit O set
+// keep the upper half of the values, the others the lower half.
+template <int O>
+__device__ __forceinline__ void tstep(float (&v)[kFPre], bool up) {
+#pragma unroll
+  for (int i = 0; i < O; ++i) {
+    const float send = up ? v[i] : v[i + O];
+    const float keep = up ? v[i + O] : v[i];
+    v[i] = keep + __shfl_xor(send, O, kWave);
   }
 }
 
 // Waves 0-3 of work-group b: z rows [n0, n0 + nrw) of every token, published
 // tagged.  The loads of the first kFPre rows and of x are all issued before
-// the first is used, in straight-line code (so that they stay together).
+// the first is used, in straight-line code (so that they stay together); the
+// kFPre partial sums are reduced together (2 transposing exchanges leave row
+// lane & 3 in every lane, 4 more finish the sum), and lane i publishes row i.
 __device__ __forceinline__ void produce_z(const FusedArgs& s, int n0, int nrw, int lane,
                                           uint32_t tag) {
+  static_assert(kFPre == 4, "the transposing reduction is written for 4 rows");
   const int R = 2 * s.g.r;
   uint4 pv[kFPre][4];
   uint4 xv[4];
@@ -137,13 +155,20 @@ __device__ __forceinline__ void produce_z(const FusedArgs& s, int n0, int nrw, i
     const int i = lane + u * kWave;
     xv[u] = i < s.din8 ? s.x[i] : make_uint4(0, 0, 0, 0);
   }
+  for (int tt = 0; tt < s.T; ++tt) {
+    float v[kFPre];
 #pragma unroll
-  for (int q = 0; q < kFPre; ++q) {
-    const int n = n0 + q;
-    if (q < nrw && n < R)
-      for (int tt = 0; tt < s.T; ++tt)
-        publish_z(s, tt, n, zdot(s, s.phi_t + (size_t)n * s.din8, pv[q], xv, tt, lane), tag,
-                  lane);
+    for (int q = 0; q < kFPre; ++q) {
+      const int n = (q < nrw && n0 + q < R) ? n0 + q : 0;
+      v[q] = zpart(s, s.phi_t + (size_t)n * s.din8, pv[q], xv, tt, lane);
+    }
+    tstep<2>(v, (lane & 2) != 0);
+    tstep<1>(v, (lane & 1) != 0);
+    float z = v[0];
+#pragma unroll
+    for (int off = 4; off < kWave; off <<= 1) z += __shfl_xor(z, off, kWave);
+    const int q = lane & 3;
+    if (lane < kFPre && q < nrw && n0 + q < R) publish_z(s, tt, n0 + q, z, tag);
   }
   for (int q = kFPre; q < nrw && n0 + q < R; ++q) {  // rows beyond the first kFPre
     const int n = n0 + q;
@@ -154,8 +179,82 @@ __device__ __forceinline__ void produce_z(const FusedArgs& s, int n0, int nrw, i
       const int i = lane + u * kWave;
       p0[u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
     }
-    for (int tt = 0; tt < s.T; ++tt)
-      publish_z(s, tt, n, zdot(s, prow, p0, xv, tt, lane), tag, lane);
+    for (int tt = 0; tt < s.T; ++tt) {
+      const float z = wave_sum(zpart(s, prow, p0, xv, tt, lane));
+      if (lane == 0) publish_z(s, tt, n, z, tag);
+    }
+  }
+}
+
+// Bounded wait until the hint counters say that every producing wave has
+// published (lane i reads counter i; 64 counters on separate lines keep the
+// producers' increments from contending).  Only a hint: the tags decide.
+__device__ __forceinline__ void wait_hint(const uint32_t* hint, uint32_t nzw) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t spins = 0;
+  while (true) {
+    const uint32_t c =
+        __hip_atomic_load(hint + kFHintStride * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float tot = wave_sum((float)c);  // exact: counts stay far below 2^24
+    if ((uint32_t)tot >= nzw || ++spins >= kFSpin / 64) break;
+    __builtin_amdgcn_s_sleep(4);
+  }
+}
+
+// The token's 2r tagged z words, copied into LDS as floats by all lanes with
+// coalesced loads.  The first read is an ordinary (L2-cached) load, issued
+// once the hint says the producers are done, so the work-groups of one XCD
+// share it; words whose tag is not there yet are re-read with device-coherent
+// loads until it is (bounded wait).  Returns false on a time-out.
+__device__ __forceinline__ bool stage_z(const uint64_t* src, int R, uint32_t tag, float* Z) {
+  uint64_t zw[kFZPer];
+#pragma unroll
+  for (int j = 0; j < kFZPer; ++j) {
+    const int i = (int)threadIdx.x + kFThreads * j;
+    zw[j] = i < R ? src[i] : ((uint64_t)tag << 32);
+  }
+  uint32_t spins = 0;
+  while (true) {
+    bool ready = true;
+#pragma unroll
+    for (int j = 0; j < kFZPer; ++j) ready &= (uint32_t)(zw[j] >> 32) == tag;
+    if (__all(ready) || spins >= kFSpin) break;
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int j = 0; j < kFZPer; ++j) {
+      const int i = (int)threadIdx.x + kFThreads * j;
+      if ((uint32_t)(zw[j] >> 32) != tag)
+        zw[j] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    ++spins;
+  }
+#pragma unroll
+  for (int j = 0; j < kFZPer; ++j) {
+    const int i = (int)threadIdx.x + kFThreads * j;
+    if (i < R) Z[i] = __uint_as_float((uint32_t)zw[j]);
+  }
+  return spins < kFSpin;
+}
+
+// Metadata of this lane's slots lp, lp + 256, ... of projection p (loads
+// issued before z is needed).
+template <int kFSper>
+struct SlotMeta {
+  uint32_t k[kFSper];
+  float a[kFSper];
+  uint32_t sm[kFSper];  // fp16 s | fp16 m << 16 (s = 1, m = 0 for 16-bit and padding)
+};
+template <int kFSper>
+__device__ __forceinline__ void load_meta(const SegProj& p, int lp, int r, SlotMeta<kFSper>& md,
+                                          bool& good) {
+#pragma unroll
+  for (int i = 0; i < kFSper; ++i) {
+    const uint32_t sl = (uint32_t)lp + kFProj * i;
+    const uint32_t k = sl < p.n_slot ? p.kidx[sl] : 0u;
+    md.a[i] = sl < p.n_slot ? p.A[sl] : 0.f;
+    md.sm[i] = sl < p.n_qslot ? ((uint32_t)p.S[sl] | ((uint32_t)p.M[sl] << 16)) : 0x3C00u;
+    good &= k < (uint32_t)r;
+    md.k[i] = k < (uint32_t)r ? k : 0u;
   }
 }
 
@@ -190,15 +289,24 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
   // ---- waves 0-3: z for their contiguous run of Phi^T rows, first ----
   const int nzw = G * kFPW;              // producing waves
   const int nrw = (R + nzw - 1) / nzw;   // rows per producing wave
-  if (pj == 0) produce_z(s, ((int)blockIdx.x * kFPW + wp) * nrw, nrw, lane, tag);
+  if (pj == 0) {
+    produce_z(s, ((int)blockIdx.x * kFPW + wp) * nrw, nrw, lane, tag);
+    if (lane == 0)
+      __hip_atomic_fetch_add(s.hint + kFHintStride * (((int)blockIdx.x * kFPW + wp) & (kFHint - 1)),
+                             1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
+  int zt_cached = -1;  // token whose z is in L.Z
+  bool zok = true;     // this lane's words of L.Z arrived (folded into every unit's ok)
   bool first = true;
   for (int u = (int)blockIdx.x; u < U || first; u += G) {
     const bool have = u < U;
     const int pair = have ? u % np : 0;
     const int sg = have ? u / np : 0;
     const int t = pair / a.ktop;
-    const int e = have ? __builtin_amdgcn_readfirstlane(a.ids[pair]) : 0;
+    // scalar load: unlike a vector load it does not wait behind this wave's
+    // outstanding z stores (vector memory counts return in order)
+    const int e = have ? (int)*(CU32*)(a.ids + pair) : 0;
     // projection of this wave; on the first unit waves 4-7 stage both
     // (4-5 gate, 6-7 up) while waves 0-3 produce z
     const int sp = first ? (wv >> 1) & 1 : pj;
@@ -220,97 +328,55 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
                                  : uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
                                                         load_rec_s(blob, e, a.E), load_hdr(blob),
                                                         a.E, a.dout, a.r));
-    // ---- coefficients of this projection's slots: every metadata load and
-    // tagged z gather is in flight before the first is used; gathers whose tag
-    // is not there yet are re-issued together ----
+    // ---- coefficients: metadata loads first, then the token's z into LDS ----
+    SlotMeta<kFSper> md;
     bool good = P.ok;
-    float cv[kFSper];  // coefficients of this lane's slots
-    float bias = 0.f, cmx = 0.f;
-    bool zready;
+    load_meta<kFSper>(P, lp, a.r, md, good);
+    if (t != zt_cached) {
+      if (zt_cached < 0) wait_hint(s.hint, (uint32_t)nzw);
+      zok = stage_z(s.zt + (size_t)t * R, R, tag, &L.Z[0]);
+      zt_cached = t;
+    }
+    __syncthreads();
+    good = good && zok;
+    float cv[kFSper];
     {
-      const uint64_t* zrow = s.zt + (size_t)t * R + (pj ? a.r : 0);
-      uint32_t kv[kFSper];
-      float av[kFSper];
-      uint32_t sm[kFSper];  // fp16 s | fp16 m << 16
-      uint64_t zw[kFSper];
+      const float* zrow = &L.Z[pj ? a.r : 0];
+      float bias = 0.f, cmx = 0.f;
 #pragma unroll
       for (int i = 0; i < kFSper; ++i) {
-        const uint32_t sl = (uint32_t)lp + kFProj * i;
-        kv[i] = sl < P.n_slot ? P.kidx[sl] : 0u;
-      }
-#pragma unroll
-      for (int i = 0; i < kFSper; ++i) {
-        const uint32_t sl = (uint32_t)lp + kFProj * i;
-        good &= kv[i] < (uint32_t)a.r;
-        kv[i] = kv[i] < (uint32_t)a.r ? kv[i] : 0u;
-        zw[i] = sl < P.n_slot
-                    ? __hip_atomic_load(zrow + kv[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                    : ((uint64_t)tag << 32);
-      }
-      // a, s and m: loaded with the gathers when registers allow (r <= 2048),
-      // else after them
-      auto load_asm = [&]() {
-#pragma unroll
-        for (int i = 0; i < kFSper; ++i) {
-          const uint32_t sl = (uint32_t)lp + kFProj * i;
-          const bool q = sl < P.n_qslot;
-          av[i] = sl < P.n_slot ? P.A[sl] : 0.f;
-          sm[i] = q ? ((uint32_t)P.S[sl] | ((uint32_t)P.M[sl] << 16)) : 0x3C00u;
-        }
-      };
-      if constexpr (kFSper <= 9) load_asm();
-      uint32_t spins = 0;
-      while (true) {
-        bool ready = true;
-#pragma unroll
-        for (int i = 0; i < kFSper; ++i) ready &= (uint32_t)(zw[i] >> 32) == tag;
-        if (__all(ready) || spins >= kFSpin) break;
-        __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-        for (int i = 0; i < kFSper; ++i)
-          if ((uint32_t)(zw[i] >> 32) != tag)
-            zw[i] = __hip_atomic_load(zrow + kv[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ++spins;
-      }
-      zready = spins < kFSpin;
-      if constexpr (kFSper > 9) load_asm();
-#pragma unroll
-      for (int i = 0; i < kFSper; ++i) {
-        const float z = __uint_as_float((uint32_t)zw[i]);
-        const float az = av[i] * z;
-        const float sv = __half2float(__ushort_as_half((unsigned short)(sm[i] & 0xFFFFu)));
-        const float mv = __half2float(__ushort_as_half((unsigned short)(sm[i] >> 16)));
+        const float az = md.a[i] * zrow[md.k[i]];
+        const float sv = __half2float(__ushort_as_half((unsigned short)(md.sm[i] & 0xFFFFu)));
+        const float mv = __half2float(__ushort_as_half((unsigned short)(md.sm[i] >> 16)));
         bias += az * mv;          // m = 0 for 16-bit and padding slots
         const float c = az * sv;  // s = 1 for 16-bit slots
         cv[i] = c;
         cmx = fmaxf(cmx, fabsf(c));
       }
-    }
-    good = good && zready;
-    {
-      float m = cmx;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+      for (int off = 32; off > 0; off >>= 1) cmx = fmaxf(cmx, __shfl_xor(cmx, off, kWave));
       const float bw = wave_sum(bias);
       const bool wok = __all(good);
       if (lane == 0) {
-        L.pmax[pj][wp] = m;
+        L.pmax[pj][wp] = cmx;
         L.pbias[pj][wp] = bw;
         L.pok[pj][wp] = wok;
       }
     }
     __syncthreads();
-    const float pmx = fmaxf(fmaxf(L.pmax[pj][0], L.pmax[pj][1]), fmaxf(L.pmax[pj][2], L.pmax[pj][3]));
-    const int S = coef_shift(pmx, 1.0f);
+    {
+      const float pmx =
+          fmaxf(fmaxf(L.pmax[pj][0], L.pmax[pj][1]), fmaxf(L.pmax[pj][2], L.pmax[pj][3]));
+      const int S = coef_shift(pmx, 1.0f);
 #pragma unroll
-    for (int i = 0; i < kFSper; ++i) {
-      const uint32_t sl = (uint32_t)lp + kFProj * i;
-      // slots up to the next multiple of 32 are written (zeros past n_slot)
-      if (sl < (P.n_slot + 31u) / 32u * 32u) {
-        _Float16 hi, lo;
-        split_coef(cv[i], S, hi, lo);
-        L.Chi[pj][sl] = hi;
-        L.Clo[pj][sl] = lo;
+      for (int i = 0; i < kFSper; ++i) {
+        const uint32_t sl = (uint32_t)lp + kFProj * i;
+        if (sl < kFMaxS) {  // zeros past n_slot
+          _Float16 hi, lo;
+          split_coef(cv[i], S, hi, lo);
+          L.Chi[pj][sl] = hi;
+          L.Clo[pj][sl] = lo;
+        }
       }
     }
     // chunk counts of both projections (they advance together)
@@ -379,6 +445,9 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     const uint32_t n =
         __hip_atomic_fetch_add(s.arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (n == (uint32_t)G - 1) {
+      for (int i = 0; i < kFHint; ++i)
+        __hip_atomic_store(s.hint + kFHintStride * i, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(s.arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(s.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

@@ -19,7 +19,8 @@ struct GateUpPlan {
   size_t z_off;       // T x 2r float32 (projection launch of the batched path)
   size_t zpart_off;   // T x ceil(2r / 16) float32: max |z| per projection work-group
   size_t zt_off;      // T x 2r uint64 tagged z (one-launch path)
-  size_t sync_off;    // uint32 epoch, uint32 grid arrival counter (left at 0)
+  size_t sync_off;    // uint32 epoch, uint32 grid arrival counter (left at 0), then
+                      // 64 hint counters 128 bytes apart (left at 0)
   size_t route_off;   // route lists (see RouteLists)
   size_t total;
 };
@@ -48,6 +49,7 @@ struct FusedArgs {
   uint64_t* zt;        // T x 2r tagged z
   uint32_t* epoch;     // tag of the previous launch
   uint32_t* arrive;    // work-groups done (0 between launches)
+  uint32_t* hint;      // 64 counters, 32 words apart: producing waves done (0 between launches)
   int grid;            // multiple of 8, all work-groups resident
 };
 size_t fused_lds_bytes();
