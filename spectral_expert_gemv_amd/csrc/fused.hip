@@ -129,49 +129,58 @@ __device__ __forceinline__ void tstep(float (&v)[kFPre], bool up) {
   }
 }
 
-// Waves 0-3 of work-group b: z rows [n0, n0 + nrw) of every token, published
-// tagged.  The loads of the first kFPre rows and of x are all issued before
-// the first is used, in straight-line code (so that they stay together); the
-// kFPre partial sums are reduced together (2 transposing exchanges leave row
-// lane & 3 in every lane, 4 more finish the sum), and lane i publishes row i.
-__device__ __forceinline__ void produce_z(const FusedArgs& s, int n0, int nrw, int lane,
-                                          uint32_t tag) {
-  static_assert(kFPre == 4, "the transposing reduction is written for 4 rows");
-  const int R = 2 * s.g.r;
+// Waves 0-3 of work-group b own z rows [n0, n0 + nrw) of every token.  The
+// loads of the first kFPre Phi^T rows and of x go out first, in straight-line
+// code (so that they stay together and ahead of anything that depends on a
+// load); z_finish then reduces the kFPre partial sums together (2 transposing
+// exchanges leave row lane & 3 in every lane, 4 more finish the sum), lane i
+// publishes row i, and rows beyond the first kFPre follow one at a time.
+struct PhiRegs {
   uint4 pv[kFPre][4];
   uint4 xv[4];
+};
+
+__device__ __forceinline__ void phi_issue(const FusedArgs& s, int n0, int nrw, int lane,
+                                          PhiRegs& q) {
+  const int R = 2 * s.g.r;
 #pragma unroll
-  for (int q = 0; q < kFPre; ++q) {
-    const int n = (q < nrw && n0 + q < R) ? n0 + q : 0;
+  for (int j = 0; j < kFPre; ++j) {
+    const int n = (j < nrw && n0 + j < R) ? n0 + j : 0;
     const uint4* prow = s.phi_t + (size_t)n * s.din8;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = lane + u * kWave;
-      pv[q][u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
+      q.pv[j][u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
     }
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = lane + u * kWave;
-    xv[u] = i < s.din8 ? s.x[i] : make_uint4(0, 0, 0, 0);
+    q.xv[u] = i < s.din8 ? s.x[i] : make_uint4(0, 0, 0, 0);
   }
+}
+
+__device__ __forceinline__ void z_finish(const FusedArgs& s, int n0, int nrw, int lane,
+                                         uint32_t tag, const PhiRegs& q) {
+  static_assert(kFPre == 4, "the transposing reduction is written for 4 rows");
+  const int R = 2 * s.g.r;
   for (int tt = 0; tt < s.T; ++tt) {
     float v[kFPre];
 #pragma unroll
-    for (int q = 0; q < kFPre; ++q) {
-      const int n = (q < nrw && n0 + q < R) ? n0 + q : 0;
-      v[q] = zpart(s, s.phi_t + (size_t)n * s.din8, pv[q], xv, tt, lane);
+    for (int j = 0; j < kFPre; ++j) {
+      const int n = (j < nrw && n0 + j < R) ? n0 + j : 0;
+      v[j] = zpart(s, s.phi_t + (size_t)n * s.din8, q.pv[j], q.xv, tt, lane);
     }
     tstep<2>(v, (lane & 2) != 0);
     tstep<1>(v, (lane & 1) != 0);
     float z = v[0];
 #pragma unroll
     for (int off = 4; off < kWave; off <<= 1) z += __shfl_xor(z, off, kWave);
-    const int q = lane & 3;
-    if (lane < kFPre && q < nrw && n0 + q < R) publish_z(s, tt, n0 + q, z, tag);
+    const int j = lane & 3;
+    if (lane < kFPre && j < nrw && n0 + j < R) publish_z(s, tt, n0 + j, z, tag);
   }
-  for (int q = kFPre; q < nrw && n0 + q < R; ++q) {  // rows beyond the first kFPre
-    const int n = n0 + q;
+  for (int j = kFPre; j < nrw && n0 + j < R; ++j) {  // rows beyond the first kFPre
+    const int n = n0 + j;
     const uint4* prow = s.phi_t + (size_t)n * s.din8;
     uint4 p0[4];
 #pragma unroll
@@ -180,7 +189,7 @@ __device__ __forceinline__ void produce_z(const FusedArgs& s, int n0, int nrw, i
       p0[u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
     }
     for (int tt = 0; tt < s.T; ++tt) {
-      const float z = wave_sum(zpart(s, prow, p0, xv, tt, lane));
+      const float z = wave_sum(zpart(s, prow, p0, q.xv, tt, lane));
       if (lane == 0) publish_z(s, tt, n, z, tag);
     }
   }
@@ -236,26 +245,58 @@ __device__ __forceinline__ bool stage_z(const uint64_t* src, int R, uint32_t tag
   return spins < kFSpin;
 }
 
-// Metadata of this lane's slots lp, lp + 256, ... of projection p (loads
-// issued before z is needed).
+// Slot metadata of one lane: kFSper = 8 V + 1 slots, the 8 V contiguous
+// slots 8 V lp .. 8 V lp + 8 V - 1 (read with 16-byte loads) and the tail
+// slot 2048 V + lp (n_slot <= r + 7 * 31 < 2048 V + 256).  Only loads: the
+// component indices are checked where they are used, so nothing here waits.
 template <int kFSper>
 struct SlotMeta {
+  static constexpr int V = (kFSper - 1) / 8;
   uint32_t k[kFSper];
   float a[kFSper];
   uint32_t sm[kFSper];  // fp16 s | fp16 m << 16 (s = 1, m = 0 for 16-bit and padding)
 };
 template <int kFSper>
-__device__ __forceinline__ void load_meta(const SegProj& p, int lp, int r, SlotMeta<kFSper>& md,
-                                          bool& good) {
+__device__ __forceinline__ uint32_t meta_slot(int lp, int i) {
+  constexpr int V = SlotMeta<kFSper>::V;
+  return i < 8 * V ? (uint32_t)(8 * V * lp + i) : (uint32_t)(2048 * V + lp);
+}
+// A 16-byte vector of array x at element index i0 is read only when i0 < n:
+// it then ends at most 28 bytes past the array, still inside the expert
+// block (the next array, or the planes and the block's 16-byte tail).
+template <int kFSper>
+__device__ __forceinline__ void load_meta(const SegProj& p, int lp, SlotMeta<kFSper>& md) {
+  constexpr int V = SlotMeta<kFSper>::V;
+  static_assert(kFSper == 8 * V + 1, "8 V contiguous slots and one tail slot");
+  const uint32_t s0 = 8u * V * (uint32_t)lp;
+  const uint4 z4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
-  for (int i = 0; i < kFSper; ++i) {
-    const uint32_t sl = (uint32_t)lp + kFProj * i;
-    const uint32_t k = sl < p.n_slot ? p.kidx[sl] : 0u;
-    md.a[i] = sl < p.n_slot ? p.A[sl] : 0.f;
-    md.sm[i] = sl < p.n_qslot ? ((uint32_t)p.S[sl] | ((uint32_t)p.M[sl] << 16)) : 0x3C00u;
-    good &= k < (uint32_t)r;
-    md.k[i] = k < (uint32_t)r ? k : 0u;
+  for (int v = 0; v < V; ++v) {
+    const uint32_t sv = s0 + 8u * v;
+    const uint4 kq = sv < p.n_slot ? *reinterpret_cast<const uint4*>(p.kidx + sv) : z4;
+    const uint4 a0 = sv < p.n_slot ? *reinterpret_cast<const uint4*>(p.A + sv) : z4;
+    const uint4 a1 = sv + 4 < p.n_slot ? *reinterpret_cast<const uint4*>(p.A + sv + 4) : z4;
+    const uint4 sq = sv < p.n_qslot ? *reinterpret_cast<const uint4*>(p.S + sv) : z4;
+    const uint4 mq = sv < p.n_qslot ? *reinterpret_cast<const uint4*>(p.M + sv) : z4;
+    const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
+    const uint32_t aw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const uint32_t sw[4] = {sq.x, sq.y, sq.z, sq.w};
+    const uint32_t mw[4] = {mq.x, mq.y, mq.z, mq.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t sl = sv + j;
+      const uint32_t sh = 16 * (j & 1);
+      md.k[8 * v + j] = sl < p.n_slot ? (kw[j >> 1] >> sh) & 0xFFFFu : 0u;
+      md.a[8 * v + j] = sl < p.n_slot ? __uint_as_float(aw[j]) : 0.f;
+      md.sm[8 * v + j] = sl < p.n_qslot
+                             ? ((sw[j >> 1] >> sh) & 0xFFFFu) | (((mw[j >> 1] >> sh) & 0xFFFFu) << 16)
+                             : 0x3C00u;
+    }
   }
+  const uint32_t sl = 2048u * V + (uint32_t)lp;
+  md.k[8 * V] = sl < p.n_slot ? p.kidx[sl] : 0u;
+  md.a[8 * V] = sl < p.n_slot ? p.A[sl] : 0.f;
+  md.sm[8 * V] = sl < p.n_qslot ? ((uint32_t)p.S[sl] | ((uint32_t)p.M[sl] << 16)) : 0x3C00u;
 }
 
 // Stage chunk [b0, b1) of segment sg of projection p into arena (nl lanes).
@@ -286,99 +327,146 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
   const int np = a.npairs;
   const int U = np * a.n_seg;
 
-  // ---- waves 0-3: z for their contiguous run of Phi^T rows, first ----
   const int nzw = G * kFPW;              // producing waves
   const int nrw = (R + nzw - 1) / nzw;   // rows per producing wave
+  const int n0 = ((int)blockIdx.x * kFPW + wp) * nrw;
+
+  // ---- prologue ----
+  // Waves 0-3 issue their Phi^T rows at once and produce z; they touch
+  // nothing else until z is published.  Waves 4-7 walk the first unit's
+  // dependent loads meanwhile: routed id -> both directory records -> the
+  // slot metadata of both projections (issued before the staging copies, so
+  // it returns first) -> the gate and up segment records into LDS (waves
+  // 4-5 gate, 6-7 up).  Waves 4-7 form the coefficients of both projections.
+  int u = (int)blockIdx.x;
+  bool have = u < U;
   if (pj == 0) {
-    produce_z(s, ((int)blockIdx.x * kFPW + wp) * nrw, nrw, lane, tag);
+    PhiRegs phr;
+    phi_issue(s, n0, nrw, lane, phr);
+    z_finish(s, n0, nrw, lane, tag, phr);
     if (lane == 0)
       __hip_atomic_fetch_add(s.hint + kFHintStride * (((int)blockIdx.x * kFPW + wp) & (kFHint - 1)),
                              1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   int zt_cached = -1;  // token whose z is in L.Z
-  bool zok = true;     // this lane's words of L.Z arrived (folded into every unit's ok)
-  bool first = true;
-  for (int u = (int)blockIdx.x; u < U || first; u += G) {
-    const bool have = u < U;
-    const int pair = have ? u % np : 0;
-    const int sg = have ? u / np : 0;
+  bool zok = true;     // every lane's words of L.Z arrived
+  for (; have; u += G, have = u < U) {
+    const int pair = u % np;
+    const int sg = u / np;
     const int t = pair / a.ktop;
-    // scalar load: unlike a vector load it does not wait behind this wave's
-    // outstanding z stores (vector memory counts return in order)
-    const int e = have ? (int)*(CU32*)(a.ids + pair) : 0;
-    // projection of this wave; on the first unit waves 4-7 stage both
-    // (4-5 gate, 6-7 up) while waves 0-3 produce z
-    const int sp = first ? (wv >> 1) & 1 : pj;
-    const uint8_t* sblob = sp ? a.blob_u : a.blob_g;
-    const SegProj SP = uniform_seg(make_seg(sblob, sp ? a.bytes_u : a.bytes_g, e,
-                                            load_rec_s(sblob, e, a.E), load_hdr(sblob), a.E,
-                                            a.dout, a.r));
-    const uint32_t c1s = chunk_end(SP, 0, kFMaxW);
-    if (have) {
-      if (first) {
-        if (pj == 1) stage_chunk(&L.W[sp][0], SP, sg, 0, c1s, (int)threadIdx.x & 127, lane, 128);
+    const int e = (int)*(CU32*)(a.ids + pair);
+    // kBoth: waves 4-7 form the coefficients of both projections; otherwise
+    // (long slot lists: too many registers) each half forms its own, waves
+    // 0-3 loading the gate metadata once z is published.
+    constexpr bool kBoth = kFSper <= 9;
+    SlotMeta<kFSper> md0, md1;  // kBoth: gate, up; otherwise md0 is this wave's projection
+    bool ok0 = true, ok1 = true;
+    if (pj == 1) {
+      const SegProj PG = uniform_seg(make_seg(a.blob_g, a.bytes_g, e,
+                                              load_rec_s(a.blob_g, e, a.E), load_hdr(a.blob_g),
+                                              a.E, a.dout, a.r));
+      const SegProj PU = uniform_seg(make_seg(a.blob_u, a.bytes_u, e,
+                                              load_rec_s(a.blob_u, e, a.E), load_hdr(a.blob_u),
+                                              a.E, a.dout, a.r));
+      if (kBoth) {
+        ok0 = PG.ok;
+        ok1 = PU.ok;
+        load_meta<kFSper>(PG, lp, md0);
+        load_meta<kFSper>(PU, lp, md1);
       } else {
-        stage_chunk(&L.W[pj][0], SP, sg, 0, c1s, lp, lane, kFProj);
+        ok0 = PU.ok;
+        load_meta<kFSper>(PU, lp, md0);
       }
+      const SegProj& SP = (wv & 2) ? PU : PG;
+      stage_chunk(&L.W[(wv >> 1) & 1][0], SP, sg, 0, chunk_end(SP, 0, kFMaxW),
+                  (int)threadIdx.x & 127, lane, 128);
+    } else if (!kBoth) {
+      const SegProj PG = uniform_seg(make_seg(a.blob_g, a.bytes_g, e,
+                                              load_rec_s(a.blob_g, e, a.E), load_hdr(a.blob_g),
+                                              a.E, a.dout, a.r));
+      ok0 = PG.ok;
+      load_meta<kFSper>(PG, lp, md0);
     }
-    if (!have) break;
-    const uint8_t* blob = pj ? a.blob_u : a.blob_g;
-    const SegProj P = (sp == pj) ? SP
-                                 : uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
-                                                        load_rec_s(blob, e, a.E), load_hdr(blob),
-                                                        a.E, a.dout, a.r));
-    // ---- coefficients: metadata loads first, then the token's z into LDS ----
-    SlotMeta<kFSper> md;
-    bool good = P.ok;
-    load_meta<kFSper>(P, lp, a.r, md, good);
     if (t != zt_cached) {
-      if (zt_cached < 0) wait_hint(s.hint, (uint32_t)nzw);
-      zok = stage_z(s.zt + (size_t)t * R, R, tag, &L.Z[0]);
+      // one wave polls the hint counters (the first time only), the rest wait
+      if (zt_cached < 0 && wv == 0) wait_hint(s.hint, (uint32_t)nzw);
+      __syncthreads();
+      zok = __syncthreads_and(stage_z(s.zt + (size_t)t * R, R, tag, &L.Z[0]) ? 1 : 0) != 0;
       zt_cached = t;
     }
-    __syncthreads();
-    good = good && zok;
-    float cv[kFSper];
-    {
-      const float* zrow = &L.Z[pj ? a.r : 0];
-      float bias = 0.f, cmx = 0.f;
+    // ---- coefficients ----
+    // (kBoth: waves 4-7 do projection 0 = gate from md0 and 1 = up from md1;
+    // otherwise every wave does its own projection pj from md0)
+    constexpr int kNQ = kBoth ? 2 : 1;
+    float cv[kNQ][kFSper];
 #pragma unroll
-      for (int i = 0; i < kFSper; ++i) {
-        const float az = md.a[i] * zrow[md.k[i]];
-        const float sv = __half2float(__ushort_as_half((unsigned short)(md.sm[i] & 0xFFFFu)));
-        const float mv = __half2float(__ushort_as_half((unsigned short)(md.sm[i] >> 16)));
-        bias += az * mv;          // m = 0 for 16-bit and padding slots
-        const float c = az * sv;  // s = 1 for 16-bit slots
-        cv[i] = c;
-        cmx = fmaxf(cmx, fabsf(c));
-      }
+    for (int j = 0; j < kNQ; ++j) {
+      if (!kBoth || pj == 1) {
+        const int q = kBoth ? j : pj;
+        SlotMeta<kFSper>& md = j ? md1 : md0;
+        const float* zrow = &L.Z[q ? a.r : 0];
+        bool good = (j ? ok1 : ok0) && zok;
+        float bias = 0.f, cmx = 0.f;
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) cmx = fmaxf(cmx, __shfl_xor(cmx, off, kWave));
-      const float bw = wave_sum(bias);
-      const bool wok = __all(good);
-      if (lane == 0) {
-        L.pmax[pj][wp] = cmx;
-        L.pbias[pj][wp] = bw;
-        L.pok[pj][wp] = wok;
-      }
-    }
-    __syncthreads();
-    {
-      const float pmx =
-          fmaxf(fmaxf(L.pmax[pj][0], L.pmax[pj][1]), fmaxf(L.pmax[pj][2], L.pmax[pj][3]));
-      const int S = coef_shift(pmx, 1.0f);
+        for (int i = 0; i < kFSper; ++i) {
+          good &= md.k[i] < (uint32_t)a.r;
+          const uint32_t k = md.k[i] < (uint32_t)a.r ? md.k[i] : 0u;
+          const float az = md.a[i] * zrow[k];
+          const float sv = __half2float(__ushort_as_half((unsigned short)(md.sm[i] & 0xFFFFu)));
+          const float mv = __half2float(__ushort_as_half((unsigned short)(md.sm[i] >> 16)));
+          bias += az * mv;          // m = 0 for 16-bit and padding slots
+          const float c = az * sv;  // s = 1 for 16-bit slots
+          cv[j][i] = c;
+          cmx = fmaxf(cmx, fabsf(c));
+        }
 #pragma unroll
-      for (int i = 0; i < kFSper; ++i) {
-        const uint32_t sl = (uint32_t)lp + kFProj * i;
-        if (sl < kFMaxS) {  // zeros past n_slot
-          _Float16 hi, lo;
-          split_coef(cv[i], S, hi, lo);
-          L.Chi[pj][sl] = hi;
-          L.Clo[pj][sl] = lo;
+        for (int off = 32; off > 0; off >>= 1) cmx = fmaxf(cmx, __shfl_xor(cmx, off, kWave));
+        const float bw = wave_sum(bias);
+        const bool wok = __all(good);
+        if (lane == 0) {
+          L.pmax[q][wp] = cmx;
+          L.pbias[q][wp] = bw;
+          L.pok[q][wp] = wok;
         }
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kNQ; ++j) {
+      if (!kBoth || pj == 1) {
+        const int q = kBoth ? j : pj;
+        const float pmx =
+            fmaxf(fmaxf(L.pmax[q][0], L.pmax[q][1]), fmaxf(L.pmax[q][2], L.pmax[q][3]));
+        const int S = coef_shift(pmx, 1.0f);
+        // (zeros past n_slot; the tail slot can lie past the arrays)
+        constexpr int V = SlotMeta<kFSper>::V;
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          union {
+            _Float16 h[8];
+            uint4 u;
+          } hi8, lo8;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) split_coef(cv[j][8 * v + i], S, hi8.h[i], lo8.h[i]);
+          const uint32_t sv = 8u * V * (uint32_t)lp + 8u * v;
+          *reinterpret_cast<uint4*>(&L.Chi[q][sv]) = hi8.u;
+          *reinterpret_cast<uint4*>(&L.Clo[q][sv]) = lo8.u;
+        }
+        const uint32_t sl = meta_slot<kFSper>(lp, 8 * V);
+        if (sl < kFMaxS) {
+          _Float16 hi, lo;
+          split_coef(cv[j][8 * V], S, hi, lo);
+          L.Chi[q][sl] = hi;
+          L.Clo[q][sl] = lo;
+        }
+      }
+    }
+    // this wave's projection (its record is in the scalar cache by now)
+    const uint8_t* blob = pj ? a.blob_u : a.blob_g;
+    const SegProj P = uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
+                                           load_rec_s(blob, e, a.E), load_hdr(blob), a.E, a.dout,
+                                           a.r));
     // chunk counts of both projections (they advance together)
     {
       int nc = 0;
@@ -437,7 +525,6 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         a.h[(size_t)pair * a.dout + row] = ok ? silu_mul(ys[0], ys[1]) : __builtin_nanf("");
     }
     __syncthreads();  // LDS is reused by the next unit
-    first = false;
   }
 
   // ---- grid arrival: the last group advances the epoch ----
