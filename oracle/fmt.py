@@ -1,4 +1,4 @@
-"""Independent writer and reader of the packed spectral-expert blob (format v2).
+"""Independent writer and reader of the packed spectral-expert blob (format v3).
 
 Test infrastructure: only the tests, the smoke check and the benchmark's CPU
 baseline use this module; the HIP library never imports it.
@@ -12,7 +12,7 @@ bytes from its own C++ code, and the tests compare the two.
 Layout (little-endian; offsets in bytes from the blob base):
 
 Header, 128 bytes
-  0 'BMOE' | 4 u32 version=2 | 8 u32 E | 12 u32 dout | 16 u32 r
+  0 'BMOE' | 4 u32 version=3 | 8 u32 E | 12 u32 dout | 16 u32 r
   20 u32 dout_pad = 32*ceil(dout/32) | 24 u32 n_seg = dout_pad/32
   28 u32 header_bytes=128 | 32 u64 total_bytes | 40 u64 dir_offset=128
   48 u32 CRC-32 (IEEE, as zlib) of bytes [128, total_bytes) | rest zero
@@ -38,7 +38,7 @@ Expert block (first at align256(128 + 64 E), blocks back to back)
          one record per 32-row segment; inside it, block after block in slot
          order, 4*w words per block of width w: for row octet i = 0..3
          (segment rows 8i..8i+7) w words.
-         w <= 8: word (i, j), j = 0..w-1 is plane j; its bit 4*rho + u is
+         w <= 8: word (i, j), j = 0..w-1 is plane j; its bit 8*u + rho is
          bit j (j = 0 least significant) of the code of segment row 8i + rho
          in slot 4*beta + u.
          w = 16: word (i, 2*rho + h) holds the fp16 values of segment row
@@ -55,7 +55,7 @@ import numpy as np
 from .quantize import quantize_expert
 
 MAGIC = b"BMOE"
-VERSION = 2
+VERSION = 3
 HEADER_BYTES = 128
 DIR_REC = 64
 SEG_ROWS = 32
@@ -66,9 +66,10 @@ def _al(x: int, a: int) -> int:
     return (x + a - 1) // a * a
 
 
-def nibble_shift(rho, u):
-    """Bit position of (row rho of an octet, slot u of a block) in a plane word."""
-    return 4 * rho + u
+def plane_bit(rho, u):
+    """Bit position of (row rho of an octet, slot u of a block) in a plane word:
+    byte u holds the octet's 8 rows of slot u."""
+    return 8 * u + rho
 
 
 GROUP_SLOTS = 32   # each width group is padded to a multiple of this
@@ -118,7 +119,7 @@ def _plane_words(Q: np.ndarray, w: int, n_seg: int) -> np.ndarray:
     V = Q.astype(np.uint32).reshape(nb, 4, n_seg, 4, 8)
     rho = np.arange(8).reshape(1, 1, 1, 1, 8)
     u = np.arange(4).reshape(1, 4, 1, 1, 1)
-    sh = nibble_shift(rho, u).astype(np.uint32)
+    sh = plane_bit(rho, u).astype(np.uint32)
     planes = []
     for j in range(w):
         bit = (V >> j) & 1
@@ -231,7 +232,7 @@ def _plane_codes(words: np.ndarray, w: int, nb: int, n_seg: int) -> np.ndarray:
         pj = Wd[:, :, :, j].transpose(1, 0, 2)             # beta, seg, i
         for u in range(4):
             for rho in range(8):
-                bit = (pj >> nibble_shift(rho, u)) & 1
+                bit = (pj >> plane_bit(rho, u)) & 1
                 Q[:, u, :, :, rho] |= (bit.astype(np.uint16) << j)
     return Q.reshape(4 * nb, n_seg * 32)
 

@@ -75,10 +75,10 @@ __device__ inline bool load_dir(const uint8_t* __restrict__ blob, uint64_t blob_
 
 // Code of segment row `row` (0..31) in slot u (0..3) of a block of width
 // w <= 8 whose record starts at `rec`: bit j from word (row / 8, j), bit
-// 4 (row % 8) + u.  Used by the lane-per-row kernels and the code dump.
+// 8 u + row % 8.  Used by the lane-per-row kernels and the code dump.
 __device__ inline uint32_t decode_code(const uint32_t* __restrict__ rec, int w, int row, int u) {
   const uint32_t* oct = rec + (row >> 3) * w;
-  const int sh = 4 * (row & 7) + u;
+  const int sh = 8 * u + (row & 7);
   uint32_t q = 0;
   for (int j = 0; j < w; ++j) q |= ((oct[j] >> sh) & 1u) << j;
   return q;

@@ -13,7 +13,7 @@
 namespace bitsmoe {
 
 constexpr uint32_t kMagic = 0x454F4D42u;  // bytes 'B','M','O','E'
-constexpr uint32_t kVersion = 2;
+constexpr uint32_t kVersion = 3;
 constexpr int kSegRows = 32;                        // rows of one segment record
 constexpr uint32_t kHeaderBytes = 128;
 constexpr uint32_t kDirRecBytes = 64;

@@ -1,11 +1,12 @@
-// Host packer and blob checker (format v2, documented in include/bitsmoe.h).
+// Host packer and blob checker (format v3, documented in include/bitsmoe.h).
 //
 // Quantizes each unit direction p_{e,k} at its own width and stores the
 // columns grouped by width, each 1..8-bit group as bit planes ("second
 // split", "Usage" and "execution" of the BitsMoE blog note's Methodology).
-// Plane words hold one 4-bit nibble per row (the row's bits of 4 adjacent
-// slots), so a lane that owns a row reads a contiguous run of words per
-// block.  The quantizer runs in IEEE float32 with no contraction so that its
+// A plane word covers 8 rows x 4 adjacent slots: byte u holds the 8 rows'
+// bits of slot u, so a lane that owns a row rotates its bits into the low
+// bit of every byte and gets 4 codes per plane with two operations; the
+// lane reads a contiguous run of words per block.  The quantizer runs in IEEE float32 with no contraction so that its
 // codes are reproducible bit for bit.
 #include <math.h>
 #include <string.h>
@@ -248,7 +249,7 @@ void fill_block(DirRec& d, int e, int dout, int r, uint32_t n_seg, const float* 
             for (int rho = 0; rho < 8; ++rho)
               for (int u = 0; u < 4; ++u)
                 v |= (uint32_t)((q4[(size_t)u * dout_pad + row0 + rho] >> j) & 1u)
-                     << (4 * rho + u);
+                     << (8 * u + rho);
             rec[oct * w + j] = v;
           }
         }

@@ -1,7 +1,7 @@
 // Device helpers shared by the MFMA gate/up kernels that work on 32-row
 // segment records: one projection's expert block (from its directory record),
 // block geometry, chunking, LDS staging with 16-byte global_load_lds, the
-// nibble decode that turns plane words into fp16 MFMA operands, and the
+// plane decode that turns plane words into fp16 MFMA operands, and the
 // v_mfma_f32_16x16x32_f16 step.
 //
 // BitsMoE blog note, Methodology: "second split" (an expert's output is the
@@ -180,15 +180,18 @@ __device__ __forceinline__ void stage16(void* dst, const void* src, uint32_t n16
                                      (lds_void*)(d + 16 * (size_t)(i - lane)), 16, 0, 0);
 }
 
-// The 4 bits of a nibble spread to bits 0, 8, 16, 24 (a 24-bit multiply by
-// 2^0 + 2^7 + 2^14 + 2^21 places bit u at 8u; the copies do not overlap).
-// The 24-bit multiply is explicit so that a following shift is not folded
-// into a constant too wide for it (which would need the quarter-rate 32-bit
-// multiply).
-__device__ __forceinline__ uint32_t spread4(uint32_t x) {
-  uint32_t mul = 0x00204081u;
-  asm("" : "+s"(mul));  // opaque to constant folding (stays a 24-bit multiply)
-  return __umul24(x, mul) & 0x01010101u;
+// The 4 codes of octet row rho in one block of width W <= 8, one per byte
+// (byte u = slot u): bit 8 u + rho of plane word j is bit j of the code, so
+// rotating word j right by rho - j (mod 32) puts every byte's bit on bit j
+// of that byte (a 4-byte mask keeps them): one v_alignbit_b32 and one
+// v_and_or_b32 per plane.
+template <int W>
+__device__ __forceinline__ uint32_t row_codes4(const uint32_t (&w)[W], int rho) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < W; ++j)
+    c |= __builtin_amdgcn_alignbit(w[j], w[j], (uint32_t)(rho - j) & 31u) & (0x01010101u << j);
+  return c;
 }
 
 // 4 byte codes -> two fp16 pairs, exact: bytes become (1024 + q) by a byte
@@ -255,7 +258,7 @@ __device__ __forceinline__ void load_oct(const uint32_t* oct, uint32_t (&w)[W]) 
 // two blocks start at rec (block 2 kg of the step) and rec + 4 W.
 template <int W>
 __device__ __forceinline__ void a_tiles_uniform(const uint32_t* rec, int m, h8& a0, h8& a1) {
-  const int sh = 4 * (m & 7), o = m >> 3;
+  const int rho = m & 7, o = m >> 3;
   uint32_t v[2][4];
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
@@ -263,12 +266,7 @@ __device__ __forceinline__ void a_tiles_uniform(const uint32_t* rec, int m, h8& 
     for (int t = 0; t < 2; ++t) {
       uint32_t w[W];
       load_oct<W>(rec + 4 * W * t + (2 * tile + o) * W, w);
-      uint32_t c = 0;
-#pragma unroll
-      for (int j = 0; j < W; ++j) {
-        c |= spread4(__builtin_amdgcn_ubfe(w[j], sh, 4)) << j;
-      }
-      codes_to_f16(c, v[tile][2 * t], v[tile][2 * t + 1]);
+      codes_to_f16(row_codes4<W>(w, rho), v[tile][2 * t], v[tile][2 * t + 1]);
     }
   }
   union {
@@ -325,49 +323,6 @@ __device__ __forceinline__ void mfma4(const h8& a0, const h8& a1, const uint4& v
   acc1 = mfma(a1, bh, acc1);
   acc0 = mfma(a0, bl, acc0);
   acc1 = mfma(a1, bl, acc1);
-}
-
-// Raw plane words of this lane's two blocks for both 16-row tiles of a K
-// step whose blocks all have width W <= 8 (rec: block 2 kg of the step).
-template <int W>
-struct StepWords {
-  uint32_t w[2][2][W];  // [tile][block][plane]
-};
-template <int W>
-__device__ __forceinline__ void load_step(const uint32_t* rec, int m, StepWords<W>& sw) {
-  const int o = m >> 3;
-#pragma unroll
-  for (int tile = 0; tile < 2; ++tile)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) load_oct<W>(rec + 4 * W * t + (2 * tile + o) * W, sw.w[tile][t]);
-}
-template <int W>
-__device__ __forceinline__ void decode_step(const StepWords<W>& sw, int m, h8& a0, h8& a1) {
-  const int sh = 4 * (m & 7);
-  uint32_t v[2][4];
-#pragma unroll
-  for (int tile = 0; tile < 2; ++tile) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int j = 0; j < W; ++j) {
-        c |= spread4(__builtin_amdgcn_ubfe(sw.w[tile][t][j], sh, 4)) << j;
-      }
-      codes_to_f16(c, v[tile][2 * t], v[tile][2 * t + 1]);
-    }
-  }
-  union {
-    uint32_t u[4];
-    h8 h;
-  } o0, o1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    o0.u[i] = v[0][i];
-    o1.u[i] = v[1][i];
-  }
-  a0 = o0.h;
-  a1 = o1.h;
 }
 
 // K steps kb = kfirst, kfirst + nw, ... < kend, all of width W (W = 16:

@@ -25,7 +25,7 @@ def test_hand_built_planes():
     bits = np.array([[2, 0, 1]], np.uint8)
     blob = fmt.pack(p, a, bits)
     H = fmt.read_header(blob)
-    assert H["magic"] == b"BMOE" and H["version"] == 2
+    assert H["magic"] == b"BMOE" and H["version"] == 3
     assert H["dout_pad"] == 32 and H["n_seg"] == 1
     base, n_nz, n_q, n_16, seg_words = struct.unpack_from("<QIIII", blob, 128)
     # each used group padded to 32 slots = 8 blocks: 4 * 8 * (1 + 2) words
@@ -45,15 +45,15 @@ def test_hand_built_planes():
     cmax, = struct.unpack_from("<f", blob, 128 + 40)
     assert cmax == np.float32(2.0) * np.float32(0.333251953125)
     words = struct.unpack_from("<96I", blob, base + p_off)
-    # group 1 (width 1), block 0, octet 0: slot 0 (column 2) has code 1 in
-    #   row 1 -> bit 4*1 + 0; octets 1-3 are rows 8..31 (padding) -> 0;
-    #   blocks 1-7 of the group are padding (4 words each)
+    # group 1 (width 1), block 0, octet 0: slot 0 (column 2, u = 0) has
+    #   code 1 in row 1 -> bit 8*0 + 1; octets 1-3 are rows 8..31 (padding)
+    #   -> 0; blocks 1-7 of the group are padding (4 words each)
     # group 2 (width 2) starts at word 4 * 8 * 1 = 32; its block 0, octet 0:
-    #   slot 32 (column 0) codes [0,1,2,3] in rows 0..3
-    #   plane 0: rows 1, 3 -> bits 4, 12; plane 1: rows 2, 3 -> bits 8, 12
+    #   slot 32 (column 0, u = 0) codes [0,1,2,3] in rows 0..3
+    #   plane 0: rows 1, 3 -> bits 1, 3; plane 1: rows 2, 3 -> bits 2, 3
     expect = [0] * 96
-    expect[0] = 0x10
-    expect[32], expect[33] = 0x1010, 0x1100
+    expect[0] = 0x2
+    expect[32], expect[33] = 0xA, 0xC
     assert words == tuple(expect)
 
 

@@ -106,5 +106,5 @@ def test_silu_sign_caught(monkeypatch):
 
 def test_plane_bit_order_caught(monkeypatch):
     # rows and slots swapped inside a plane word
-    monkeypatch.setattr(fmt, "nibble_shift", lambda rho, u: 8 * u + rho)
+    monkeypatch.setattr(fmt, "plane_bit", lambda rho, u: 4 * rho + u)
     assert _fails(T_fmt.test_hand_built_planes)
