@@ -370,7 +370,7 @@ GateUpPlan gateup_plan(int T, int k, int E, int r) {
   p.z_off = 0;
   p.zpart_off = align_up((size_t)T * 2 * r * sizeof(float), 256);
   p.zt_off = align_up(p.zpart_off + (size_t)T * nzp * sizeof(float), 256);
-  p.sync_off = align_up(p.zt_off + (size_t)T * 2 * r * sizeof(uint64_t), 256);
+  p.sync_off = align_up(p.zt_off + (size_t)kZRing * T * 2 * r * sizeof(uint64_t), 256);
   p.route_off = align_up(p.sync_off + 128 + 64 * 128, 256);
   p.total = align_up(p.route_off + (1 + 3 * (size_t)tile_cap(T, k, E) + P) * sizeof(int), 256);
   return p;

@@ -74,6 +74,7 @@ struct __align__(16) FusedLds {
   float pbias[2][kFPW];
   uint32_t pok[2][kFPW];
   int nch[2];
+  uint32_t go;  // = tag once wave 4 has issued the first unit's record loads
 };
 
 __device__ __forceinline__ float fdot8(uint4 a, uint4 b, float acc) {
@@ -111,10 +112,10 @@ __device__ __forceinline__ float zpart(const FusedArgs& s, const uint4* prow, co
   return acc;
 }
 
-__device__ __forceinline__ void publish_z(const FusedArgs& s, int tt, int n, float v, uint32_t tag) {
+__device__ __forceinline__ void publish_z(uint64_t* zt, int r, int tt, int n, float v,
+                                          uint32_t tag) {
   const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
-  __hip_atomic_store(&s.zt[(size_t)tt * 2 * s.g.r + n], w, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&zt[(size_t)tt * 2 * r + n], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One transposing exchange of a kFPre-value reduction: lanes with bit O set
@@ -160,8 +161,8 @@ __device__ __forceinline__ void phi_issue(const FusedArgs& s, int n0, int nrw, i
   }
 }
 
-__device__ __forceinline__ void z_finish(const FusedArgs& s, int n0, int nrw, int lane,
-                                         uint32_t tag, const PhiRegs& q) {
+__device__ __forceinline__ void z_finish(const FusedArgs& s, uint64_t* zt, int n0, int nrw,
+                                         int lane, uint32_t tag, const PhiRegs& q) {
   static_assert(kFPre == 4, "the transposing reduction is written for 4 rows");
   const int R = 2 * s.g.r;
   for (int tt = 0; tt < s.T; ++tt) {
@@ -177,7 +178,7 @@ __device__ __forceinline__ void z_finish(const FusedArgs& s, int n0, int nrw, in
 #pragma unroll
     for (int off = 4; off < kWave; off <<= 1) z += __shfl_xor(z, off, kWave);
     const int j = lane & 3;
-    if (lane < kFPre && j < nrw && n0 + j < R) publish_z(s, tt, n0 + j, z, tag);
+    if (lane < kFPre && j < nrw && n0 + j < R) publish_z(zt, s.g.r, tt, n0 + j, z, tag);
   }
   for (int j = kFPre; j < nrw && n0 + j < R; ++j) {  // rows beyond the first kFPre
     const int n = n0 + j;
@@ -190,7 +191,7 @@ __device__ __forceinline__ void z_finish(const FusedArgs& s, int n0, int nrw, in
     }
     for (int tt = 0; tt < s.T; ++tt) {
       const float z = wave_sum(zpart(s, prow, p0, q.xv, tt, lane));
-      if (lane == 0) publish_z(s, tt, n, z, tag);
+      if (lane == 0) publish_z(zt, s.g.r, tt, n, z, tag);
     }
   }
 }
@@ -212,9 +213,11 @@ __device__ __forceinline__ void wait_hint(const uint32_t* hint, uint32_t nzw) {
 
 // The token's 2r tagged z words, copied into LDS as floats by all lanes with
 // coalesced loads.  The first read is an ordinary (L2-cached) load, issued
-// once the hint says the producers are done, so the work-groups of one XCD
-// share it; words whose tag is not there yet are re-read with device-coherent
-// loads until it is (bounded wait).  Returns false on a time-out.
+// once the hint counters say that every producer's z stores have completed,
+// so the work-groups of one XCD share one fetch; words whose tag is not
+// there (a line the L2 kept from an older launch) are re-read with
+// device-coherent loads until it is (bounded wait).  Returns false on a
+// time-out.
 __device__ __forceinline__ bool stage_z(const uint64_t* src, int R, uint32_t tag, float* Z) {
   uint64_t zw[kFZPer];
 #pragma unroll
@@ -247,56 +250,84 @@ __device__ __forceinline__ bool stage_z(const uint64_t* src, int R, uint32_t tag
 
 // Slot metadata of one lane: kFSper = 8 V + 1 slots, the 8 V contiguous
 // slots 8 V lp .. 8 V lp + 8 V - 1 (read with 16-byte loads) and the tail
-// slot 2048 V + lp (n_slot <= r + 7 * 31 < 2048 V + 256).  Only loads: the
-// component indices are checked where they are used, so nothing here waits.
+// slot 2048 V + lp (n_slot <= r + 7 * 31 < 2048 V + 256).  The raw loaded
+// words are kept as they are and unpacked only where the coefficients are
+// formed, so that nothing before that point waits for these loads.
 template <int kFSper>
 struct SlotMeta {
   static constexpr int V = (kFSper - 1) / 8;
-  uint32_t k[kFSper];
-  float a[kFSper];
-  uint32_t sm[kFSper];  // fp16 s | fp16 m << 16 (s = 1, m = 0 for 16-bit and padding)
+  uint4 kq[V], a0[V], a1[V], sq[V], mq[V];  // kidx, a (2 x 4), s, m of 8 slots each
+  uint32_t kt, at, st, mt;                  // the tail slot
 };
 template <int kFSper>
 __device__ __forceinline__ uint32_t meta_slot(int lp, int i) {
   constexpr int V = SlotMeta<kFSper>::V;
   return i < 8 * V ? (uint32_t)(8 * V * lp + i) : (uint32_t)(2048 * V + lp);
 }
-// A 16-byte vector of array x at element index i0 is read only when i0 < n:
-// it then ends at most 28 bytes past the array, still inside the expert
+// Every load is issued unconditionally (an index past the array is replaced
+// by 0, inside the expert block) and through a global address (the
+// descriptor's pointers are global ones); a load inside a branch, or a flat
+// load (which also counts on the LDS counter), would make the wave wait for
+// all of its outstanding loads right there.  A 16-byte vector that starts
+// inside an array ends at most 28 bytes past it, still inside the expert
 // block (the next array, or the planes and the block's 16-byte tail).
 template <int kFSper>
 __device__ __forceinline__ void load_meta(const SegProj& p, int lp, SlotMeta<kFSper>& md) {
   constexpr int V = SlotMeta<kFSper>::V;
   static_assert(kFSper == 8 * V + 1, "8 V contiguous slots and one tail slot");
   const uint32_t s0 = 8u * V * (uint32_t)lp;
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const uint32_t sv = s0 + 8u * v;
-    const uint4 kq = sv < p.n_slot ? *reinterpret_cast<const uint4*>(p.kidx + sv) : z4;
-    const uint4 a0 = sv < p.n_slot ? *reinterpret_cast<const uint4*>(p.A + sv) : z4;
-    const uint4 a1 = sv + 4 < p.n_slot ? *reinterpret_cast<const uint4*>(p.A + sv + 4) : z4;
-    const uint4 sq = sv < p.n_qslot ? *reinterpret_cast<const uint4*>(p.S + sv) : z4;
-    const uint4 mq = sv < p.n_qslot ? *reinterpret_cast<const uint4*>(p.M + sv) : z4;
-    const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
-    const uint32_t aw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const uint32_t sw[4] = {sq.x, sq.y, sq.z, sq.w};
-    const uint32_t mw[4] = {mq.x, mq.y, mq.z, mq.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t sl = sv + j;
-      const uint32_t sh = 16 * (j & 1);
-      md.k[8 * v + j] = sl < p.n_slot ? (kw[j >> 1] >> sh) & 0xFFFFu : 0u;
-      md.a[8 * v + j] = sl < p.n_slot ? __uint_as_float(aw[j]) : 0.f;
-      md.sm[8 * v + j] = sl < p.n_qslot
-                             ? ((sw[j >> 1] >> sh) & 0xFFFFu) | (((mw[j >> 1] >> sh) & 0xFFFFu) << 16)
-                             : 0x3C00u;
-    }
+    const uint32_t iq = sv < p.n_slot ? sv : 0u, ia = sv + 4 < p.n_slot ? sv + 4 : 0u;
+    const uint32_t is = sv < p.n_qslot ? sv : 0u;
+    md.kq[v] = ld16(p.kidx + iq);
+    md.a0[v] = ld16(p.A + iq);
+    md.a1[v] = ld16(p.A + ia);
+    md.sq[v] = ld16(p.S + is);
+    md.mq[v] = ld16(p.M + is);
   }
   const uint32_t sl = 2048u * V + (uint32_t)lp;
-  md.k[8 * V] = sl < p.n_slot ? p.kidx[sl] : 0u;
-  md.a[8 * V] = sl < p.n_slot ? p.A[sl] : 0.f;
-  md.sm[8 * V] = sl < p.n_qslot ? ((uint32_t)p.S[sl] | ((uint32_t)p.M[sl] << 16)) : 0x3C00u;
+  const uint32_t ic = sl < p.n_slot ? sl : 0u, iq = sl < p.n_qslot ? sl : 0u;
+  // 16-bit values through the aligned 32-bit word that holds them (the half
+  // is picked where they are used)
+  md.kt = *(const gu32*)(p.kidx + (ic & ~1u));
+  md.at = *(const gu32*)(p.A + ic);
+  md.st = *(const gu32*)(p.S + (iq & ~1u));
+  md.mt = *(const gu32*)(p.M + (iq & ~1u));
+}
+// Slot i of the lane (see SlotMeta): component index k, magnitude a and
+// fp16 s, m as floats; slots past the arrays give k = 0, a = 0, s = 1, m = 0.
+template <int kFSper>
+__device__ __forceinline__ void meta_get(const SlotMeta<kFSper>& md, int lp, int i,
+                                         uint32_t n_slot, uint32_t n_qslot, uint32_t& k,
+                                         float& a, float& sv, float& mv) {
+  constexpr int V = SlotMeta<kFSper>::V;
+  const uint32_t sl = meta_slot<kFSper>(lp, i);
+  uint32_t kk, aa, ss, mm;
+  if (i < 8 * V) {
+    const int v = i >> 3, j = i & 7;
+    const uint32_t kw[4] = {md.kq[v].x, md.kq[v].y, md.kq[v].z, md.kq[v].w};
+    const uint32_t sw[4] = {md.sq[v].x, md.sq[v].y, md.sq[v].z, md.sq[v].w};
+    const uint32_t mw[4] = {md.mq[v].x, md.mq[v].y, md.mq[v].z, md.mq[v].w};
+    const uint32_t aw[8] = {md.a0[v].x, md.a0[v].y, md.a0[v].z, md.a0[v].w,
+                            md.a1[v].x, md.a1[v].y, md.a1[v].z, md.a1[v].w};
+    const uint32_t sh = 16 * (j & 1);
+    kk = (kw[j >> 1] >> sh) & 0xFFFFu;
+    ss = (sw[j >> 1] >> sh) & 0xFFFFu;
+    mm = (mw[j >> 1] >> sh) & 0xFFFFu;
+    aa = aw[j];
+  } else {
+    const uint32_t sh = 16 * (sl & 1);  // the tail slot's half of the loaded words
+    kk = (md.kt >> sh) & 0xFFFFu;
+    aa = md.at;
+    ss = (md.st >> sh) & 0xFFFFu;
+    mm = (md.mt >> sh) & 0xFFFFu;
+  }
+  k = sl < n_slot ? kk : 0u;
+  a = sl < n_slot ? __uint_as_float(aa) : 0.f;
+  sv = sl < n_qslot ? __half2float(__ushort_as_half((unsigned short)ss)) : 1.f;
+  mv = sl < n_qslot ? __half2float(__ushort_as_half((unsigned short)mm)) : 0.f;
 }
 
 // Stage chunk [b0, b1) of segment sg of projection p into arena (nl lanes).
@@ -319,6 +350,9 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
   // not hold up the Phi^T loads behind it.
   typedef __attribute__((address_space(4))) const uint32_t CU32;
   const uint32_t tag = *(CU32*)s.epoch + 1u;
+  // this launch's tagged z buffer: a line that an XCD's L2 still holds from
+  // the launch kZRing launches back carries an old tag and is re-read
+  uint64_t* const zt = s.zt + (size_t)(tag % kZRing) * s.T * 2 * a.r;
   const int pj = wv >= kFPW ? 1 : 0;           // waves 0-3 gate, 4-7 up
   const int wp = wv & (kFPW - 1);
   const int lp = (int)threadIdx.x & (kFProj - 1);
@@ -332,18 +366,29 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
   const int n0 = ((int)blockIdx.x * kFPW + wp) * nrw;
 
   // ---- prologue ----
-  // Waves 0-3 issue their Phi^T rows at once and produce z; they touch
-  // nothing else until z is published.  Waves 4-7 walk the first unit's
-  // dependent loads meanwhile: routed id -> both directory records -> the
-  // slot metadata of both projections (issued before the staging copies, so
-  // it returns first) -> the gate and up segment records into LDS (waves
-  // 4-5 gate, 6-7 up).  Waves 4-7 form the coefficients of both projections.
+  // The first unit's routed id is the first load of every wave (scalar).
+  // Waves 0-3 wait for it before they issue their Phi^T rows, so that the
+  // directory records, which waves 4-7 request as soon as the id is back,
+  // are not queued behind the Phi^T flood; then they produce z and touch
+  // nothing else until it is published.  Waves 4-7 issue the slot metadata
+  // (before the staging copies, so it returns first) and copy the unit's
+  // gate and up segment records into LDS (waves 4-5 gate, 6-7 up).
   int u = (int)blockIdx.x;
   bool have = u < U;
+  int pair = have ? u % np : 0;
+  int e = have ? (int)*(CU32*)(a.ids + pair) : 0;
+  const HdrF hg = load_hdr(a.blob_g), hu = load_hdr(a.blob_u);
   if (pj == 0) {
+    // wait (bounded) until wave 4 has issued its record loads
+    for (uint32_t sp = 0; have && sp < kFSpin; ++sp) {
+      if (__hip_atomic_load(&L.go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == tag) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
     PhiRegs phr;
     phi_issue(s, n0, nrw, lane, phr);
-    z_finish(s, n0, nrw, lane, tag, phr);
+    z_finish(s, zt, n0, nrw, lane, tag, phr);
+    // the hint counts a wave only once its z stores have completed
+    __builtin_amdgcn_s_waitcnt(0);
     if (lane == 0)
       __hip_atomic_fetch_add(s.hint + kFHintStride * (((int)blockIdx.x * kFPW + wp) & (kFHint - 1)),
                              1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -351,48 +396,55 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
 
   int zt_cached = -1;  // token whose z is in L.Z
   bool zok = true;     // every lane's words of L.Z arrived
-  for (; have; u += G, have = u < U) {
-    const int pair = u % np;
+  for (bool first = true; have; u += G, have = u < U, first = false) {
+    if (!first) {
+      pair = u % np;
+      e = (int)*(CU32*)(a.ids + pair);
+    }
+    const DirRec rg = load_rec_s(a.blob_g, e, a.E);
+    const DirRec ru = load_rec_s(a.blob_u, e, a.E);
+    if (first && wv == kFPW) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (lane == 0) __hip_atomic_store(&L.go, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     const int sg = u / np;
     const int t = pair / a.ktop;
-    const int e = (int)*(CU32*)(a.ids + pair);
     // kBoth: waves 4-7 form the coefficients of both projections; otherwise
     // (long slot lists: too many registers) each half forms its own, waves
     // 0-3 loading the gate metadata once z is published.
     constexpr bool kBoth = kFSper <= 9;
     SlotMeta<kFSper> md0, md1;  // kBoth: gate, up; otherwise md0 is this wave's projection
     bool ok0 = true, ok1 = true;
+    uint32_t ns0 = 0, nq0 = 0, ns1 = 0, nq1 = 0;  // n_slot, n_qslot of md0, md1
     if (pj == 1) {
-      const SegProj PG = uniform_seg(make_seg(a.blob_g, a.bytes_g, e,
-                                              load_rec_s(a.blob_g, e, a.E), load_hdr(a.blob_g),
-                                              a.E, a.dout, a.r));
-      const SegProj PU = uniform_seg(make_seg(a.blob_u, a.bytes_u, e,
-                                              load_rec_s(a.blob_u, e, a.E), load_hdr(a.blob_u),
-                                              a.E, a.dout, a.r));
+      const SegProj PG = uniform_seg(make_seg(a.blob_g, a.bytes_g, e, rg, hg, a.E, a.dout, a.r));
+      const SegProj PU = uniform_seg(make_seg(a.blob_u, a.bytes_u, e, ru, hu, a.E, a.dout, a.r));
       if (kBoth) {
         ok0 = PG.ok;
         ok1 = PU.ok;
+        ns0 = PG.n_slot; nq0 = PG.n_qslot;
+        ns1 = PU.n_slot; nq1 = PU.n_qslot;
         load_meta<kFSper>(PG, lp, md0);
         load_meta<kFSper>(PU, lp, md1);
       } else {
         ok0 = PU.ok;
+        ns0 = PU.n_slot; nq0 = PU.n_qslot;
         load_meta<kFSper>(PU, lp, md0);
       }
       const SegProj& SP = (wv & 2) ? PU : PG;
       stage_chunk(&L.W[(wv >> 1) & 1][0], SP, sg, 0, chunk_end(SP, 0, kFMaxW),
                   (int)threadIdx.x & 127, lane, 128);
     } else if (!kBoth) {
-      const SegProj PG = uniform_seg(make_seg(a.blob_g, a.bytes_g, e,
-                                              load_rec_s(a.blob_g, e, a.E), load_hdr(a.blob_g),
-                                              a.E, a.dout, a.r));
+      const SegProj PG = uniform_seg(make_seg(a.blob_g, a.bytes_g, e, rg, hg, a.E, a.dout, a.r));
       ok0 = PG.ok;
+      ns0 = PG.n_slot; nq0 = PG.n_qslot;
       load_meta<kFSper>(PG, lp, md0);
     }
     if (t != zt_cached) {
       // one wave polls the hint counters (the first time only), the rest wait
       if (zt_cached < 0 && wv == 0) wait_hint(s.hint, (uint32_t)nzw);
       __syncthreads();
-      zok = __syncthreads_and(stage_z(s.zt + (size_t)t * R, R, tag, &L.Z[0]) ? 1 : 0) != 0;
+      zok = __syncthreads_and(stage_z(zt + (size_t)t * R, R, tag, &L.Z[0]) ? 1 : 0) != 0;
       zt_cached = t;
     }
     // ---- coefficients ----
@@ -404,17 +456,19 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     for (int j = 0; j < kNQ; ++j) {
       if (!kBoth || pj == 1) {
         const int q = kBoth ? j : pj;
-        SlotMeta<kFSper>& md = j ? md1 : md0;
+        const SlotMeta<kFSper>& md = j ? md1 : md0;
         const float* zrow = &L.Z[q ? a.r : 0];
         bool good = (j ? ok1 : ok0) && zok;
         float bias = 0.f, cmx = 0.f;
+        const uint32_t ns = j ? ns1 : ns0, nq = j ? nq1 : nq0;
 #pragma unroll
         for (int i = 0; i < kFSper; ++i) {
-          good &= md.k[i] < (uint32_t)a.r;
-          const uint32_t k = md.k[i] < (uint32_t)a.r ? md.k[i] : 0u;
-          const float az = md.a[i] * zrow[k];
-          const float sv = __half2float(__ushort_as_half((unsigned short)(md.sm[i] & 0xFFFFu)));
-          const float mv = __half2float(__ushort_as_half((unsigned short)(md.sm[i] >> 16)));
+          uint32_t k;
+          float av, sv, mv;
+          meta_get<kFSper>(md, lp, i, ns, nq, k, av, sv, mv);
+          good &= k < (uint32_t)a.r;
+          k = k < (uint32_t)a.r ? k : 0u;
+          const float az = av * zrow[k];
           bias += az * mv;          // m = 0 for 16-bit and padding slots
           const float c = az * sv;  // s = 1 for 16-bit slots
           cv[j][i] = c;
@@ -462,11 +516,9 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         }
       }
     }
-    // this wave's projection (its record is in the scalar cache by now)
-    const uint8_t* blob = pj ? a.blob_u : a.blob_g;
-    const SegProj P = uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
-                                           load_rec_s(blob, e, a.E), load_hdr(blob), a.E, a.dout,
-                                           a.r));
+    // this wave's projection
+    const SegProj P = pj ? uniform_seg(make_seg(a.blob_u, a.bytes_u, e, ru, hu, a.E, a.dout, a.r))
+                         : uniform_seg(make_seg(a.blob_g, a.bytes_g, e, rg, hg, a.E, a.dout, a.r));
     // chunk counts of both projections (they advance together)
     {
       int nc = 0;

@@ -8,6 +8,7 @@ namespace bitsmoe {
 
 constexpr int kFusedMaxTokens = 4;   // one-launch path: T <= this
 constexpr int kFusedMaxR = 4096;     //   and r <= this
+constexpr int kZRing = 8;            // tagged z buffers of the one-launch path (by launch)
 constexpr int kGroupMaxR = 4096;     // grouped path: r <= this
 constexpr int kGroupMaxE = 16384;    //   and E <= this (route histogram in LDS)
 constexpr int kGroupMaxDin = 4096;   //   and din <= this (row-blocked projection)
@@ -46,7 +47,7 @@ struct FusedArgs {
   const uint4* phi_t;  // 2r x din fp16
   const uint4* x;      // T x din fp16
   int din8, T;
-  uint64_t* zt;        // T x 2r tagged z
+  uint64_t* zt;        // kZRing x T x 2r tagged z (launch with tag g uses buffer g % kZRing)
   uint32_t* epoch;     // tag of the previous launch
   uint32_t* arrive;    // work-groups done (0 between launches)
   uint32_t* hint;      // 64 counters, 32 words apart: producing waves done (0 between launches)

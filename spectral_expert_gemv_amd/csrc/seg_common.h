@@ -36,13 +36,31 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr int kBlkPerK = 8;  // 4-slot blocks per 32-slot K step
 constexpr int kPW = 4;       // waves per projection sharing a segment's K steps
 
+// Global-memory pointer types: loads through them are global (or buffer)
+// loads counted only on the vector memory counter.  A pointer rebuilt from
+// integers (as the uniform copies below are) would otherwise be a generic
+// one, whose flat loads the compiler must also wait for before any LDS or
+// scalar result is used.
+typedef __attribute__((address_space(1))) const uint16_t gu16;
+typedef __attribute__((address_space(1))) const uint32_t gu32;
+typedef __attribute__((address_space(1))) const float gf32;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 gv4;
+
+// 16-byte global load (p 16-byte aligned).
+template <typename T>
+__device__ __forceinline__ uint4 ld16(const T* p) {
+  const u32x4 v = *(const gv4*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // One projection's expert block, uniform across the work-group (SGPRs).
 struct SegProj {
-  const uint16_t* kidx;
-  const float* A;
-  const uint16_t* S;
-  const uint16_t* M;
-  const uint32_t* planes;  // segment 0's record
+  const gu16* kidx;
+  const gf32* A;
+  const gu16* S;
+  const gu16* M;
+  const gu32* planes;  // segment 0's record
   uint32_t seg_words, n_slot, n_qslot, n_blk;
   uint32_t b1, b2, b3, b4, b5, b6;  // first block of groups 1..6 (widths 2,3,4,6,8,16)
   uint32_t w1, w2, w3, w4, w5, w6;  // first word of groups 1..6 inside a segment record
@@ -70,12 +88,12 @@ __device__ __forceinline__ SegProj make_seg(const uint8_t* blob, uint64_t bytes,
                                             int r) {
   SegProj p;
   p.ok = check_dir(h, d, bytes, e, E, dout, r);
-  const uint8_t* blk = blob + (p.ok ? d.block_offset : 0);
-  p.kidx = reinterpret_cast<const uint16_t*>(blk);
-  p.A = reinterpret_cast<const float*>(blk + d.a_off);
-  p.S = reinterpret_cast<const uint16_t*>(blk + d.s_off);
-  p.M = reinterpret_cast<const uint16_t*>(blk + d.m_off);
-  p.planes = reinterpret_cast<const uint32_t*>(blk + d.planes_off);
+  const uint64_t blk = reinterpret_cast<uint64_t>(blob) + (p.ok ? d.block_offset : 0);
+  p.kidx = (const gu16*)blk;
+  p.A = (const gf32*)(blk + d.a_off);
+  p.S = (const gu16*)(blk + d.s_off);
+  p.M = (const gu16*)(blk + d.m_off);
+  p.planes = (const gu32*)(blk + d.planes_off);
   const SlotGeo geo = slot_geo(d.count);
   uint32_t nb[kNumGroups];
 #pragma unroll
@@ -102,8 +120,8 @@ __device__ __forceinline__ uint32_t rfl(uint32_t v) { return __builtin_amdgcn_re
 
 template <typename T>
 __device__ __forceinline__ T* rfl_ptr(T* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  return reinterpret_cast<T*>(((uint64_t)rfl((uint32_t)(v >> 32)) << 32) | rfl((uint32_t)v));
+  const uint64_t v = (uint64_t)p;
+  return (T*)(((uint64_t)rfl((uint32_t)(v >> 32)) << 32) | rfl((uint32_t)v));
 }
 
 // The record is the same for every lane; this keeps it in scalar registers
@@ -171,12 +189,13 @@ __device__ __forceinline__ uint32_t chunk_end(const SegProj& p, uint32_t b0, uin
 
 // Copy n16 16-byte units from src to the LDS arena dst with nl lanes
 // (lp = 0..nl-1; each wave writes the 1 KB behind its first lane's unit).
-__device__ __forceinline__ void stage16(void* dst, const void* src, uint32_t n16, int lp,
+__device__ __forceinline__ void stage16(void* dst, const gu32* src, uint32_t n16, int lp,
                                         int lane, int nl) {
-  const uint8_t* s = static_cast<const uint8_t*>(src);
+  typedef __attribute__((address_space(1))) void gvoid;
+  const uint64_t s = (uint64_t)src;
   uint8_t* d = static_cast<uint8_t*>(dst);
   for (int i = lp; i < (int)n16; i += nl)
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(s + 16 * (size_t)i),
+    __builtin_amdgcn_global_load_lds((gvoid*)(s + 16 * (uint64_t)i),
                                      (lds_void*)(d + 16 * (size_t)(i - lane)), 16, 0, 0);
 }
 
