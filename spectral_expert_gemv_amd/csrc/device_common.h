@@ -90,6 +90,36 @@ __device__ inline uint32_t decode_f16(const uint32_t* __restrict__ rec, int row,
   return (u & 1) ? (wv >> 16) : (wv & 0xFFFFu);
 }
 
+// Wave-wide sum and max through DPP row operations (no LDS round trips):
+// two quad permutes, the half-row and row mirrors leave every row's total in
+// all its lanes, then row broadcasts 15 (into rows 1, 3) and 31 (into rows
+// 2, 3) leave the wave total in lane 63, read back as a uniform value.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp_move(float v, float fill) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                                                __builtin_bit_cast(int, v), kCtrl,
+                                                                kRowMask, 0xF, false));
+}
+__device__ inline float wave_sum_dpp(float v) {
+  v += dpp_move<0xB1>(v, 0.f);        // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E>(v, 0.f);        // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v, 0.f);       // row_half_mirror
+  v += dpp_move<0x140>(v, 0.f);       // row_mirror
+  v += dpp_move<0x142, 0xA>(v, 0.f);  // row_bcast:15
+  v += dpp_move<0x143, 0xC>(v, 0.f);  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+// (v >= 0 in every lane)
+__device__ inline float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v, 0.f));
+  v = fmaxf(v, dpp_move<0x4E>(v, 0.f));
+  v = fmaxf(v, dpp_move<0x141>(v, 0.f));
+  v = fmaxf(v, dpp_move<0x140>(v, 0.f));
+  v = fmaxf(v, dpp_move<0x142, 0xA>(v, 0.f));
+  v = fmaxf(v, dpp_move<0x143, 0xC>(v, 0.f));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);

@@ -74,7 +74,9 @@ struct __align__(16) FusedLds {
   float pbias[2][kFPW];
   uint32_t pok[2][kFPW];
   int nch[2];
-  uint32_t go;  // = tag once wave 4 has issued the first unit's record loads
+  uint32_t go;     // = tag once wave 4 has issued the first unit's record loads
+  uint32_t zok[kFWaves];  // each wave's staged z words arrived
+  SegProj desc[2];  // the unit's gate and up descriptors (written by wave 4)
 };
 
 __device__ __forceinline__ float fdot8(uint4 a, uint4 b, float acc) {
@@ -205,7 +207,7 @@ __device__ __forceinline__ void wait_hint(const uint32_t* hint, uint32_t nzw) {
   while (true) {
     const uint32_t c =
         __hip_atomic_load(hint + kFHintStride * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    float tot = wave_sum((float)c);  // exact: counts stay far below 2^24
+    float tot = wave_sum_dpp((float)c);  // exact: counts stay far below 2^24
     if ((uint32_t)tot >= nzw || ++spins >= kFSpin / 64) break;
     __builtin_amdgcn_s_sleep(4);
   }
@@ -375,9 +377,6 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
   // gate and up segment records into LDS (waves 4-5 gate, 6-7 up).
   int u = (int)blockIdx.x;
   bool have = u < U;
-  int pair = have ? u % np : 0;
-  int e = have ? (int)*(CU32*)(a.ids + pair) : 0;
-  const HdrF hg = load_hdr(a.blob_g), hu = load_hdr(a.blob_u);
   if (pj == 0) {
     // wait (bounded) until wave 4 has issued its record loads
     for (uint32_t sp = 0; have && sp < kFSpin; ++sp) {
@@ -395,28 +394,29 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
   }
 
   int zt_cached = -1;  // token whose z is in L.Z
-  bool zok = true;     // every lane's words of L.Z arrived
+  bool zok = true;     // this wave's words of L.Z arrived
   for (bool first = true; have; u += G, have = u < U, first = false) {
-    if (!first) {
-      pair = u % np;
-      e = (int)*(CU32*)(a.ids + pair);
-    }
-    const DirRec rg = load_rec_s(a.blob_g, e, a.E);
-    const DirRec ru = load_rec_s(a.blob_u, e, a.E);
-    if (first && wv == kFPW) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (lane == 0) __hip_atomic_store(&L.go, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
+    const int pair = u % np;
     const int sg = u / np;
     const int t = pair / a.ktop;
     // kBoth: waves 4-7 form the coefficients of both projections; otherwise
     // (long slot lists: too many registers) each half forms its own, waves
-    // 0-3 loading the gate metadata once z is published.
+    // 0-3 loading the gate metadata after the descriptors are published.
     constexpr bool kBoth = kFSper <= 9;
     SlotMeta<kFSper> md0, md1;  // kBoth: gate, up; otherwise md0 is this wave's projection
     bool ok0 = true, ok1 = true;
     uint32_t ns0 = 0, nq0 = 0, ns1 = 0, nq1 = 0;  // n_slot, n_qslot of md0, md1
     if (pj == 1) {
+      // routed id -> both directory records (scalar loads) -> slot metadata,
+      // staging copies (waves 4-5 gate, 6-7 up) and the descriptors in LDS
+      const int e = (int)*(CU32*)(a.ids + pair);
+      const DirRec rg = load_rec_s(a.blob_g, e, a.E);
+      const DirRec ru = load_rec_s(a.blob_u, e, a.E);
+      if (first && wv == kFPW) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (lane == 0) __hip_atomic_store(&L.go, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      const HdrF hg = load_hdr(a.blob_g), hu = load_hdr(a.blob_u);
       const SegProj PG = uniform_seg(make_seg(a.blob_g, a.bytes_g, e, rg, hg, a.E, a.dout, a.r));
       const SegProj PU = uniform_seg(make_seg(a.blob_u, a.bytes_u, e, ru, hu, a.E, a.dout, a.r));
       if (kBoth) {
@@ -434,50 +434,79 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
       const SegProj& SP = (wv & 2) ? PU : PG;
       stage_chunk(&L.W[(wv >> 1) & 1][0], SP, sg, 0, chunk_end(SP, 0, kFMaxW),
                   (int)threadIdx.x & 127, lane, 128);
-    } else if (!kBoth) {
-      const SegProj PG = uniform_seg(make_seg(a.blob_g, a.bytes_g, e, rg, hg, a.E, a.dout, a.r));
-      ok0 = PG.ok;
-      ns0 = PG.n_slot; nq0 = PG.n_qslot;
-      load_meta<kFSper>(PG, lp, md0);
+      if (wv == kFPW && lane == 0) {
+        L.desc[0] = PG;
+        L.desc[1] = PU;
+        int nc = 0;
+        for (uint32_t b = 0; b < PG.n_blk; b = chunk_end(PG, b, kFMaxW)) ++nc;
+        L.nch[0] = nc;
+        nc = 0;
+        for (uint32_t b = 0; b < PU.n_blk; b = chunk_end(PU, b, kFMaxW)) ++nc;
+        L.nch[1] = nc;
+      }
+    }
+    __syncthreads();  // descriptors published
+    // this wave's projection
+    const SegProj P = uniform_seg(L.desc[pj]);
+    if (!kBoth && pj == 0) {
+      ok0 = P.ok;
+      ns0 = P.n_slot; nq0 = P.n_qslot;
+      load_meta<kFSper>(P, lp, md0);
     }
     if (t != zt_cached) {
       // one wave polls the hint counters (the first time only), the rest wait
       if (zt_cached < 0 && wv == 0) wait_hint(s.hint, (uint32_t)nzw);
       __syncthreads();
-      zok = __syncthreads_and(stage_z(zt + (size_t)t * R, R, tag, &L.Z[0]) ? 1 : 0) != 0;
+      zok = stage_z(zt + (size_t)t * R, R, tag, &L.Z[0]);
+      zok = __all(zok);
+      if (lane == 0) L.zok[wv] = zok;  // every wave's words: combined in the epilogue
+      __syncthreads();                  // L.Z complete
       zt_cached = t;
     }
     // ---- coefficients ----
     // (kBoth: waves 4-7 do projection 0 = gate from md0 and 1 = up from md1;
-    // otherwise every wave does its own projection pj from md0)
+    // otherwise every wave does its own projection pj from md0).  All the
+    // z gathers from LDS are issued before any is used.
     constexpr int kNQ = kBoth ? 2 : 1;
     float cv[kNQ][kFSper];
+    if (!kBoth || pj == 1) {
+      uint32_t kk[kNQ][kFSper];
+      float av[kNQ][kFSper], sv[kNQ][kFSper], mv[kNQ][kFSper], zv[kNQ][kFSper];
+      bool good[kNQ];
 #pragma unroll
-    for (int j = 0; j < kNQ; ++j) {
-      if (!kBoth || pj == 1) {
-        const int q = kBoth ? j : pj;
+      for (int j = 0; j < kNQ; ++j) {
         const SlotMeta<kFSper>& md = j ? md1 : md0;
-        const float* zrow = &L.Z[q ? a.r : 0];
-        bool good = (j ? ok1 : ok0) && zok;
-        float bias = 0.f, cmx = 0.f;
         const uint32_t ns = j ? ns1 : ns0, nq = j ? nq1 : nq0;
+        good[j] = (j ? ok1 : ok0) && zok;
 #pragma unroll
         for (int i = 0; i < kFSper; ++i) {
-          uint32_t k;
-          float av, sv, mv;
-          meta_get<kFSper>(md, lp, i, ns, nq, k, av, sv, mv);
-          good &= k < (uint32_t)a.r;
-          k = k < (uint32_t)a.r ? k : 0u;
-          const float az = av * zrow[k];
-          bias += az * mv;          // m = 0 for 16-bit and padding slots
-          const float c = az * sv;  // s = 1 for 16-bit slots
+          meta_get<kFSper>(md, lp, i, ns, nq, kk[j][i], av[j][i], sv[j][i], mv[j][i]);
+          good[j] &= kk[j][i] < (uint32_t)a.r;
+          kk[j][i] = kk[j][i] < (uint32_t)a.r ? kk[j][i] : 0u;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kNQ; ++j) {
+        const int q = kBoth ? j : pj;
+        const float* zrow = &L.Z[q ? a.r : 0];
+#pragma unroll
+        for (int i = 0; i < kFSper; ++i) zv[j][i] = zrow[kk[j][i]];
+      }
+#pragma unroll
+      for (int j = 0; j < kNQ; ++j) {
+        const int q = kBoth ? j : pj;
+        float bias = 0.f, cmx = 0.f;
+#pragma unroll
+        for (int i = 0; i < kFSper; ++i) {
+          const float az = av[j][i] * zv[j][i];
+          bias += az * mv[j][i];          // m = 0 for 16-bit and padding slots
+          const float c = az * sv[j][i];  // s = 1 for 16-bit slots
           cv[j][i] = c;
           cmx = fmaxf(cmx, fabsf(c));
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) cmx = fmaxf(cmx, __shfl_xor(cmx, off, kWave));
-        const float bw = wave_sum(bias);
-        const bool wok = __all(good);
+        cmx = wave_max_dpp(cmx);
+        const float bw = wave_sum_dpp(bias);
+        const bool wok = __all(good[j]);
         if (lane == 0) {
           L.pmax[q][wp] = cmx;
           L.pbias[q][wp] = bw;
@@ -515,15 +544,6 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
           L.Clo[q][sl] = lo;
         }
       }
-    }
-    // this wave's projection
-    const SegProj P = pj ? uniform_seg(make_seg(a.blob_u, a.bytes_u, e, ru, hu, a.E, a.dout, a.r))
-                         : uniform_seg(make_seg(a.blob_g, a.bytes_g, e, rg, hg, a.E, a.dout, a.r));
-    // chunk counts of both projections (they advance together)
-    {
-      int nc = 0;
-      for (uint32_t b = 0; b < P.n_blk; b = chunk_end(P, b, kFMaxW)) ++nc;
-      if (threadIdx.x == (unsigned)(pj * kFProj)) L.nch[pj] = nc;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -570,6 +590,8 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
           bsum += L.pbias[q][w];
           ok = ok && L.pok[q][w];
         }
+#pragma unroll
+        for (int w = 0; w < kFWaves; ++w) ok = ok && L.zok[w];
         ys[q] = ldexpf(sum, -Sq) + bsum;
       }
       const int row = sg * kSegRows + lane;

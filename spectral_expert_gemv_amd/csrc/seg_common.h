@@ -356,7 +356,7 @@ __device__ __forceinline__ void ksteps_uniform(const uint32_t* rec0, uint32_t kf
   constexpr uint32_t nw = kPW;
   const uint32_t rstep = nw * kBlkPerK * 4u * (W == 16 ? 16u : (uint32_t)W);
   if constexpr (W == 16) {
-#pragma unroll 1
+#pragma unroll 2
     for (uint32_t kb = kfirst; kb < kend; kb += nw, rec0 += rstep) {
       uint4 vh, vl;
       b_operand(chi, clo, cstride, s0, nt, kb, m, kg, vh, vl);
@@ -365,7 +365,7 @@ __device__ __forceinline__ void ksteps_uniform(const uint32_t* rec0, uint32_t kf
       mfma4(a0, a1, vh, vl, acc0, acc1);
     }
   } else {
-#pragma unroll 1
+#pragma unroll 2
     for (uint32_t kb = kfirst; kb < kend; kb += nw, rec0 += rstep) {
       uint4 vh, vl;
       b_operand(chi, clo, cstride, s0, nt, kb, m, kg, vh, vl);
