@@ -57,7 +57,7 @@ typedef struct ihipStream_t* bitsmoe_stream_t; /* same type as hipStream_t */
 #define BITSMOE_EFORMAT  -5  /* blob magic, version, CRC or directory invalid */
 #define BITSMOE_EHIP     -6  /* HIP runtime or launch error */
 
-#define BITSMOE_FORMAT_VERSION 1
+#define BITSMOE_FORMAT_VERSION 3
 
 /* Library version (major*10000 + minor*100 + patch). */
 int bitsmoe_version(void);
@@ -75,22 +75,31 @@ const char* bitsmoe_last_error_detail(void);
  *   s = fp16_rne((max p - min p) / (2^b - 1)), s = 1 if it rounds to 0;
  *   m = fp16_rne(min p); q_i = clamp(nearbyint((p_i - m) / s), 0, 2^b - 1)
  *   with ties to even.  16 bits: fp16_rne(p_i).  0 bits: no entry.
- * Blob layout (format v1, little-endian, offsets from the blob base):
- *   header 128 B: "BMOE", u32 version, E, dout, r, dout_pad (=64*ceil(dout/64)),
- *     n_slabs (=dout_pad/64), header_bytes(=128); u64 total_bytes at 32,
- *     u64 dir_offset(=128) at 40, u32 CRC-32 (IEEE) of [128, total) at 48.
+ * Blob layout (format v3, little-endian, offsets from the blob base):
+ *   header 128 B: "BMOE", u32 version(=3), E, dout, r, dout_pad
+ *     (=32*ceil(dout/32)), n_seg (=dout_pad/32), header_bytes(=128);
+ *     u64 total_bytes at 32, u64 dir_offset(=128) at 40, u32 CRC-32 (IEEE)
+ *     of [128, total) at 48.
  *   directory: E records of 64 B: u64 block_offset; u32 n_nz, n_q, n_16,
- *     masks_per_slab (= sum of b over 1..8-bit columns), a_off, s_off, m_off,
- *     planes_off, f16_off, block_bytes (offsets relative to the block);
- *     u16 count[7] of widths 1,2,3,4,6,8,16 at 48.
- *   expert block (256-aligned, back to back): columns ordered by width group
- *     1,2,3,4,6,8,16 and by ascending k inside a group;
- *     u16 kidx[n_nz] @0, f32 a[n_nz] @a_off, f16 s[n_q] @s_off,
- *     f16 m[n_q] @m_off, u64 planes[n_slabs][masks_per_slab] @planes_off
- *     (per 64-row slab, per 1..8-bit column, per plane j from the least
- *     significant: bit t = bit j of q[64*slab + t], 0 for rows >= dout),
- *     f16 values[n_16][dout_pad] @f16_off = align256(planes end + 16).
- *     Padding bytes are zero.
+ *     seg_words (u32 words of one 32-row segment record), a_off, s_off,
+ *     m_off, planes_off; f32 cmax (largest |a|*s over 1..8-bit columns,
+ *     |a| over 16-bit ones); u32 block_bytes; u16 count[7] of widths
+ *     1,2,3,4,6,8,16 at 48 (offsets relative to the expert block).
+ *   expert block (256-aligned, back to back): slots ordered by width group
+ *     1,2,3,4,6,8,16, ascending k inside a group, each group padded with
+ *     zero slots to a multiple of 32 (so a 32-slot step has one width);
+ *     0-bit columns have no slot.  n_slot slots, n_qslot of width <= 8:
+ *     u16 kidx[n_slot] @0, f32 a[n_slot] @a_off, f16 s[n_qslot] @s_off,
+ *     f16 m[n_qslot] @m_off (padding slots: all 0), then
+ *     u32 planes[n_seg][seg_words] @planes_off: one record per 32 output
+ *     rows; in it, 4-slot block after block, 4*w words per block of width
+ *     w: for row octet i = 0..3, w words.  w <= 8: word (i, j) is plane j,
+ *     its bit 8*u + rho is bit j of the code of row 8i + rho in slot u of
+ *     the block (byte u holds the octet's 8 rows of slot u).  w = 16: word
+ *     (i, 2*rho + h) holds the fp16 values of row 8i + rho in slots 2h
+ *     (low half) and 2h + 1.  Rows >= dout are 0.
+ *   block_bytes = align256(planes_off + 4*n_seg*seg_words + 16); all
+ *     padding bytes are zero.
  * bitsmoe_pack_size: bytes the blob needs.  bitsmoe_pack: writes it into the
  * host buffer `out` (out_bytes >= that size, else BITSMOE_ENOSPC).
  */

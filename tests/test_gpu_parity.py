@@ -155,6 +155,39 @@ def test_gateup_full(bm, wl_name, steps):
         _say("  worst %.3g" % worst)
 
 
+def _sample_pairs(ids, n, seed):
+    """n (token, slot) pairs: the first and last token, every slot of the
+    most-routed expert's first token, the rest drawn at random."""
+    T, K = ids.shape
+    rng = np.random.default_rng(seed)
+    vals, cnt = np.unique(ids, return_counts=True)
+    top = int(vals[np.argmax(cnt)])
+    tt, ss = np.nonzero(ids == top)
+    pick = {(0, s) for s in range(K)} | {(T - 1, s) for s in range(K)}
+    pick |= {(int(t), int(s_)) for t, s_ in zip(tt[:4], ss[:4])}
+    while len(pick) < min(n, T * K):
+        pick.add((int(rng.integers(T)), int(rng.integers(K))))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("wl_name,n_pairs", [("mixtral_8x7b_t1", 0), ("mixtral_8x7b_t8", 4),
+                                             ("deepseek_moe_16b_t512", 48)])
+def test_gateup_full_size_sampled(bm, wl_name, n_pairs):
+    """The remaining full-size workloads in the launch configuration the
+    benchmark times (the whole batch in one call); the oracle evaluates a
+    sample of (token, slot) pairs (all of them when n_pairs is 0)."""
+    wl = synth.workload(wl_name)
+    L, dev = device_layer(wl.layer.name)
+    x, ids = synth.make_batch(wl, L, step=0)
+    _say("gateup %s T=%d" % (wl_name, x.shape[0]))
+    got = _run_gateup(dev, x, ids)
+    assert np.all(np.isfinite(got))
+    pairs = None if n_pairs == 0 else _sample_pairs(ids, n_pairs, seed=len(wl_name))
+    _say("  oracle on %s pairs" % ("all" if pairs is None else len(pairs)))
+    worst = _check_h(got, pairs_ref(L, x, ids, pairs=pairs))
+    _say("  worst %.3g" % worst)
+
+
 @pytest.mark.parametrize("wl_name", ["qwen3_30b_a3b_t1", "qwen3_30b_a3b_t32"])
 def test_repeat_runs_bit_identical(bm, wl_name):
     wl = synth.workload(wl_name)
