@@ -14,19 +14,24 @@
 //    column metadata to all of them.
 //  * Waves 0-3 of every work-group issue the loads of their contiguous run
 //    of Phi^T rows first (the rows do not depend on anything), compute z for
-//    them once the loads are in (v_dot2_f32_f16, wave reduction) and publish
-//    each value as one 64-bit word (float bits | epoch tag << 32,
-//    device-coherent store): a consumer can tell a fresh value from a stale
-//    one without any fence or shared counter.  Waves 4-7 meanwhile read the
-//    routed id and the two directory records and copy the unit's gate and up
-//    segment records into LDS (16-byte global_load_lds).
-//  * Coefficients: lane l of projection p owns slots l, l + 256, ...; all its
-//    metadata loads and tagged z gathers go out together; the gathers whose
-//    tag is not there yet are re-issued together until all are, then it forms
-//    c = a s z (a z for 16-bit slots) and a m z, and after a block-wide max
-//    writes the fp16 pair hi + lo of c 2^S into LDS.
+//    them (v_dot2_f32_f16, a transposing 4-row reduction) and publish each
+//    value as one 64-bit word (float bits | launch tag << 32, device-coherent
+//    store), wait for their stores and count themselves on one of 64 hint
+//    counters.  A reader can tell a fresh value from a stale one by its tag,
+//    without fences.
+//  * Waves 4-7 meanwhile read the routed id and the two directory records,
+//    issue the slot metadata of both projections and copy the unit's gate
+//    and up segment records into LDS (16-byte global_load_lds); wave 4
+//    publishes both segment descriptors in LDS.
+//  * One wave polls the hint counters; then the work-group copies the
+//    token's 2r tagged words into LDS (coalesced, L2-shared, re-reading
+//    stale words device-coherently).
+//  * Coefficients (waves 4-7): lane l owns slots 8l .. 8l + 7 and the tail
+//    slot 2048 + l of each projection; it forms c = a s z (a z for 16-bit
+//    slots) and a m z, and after block-wide DPP reductions writes the fp16
+//    pair hi + lo of c 2^S into LDS.
 //  * Apply: each wave of a projection takes every 4th 32-slot K step; the
-//    codes of its 16-row tiles are unpacked from the plane nibbles straight
+//    codes of its 16-row tiles are decoded from the plane words straight
 //    into fp16 A operands and multiplied with the coefficient column (B,
 //    token column 0) by v_mfma_f32_16x16x32_f16, hi and lo parts.
 //  * The 4 waves' row sums meet in LDS; wave 0 scales back by 2^-S, adds the
@@ -35,7 +40,8 @@
 // steps.  Work-groups wait for other groups' z, so the host launches at most
 // as many groups as can be resident at once; all waits are bounded (a
 // time-out gives NaN rows, the kernel still exits).  The last group of the
-// grid advances the epoch.
+// grid advances the epoch.  Barriers order LDS only (lds_sync): the
+// staging copies are waited for explicitly where their data is needed.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -74,7 +80,6 @@ struct __align__(16) FusedLds {
   float pbias[2][kFPW];
   uint32_t pok[2][kFPW];
   int nch[2];
-  uint32_t go;     // = tag once wave 4 has issued the first unit's record loads
   uint32_t zok[kFWaves];  // each wave's staged z words arrived
   SegProj desc[2];  // the unit's gate and up descriptors (written by wave 4)
 };
@@ -368,21 +373,12 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
   const int n0 = ((int)blockIdx.x * kFPW + wp) * nrw;
 
   // ---- prologue ----
-  // The first unit's routed id is the first load of every wave (scalar).
-  // Waves 0-3 wait for it before they issue their Phi^T rows, so that the
-  // directory records, which waves 4-7 request as soon as the id is back,
-  // are not queued behind the Phi^T flood; then they produce z and touch
-  // nothing else until it is published.  Waves 4-7 issue the slot metadata
-  // (before the staging copies, so it returns first) and copy the unit's
-  // gate and up segment records into LDS (waves 4-5 gate, 6-7 up).
+  // Waves 0-3 issue their Phi^T rows at once and produce z, touching nothing
+  // else until it is published; the unit's loads are all made by waves 4-7
+  // (below), which need them only once z has been exchanged.
   int u = (int)blockIdx.x;
   bool have = u < U;
   if (pj == 0) {
-    // wait (bounded) until wave 4 has issued its record loads
-    for (uint32_t sp = 0; have && sp < kFSpin; ++sp) {
-      if (__hip_atomic_load(&L.go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == tag) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
     PhiRegs phr;
     phi_issue(s, n0, nrw, lane, phr);
     z_finish(s, zt, n0, nrw, lane, tag, phr);
@@ -395,7 +391,7 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
 
   int zt_cached = -1;  // token whose z is in L.Z
   bool zok = true;     // this wave's words of L.Z arrived
-  for (bool first = true; have; u += G, have = u < U, first = false) {
+  for (; have; u += G, have = u < U) {
     const int pair = u % np;
     const int sg = u / np;
     const int t = pair / a.ktop;
@@ -412,10 +408,6 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
       const int e = (int)*(CU32*)(a.ids + pair);
       const DirRec rg = load_rec_s(a.blob_g, e, a.E);
       const DirRec ru = load_rec_s(a.blob_u, e, a.E);
-      if (first && wv == kFPW) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (lane == 0) __hip_atomic_store(&L.go, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
       const HdrF hg = load_hdr(a.blob_g), hu = load_hdr(a.blob_u);
       const SegProj PG = uniform_seg(make_seg(a.blob_g, a.bytes_g, e, rg, hg, a.E, a.dout, a.r));
       const SegProj PU = uniform_seg(make_seg(a.blob_u, a.bytes_u, e, ru, hu, a.E, a.dout, a.r));
@@ -445,22 +437,24 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         L.nch[1] = nc;
       }
     }
-    __syncthreads();  // descriptors published
-    // this wave's projection
-    const SegProj P = uniform_seg(L.desc[pj]);
-    if (!kBoth && pj == 0) {
-      ok0 = P.ok;
-      ns0 = P.n_slot; nq0 = P.n_qslot;
-      load_meta<kFSper>(P, lp, md0);
+    if (!kBoth) {
+      // waves 0-3 load the gate metadata themselves: descriptors first
+      lds_sync();
+      if (pj == 0) {
+        const SegProj PG = uniform_seg(L.desc[0]);
+        ok0 = PG.ok;
+        ns0 = PG.n_slot; nq0 = PG.n_qslot;
+        load_meta<kFSper>(PG, lp, md0);
+      }
     }
     if (t != zt_cached) {
       // one wave polls the hint counters (the first time only), the rest wait
       if (zt_cached < 0 && wv == 0) wait_hint(s.hint, (uint32_t)nzw);
-      __syncthreads();
+      lds_sync();
       zok = stage_z(zt + (size_t)t * R, R, tag, &L.Z[0]);
       zok = __all(zok);
       if (lane == 0) L.zok[wv] = zok;  // every wave's words: combined in the epilogue
-      __syncthreads();                  // L.Z complete
+      lds_sync();                  // L.Z complete
       zt_cached = t;
     }
     // ---- coefficients ----
@@ -514,7 +508,10 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         }
       }
     }
-    __syncthreads();
+    lds_sync();
+    // this wave's projection (wave 4 published the descriptors before any
+    // barrier of this unit that came before this one)
+    const SegProj P = uniform_seg(L.desc[pj]);
 #pragma unroll
     for (int j = 0; j < kNQ; ++j) {
       if (!kBoth || pj == 1) {
@@ -546,7 +543,7 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    lds_sync();
     const int nch = __builtin_amdgcn_readfirstlane(max(L.nch[0], L.nch[1]));  // uniform
     // ---- apply ----
     f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -554,10 +551,10 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     for (int ch = 0; ch < max(nch, 1); ++ch) {
       const uint32_t b1 = chunk_end(P, b0, kFMaxW);
       if (ch > 0) {
-        __syncthreads();  // every wave is done with the previous chunk
+        lds_sync();  // every wave is done with the previous chunk
         stage_chunk(&L.W[pj][0], P, sg, b0, b1, lp, lane, kFProj);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        lds_sync();
       }
       if (b1 > b0) {
         const uint32_t* base = &L.W[pj][0] - block_word(P, b0);
@@ -575,7 +572,7 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         L.red[pj][wp][16 + 4 * kg + i] = acc1[i];
       }
     }
-    __syncthreads();
+    lds_sync();
     if (wv == 0 && lane < kSegRows) {
       float ys[2];
       bool ok = true;
@@ -598,9 +595,13 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
       if (row < a.dout)
         a.h[(size_t)pair * a.dout + row] = ok ? silu_mul(ys[0], ys[1]) : __builtin_nanf("");
     }
-    __syncthreads();  // LDS is reused by the next unit
+    lds_sync();  // LDS is reused by the next unit
   }
 
+  // every wave's hint increment has landed before the group arrives, so the
+  // last group's reset of the counters cannot be overtaken by one of them
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_sync();
   // ---- grid arrival: the last group advances the epoch ----
   if (threadIdx.x == 0) {
     const uint32_t n =

@@ -118,6 +118,16 @@ __device__ __forceinline__ SegProj make_seg(const uint8_t* blob, uint64_t bytes,
 
 __device__ __forceinline__ uint32_t rfl(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Work-group barrier that orders LDS accesses only.  Unlike __syncthreads it
+// does not make the wave wait for its outstanding global loads, including
+// global_load_lds copies into LDS: a caller that needs those copies landed
+// waits for them itself (s_waitcnt) before the barrier.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename T>
 __device__ __forceinline__ T* rfl_ptr(T* p) {
   const uint64_t v = (uint64_t)p;
