@@ -470,7 +470,6 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     fa.T = T;
     fa.zt = (uint64_t*)(wsb + plan.zt_off);
     fa.epoch = (uint32_t*)(wsb + plan.sync_off);
-    fa.arrive = fa.epoch + 1;
     fa.hint = fa.epoch + 32;
     fa.grid = fgrid;
     launch_gateup_fused(fa, s);

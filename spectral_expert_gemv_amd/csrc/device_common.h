@@ -120,6 +120,21 @@ __device__ inline float wave_max_dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Wave-wide sum of unsigned words (modulo 2^32), same DPP pattern.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_move_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, false);
+}
+__device__ inline uint32_t wave_sum_u32_dpp(uint32_t v) {
+  v += dpp_move_u<0xB1>(v);
+  v += dpp_move_u<0x4E>(v);
+  v += dpp_move_u<0x141>(v);
+  v += dpp_move_u<0x140>(v);
+  v += dpp_move_u<0x142, 0xA>(v);
+  v += dpp_move_u<0x143, 0xC>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);

@@ -73,11 +73,12 @@ constexpr int kFZPer = kFZ / kFThreads;     // tagged z words per lane
 struct __align__(16) FusedLds {
   uint32_t W[2][kFMaxW + 64];
   float Z[kFZ];
-  _Float16 Chi[2][kFMaxS];
-  _Float16 Clo[2][kFMaxS];
+  int8_t Lb[2][kDigits][kFMaxS];  // coefficient digits per projection (v = sum 2^(8 l) d_l)
   float red[2][kFPW][kSegRows];
-  float pmax[2][kFPW];
+  float pmax[2][kFPW];    // largest |c| of 1..8-bit slots
+  float pmax16[2][kFPW];  // largest |c| of 16-bit slots
   float pbias[2][kFPW];
+  float pcorr[2][kFPW];  // 128 * sum of v 2^-S over width-8 slots (those enter as code - 128)
   uint32_t pok[2][kFPW];
   int nch[2];
   uint32_t zok[kFWaves];  // each wave's staged z words arrived
@@ -203,17 +204,19 @@ __device__ __forceinline__ void z_finish(const FusedArgs& s, uint64_t* zt, int n
   }
 }
 
-// Bounded wait until the hint counters say that every producing wave has
-// published (lane i reads counter i; 64 counters on separate lines keep the
-// producers' increments from contending).  Only a hint: the tags decide.
-__device__ __forceinline__ void wait_hint(const uint32_t* hint, uint32_t nzw) {
+// Bounded wait until the hint counters say that every producing wave of this
+// launch has published: the counters are never reset, so after the launch
+// with tag g their sum is g times the number of producing waves (modulo
+// 2^32).  Lane i reads counter i; 64 counters on separate lines keep the
+// producers' increments from contending.  Only a hint: the tags decide.
+__device__ __forceinline__ void wait_hint(const uint32_t* hint, uint32_t target) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t spins = 0;
   while (true) {
     const uint32_t c =
         __hip_atomic_load(hint + kFHintStride * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    float tot = wave_sum_dpp((float)c);  // exact: counts stay far below 2^24
-    if ((uint32_t)tot >= nzw || ++spins >= kFSpin / 64) break;
+    const uint32_t tot = wave_sum_u32_dpp(c);  // modulo 2^32, like the target
+    if ((int32_t)(tot - target) >= 0 || ++spins >= kFSpin / 64) break;
     __builtin_amdgcn_s_sleep(4);
   }
 }
@@ -382,8 +385,8 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     PhiRegs phr;
     phi_issue(s, n0, nrw, lane, phr);
     z_finish(s, zt, n0, nrw, lane, tag, phr);
-    // the hint counts a wave only once its z stores have completed
-    __builtin_amdgcn_s_waitcnt(0);
+    // (the hint may run ahead of the z stores: a reader that comes too early
+    // finds old tags and re-reads those words)
     if (lane == 0)
       __hip_atomic_fetch_add(s.hint + kFHintStride * (((int)blockIdx.x * kFPW + wp) & (kFHint - 1)),
                              1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -399,9 +402,11 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     // (long slot lists: too many registers) each half forms its own, waves
     // 0-3 loading the gate metadata after the descriptors are published.
     constexpr bool kBoth = kFSper <= 9;
+    constexpr int V = SlotMeta<kFSper>::V;
     SlotMeta<kFSper> md0, md1;  // kBoth: gate, up; otherwise md0 is this wave's projection
     bool ok0 = true, ok1 = true;
     uint32_t ns0 = 0, nq0 = 0, ns1 = 0, nq1 = 0;  // n_slot, n_qslot of md0, md1
+    uint32_t e8a0 = 0, e8b0 = 0, e8a1 = 0, e8b1 = 0;  // width-8 slot ranges of md0, md1
     if (pj == 1) {
       // routed id -> both directory records (scalar loads) -> slot metadata,
       // staging copies (waves 4-5 gate, 6-7 up) and the descriptors in LDS
@@ -416,11 +421,14 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         ok1 = PU.ok;
         ns0 = PG.n_slot; nq0 = PG.n_qslot;
         ns1 = PU.n_slot; nq1 = PU.n_qslot;
+        e8a0 = 4u * PG.b5; e8b0 = 4u * PG.b6;
+        e8a1 = 4u * PU.b5; e8b1 = 4u * PU.b6;
         load_meta<kFSper>(PG, lp, md0);
         load_meta<kFSper>(PU, lp, md1);
       } else {
         ok0 = PU.ok;
         ns0 = PU.n_slot; nq0 = PU.n_qslot;
+        e8a0 = 4u * PU.b5; e8b0 = 4u * PU.b6;
         load_meta<kFSper>(PU, lp, md0);
       }
       const SegProj& SP = (wv & 2) ? PU : PG;
@@ -444,12 +452,13 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         const SegProj PG = uniform_seg(L.desc[0]);
         ok0 = PG.ok;
         ns0 = PG.n_slot; nq0 = PG.n_qslot;
+        e8a0 = 4u * PG.b5; e8b0 = 4u * PG.b6;
         load_meta<kFSper>(PG, lp, md0);
       }
     }
     if (t != zt_cached) {
       // one wave polls the hint counters (the first time only), the rest wait
-      if (zt_cached < 0 && wv == 0) wait_hint(s.hint, (uint32_t)nzw);
+      if (zt_cached < 0 && wv == 0) wait_hint(s.hint, tag * (uint32_t)nzw);
       lds_sync();
       zok = stage_z(zt + (size_t)t * R, R, tag, &L.Z[0]);
       zok = __all(zok);
@@ -489,20 +498,41 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
 #pragma unroll
       for (int j = 0; j < kNQ; ++j) {
         const int q = kBoth ? j : pj;
-        float bias = 0.f, cmx = 0.f;
+        const uint32_t nq = j ? nq1 : nq0;
+        float bias = 0.f, cmx = 0.f, cmx16 = 0.f;
 #pragma unroll
         for (int i = 0; i < kFSper; ++i) {
           const float az = av[j][i] * zv[j][i];
           bias += az * mv[j][i];          // m = 0 for 16-bit and padding slots
           const float c = az * sv[j][i];  // s = 1 for 16-bit slots
           cv[j][i] = c;
-          cmx = fmaxf(cmx, fabsf(c));
+          if (meta_slot<kFSper>(lp, i) < nq)
+            cmx = fmaxf(cmx, fabsf(c));
+          else
+            cmx16 = fmaxf(cmx16, fabsf(c));
         }
         cmx = wave_max_dpp(cmx);
+        cmx16 = wave_max_dpp(cmx16);
         const float bw = wave_sum_dpp(bias);
         const bool wok = __all(good[j]);
+        if (kBoth) {
+          // the coefficients go through LDS (the digit table's space, as
+          // floats) so that all eight waves split them, each its own
+          // projection
+          float* cz = reinterpret_cast<float*>(&L.Lb[q][0][0]);
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            const uint32_t sv = 8u * V * (uint32_t)lp + 8u * v;
+            *reinterpret_cast<float4*>(cz + sv) =
+                make_float4(cv[j][8 * v], cv[j][8 * v + 1], cv[j][8 * v + 2], cv[j][8 * v + 3]);
+            *reinterpret_cast<float4*>(cz + sv + 4) =
+                make_float4(cv[j][8 * v + 4], cv[j][8 * v + 5], cv[j][8 * v + 6], cv[j][8 * v + 7]);
+          }
+          cz[meta_slot<kFSper>(lp, 8 * V)] = cv[j][8 * V];
+        }
         if (lane == 0) {
           L.pmax[q][wp] = cmx;
+          L.pmax16[q][wp] = cmx16;
           L.pbias[q][wp] = bw;
           L.pok[q][wp] = wok;
         }
@@ -512,41 +542,68 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     // this wave's projection (wave 4 published the descriptors before any
     // barrier of this unit that came before this one)
     const SegProj P = uniform_seg(L.desc[pj]);
-#pragma unroll
-    for (int j = 0; j < kNQ; ++j) {
-      if (!kBoth || pj == 1) {
-        const int q = kBoth ? j : pj;
-        const float pmx =
-            fmaxf(fmaxf(L.pmax[q][0], L.pmax[q][1]), fmaxf(L.pmax[q][2], L.pmax[q][3]));
-        const int S = coef_shift(pmx, 1.0f);
-        // (zeros past n_slot; the tail slot can lie past the arrays)
-        constexpr int V = SlotMeta<kFSper>::V;
+    {
+      float cq[kFSper];
+      if (kBoth) {
+        const float* cz = reinterpret_cast<const float*>(&L.Lb[pj][0][0]);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-          union {
-            _Float16 h[8];
-            uint4 u;
-          } hi8, lo8;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) split_coef(cv[j][8 * v + i], S, hi8.h[i], lo8.h[i]);
           const uint32_t sv = 8u * V * (uint32_t)lp + 8u * v;
-          *reinterpret_cast<uint4*>(&L.Chi[q][sv]) = hi8.u;
-          *reinterpret_cast<uint4*>(&L.Clo[q][sv]) = lo8.u;
+          const float4 c0 = *reinterpret_cast<const float4*>(cz + sv);
+          const float4 c1 = *reinterpret_cast<const float4*>(cz + sv + 4);
+          cq[8 * v] = c0.x; cq[8 * v + 1] = c0.y; cq[8 * v + 2] = c0.z; cq[8 * v + 3] = c0.w;
+          cq[8 * v + 4] = c1.x; cq[8 * v + 5] = c1.y; cq[8 * v + 6] = c1.z; cq[8 * v + 7] = c1.w;
         }
-        const uint32_t sl = meta_slot<kFSper>(lp, 8 * V);
-        if (sl < kFMaxS) {
-          _Float16 hi, lo;
-          split_coef(cv[j][8 * V], S, hi, lo);
-          L.Chi[q][sl] = hi;
-          L.Clo[q][sl] = lo;
-        }
+        cq[8 * V] = cz[meta_slot<kFSper>(lp, 8 * V)];
+        lds_sync();  // every wave has its coefficients before the digits overwrite them
+      } else {
+#pragma unroll
+        for (int i = 0; i < kFSper; ++i) cq[i] = cv[0][i];
       }
+      const float pmx =
+          fmaxf(fmaxf(L.pmax[pj][0], L.pmax[pj][1]), fmaxf(L.pmax[pj][2], L.pmax[pj][3]));
+      const float pmx16 =
+          fmaxf(fmaxf(L.pmax16[pj][0], L.pmax16[pj][1]), fmaxf(L.pmax16[pj][2], L.pmax16[pj][3]));
+      const int S = digit_shift(pmx), S16 = digit_shift(pmx16);
+      const uint32_t nq = P.n_qslot, e8a = 4u * P.b5, e8b = 4u * P.b6;
+      // digits of v = rint(c 2^S) (2^S16 for 16-bit slots; zeros past
+      // n_slot; the tail slot can lie past the arrays), and the width-8
+      // correction
+      float corr = 0.f;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const uint32_t sv = 8u * V * (uint32_t)lp + 8u * v;
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int vi = (int)rintf(ldexpf(cq[8 * v + i], sv + i < nq ? S : S16));
+          w[i] = digit_bytes(vi);
+          corr += (sv + i >= e8a && sv + i < e8b) ? (float)vi : 0.f;
+        }
+        uint32_t r0[4], r1[4];
+        transpose4(w[0], w[1], w[2], w[3], r0);
+        transpose4(w[4], w[5], w[6], w[7], r1);
+#pragma unroll
+        for (int l = 0; l < kDigits; ++l)
+          *reinterpret_cast<uint2*>(&L.Lb[pj][l][sv]) = make_uint2(r0[l], r1[l]);
+      }
+      const uint32_t sl = meta_slot<kFSper>(lp, 8 * V);
+      if (sl < kFMaxS) {
+        const int vi = (int)rintf(ldexpf(cq[8 * V], sl < nq ? S : S16));
+        const uint32_t wt = digit_bytes(vi);
+#pragma unroll
+        for (int l = 0; l < kDigits; ++l) L.Lb[pj][l][sl] = (int8_t)(wt >> (8 * l));
+        corr += (sl >= e8a && sl < e8b) ? (float)vi : 0.f;
+      }
+      corr = wave_sum_dpp(corr);
+      if (lane == 0) L.pcorr[pj][wp] = ldexpf(128.f * corr, -S);
     }
     __builtin_amdgcn_s_waitcnt(0);
     lds_sync();
     const int nch = __builtin_amdgcn_readfirstlane(max(L.nch[0], L.nch[1]));  // uniform
     // ---- apply ----
-    f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    i32x4 acc_0 = {0, 0, 0, 0}, acc_1 = {0, 0, 0, 0};  // column n: digit n
+    f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};  // fp16 columns: hi, lo
     uint32_t b0 = 0;
     for (int ch = 0; ch < max(nch, 1); ++ch) {
       const uint32_t b1 = chunk_end(P, b0, kFMaxW);
@@ -558,18 +615,33 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
       }
       if (b1 > b0) {
         const uint32_t* base = &L.W[pj][0] - block_word(P, b0);
-        mfma_ksteps(P, base, &L.Chi[pj][0], &L.Clo[pj][0], 0, 0u, 1,
-                    b0 / kBlkPerK, (b1 + kBlkPerK - 1) / kBlkPerK, wp, lane, acc0, acc1);
+        i8_ksteps(P, base, &L.Lb[pj][0][0], kFMaxS, b0 / kBlkPerK,
+                  (b1 + kBlkPerK - 1) / kBlkPerK, wp, lane, acc_0, acc_1, acc0, acc1);
       }
       b0 = b1;
     }
     // ---- row sums of the 4 waves, SiLU * mul ----
-    if ((lane & 15) == 0) {
-      const int kg = lane >> 4;
+    {
+      // fold the columns: lane (n, quarter) holds column n of rows 4 quarter
+      // .. + 3; integer column n is worth 2^(8 n - S), fp16 columns 0, 1
+      // 2^(16 - S16); a quad sum leaves each row's total in column 0
+      const float mq = fmaxf(fmaxf(L.pmax[pj][0], L.pmax[pj][1]), fmaxf(L.pmax[pj][2], L.pmax[pj][3]));
+      const float m16 =
+          fmaxf(fmaxf(L.pmax16[pj][0], L.pmax16[pj][1]), fmaxf(L.pmax16[pj][2], L.pmax16[pj][3]));
+      const int S = digit_shift(mq), S16 = digit_shift(m16);
+      const int n = lane & 15, kg = lane >> 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        L.red[pj][wp][4 * kg + i] = acc0[i];
-        L.red[pj][wp][16 + 4 * kg + i] = acc1[i];
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const i32x4& ai = t2 ? acc_1 : acc_0;
+        const f4& a16 = t2 ? acc1 : acc0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = (n < kDigits ? ldexpf((float)ai[i], 8 * n - S) : 0.f) +
+                    (n < 2 ? ldexpf(a16[i], 16 - S16) : 0.f);
+          v += dpp_move<0xB1>(v, 0.f);  // quad_perm [1,0,3,2]
+          v += dpp_move<0x4E>(v, 0.f);  // quad_perm [2,3,0,1]
+          if (n == 0) L.red[pj][wp][16 * t2 + 4 * kg + i] = v;
+        }
       }
     }
     lds_sync();
@@ -578,18 +650,16 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
       bool ok = true;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const float mx = fmaxf(fmaxf(L.pmax[q][0], L.pmax[q][1]), fmaxf(L.pmax[q][2], L.pmax[q][3]));
-        const int Sq = coef_shift(mx, 1.0f);
         float sum = 0.f, bsum = 0.f;
 #pragma unroll
         for (int w = 0; w < kFPW; ++w) {
-          sum += L.red[q][w][lane];
+          sum += L.red[q][w][lane] + L.pcorr[q][w];
           bsum += L.pbias[q][w];
           ok = ok && L.pok[q][w];
         }
 #pragma unroll
         for (int w = 0; w < kFWaves; ++w) ok = ok && L.zok[w];
-        ys[q] = ldexpf(sum, -Sq) + bsum;
+        ys[q] = sum + bsum;
       }
       const int row = sg * kSegRows + lane;
       if (row < a.dout)
@@ -598,21 +668,12 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     lds_sync();  // LDS is reused by the next unit
   }
 
-  // every wave's hint increment has landed before the group arrives, so the
-  // last group's reset of the counters cannot be overtaken by one of them
-  __builtin_amdgcn_s_waitcnt(0);
-  lds_sync();
-  // ---- grid arrival: the last group advances the epoch ----
-  if (threadIdx.x == 0) {
-    const uint32_t n =
-        __hip_atomic_fetch_add(s.arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (n == (uint32_t)G - 1) {
-      for (int i = 0; i < kFHint; ++i)
-        __hip_atomic_store(s.hint + kFHintStride * i, 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(s.arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(s.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+  // Work-group 0 advances the epoch once every producing wave has counted
+  // itself: by then every work-group has read the old epoch (its tag is in
+  // its registers), and the next launch reads the new one.
+  if (blockIdx.x == 0 && wv == 0) {
+    if (zt_cached < 0) wait_hint(s.hint, tag * (uint32_t)nzw);
+    if (lane == 0) __hip_atomic_store(s.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

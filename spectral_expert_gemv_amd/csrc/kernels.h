@@ -49,8 +49,7 @@ struct FusedArgs {
   int din8, T;
   uint64_t* zt;        // kZRing x T x 2r tagged z (launch with tag g uses buffer g % kZRing)
   uint32_t* epoch;     // tag of the previous launch
-  uint32_t* arrive;    // work-groups done (0 between launches)
-  uint32_t* hint;      // 64 counters, 32 words apart: producing waves done (0 between launches)
+  uint32_t* hint;      // 64 counters, 32 words apart: producing waves done, cumulative over launches
   int grid;            // multiple of 8, all work-groups resident
 };
 size_t fused_lds_bytes();

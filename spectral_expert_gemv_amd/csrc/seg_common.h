@@ -427,5 +427,188 @@ __device__ __forceinline__ void mfma_ksteps(const SegProj& p, const uint32_t* ba
   group_steps<16>(base, p.b6, p.n_blk, p.w6, kb0, kb1, wp, chi, clo, cstride, s0, nt, m, kg, acc0, acc1);
 }
 
+// ---------------------------------------------------------------------------
+// Integer apply for one token column (the one-launch kernel).
+//
+// Coefficients of 1..8-bit slots become integers v = rint(c 2^S) with
+// |v| < 2^30 (S from the largest such |c| of the projection), stored as four
+// signed 8-bit digits v = sum_n 2^(8 n) d_n (each in [-128, 127]); v keeps
+// the full float precision of every c within 2^6 of that maximum.  With one
+// token, the B operand's 16 columns carry the four digit rows (column n =
+// digit n, columns 4..15 zero), so one v_mfma_i32_16x16x64_i8 per 16-row
+// tile applies a 64-slot step: the decoded code bytes are the A operand as
+// they come out of the plane decode, and every product and sum is exact in
+// int32 (|code| <= 128, |digit| <= 128, <= 4.4k slots).  The columns are
+// folded once per unit: y = sum_n 2^(8 n) C[., n].  Width-8 codes (0..255)
+// enter as code - 128; the caller adds back 128 * sum of their v.  16-bit
+// slots have a scale S16 of their own and use v_mfma_f32_16x16x32_f16 with
+// the fp16 hi and lo parts of v 2^-16 in columns 0 and 1.  Lane l holds row
+// l % 16 of a tile and the slots of one quarter (l / 16) of the step, in A
+// and B alike, so the contraction covers the whole step.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kDigits = 4;
+
+// S for coefficients bounded by mx: |c| 2^S < 2^30 (0 when mx is 0 or not
+// finite).
+__device__ __forceinline__ int digit_shift(float mx) {
+  if (!(mx > 0.f) || !(mx < 3.0e38f)) return 0;
+  int e;
+  (void)frexpf(mx, &e);
+  return 30 - e;
+}
+
+// The four digit bytes of v in one word (byte n = digit n): adding 0x80 to
+// every byte lets the carries of a 32-bit add perform the balanced
+// base-256 split, and the xor recentres each byte (|v| <= 2^30).
+__device__ __forceinline__ uint32_t digit_bytes(int v) {
+  return ((uint32_t)v + 0x80808080u) ^ 0x80808080u;
+}
+
+// 4 x 4 byte transpose: words a, b, c, d (one slot each, byte n = digit n)
+// become rows r[n] = digit n of (a, b, c, d) in bytes 0..3.
+__device__ __forceinline__ void transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                           uint32_t (&r)[4]) {
+  const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
+  const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
+  const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);
+  const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);
+  r[0] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);
+  r[1] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);
+  r[2] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+  r[3] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
+}
+
+__device__ __forceinline__ i32x4 mfma_i8(i32x4 a, i32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
+// A operand of tile `tile` (rows 16 tile .. + 15) for this lane's 4 blocks of
+// width W <= 8 starting at `rec` (block record words, 4 W per block).
+template <int W>
+__device__ __forceinline__ i32x4 a_i8(const uint32_t* rec, int m, int tile) {
+  i32x4 a;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t w[W];
+    load_oct<W>(rec + 4 * W * d + (2 * tile + (m >> 3)) * W, w);
+    uint32_t c = row_codes4<W>(w, m & 7);
+    if constexpr (W == 8) c ^= 0x80808080u;  // code - 128 in every byte
+    a[d] = (int)c;
+  }
+  return a;
+}
+
+// Steps of one width group W <= 8 inside K32 range [s, e) (K32 index k =
+// slots 32 k .. + 31): 64-slot steps from s, the wave taking the steps i
+// with (i + off) % 4 == wp; a trailing half step (e - s odd) uses zero codes
+// and digits in its upper lanes and reads nothing there.  Block b's record:
+// base + ws + (b - bs) 4 W.  lb: digit rows, row n at lb + n * ldig.
+template <int W>
+__device__ __forceinline__ void i8_group(const uint32_t* base, uint32_t bs, uint32_t ws,
+                                         uint32_t s, uint32_t e, uint32_t off, int wp,
+                                         const int8_t* lb, uint32_t ldig, int lane,
+                                         i32x4& acc0, i32x4& acc1) {
+  if (e <= s) return;
+  const int m = lane & 15, g = lane >> 4;
+  const uint32_t n64 = (e - s + 1) / 2;
+  const uint32_t i0 = ((uint32_t)wp + 4u - (off & 3u)) & 3u;
+  const i32x4 zero = {0, 0, 0, 0};
+  const int8_t* lbn = lb + (m & 3) * ldig;  // this lane's digit row (columns >= 4: zero)
+#pragma unroll 1
+  for (uint32_t i = i0; i < n64; i += 4) {
+    const uint32_t k = s + 2 * i;
+    const bool valid = g < 2 || k + 1 < e;
+    i32x4 b = zero, a0 = zero, a1 = zero;
+    if (valid) {
+      const i32x4 bv = *reinterpret_cast<const i32x4*>(lbn + 32u * k + 16u * (uint32_t)g);
+      b = m < kDigits ? bv : zero;
+      const uint32_t* rec = base + ws + (8u * k + 4u * (uint32_t)g - bs) * 4u * W;
+      a0 = a_i8<W>(rec, m, 0);
+      a1 = a_i8<W>(rec, m, 1);
+    }
+    acc0 = mfma_i8(a0, b, acc0);
+    acc1 = mfma_i8(a1, b, acc1);
+  }
+}
+
+// 16-bit group steps [s, e) (K32) on the fp16 path: A = the stored fp16
+// values, B column 0 = hi and column 1 = lo fp16 parts of v 2^-16 rebuilt
+// from v's digits (|v 2^-16| < 2^14 stays in fp16 range; hi + lo keeps 22
+// bits of v): the sums are in units of 2^(16 - S16).
+__device__ __forceinline__ void f16_group(const uint32_t* base, uint32_t bs, uint32_t ws,
+                                          uint32_t s, uint32_t e, uint32_t off, int wp,
+                                          const int8_t* lb, uint32_t ldig, int lane, f4& acc0,
+                                          f4& acc1) {
+  if (e <= s) return;
+  const int m = lane & 15, kg = lane >> 4;
+  const uint32_t i0 = ((uint32_t)wp + 4u - (off & 3u)) & 3u;
+#pragma unroll 1
+  for (uint32_t k = s + i0; k < e; k += 4) {
+    uint4 bv = make_uint4(0, 0, 0, 0);
+    if (m < 2) {
+      const uint32_t so = 32u * k + 8u * (uint32_t)kg;
+      uint2 q[kDigits];
+#pragma unroll
+      for (int l = 0; l < kDigits; ++l) q[l] = *reinterpret_cast<const uint2*>(lb + l * ldig + so);
+      union {
+        _Float16 h[8];
+        uint4 u;
+      } hv;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sh = 8 * (j & 3);
+        float fv = 0.f;
+#pragma unroll
+        for (int l = kDigits - 1; l >= 0; --l)
+          // sign extension through int8_t: the sbfe builtin's result was
+          // converted as unsigned by this compiler
+          fv = fv * 256.f + (float)(int)(int8_t)((j < 4 ? q[l].x : q[l].y) >> sh);
+        fv *= 1.52587890625e-05f;  // 2^-16, exact
+        const _Float16 hi = (_Float16)fv;
+        hv.h[j] = m == 0 ? hi : (_Float16)(fv - (float)hi);
+      }
+      bv = hv.u;
+    }
+    h8 a0, a1;
+    a_tiles_f16(base + ws + (8u * k + 2u * (uint32_t)kg - bs) * 64u, m, a0, a1);
+    const h8 b = h8_of(bv);
+    acc0 = mfma(a0, b, acc0);
+    acc1 = mfma(a1, b, acc1);
+  }
+}
+
+// This wave's share of the K32 steps [kb0, kb1) of a segment (the staged
+// chunk holds them; base: word 0 of the segment record).  Integer sums go
+// to acc_t (tile t, column n = digit n, units of 2^(8 n - S)), fp16-column
+// sums to acc16_t (column 0 hi, 1 lo, units of 2^(16 - S16)).  Steps are
+// dealt to the waves round-robin across groups.
+__device__ __forceinline__ void i8_ksteps(const SegProj& p, const uint32_t* base,
+                                          const int8_t* lb, uint32_t ldig, uint32_t kb0,
+                                          uint32_t kb1, int wp, int lane, i32x4& acc_0,
+                                          i32x4& acc_1, f4& acc16_0, f4& acc16_1) {
+  kb0 = rfl(kb0);
+  kb1 = rfl(kb1);
+  const uint32_t gb[kNumGroups + 1] = {0u, p.b1, p.b2, p.b3, p.b4, p.b5, p.b6, p.n_blk};
+  const uint32_t gw[kNumGroups] = {0u, p.w1, p.w2, p.w3, p.w4, p.w5, p.w6};
+  uint32_t off = 0;
+#pragma unroll
+  for (int g = 0; g < kNumGroups; ++g) {
+    const uint32_t s = max(gb[g] / kBlkPerK, kb0), e = min(gb[g + 1] / kBlkPerK, kb1);
+    const uint32_t n = e > s ? e - s : 0u;
+    switch (g) {
+      case 0: i8_group<1>(base, gb[g], gw[g], s, e, off, wp, lb, ldig, lane, acc_0, acc_1); break;
+      case 1: i8_group<2>(base, gb[g], gw[g], s, e, off, wp, lb, ldig, lane, acc_0, acc_1); break;
+      case 2: i8_group<3>(base, gb[g], gw[g], s, e, off, wp, lb, ldig, lane, acc_0, acc_1); break;
+      case 3: i8_group<4>(base, gb[g], gw[g], s, e, off, wp, lb, ldig, lane, acc_0, acc_1); break;
+      case 4: i8_group<6>(base, gb[g], gw[g], s, e, off, wp, lb, ldig, lane, acc_0, acc_1); break;
+      case 5: i8_group<8>(base, gb[g], gw[g], s, e, off, wp, lb, ldig, lane, acc_0, acc_1); break;
+      default:
+        f16_group(base, gb[g], gw[g], s, e, off, wp, lb, ldig, lane, acc16_0, acc16_1);
+        break;
+    }
+    off += g < kNumGroups - 1 ? (n + 1) / 2 : n;
+  }
+}
+
 }  // namespace seg
 }  // namespace bitsmoe
