@@ -646,8 +646,10 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     }
     lds_sync();
     if (wv == 0 && lane < kSegRows) {
+      // every flag read first and combined without branches (a short-circuit
+      // && would wait for each LDS read in turn)
       float ys[2];
-      bool ok = true;
+      uint32_t okw = 1u;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         float sum = 0.f, bsum = 0.f;
@@ -655,12 +657,13 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         for (int w = 0; w < kFPW; ++w) {
           sum += L.red[q][w][lane] + L.pcorr[q][w];
           bsum += L.pbias[q][w];
-          ok = ok && L.pok[q][w];
+          okw &= L.pok[q][w];
         }
-#pragma unroll
-        for (int w = 0; w < kFWaves; ++w) ok = ok && L.zok[w];
         ys[q] = sum + bsum;
       }
+#pragma unroll
+      for (int w = 0; w < kFWaves; ++w) okw &= L.zok[w];
+      const bool ok = okw != 0u;
       const int row = sg * kSegRows + lane;
       if (row < a.dout)
         a.h[(size_t)pair * a.dout + row] = ok ? silu_mul(ys[0], ys[1]) : __builtin_nanf("");
