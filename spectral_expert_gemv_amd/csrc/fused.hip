@@ -173,7 +173,11 @@ __device__ __forceinline__ void z_finish(const FusedArgs& s, uint64_t* zt, int n
                                          int lane, uint32_t tag, const PhiRegs& q) {
   static_assert(kFPre == 4, "the transposing reduction is written for 4 rows");
   const int R = 2 * s.g.r;
-  for (int tt = 0; tt < s.T; ++tt) {
+  // (T >= 1: a do-while leaves no path on which the x and Phi^T loads are
+  // still outstanding when the hint increment is issued, which would make the
+  // compiler wait for every store first)
+  int tt = 0;
+  do {
     float v[kFPre];
 #pragma unroll
     for (int j = 0; j < kFPre; ++j) {
@@ -187,7 +191,7 @@ __device__ __forceinline__ void z_finish(const FusedArgs& s, uint64_t* zt, int n
     for (int off = 4; off < kWave; off <<= 1) z += __shfl_xor(z, off, kWave);
     const int j = lane & 3;
     if (lane < kFPre && j < nrw && n0 + j < R) publish_z(zt, s.g.r, tt, n0 + j, z, tag);
-  }
+  } while (++tt < s.T);
   for (int j = kFPre; j < nrw && n0 + j < R; ++j) {  // rows beyond the first kFPre
     const int n = n0 + j;
     const uint4* prow = s.phi_t + (size_t)n * s.din8;
