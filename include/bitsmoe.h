@@ -73,7 +73,8 @@ const char* bitsmoe_last_error_detail(void);
  *   bits : E*r uint8 widths in {0,1,2,3,4,6,8,16}
  * Quantizer (1..8 bits), all in IEEE float32 without fused operations:
  *   s = fp16_rne((max p - min p) / (2^b - 1)), s = 1 if it rounds to 0;
- *   m = fp16_rne(min p); q_i = clamp(nearbyint((p_i - m) / s), 0, 2^b - 1)
+ *   m = fp16_rne(min p) (-0 below +0); q_i = clamp(nearbyint((p_i - m) / s),
+ *   0, 2^b - 1)
  *   with ties to even.  16 bits: fp16_rne(p_i).  0 bits: no entry.
  * Blob layout (format v3, little-endian, offsets from the blob base):
  *   header 128 B: "BMOE", u32 version(=3), E, dout, r, dout_pad
@@ -106,6 +107,28 @@ const char* bitsmoe_last_error_detail(void);
 int bitsmoe_pack_size(int E, int dout, int r, const uint8_t* bits, size_t* out_bytes);
 int bitsmoe_pack(int E, int dout, int r, const float* p, const float* a,
                  const uint8_t* bits, void* out, size_t out_bytes);
+
+/* Device packer: the same blob bytes as bitsmoe_pack, produced on the GPU
+ * ("second split", "Usage", "execution").
+ *   p, a : device float32 arrays laid out as for bitsmoe_pack
+ *   bits : HOST array of E*r widths (the layout is planned on the host)
+ *   out  : device buffer of out_bytes >= bitsmoe_pack_size() bytes, 16-byte
+ *          aligned; on success it holds the complete blob (header and CRC
+ *          included)
+ *   ws   : device workspace of >= bitsmoe_pack_device_workspace_size()
+ *          bytes, 16-byte aligned (slot table, checksum chunks, flags)
+ * The quantizer is the one above, in IEEE float32 without contraction, so
+ * the codes match the host packer's bit for bit; the CRC is taken over 4 KiB
+ * chunks on the device and folded on the host.  Work is issued on `stream`
+ * and the call returns after synchronizing it (the host folds the checksum
+ * and reads the validation flags).  BITSMOE_EBITS for a non-finite a or a
+ * stored p that is not finite or has |p| > 60000 (out is then unspecified);
+ * E must not exceed 65535. */
+int bitsmoe_pack_device_workspace_size(int E, int dout, int r, const uint8_t* bits,
+                                       size_t* bytes);
+int bitsmoe_pack_device(int E, int dout, int r, const float* p, const float* a,
+                        const uint8_t* bits, void* out, size_t out_bytes, void* ws,
+                        size_t ws_bytes, bitsmoe_stream_t stream);
 
 /* Host-side check of a blob in host memory: magic, version, sizes, CRC and
  * every directory record.  Fills E, dout, r when the pointers are non-null.

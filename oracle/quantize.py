@@ -11,6 +11,8 @@ offset being a value, not an integer zero point):
 
   for 1 <= b <= 8, with all arithmetic in IEEE float32 and no fused ops:
     lo = min_i p_i, hi = max_i p_i, L = 2^b - 1
+      (lo orders -0 below +0, as the IEEE 754 minimum does: a column whose
+      smallest value is zero with both signs present gets m = -0)
     s = fp16_rne((hi - lo) / L); if s == 0 then s = 1
     m = fp16_rne(lo)
     q_i = clamp(round_half_even((p_i - m) / s), 0, L)
@@ -49,6 +51,10 @@ def quantize_columns(P: np.ndarray, b: int):
         raise ValueError("width %r not in %r" % (b, WIDTHS))
     L = np.float32(2 ** b - 1)
     lo = P.min(axis=1)
+    # the sign of a zero minimum: -0 if any -0 is present (IEEE minimum)
+    neg0 = np.any((P == 0) & np.signbit(P), axis=1)
+    lo = np.where(lo == 0, np.where(neg0, np.float32(-0.0), np.float32(0.0)),
+                  lo).astype(np.float32)
     hi = P.max(axis=1)
     s32 = (hi - lo) / L                       # float32 subtract, float32 divide
     s = fp16_rne(s32)

@@ -18,6 +18,7 @@
 #include "bitsmoe.h"
 #include "common.h"
 #include "format.h"
+#include "pack_plan.h"
 
 #pragma clang fp contract(off)
 
@@ -131,8 +132,10 @@ int check_dims(int E, int dout, int r) {
   return BITSMOE_OK;
 }
 
+}  // namespace
+
 // Per-expert directory records and the total size; validates widths.
-int plan(int E, int dout, int r, const uint8_t* bits, std::vector<DirRec>& dirs,
+int pack_plan(int E, int dout, int r, const uint8_t* bits, std::vector<DirRec>& dirs,
          uint64_t& total) {
   int st = check_dims(E, dout, r);
   if (st) return st;
@@ -161,11 +164,15 @@ int plan(int E, int dout, int r, const uint8_t* bits, std::vector<DirRec>& dirs,
   return BITSMOE_OK;
 }
 
+namespace {
+
 void quantize_col(const float* p, int dout, int b, uint8_t* q, uint16_t* s_bits,
                   uint16_t* m_bits) {
   float lo = p[0], hi = p[0];
   for (int i = 1; i < dout; ++i) {
-    lo = std::min(lo, p[i]);
+    // -0 counts as below +0 (IEEE minimum), so the sign of a zero minimum
+    // does not depend on the order of the rows
+    if (p[i] < lo || (p[i] == lo && signbit(p[i]))) lo = p[i];
     hi = std::max(hi, p[i]);
   }
   const float L = (float)((1 << b) - 1);
@@ -183,9 +190,11 @@ void quantize_col(const float* p, int dout, int b, uint8_t* q, uint16_t* s_bits,
   *m_bits = mb;
 }
 
+}  // namespace
+
 // Slot -> column list of one expert: groups of width 1,2,3,4,6,8,16, columns
 // in ascending k, each group padded with -1 to a multiple of 32.
-std::vector<int> slot_columns(const uint8_t* bits_e, int r) {
+std::vector<int> pack_slot_columns(const uint8_t* bits_e, int r) {
   std::vector<int> cols;
   for (int g = 0; g < kNumGroups; ++g) {
     for (int k = 0; k < r; ++k)
@@ -195,10 +204,12 @@ std::vector<int> slot_columns(const uint8_t* bits_e, int r) {
   return cols;
 }
 
+namespace {
+
 void fill_block(DirRec& d, int e, int dout, int r, uint32_t n_seg, const float* p,
                 const float* a, const uint8_t* bits, uint8_t* blk) {
   const SlotGeo geo = slot_geo(d.count);
-  const std::vector<int> cols = slot_columns(bits + (size_t)e * r, r);
+  const std::vector<int> cols = pack_slot_columns(bits + (size_t)e * r, r);
   uint16_t* kidx = (uint16_t*)blk;
   float* A = (float*)(blk + d.a_off);
   uint16_t* S = (uint16_t*)(blk + d.s_off);
@@ -270,7 +281,7 @@ int bitsmoe_pack_size(int E, int dout, int r, const uint8_t* bits, size_t* out_b
   if (!out_bytes) return fail(BITSMOE_EINVAL, "out_bytes is null");
   std::vector<DirRec> dirs;
   uint64_t total = 0;
-  const int st = plan(E, dout, r, bits, dirs, total);
+  const int st = pack_plan(E, dout, r, bits, dirs, total);
   if (st) return st;
   *out_bytes = (size_t)total;
   return BITSMOE_OK;
@@ -281,7 +292,7 @@ int bitsmoe_pack(int E, int dout, int r, const float* p, const float* a,
   if (!p || !a || !out) return fail(BITSMOE_EINVAL, "null pointer argument");
   std::vector<DirRec> dirs;
   uint64_t total = 0;
-  int st = plan(E, dout, r, bits, dirs, total);
+  int st = pack_plan(E, dout, r, bits, dirs, total);
   if (st) return st;
   if (out_bytes < total)
     return fail(BITSMOE_ENOSPC, "out_bytes=%zu < %llu", out_bytes, (unsigned long long)total);

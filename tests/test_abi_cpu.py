@@ -79,6 +79,8 @@ def test_library_packer_rounding_edge_values():
         [0.25, 0.5, 0.375, 0.25], [0.0, 0.375, 0.75, 0.0], [0.1, 0.1, 0.1, 0.1],
         [0.7, 0.8, 0.75, 0.7], [1e-6, 2e-6, 3e-6, 1.5e-6], [-1e-7, 1e-7, 0, 0],
         [-0.5, -0.1, 0.2, 0.5], [6e-5, 6.1e-5, 6.2e-5, 6.3e-5],
+        [0.0, -0.0, 0.5, 0.25], [-0.0, 0.0, 0.5, 0.25], [-0.0, -0.0, -0.0, -0.0],
+        [30000.0, -30000.0, 1.0, 0.0],
     ]
     p = np.array(cols, np.float32)[None]
     for b in (1, 2, 3, 4, 6, 8, 16):
@@ -178,3 +180,27 @@ def test_device_entry_points_validate_before_launch():
     assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 0, None, None) == bm.EINVAL
     assert L.bitsmoe_workspace_init(None, 16, None) == bm.EINVAL
     assert bm._lib.bitsmoe_last_error_detail()
+
+
+def test_device_packer_validates_before_launch():
+    L = bm._lib
+    E, dout, r = 2, 40, 8
+    bits = np.full((E, r), 3, np.uint8)
+    need = bm.pack_size(E, dout, r, bits)
+    ws_need = bm.pack_device_workspace_size(E, dout, r, bits)
+    assert ws_need >= 16 + 4 * (E + 1) + 4 * 2 * 32
+
+    def pk(E=E, p=FAKE, a=FAKE, bits=bits, out=FAKE, out_bytes=need, ws=FAKE, ws_bytes=ws_need):
+        return L.bitsmoe_pack_device(E, dout, r, p, a, bits.ctypes.data, out, out_bytes, ws,
+                                     ws_bytes, None)
+    assert pk(p=None) == bm.EINVAL
+    assert pk(ws=None) == bm.EINVAL
+    assert pk(out=FAKE + 8) == bm.EINVAL
+    assert pk(a=FAKE + 2) == bm.EINVAL
+    assert pk(out_bytes=need - 1) == bm.ENOSPC
+    assert pk(ws_bytes=ws_need - 1) == bm.ENOSPC
+    bad = bits.copy()
+    bad[1, 3] = 7
+    assert pk(bits=bad) == bm.EBITS
+    assert pk(E=70000) == bm.ESHAPE
+    assert L.bitsmoe_pack_device_workspace_size(E, dout, r, bits.ctypes.data, None) == bm.EINVAL

@@ -115,3 +115,19 @@ def test_zero_width_absent_and_expert_layout():
 def test_rejects_bad_width():
     with pytest.raises(ValueError):
         quantize_columns(np.zeros((1, 4), np.float32), 5)
+
+
+def test_zero_minimum_sign_is_order_free():
+    # the offset of a column whose minimum is zero: -0 when a -0 is present
+    # (IEEE minimum), whatever the order of the rows; +0 otherwise
+    rng = np.random.default_rng(3)
+    base = np.array([0.0, -0.0, 0.5, 0.25, 0.0, 0.75], np.float32)
+    for _ in range(20):
+        col = rng.permutation(base)
+        for b in (1, 3, 8):
+            q, s, m = quantize_column(col, b)
+            assert m == 0 and np.signbit(m), (col, b)
+    q, s, m = quantize_column(np.array([0.0, 0.5, 0.0], np.float32), 2)
+    assert m == 0 and not np.signbit(m)
+    q, s, m = quantize_column(np.array([-0.0, -0.0], np.float32), 2)
+    assert np.signbit(m) and s == 1 and np.all(q == 0)
