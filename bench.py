@@ -105,12 +105,79 @@ def cpu_baseline(layer, batches, seconds):
                       % (i, tok, cores, el)}
 
 
+def bench_pack(args):
+    """Device packer on one projection of a full layer: p and a resident in
+    HBM, widths on the host; each call returns with the blob complete (it
+    synchronizes), so the wall time of the call is the measure."""
+    import time
+
+    import torch
+    import synth
+    from oracle import fmt
+    from spectral_expert_gemv_amd import bitsmoe
+
+    name = args.workload[len("pack_"):]
+    spec = synth.LAYERS[name]
+    L = synth.make_layer(spec)
+    dev = torch.device("cuda:0")
+    p, a, bits = L.p["gate"], L.a["gate"], L.bits["gate"]
+    pd = torch.from_numpy(np.ascontiguousarray(p)).to(dev)
+    ad = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    n = bitsmoe.pack_size(spec.E, spec.dout, spec.r, bits)
+    out = torch.empty(n, dtype=torch.uint8, device=dev)
+    ws = torch.empty(bitsmoe.pack_device_workspace_size(spec.E, spec.dout, spec.r, bits),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+    K, W = max(1, args.steps), args.warmup
+    for _ in range(W):
+        bitsmoe.pack_device(pd, ad, bits, out=out, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        bitsmoe.pack_device(pd, ad, bits, out=out, ws=ws, stream=stream)
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    stored = int((bits > 0).sum())
+    alg = stored * spec.dout * 4 + bits.size * 4 + n     # read stored p and a, write the blob
+    gbs = alg / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "device_pack_ms", "value": round(ms, 4), "unit": "ms/projection",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "E": spec.E, "dout": spec.dout, "r": spec.r,
+                   "stored_columns": stored, "blob_bytes": n,
+                   "inputs": "fp32 p and a in HBM, widths on the host"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": alg,
+                     "note": "whole call (planning, copies, pack and checksum kernels, "
+                             "host fold of the checksum) over the algorithmic bytes"},
+    }
+    if not args.no_cpu:
+        # the oracle packer on a sample of experts, scaled to the layer
+        ne = 4
+        t0 = time.perf_counter()
+        fmt.pack(p[:ne], a[:ne], bits[:ne])
+        el = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        bitsmoe.pack(p, a, bits)
+        host_ms = (time.perf_counter() - t0) * 1e3
+        res["cpu_baseline"] = {"value": round(el * 1e3 * spec.E / ne, 1), "unit": "ms/projection",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "numpy oracle packer on %d of %d experts (%.2f s), "
+                                         "scaled to the layer" % (ne, spec.E, el),
+                               "host_library_packer_ms": round(host_ms, 1)}
+    print(json.dumps(res, ensure_ascii=False), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode "
               "(got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.workload.startswith("pack_"):
+        return bench_pack(args)
     import torch
     import synth
     from spectral_expert_gemv_amd import bitsmoe

@@ -57,6 +57,8 @@ _SIGS = {
                             _vp, _vp, _sz, _vp], _i),
     "bitsmoe_workspace_init": ([_vp, _sz, _vp], _i),
     "bitsmoe_dump_codes": ([_vp, _sz, _i, _i, _i, _i, _vp, _vp], _i),
+    "bitsmoe_pack_device_workspace_size": ([_i, _i, _i, _vp, _psz], _i),
+    "bitsmoe_pack_device": ([_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp], _i),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -175,3 +177,35 @@ def workspace_init(ws, stream=None):
 def dump_codes(packed, E, dout, r, e, codes, stream=None):
     _check(_lib.bitsmoe_dump_codes(_ptr(packed), _nbytes(packed), E, dout, r, e, _ptr(codes),
                                    _stream(stream)))
+
+
+def pack_device_workspace_size(E, dout, r, bits):
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    out = ctypes.c_size_t(0)
+    _check(_lib.bitsmoe_pack_device_workspace_size(E, dout, r, bits.ctypes.data,
+                                                   ctypes.byref(out)))
+    return out.value
+
+
+def pack_device(p, a, bits, out=None, ws=None, stream=None):
+    """Quantize and pack one linear type on the GPU.  p: E x r x dout and a:
+    E x r float32 device tensors; bits: E x r host widths.  Returns the blob as
+    a uint8 device tensor (`out` if given); the call returns once it is
+    complete."""
+    import torch
+    bits = np.ascontiguousarray(bits, dtype=np.uint8)
+    E, r, dout = p.shape
+    if tuple(a.shape) != (E, r) or bits.shape != (E, r):
+        raise ValueError("a and bits must be E x r")
+    if p.dtype != torch.float32 or a.dtype != torch.float32:
+        raise ValueError("p and a must be float32")
+    if not (p.is_contiguous() and a.is_contiguous()):
+        raise ValueError("p and a must be contiguous")
+    if out is None:
+        out = torch.empty(pack_size(E, dout, r, bits), dtype=torch.uint8, device=p.device)
+    if ws is None:
+        ws = torch.empty(pack_device_workspace_size(E, dout, r, bits), dtype=torch.uint8,
+                         device=p.device)
+    _check(_lib.bitsmoe_pack_device(E, dout, r, _ptr(p), _ptr(a), bits.ctypes.data, _ptr(out),
+                                    _nbytes(out), _ptr(ws), _nbytes(ws), _stream(stream)))
+    return out

@@ -93,10 +93,19 @@ uint32_t crc32_ieee(const uint8_t* p, size_t n) {
   return c ^ 0xFFFFFFFFu;
 }
 
-int width_group(int b) {
-  for (int g = 0; g < kNumGroups; ++g)
-    if (kGroupWidth[g] == b) return g;
-  return -1;
+// width -> group index; 0-bit columns map to kNumGroups, invalid widths to
+// kNumGroups + 1 (one table lookup per column instead of a search)
+struct GroupLut {
+  uint8_t g[256];
+  GroupLut() {
+    for (int b = 0; b < 256; ++b) g[b] = kNumGroups + 1;
+    g[0] = kNumGroups;
+    for (int i = 0; i < kNumGroups; ++i) g[kGroupWidth[i]] = (uint8_t)i;
+  }
+};
+const GroupLut& group_lut() {
+  static const GroupLut lut;  // thread-safe static initialisation
+  return lut;
 }
 
 // Canonical block layout of one expert from its per-width column counts
@@ -143,15 +152,18 @@ int pack_plan(int E, int dout, int r, const uint8_t* bits, std::vector<DirRec>& 
   const uint32_t n_seg = (uint32_t)(align_up(dout, kSegRows) / kSegRows);
   dirs.resize(E);
   uint64_t pos = align_up(kHeaderBytes + (uint64_t)kDirRecBytes * E, 256);
+  const uint8_t* lut = group_lut().g;
   for (int e = 0; e < E; ++e) {
-    uint16_t count[kNumGroups] = {0, 0, 0, 0, 0, 0, 0};
-    for (int k = 0; k < r; ++k) {
-      const int b = bits[(size_t)e * r + k];
-      if (b == 0) continue;
-      const int g = width_group(b);
-      if (g < 0) return fail(BITSMOE_EBITS, "bits[%d,%d]=%d not in {0,1,2,3,4,6,8,16}", e, k, b);
-      ++count[g];
+    uint32_t c[kNumGroups + 2] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+    const uint8_t* be = bits + (size_t)e * r;
+    for (int k = 0; k < r; ++k) ++c[lut[be[k]]];
+    if (c[kNumGroups + 1]) {
+      for (int k = 0; k < r; ++k)
+        if (lut[be[k]] == kNumGroups + 1)
+          return fail(BITSMOE_EBITS, "bits[%d,%d]=%d not in {0,1,2,3,4,6,8,16}", e, k, be[k]);
     }
+    uint16_t count[kNumGroups];
+    for (int g = 0; g < kNumGroups; ++g) count[g] = (uint16_t)c[g];
     const SlotGeo g = slot_geo(count);
     if (align_up(2ull * g.n_slot + 8ull * g.n_slot, 256) + 4ull * n_seg * g.seg_words + 512 >
         0xFFFFFFFFull)
@@ -195,11 +207,18 @@ void quantize_col(const float* p, int dout, int b, uint8_t* q, uint16_t* s_bits,
 // Slot -> column list of one expert: groups of width 1,2,3,4,6,8,16, columns
 // in ascending k, each group padded with -1 to a multiple of 32.
 std::vector<int> pack_slot_columns(const uint8_t* bits_e, int r) {
-  std::vector<int> cols;
+  const uint8_t* lut = group_lut().g;
+  uint32_t count[kNumGroups + 2] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+  for (int k = 0; k < r; ++k) ++count[lut[bits_e[k]]];
+  uint32_t pos[kNumGroups + 2], n = 0;
   for (int g = 0; g < kNumGroups; ++g) {
-    for (int k = 0; k < r; ++k)
-      if (bits_e[k] == kGroupWidth[g]) cols.push_back(k);
-    while (cols.size() % kGroupSlots) cols.push_back(-1);
+    pos[g] = n;
+    n += (count[g] + kGroupSlots - 1) / kGroupSlots * kGroupSlots;
+  }
+  std::vector<int> cols(n, -1);
+  for (int k = 0; k < r; ++k) {
+    const uint32_t g = lut[bits_e[k]];
+    if (g < (uint32_t)kNumGroups) cols[pos[g]++] = k;
   }
   return cols;
 }
