@@ -1,0 +1,169 @@
+"""Pins of the FQCM oracle (oracle/fqcm.py).
+
+* distortion: eps(0) against an exactly rounded sum of squares; the golden
+  hand-derived quantizer cases (tests/golden/quantizer_cases.json) give eps(b)
+  from their printed codes, scale and offset; columns that the quantizer
+  represents exactly give 0 (two-level columns at b = 1, fp16 values at 16).
+* beta: the one-hot routing matrix form G^T (z * z), a different order of
+  summation; linearity in the routing weights; unrouted experts stay 0.
+* allocation: brute force over every allocation of tiny instances (the
+  result is optimal for the bits it uses); an exact dynamic program over
+  the budget on small instances (never better than the optimum at the bits
+  used, never worse than the Lagrangian at the full budget); the end points
+  of the budget.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import fqcm
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "quantizer_cases.json")
+W = np.array(fqcm.WIDTHS)
+
+
+def _unit(n, dout, seed):
+    rng = np.random.default_rng(seed)
+    P = rng.standard_normal((n, dout)).astype(np.float32)
+    return (P / np.linalg.norm(P, axis=1, keepdims=True)).astype(np.float32)
+
+
+def test_eps_zero_width_is_the_squared_norm():
+    P = _unit(7, 50, 1)
+    eps = fqcm.distortion(P)
+    for i in range(7):
+        ref = math.fsum(float(v) * float(v) for v in P[i])
+        assert abs(eps[i, 0] - ref) <= 1e-15 * ref
+
+
+def test_eps_from_hand_derived_cases():
+    with open(GOLD) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        p = np.array(c["p"], np.float32)
+        s = float(np.uint16(int(c["s_bits"], 16)).view(np.float16))
+        m = float(np.uint16(int(c["m_bits"], 16)).view(np.float16))
+        ref = math.fsum((float(pi) - (m + s * qi)) ** 2 for pi, qi in zip(p, c["q"]))
+        got = fqcm.distortion(p[None])[0, list(fqcm.WIDTHS).index(c["b"])]
+        assert abs(got - ref) <= 1e-15 * max(ref, 1e-30), c
+
+
+def test_eps_exact_columns_are_zero():
+    # two fp16 values whose difference is an fp16 value: exact at one bit
+    col = np.array([0.25, 0.75, 0.25, 0.75, 0.25], np.float32)
+    eps = fqcm.distortion(col[None])[0]
+    assert eps[1] == 0.0 and eps[7] == 0.0 and eps[0] > 0
+    # fp16 values: exact at 16 bits
+    col = np.array([0.1, -0.3, 0.7], np.float32).astype(np.float16).astype(np.float32)
+    assert fqcm.distortion(col[None])[0, 7] == 0.0
+
+
+def test_beta_matches_routing_matrix_form():
+    rng = np.random.default_rng(2)
+    T, k, E, r = 9, 3, 5, 11
+    z = rng.standard_normal((T, r)).astype(np.float32)
+    ids = rng.integers(0, E - 1, size=(T, k))          # expert E-1 never routed
+    g = rng.random((T, k)).astype(np.float32)
+    G = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            G[t, ids[t, j]] += np.float64(g[t, j])
+    ref = G.T @ (z.astype(np.float64) ** 2)
+    got = fqcm.beta(z, ids, g, E)
+    assert np.allclose(got, ref, rtol=1e-13, atol=0)
+    assert np.all(got[E - 1] == 0)
+    assert np.allclose(fqcm.beta(z, ids, 2 * g, E), 2 * got, rtol=1e-15, atol=0)
+
+
+def _tiny(n, seed, dout=6):
+    rng = np.random.default_rng(seed)
+    P = _unit(n, dout, seed + 50)
+    eps = fqcm.distortion(P)
+    a = rng.lognormal(0, 0.7, n).astype(np.float32)
+    bet = rng.lognormal(0, 1.0, n)
+    return a, bet, eps, dout
+
+
+def _brute_best(L, dout, budget):
+    best = math.inf
+    for combo in itertools.product(range(len(W)), repeat=L.shape[0]):
+        used = int(W[list(combo)].sum()) * dout
+        if used <= budget:
+            best = min(best, float(sum(L[i, c] for i, c in enumerate(combo))))
+    return best
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_allocation_is_optimal_for_the_bits_it_uses(seed):
+    a, bet, eps, dout = _tiny(4, seed)
+    L = fqcm.losses(a, bet, eps)
+    for budget in (0, dout, 5 * dout, 11 * dout, 23 * dout, 40 * dout, 64 * dout):
+        bits, lam, used = fqcm.allocate(a, bet, eps, dout, budget)
+        assert used <= budget and used == int(bits.astype(np.int64).sum()) * dout
+        got = fqcm.total_loss(a, bet, eps, bits)
+        best = _brute_best(L, dout, used)
+        assert got <= best * (1 + 1e-12) + 1e-300, (seed, budget, got, best)
+
+
+def _dp_best(L, dout, budget):
+    """Exact multiple-choice knapsack over budget units of dout bits."""
+    units = budget // dout
+    cur = np.zeros(units + 1)
+    for i in range(L.shape[0]):
+        nxt = np.full(units + 1, np.inf)
+        for c, w in enumerate(W):
+            if w <= units:
+                cand = np.full(units + 1, np.inf)
+                cand[w:] = cur[:units + 1 - w] + L[i, c]
+                nxt = np.minimum(nxt, cand)
+        cur = np.minimum.accumulate(nxt)
+    return float(cur[units])
+
+
+@pytest.mark.parametrize("seed", [4, 5])
+def test_allocation_against_exact_dynamic_program(seed):
+    a, bet, eps, dout = _tiny(12, seed)
+    L = fqcm.losses(a, bet, eps)
+    for units in (3, 17, 40, 77, 150):
+        budget = units * dout
+        bits, lam, used = fqcm.allocate(a, bet, eps, dout, budget)
+        got = fqcm.total_loss(a, bet, eps, bits)
+        assert _dp_best(L, dout, budget) <= got * (1 + 1e-12)
+        assert abs(_dp_best(L, dout, used) - got) <= 1e-12 * got
+
+
+def test_allocation_end_points():
+    a, bet, eps, dout = _tiny(6, 9)
+    bits, lam, used = fqcm.allocate(a, bet, eps, dout, 0)
+    assert np.all(bits == 0) and used == 0
+    bits, lam, used = fqcm.allocate(a, bet, eps, dout, 10 ** 9)
+    assert lam == 0.0
+    L = fqcm.losses(a, bet, eps)
+    assert np.array_equal(bits, W[np.argmin(L, axis=1)])
+    # an expert that calibration never routes to gets no bits
+    bet0 = bet.copy()
+    bet0[2] = 0.0
+    bits, lam, used = fqcm.allocate(a, bet0, eps, dout, 30 * dout)
+    assert bits[2] == 0
+    # more budget never raises the loss
+    prev = math.inf
+    for units in range(0, 60, 3):
+        b, _, _ = fqcm.allocate(a, bet, eps, dout, units * dout)
+        cur = fqcm.total_loss(a, bet, eps, b)
+        assert cur <= prev * (1 + 1e-12)
+        prev = cur
+
+
+def test_losses_scale_with_a_squared_and_beta():
+    a, bet, eps, dout = _tiny(5, 11)
+    L = fqcm.losses(a, bet, eps)
+    assert np.allclose(fqcm.losses(2 * a, bet, eps), 4 * L, rtol=1e-15, atol=0)
+    assert np.allclose(fqcm.losses(a, 3 * bet, eps), 3 * L, rtol=1e-15, atol=0)
+    assert np.all(fqcm.losses(a, bet, 0 * eps) == 0)
+    # one column, one width: the product of the three factors
+    i, c = 3, 2
+    assert L[i, c] == pytest.approx(float(a[i]) ** 2 * bet[i] * eps[i, c], rel=1e-15)

@@ -108,3 +108,71 @@ def test_plane_bit_order_caught(monkeypatch):
     # rows and slots swapped inside a plane word
     monkeypatch.setattr(fmt, "plane_bit", lambda rho, u: 4 * rho + u)
     assert _fails(T_fmt.test_hand_built_planes)
+
+
+# ---- FQCM oracle ----
+from oracle import fqcm  # noqa: E402
+import tests.test_oracle_fqcm as T_f  # noqa: E402
+
+_orig_losses = fqcm.losses
+_orig_allocate = fqcm.allocate
+
+
+def _losses_a_not_squared(a, bet, eps):
+    a = np.asarray(a, dtype=np.float32).astype(np.float64)
+    return (a * np.asarray(bet, dtype=np.float64))[..., None] * np.asarray(eps, dtype=np.float64)
+
+
+def _beta_not_squared(z, ids, g, E):
+    z = np.asarray(z, dtype=np.float32)
+    out = np.zeros((E, z.shape[1]))
+    for t in range(ids.shape[0]):
+        for j in range(ids.shape[1]):
+            out[int(ids[t, j])] += np.float64(g[t, j]) * z[t].astype(np.float64)   # z, not z^2
+    return out
+
+
+def _distortion_m_minus(P):
+    P = np.asarray(P, dtype=np.float32)
+    res = np.zeros((P.shape[0], 8))
+    p64 = P.astype(np.float64)
+    res[:, 0] = (p64 * p64).sum(axis=1)
+    for i, b in enumerate(fqcm.WIDTHS):
+        if b in (0, 16):
+            continue
+        q, s, m = quantize.quantize_columns(P, b)
+        phat = m.astype(np.float64)[:, None] - s.astype(np.float64)[:, None] * q   # sign slip
+        res[:, i] = ((p64 - phat) ** 2).sum(axis=1)
+    res[:, 7] = ((p64 - P.astype(np.float16).astype(np.float64)) ** 2).sum(axis=1)
+    return res
+
+
+def _allocate_over_budget(a, bet, eps, dout, budget):
+    bits, lam, used = _orig_allocate(a, bet, eps, dout, budget)
+    if lam > 0:       # the last multiplier that did not fit
+        L = _orig_losses(a, bet, eps)
+        lam2 = float(np.nextafter(lam, 0.0))
+        idx = fqcm.choose(L, dout, lam2)
+        bits = np.array(fqcm.WIDTHS, np.uint8)[idx]
+        used = int(bits.astype(np.int64).sum()) * dout
+    return bits, lam, used
+
+
+def test_fqcm_loss_without_a_squared_caught(monkeypatch):
+    monkeypatch.setattr(fqcm, "losses", _losses_a_not_squared)
+    assert _fails(T_f.test_losses_scale_with_a_squared_and_beta)
+
+
+def test_fqcm_beta_slip_caught(monkeypatch):
+    monkeypatch.setattr(fqcm, "beta", _beta_not_squared)
+    assert _fails(T_f.test_beta_matches_routing_matrix_form)
+
+
+def test_fqcm_distortion_sign_caught(monkeypatch):
+    monkeypatch.setattr(fqcm, "distortion", _distortion_m_minus)
+    assert _fails(T_f.test_eps_from_hand_derived_cases)
+
+
+def test_fqcm_allocation_over_budget_caught(monkeypatch):
+    monkeypatch.setattr(fqcm, "allocate", _allocate_over_budget)
+    assert any(_fails(T_f.test_allocation_is_optimal_for_the_bits_it_uses, s) for s in range(4))
