@@ -170,6 +170,113 @@ def bench_pack(args):
     print(json.dumps(res, ensure_ascii=False), flush=True)
 
 
+def bench_fqcm(args):
+    """FQCM inputs and the allocation for one projection of a full layer:
+    eps of every column, beta from 512 calibration tokens (z = Phi^T x on
+    the device, the workload's routing, uniform weights) and the Lagrangian
+    allocation under the synthetic layer's own bit total.  p, a, x resident
+    in HBM; each part timed with events on its stream (the allocation
+    synchronizes once per bisection step, so its wall time is used)."""
+    import time
+
+    import torch
+    import synth
+    from oracle import fqcm
+    from spectral_expert_gemv_amd import bitsmoe
+
+    name = args.workload[len("fqcm_"):]
+    spec = synth.LAYERS[name]
+    L = synth.make_layer(spec)
+    dev = torch.device("cuda:0")
+    P, a, bits = L.p["gate"], L.a["gate"], L.bits["gate"]
+    pd = torch.from_numpy(np.ascontiguousarray(P)).to(dev)
+    ad = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    wl = [w for w in synth.WORKLOADS.values() if w.layer.name == name and w.T > 1]
+    wl = wl[0] if wl else synth.workload(name + "_t1")
+    xs, idss = [], []
+    while sum(x.shape[0] for x in xs) < 512:
+        x, ids = synth.make_batch(wl, L, step=len(xs))
+        xs.append(x)
+        idss.append(ids)
+    x = np.concatenate(xs)[:512]
+    ids = np.concatenate(idss)[:512].astype(np.int32)
+    T = x.shape[0]
+    phi_t = torch.from_numpy(np.ascontiguousarray(np.asarray(L.phi["gate"], np.float16).T)).to(dev)
+    z = torch.empty((T, spec.r), dtype=torch.float32, device=dev)
+    bitsmoe.spectral_proj(phi_t, torch.from_numpy(x).to(dev), z)
+    idd = torch.from_numpy(ids).to(dev)
+    g = torch.full(ids.shape, 1.0 / ids.shape[1], dtype=torch.float32, device=dev)
+    eps = torch.empty((spec.E, spec.r, 8), dtype=torch.float64, device=dev)
+    beta = torch.empty((spec.E, spec.r), dtype=torch.float64, device=dev)
+    budget = int(bits.astype(np.int64).sum()) * spec.dout
+    stream = torch.cuda.Stream(device=dev)
+    K, W = max(1, args.steps), args.warmup
+
+    def timed(fn):
+        for _ in range(W):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(K):
+                fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    ms_eps = timed(lambda: bitsmoe.fqcm_distortion(pd, eps=eps, stream=stream))
+    ms_beta = timed(lambda: bitsmoe.fqcm_beta(z, idd, g, spec.E, beta=beta, stream=stream))
+    out_bits = torch.empty((spec.E, spec.r), dtype=torch.uint8, device=dev)
+    for _ in range(W):
+        bitsmoe.fqcm_allocate(ad, beta, eps, spec.dout, budget, bits=out_bits, stream=stream)
+    t0 = time.perf_counter()
+    for _ in range(K):
+        res = bitsmoe.fqcm_allocate(ad, beta, eps, spec.dout, budget, bits=out_bits,
+                                    stream=stream)
+    ms_alloc = (time.perf_counter() - t0) * 1e3 / K
+    ncol = spec.E * spec.r
+    eps_bytes = ncol * spec.dout * 4 + ncol * 8 * 8
+    gbs = eps_bytes / (ms_eps * 1e-3) / 1e9
+    total = ms_eps + ms_beta + ms_alloc
+    out = {
+        "metric": "fqcm_allocation_ms", "value": round(total, 4), "unit": "ms/projection",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(total, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "E": spec.E, "dout": spec.dout, "r": spec.r,
+                   "calibration_tokens": T, "budget_bits": budget,
+                   "bits_used": int(res[2]), "lambda": res[1]},
+        "parts_ms": {"distortion": round(ms_eps, 4), "beta": round(ms_beta, 4),
+                     "allocate": round(ms_alloc, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": eps_bytes, "kernel": "k_fqcm_eps",
+                     "launch_us_avg": round(ms_eps * 1e3, 2)},
+    }
+    if not args.no_cpu:
+        # the oracle on a sample: eps of 512 columns, then the allocation
+        # over the whole layer from the device inputs' shapes (seeded values)
+        ne = 512
+        flat = P.reshape(-1, spec.dout)
+        t0 = time.perf_counter()
+        fqcm.distortion(flat[:ne])
+        el_eps = (time.perf_counter() - t0) * ncol / ne
+        t0 = time.perf_counter()
+        fqcm.beta(z.cpu().numpy()[:64], ids[:64], np.full((64, ids.shape[1]), 1.0 / ids.shape[1],
+                                                          np.float32), spec.E)
+        el_beta = (time.perf_counter() - t0) * T / 64
+        t0 = time.perf_counter()
+        fqcm.allocate(a, beta.cpu().numpy(), eps.cpu().numpy(), spec.dout, budget)
+        el_alloc = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round((el_eps + el_beta + el_alloc) * 1e3, 1), "unit": "ms/projection",
+            "cores": 1, "kind": "oracle",
+            "sample": "numpy oracle: distortion of %d columns scaled to %d, beta of 64 tokens "
+                      "scaled to %d, the full allocation (%.2f s)" % (ne, ncol, T, el_alloc)}
+    print(json.dumps(out, ensure_ascii=False), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -178,6 +285,8 @@ def main():
         sys.exit(2)
     if args.workload.startswith("pack_"):
         return bench_pack(args)
+    if args.workload.startswith("fqcm_"):
+        return bench_fqcm(args)
     import torch
     import synth
     from spectral_expert_gemv_amd import bitsmoe

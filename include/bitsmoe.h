@@ -130,6 +130,40 @@ int bitsmoe_pack_device(int E, int dout, int r, const float* p, const float* a,
                         const uint8_t* bits, void* out, size_t out_bytes, void* ws,
                         size_t ws_bytes, bitsmoe_stream_t stream);
 
+/* ------------------------------------------------------------------ FQCM
+ * Inputs of the width allocation (BitsMoE blog note, Methodology: the FQCM
+ * importance, loss and marginal gain; "Usage": widths chosen jointly under a
+ * bit budget).  All arrays are device memory.
+ *
+ * bitsmoe_fqcm_distortion: eps[(e*r + k)*8 + i] (float64) for the widths
+ *   (0,1,2,3,4,6,8,16)[i] of column p_{e,k} (p laid out as for bitsmoe_pack):
+ *   eps(0) = ||p||^2, eps(b) = ||p - (m + s q)||^2 with the quantizer above,
+ *   eps(16) = ||p - fp16(p)||^2; float64 sums.  Async on `stream`.
+ * bitsmoe_fqcm_beta: beta[e*r + k] = sum over the pairs (t, j) with
+ *   ids[t*k + j] = e, in that order, of g[t*k + j] * z[t*z_stride + k]^2
+ *   (float64; z = Phi^T x of T calibration tokens, e.g. from
+ *   bitsmoe_spectral_proj; g: float32 routing weights; pairs whose id is
+ *   outside [0, E) are skipped).  Async on `stream`.
+ * bitsmoe_fqcm_allocate: widths bits[e*r + k] (device uint8) minimising
+ *   sum L(b) with L(b) = ((a*a)*beta)*eps(b) (float64) subject to
+ *   sum dout*b <= budget_bits, by the Lagrangian relaxation: each column
+ *   minimises L(b) + lam*(dout*b) (ties to the narrower width) at the
+ *   smallest double lam >= 0 whose total fits (bisection over the bit
+ *   patterns of doubles).  The result is an exact optimum for the bits it
+ *   uses (*used_bits <= budget_bits); *lambda gets lam.  ws: device memory
+ *   of BITSMOE_FQCM_WS_BYTES bytes, 8-byte aligned.  The call synchronizes
+ *   `stream` once per bisection step (at most 65 steps).
+ */
+#define BITSMOE_FQCM_WS_BYTES 1024
+int bitsmoe_fqcm_distortion(const float* p, int E, int r, int dout, double* eps,
+                            bitsmoe_stream_t stream);
+int bitsmoe_fqcm_beta(const float* z, int z_stride, const int32_t* ids, const float* g, int T,
+                      int k, int E, int r, double* beta, bitsmoe_stream_t stream);
+int bitsmoe_fqcm_allocate(const float* a, const double* beta, const double* eps, int E, int r,
+                          int dout, uint64_t budget_bits, uint8_t* bits, double* lambda,
+                          uint64_t* used_bits, void* ws, size_t ws_bytes,
+                          bitsmoe_stream_t stream);
+
 /* Host-side check of a blob in host memory: magic, version, sizes, CRC and
  * every directory record.  Fills E, dout, r when the pointers are non-null.
  * BITSMOE_EFORMAT on any inconsistency. */

@@ -59,7 +59,13 @@ _SIGS = {
     "bitsmoe_dump_codes": ([_vp, _sz, _i, _i, _i, _i, _vp, _vp], _i),
     "bitsmoe_pack_device_workspace_size": ([_i, _i, _i, _vp, _psz], _i),
     "bitsmoe_pack_device": ([_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp], _i),
+    "bitsmoe_fqcm_distortion": ([_vp, _i, _i, _i, _vp, _vp], _i),
+    "bitsmoe_fqcm_beta": ([_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp], _i),
+    "bitsmoe_fqcm_allocate": ([_vp, _vp, _vp, _i, _i, _i, ctypes.c_uint64, _vp,
+                               ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64),
+                               _vp, _sz, _vp], _i),
 }
+FQCM_WS_BYTES = 1024
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
     _f.argtypes = _args
@@ -209,3 +215,51 @@ def pack_device(p, a, bits, out=None, ws=None, stream=None):
     _check(_lib.bitsmoe_pack_device(E, dout, r, _ptr(p), _ptr(a), bits.ctypes.data, _ptr(out),
                                     _nbytes(out), _ptr(ws), _nbytes(ws), _stream(stream)))
     return out
+
+
+def fqcm_distortion(p, eps=None, stream=None):
+    """eps (E x r x 8 float64 device tensor) of the unit directions p
+    (E x r x dout float32 device tensor)."""
+    import torch
+    E, r, dout = p.shape
+    if p.dtype != torch.float32 or not p.is_contiguous():
+        raise ValueError("p must be contiguous float32")
+    if eps is None:
+        eps = torch.empty((E, r, 8), dtype=torch.float64, device=p.device)
+    _check(_lib.bitsmoe_fqcm_distortion(_ptr(p), E, r, dout, _ptr(eps), _stream(stream)))
+    return eps
+
+
+def fqcm_beta(z, ids, g, E, beta=None, stream=None):
+    """beta (E x r float64) from z (T x r float32, row stride z.stride(0)),
+    ids (T x k int32) and routing weights g (T x k float32), device tensors."""
+    import torch
+    T, r = z.shape
+    k = ids.shape[1]
+    if z.dtype != torch.float32 or z.stride(1) != 1:
+        raise ValueError("z must be float32 with unit column stride")
+    if ids.dtype != torch.int32 or g.dtype != torch.float32 or tuple(g.shape) != (T, k):
+        raise ValueError("ids must be int32 and g float32, both T x k")
+    if beta is None:
+        beta = torch.empty((E, r), dtype=torch.float64, device=z.device)
+    _check(_lib.bitsmoe_fqcm_beta(_ptr(z), z.stride(0), _ptr(ids.contiguous()),
+                                  _ptr(g.contiguous()), T, k, E, r, _ptr(beta), _stream(stream)))
+    return beta
+
+
+def fqcm_allocate(a, beta, eps, dout, budget_bits, bits=None, ws=None, stream=None):
+    """Widths under the bit budget; returns (bits uint8 device tensor E x r,
+    lam, bits used)."""
+    import torch
+    E, r = a.shape
+    if bits is None:
+        bits = torch.empty((E, r), dtype=torch.uint8, device=a.device)
+    if ws is None:
+        ws = torch.empty(FQCM_WS_BYTES, dtype=torch.uint8, device=a.device)
+    lam = ctypes.c_double(0.0)
+    used = ctypes.c_uint64(0)
+    _check(_lib.bitsmoe_fqcm_allocate(_ptr(a), _ptr(beta), _ptr(eps), E, r, dout,
+                                      int(budget_bits), _ptr(bits), ctypes.byref(lam),
+                                      ctypes.byref(used), _ptr(ws), _nbytes(ws),
+                                      _stream(stream)))
+    return bits, lam.value, used.value

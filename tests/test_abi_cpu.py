@@ -204,3 +204,22 @@ def test_device_packer_validates_before_launch():
     assert pk(bits=bad) == bm.EBITS
     assert pk(E=70000) == bm.ESHAPE
     assert L.bitsmoe_pack_device_workspace_size(E, dout, r, bits.ctypes.data, None) == bm.EINVAL
+
+
+def test_fqcm_entry_points_validate_before_launch():
+    L = bm._lib
+    assert L.bitsmoe_fqcm_distortion(None, 2, 3, 4, FAKE, None) == bm.EINVAL
+    assert L.bitsmoe_fqcm_distortion(FAKE, 0, 3, 4, FAKE, None) == bm.ESHAPE
+    assert L.bitsmoe_fqcm_distortion(FAKE, 2, 3, 4, FAKE + 4, None) == bm.EINVAL
+    assert L.bitsmoe_fqcm_beta(FAKE, 7, FAKE, FAKE, 4, 2, 3, 8, FAKE, None) == bm.ESHAPE
+    assert L.bitsmoe_fqcm_beta(FAKE, 8, FAKE, FAKE, 0, 2, 3, 8, FAKE, None) == bm.EINVAL
+    assert L.bitsmoe_fqcm_beta(None, 8, FAKE, FAKE, 4, 2, 3, 8, FAKE, None) == bm.EINVAL
+    lam = ctypes.c_double()
+    used = ctypes.c_uint64()
+    def al(ws_bytes=bm.FQCM_WS_BYTES, ws=FAKE, bits=FAKE, E=2):
+        return L.bitsmoe_fqcm_allocate(FAKE, FAKE, FAKE, E, 3, 4, 100, bits, ctypes.byref(lam),
+                                       ctypes.byref(used), ws, ws_bytes, None)
+    assert al(ws_bytes=bm.FQCM_WS_BYTES - 1) == bm.ENOSPC
+    assert al(ws=None) == bm.EINVAL
+    assert al(bits=None) == bm.EINVAL
+    assert al(E=0) == bm.ESHAPE
