@@ -78,3 +78,35 @@ def dequantized_layer(p: np.ndarray, bits: np.ndarray, experts=None) -> np.ndarr
     for e in (range(E) if experts is None else experts):
         out[e] = quantize_expert(p[e], bits[e])["phat"]
     return out
+
+
+def moe_down(phi_d, a_d, phat_d, bits_d, h: np.ndarray, ids: np.ndarray,
+             g: np.ndarray) -> np.ndarray:
+    """out[t, :] = sum over slots j (ascending) of g[t, j] * y_{t,j}, with
+    y_{t,j} = sum_k a_{e,k} z_k p_hat_{e,k} for e = ids[t, j] and
+    z = Phi_down^T fp16(h[t, j]).
+
+    The down projection restated with the same two splits (BitsMoE blog
+    note, Methodology): its shared basis Phi_down (dout x r_d) lives in the
+    input space of down_proj, so z depends on the pair's own h and is formed
+    per (token, slot); the pages name only gate and up, so this is the plain
+    extension.  Reading: the down projection's input is h rounded to fp16
+    (the activation precision of the path); the routing weights g are
+    applied once, after the expert products.  phat_d: E x r_d x din float64.
+    h: T x k x dout; returns T x din float64.  Pairs whose id is outside
+    [0, E) are skipped.
+    """
+    ids = np.asarray(ids)
+    T, K = ids.shape
+    E = phat_d.shape[0]
+    h16 = np.asarray(h, dtype=np.float32).astype(np.float16)
+    out = np.zeros((T, phat_d.shape[2]), dtype=np.float64)
+    for t in range(T):
+        for j in range(K):
+            e = int(ids[t, j])
+            if not 0 <= e < E:
+                continue
+            z = spectral_proj(phi_d, h16[t, j])
+            y = expert_apply(z, a_d[e], phat_d[e], bits_d[e])[0]
+            out[t] += np.float64(g[t, j]) * y
+    return out

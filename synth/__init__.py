@@ -8,9 +8,9 @@ projection or expert products live here.  Both the CPU oracle tests and the
 GPU tests/benchmark draw their inputs from it.
 """
 from .configs import LAYERS, WORKLOADS, LayerSpec, Workload, workload
-from .generate import Layer, make_layer, make_batch, histogram_bits
+from .generate import DownType, Layer, make_layer, make_batch, make_down, make_gates, histogram_bits
 
 __all__ = [
     "LAYERS", "WORKLOADS", "LayerSpec", "Workload", "workload",
-    "Layer", "make_layer", "make_batch", "histogram_bits",
+    "Layer", "DownType", "make_layer", "make_batch", "make_down", "make_gates", "histogram_bits",
 ]

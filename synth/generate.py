@@ -15,6 +15,9 @@ Recipe (all draws from numpy's PCG64, one independent stream per
   histogram percentages.
 * x (T x din): N(0,1), a fixed per-layer set of round(outlier_frac * din)
   channels multiplied by outlier_scale for every token, rounded to fp16.
+* down projection (make_down): the same recipe with input dout, output din
+  and rank r_d = min(r, dout), streams named "..._down".
+* g (T x k, make_gates): softmax over each token's k slots of N(0,1) logits.
 * ids (T x k): per token k distinct experts; "uniform" draws them uniformly
   without replacement; "zipf" gives experts popularity weights rank^-s (ranks
   from a seeded permutation) and takes, per token, the k largest
@@ -73,25 +76,27 @@ class Layer:
     outlier_channels: np.ndarray  # int64 indices into din
 
 
-def _make_type(spec: LayerSpec, proj: str):
+def _make_type(spec: LayerSpec, proj: str, n_in: int = 0, n_out: int = 0, r: int = 0):
+    """Factors of one linear type: Phi (n_in x r), a (E x r), p (E x r x
+    n_out), bits (E x r); gate and up use (din, dout, r)."""
     fam = spec.name
-    phi = _orthogonal(spec.din, _rng(fam, "phi_" + proj))[:, :spec.r]
+    n_in, n_out, r = n_in or spec.din, n_out or spec.dout, r or spec.r
+    phi = _orthogonal(n_in, _rng(fam, "phi_" + proj))[:, :r]
     phi = phi.astype(np.float16) if spec.phi_fp16 else phi.astype(np.float32)
     rng_a = _rng(fam, "a_" + proj)
-    kk = np.arange(1, spec.r + 1, dtype=np.float64)
+    kk = np.arange(1, r + 1, dtype=np.float64)
     a = (kk[None, :] ** (-spec.decay)) * np.exp(
-        spec.ln_sigma * rng_a.standard_normal((spec.E, spec.r)))
+        spec.ln_sigma * rng_a.standard_normal((spec.E, r)))
     a = a.astype(np.float32)
-    p = np.empty((spec.E, spec.r, spec.dout), dtype=np.float32)
+    p = np.empty((spec.E, r, n_out), dtype=np.float32)
     for e in range(spec.E):
-        g = _rng(fam, "p_" + proj, e).standard_normal((spec.r, spec.dout),
-                                                      dtype=np.float32)
+        g = _rng(fam, "p_" + proj, e).standard_normal((r, n_out), dtype=np.float32)
         nrm = np.sqrt(np.einsum("kd,kd->k", g.astype(np.float64),
                                 g.astype(np.float64)))
         p[e] = (g / nrm[:, None]).astype(np.float32)
     if spec.bits == "uniform":
         idx = _rng(fam, "bits_" + proj).integers(0, len(WIDTH_SET),
-                                                 size=(spec.E, spec.r))
+                                                 size=(spec.E, r))
         bits = np.asarray(WIDTH_SET, dtype=np.uint8)[idx]
     else:
         bits = histogram_bits(a, spec.bits)
@@ -114,6 +119,38 @@ def make_layer(spec: LayerSpec, cache: bool = True) -> Layer:
     if cache:
         _LAYER_CACHE[spec.name] = layer
     return layer
+
+
+@dataclass
+class DownType:
+    """Factors of the down projection (input dout, output din): Phi_down
+    (dout x r_d), a (E x r_d), p (E x r_d x din), bits (E x r_d), with
+    r_d = min(r, dout)."""
+    phi: np.ndarray
+    a: np.ndarray
+    p: np.ndarray
+    bits: np.ndarray
+
+
+_DOWN_CACHE: Dict[str, DownType] = {}
+
+
+def make_down(layer: Layer) -> DownType:
+    spec = layer.spec
+    if spec.name not in _DOWN_CACHE:
+        rd = min(spec.r, spec.dout)
+        phi, a, p, bits = _make_type(spec, "down", n_in=spec.dout, n_out=spec.din, r=rd)
+        _DOWN_CACHE[spec.name] = DownType(phi, a, p, bits)
+    return _DOWN_CACHE[spec.name]
+
+
+def make_gates(wl: Workload, layer: Layer, step: int = 0, T: Optional[int] = None):
+    """Routing weights g (T x k, float32) for the routed slots: a softmax of
+    N(0,1) logits over each token's k slots (they sum to 1 per token)."""
+    T = wl.T if T is None else T
+    lg = _rng(wl.name, "gates", step).standard_normal((T, layer.spec.k))
+    w = np.exp(lg - lg.max(axis=1, keepdims=True))
+    return (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
 def make_batch(wl: Workload, layer: Layer, step: int = 0, T: Optional[int] = None):

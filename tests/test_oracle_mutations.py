@@ -176,3 +176,22 @@ def test_fqcm_distortion_sign_caught(monkeypatch):
 def test_fqcm_allocation_over_budget_caught(monkeypatch):
     monkeypatch.setattr(fqcm, "allocate", _allocate_over_budget)
     assert any(_fails(T_f.test_allocation_is_optimal_for_the_bits_it_uses, s) for s in range(4))
+
+
+_orig_down = path.moe_down
+
+
+def _down_no_fp16(phi_d, a_d, phat_d, bits_d, h, ids, g):
+    return _orig_down(phi_d, a_d, phat_d, bits_d,
+                      np.asarray(h, np.float64).astype(np.float32) * np.float32(1 + 2 ** -12),
+                      ids, g)
+
+
+def _down_gate_squared(phi_d, a_d, phat_d, bits_d, h, ids, g):
+    return _orig_down(phi_d, a_d, phat_d, bits_d, h, ids, np.asarray(g, np.float32) ** 2)
+
+
+@pytest.mark.parametrize("bad", [_down_no_fp16, _down_gate_squared])
+def test_moe_down_slips_caught(monkeypatch, bad):
+    monkeypatch.setattr(path, "moe_down", bad)
+    assert _fails(T_path.test_moe_down_against_dense_expert_matrices)

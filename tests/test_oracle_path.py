@@ -162,3 +162,57 @@ def test_reconstruct_tiny_layer_matches_matrix_product():
             ref = (L.p[proj][e].astype(np.float64).T * L.a[proj][e].astype(np.float64)[None, :]) \
                 @ L.phi[proj].astype(np.float64).T
             assert np.linalg.norm(W[e] - ref) / np.linalg.norm(ref) <= 1e-12
+
+
+# ---- down projection and combine ------------------------------------------
+
+def _down_case(seed=3, E=4, dout=40, din=24, rd=16, T=3, K=2):
+    rng = np.random.default_rng(seed)
+    phi = np.linalg.qr(rng.standard_normal((dout, dout)))[0][:, :rd]
+    a = rng.lognormal(0, 0.5, (E, rd)).astype(np.float32)
+    p = _unit((E, rd, din), seed + 1)
+    bits = rng.choice([0, 1, 2, 3, 4, 6, 8, 16], size=(E, rd)).astype(np.uint8)
+    phat = np.stack([quantize_expert(p[e], bits[e])["phat"] for e in range(E)])
+    h = rng.standard_normal((T, K, dout)).astype(np.float32)   # not fp16-exact
+    ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)])
+    g = rng.random((T, K)).astype(np.float32)
+    return phi, a, phat, bits, h, ids, g
+
+
+def test_moe_down_against_dense_expert_matrices():
+    phi, a, phat, bits, h, ids, g = _down_case()
+    E = phat.shape[0]
+    # W_e = sum_k a_k p_hat_k phi_k^T (din x dout), built densely
+    Wd = np.zeros((E, phat.shape[2], phi.shape[0]))
+    for e in range(E):
+        for k in range(phi.shape[1]):
+            if bits[e, k]:
+                Wd[e] += np.float64(a[e, k]) * np.outer(phat[e, k], phi[:, k])
+    h16 = h.astype(np.float16).astype(np.float64)
+    ref = np.zeros((h.shape[0], phat.shape[2]))
+    for t in range(h.shape[0]):
+        for j in range(h.shape[1]):
+            ref[t] += np.float64(g[t, j]) * (Wd[ids[t, j]] @ h16[t, j])
+    out = path.moe_down(phi, a, phat, bits, h, ids, g)
+    assert np.allclose(out, ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+
+
+def test_moe_down_one_hot_gates_and_linearity():
+    phi, a, phat, bits, h, ids, g = _down_case(seed=8)
+    T, K = ids.shape
+    one = np.zeros_like(g)
+    one[:, 1] = 1.0
+    out1 = path.moe_down(phi, a, phat, bits, h, ids, one)
+    for t in range(T):
+        z = path.spectral_proj(phi, h[t, 1].astype(np.float16))
+        y = path.expert_apply(z, a[ids[t, 1]], phat[ids[t, 1]], bits[ids[t, 1]])[0]
+        assert np.array_equal(out1[t], y)
+    both = path.moe_down(phi, a, phat, bits, h, ids, g)
+    sep = sum(path.moe_down(phi, a, phat, bits, h, ids, np.where(
+        np.arange(K)[None, :] == j, g, 0).astype(np.float32)) for j in range(K))
+    assert np.allclose(both, sep, rtol=1e-13, atol=0)
+    bad = ids.copy()
+    bad[0, 0] = phat.shape[0] + 5          # an id outside [0, E) contributes nothing
+    only = np.where(np.arange(K)[None, :] == 0, 0, g).astype(np.float32)
+    assert np.array_equal(path.moe_down(phi, a, phat, bits, h, bad, g)[0],
+                          path.moe_down(phi, a, phat, bits, h, ids, only)[0])
