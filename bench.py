@@ -277,6 +277,98 @@ def bench_fqcm(args):
     print(json.dumps(out, ensure_ascii=False), flush=True)
 
 
+def bench_down(args):
+    """Down projection + routing-weighted combine for the tokens of a
+    gate/up workload (down_<workload>): the layer's down blob and Phi_down
+    rotated over enough copies that >= 1 GiB is touched between two uses of
+    one copy, h (the gate/up output shape) resident; K back-to-back calls
+    timed with events on the launch stream."""
+    import time
+
+    import torch
+    import synth
+    from oracle import path
+    from oracle.quantize import quantize_expert
+    from spectral_expert_gemv_amd import bitsmoe
+
+    wl = synth.workload(args.workload[len("down_"):])
+    spec = wl.layer
+    L = synth.make_layer(spec)
+    D = synth.make_down(L)
+    rd = D.phi.shape[1]
+    dev = torch.device("cuda:0")
+    blob = bitsmoe.pack(D.p, D.a, D.bits)
+    phi16 = np.asarray(D.phi, np.float16)
+    phit = np.ascontiguousarray(phi16.T)
+    per_e = layer_bytes_per_expert(D.bits, spec.din)
+    NB = max(1, args.batches)
+    host = []
+    for i in range(NB):
+        _, ids = synth.make_batch(wl, L, step=i)
+        g = synth.make_gates(wl, L, step=i)
+        h = (np.random.default_rng(1000 + i).standard_normal((wl.T, spec.k, spec.dout)) * 0.3
+             ).astype(np.float32)
+        host.append((h, ids.astype(np.int32), g))
+    T, k = host[0][1].shape
+    alg = [rd * spec.dout * 2 + int(per_e[np.unique(ids)].sum()) + h.nbytes + ids.nbytes +
+           g.nbytes + T * spec.din * 4 for h, ids, g in host]
+    C = args.copies or max(2, min(64, math.ceil((1 << 30) / (blob.nbytes + phit.nbytes))))
+    copies = [(torch.from_numpy(blob).to(dev), torch.from_numpy(phit).to(dev)) for _ in range(C)]
+    dbat = [tuple(torch.from_numpy(a).to(dev) for a in b) for b in host]
+    out = torch.empty((T, spec.din), dtype=torch.float32, device=dev)
+    ws = torch.empty(bitsmoe.moe_down_workspace_size(T, k, spec.E, spec.dout, spec.din, rd),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream(device=dev)
+
+    def step(i):
+        bl, ph = copies[i % C]
+        h, ids, g = dbat[i % NB]
+        bitsmoe.moe_down(bl, ph, h, ids, g, spec.E, spec.din, rd, out=out, ws=ws, stream=stream)
+
+    K, W = args.steps, args.warmup
+    with torch.cuda.stream(stream):
+        for i in range(W):
+            step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(K):
+            step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    avg = sum(alg[i % NB] for i in range(K)) / K
+    gbs = avg / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "down_combine_us_per_token", "value": round(ms * 1e3 / T, 4),
+        "unit": "µs/token", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms, 6),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "E": spec.E, "din": spec.din, "dout": spec.dout,
+                   "r_down": rd, "top_k": spec.k, "tokens": T, "layer_copies": C,
+                   "inputs": "fp32 h (rounded to fp16), fp16 Phi_down, packed down directions"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": round(avg),
+                     "note": "one call = fp16 cast, projection, expert apply, combine"},
+    }
+    if not args.no_cpu:
+        h, ids, g = host[0]
+        t0 = time.perf_counter()
+        phat = np.zeros((spec.E, rd, spec.din))
+        for e in np.unique(ids):
+            phat[e] = quantize_expert(D.p[e], D.bits[e])["phat"]
+        path.moe_down(phi16, D.a, phat, D.bits, h, ids, g)
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(el * 1e6 / T, 1), "unit": "µs/token", "cores": 1,
+                               "kind": "oracle",
+                               "sample": "one batch of %d token(s) through the float64 oracle "
+                                         "(dequantize routed experts, z per pair, expert "
+                                         "products, combine): %.2f s" % (T, el)}
+    print(json.dumps(res, ensure_ascii=False), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -287,6 +379,8 @@ def main():
         return bench_pack(args)
     if args.workload.startswith("fqcm_"):
         return bench_fqcm(args)
+    if args.workload.startswith("down_"):
+        return bench_down(args)
     import torch
     import synth
     from spectral_expert_gemv_amd import bitsmoe

@@ -212,6 +212,28 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes,
                        int r, float* h, void* ws, size_t ws_bytes,
                        bitsmoe_stream_t stream);
 
+/* ---------------------------------------------------------- down + combine
+ * out[t*din + i] = sum over slots j (ascending) of g[t*k + j] * y_{t,j}[i],
+ *   y_{t,j} = sum_{c: b>0} a_{e,c} z_c p_hat_{e,c},  z = Phi_down^T fp16(h_{t,j}),
+ *   e = ids[t*k + j]; a pair whose id is outside [0, E) contributes nothing.
+ * The down projection with the same two splits as gate/up (BitsMoE blog
+ * note, Methodology); its basis lives in the input space of down_proj, so z
+ * is formed per (token, slot) from that pair's h.
+ *   packed_down      : device blob (bitsmoe_pack with rows = din, r = r_d)
+ *   phi_t_down_f16   : r_d*dout fp16, row c = phi_c (Phi_down transposed)
+ *   h                : T*k*dout float32 (the gate/up output), rounded to fp16
+ *   ids, g           : T*k int32 expert ids and float32 routing weights
+ *   out              : T*din float32
+ *   ws               : >= bitsmoe_moe_down_workspace_size() bytes, 256-byte
+ *                      aligned (fp16 h, z and the per-pair outputs)
+ * dout must be a multiple of 8.  Async on `stream`. */
+int bitsmoe_moe_down_workspace_size(int T, int k, int E, int dout, int din, int r_d,
+                                    size_t* bytes);
+int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi_t_down_f16,
+                     const float* h, const int32_t* ids, const float* g, int T, int k, int E,
+                     int dout, int din, int r_d, float* out, void* ws, size_t ws_bytes,
+                     bitsmoe_stream_t stream);
+
 /* Zero-fills a workspace with a kernel (no memset node), on `stream`. */
 int bitsmoe_workspace_init(void* ws, size_t ws_bytes, bitsmoe_stream_t stream);
 

@@ -64,6 +64,9 @@ _SIGS = {
     "bitsmoe_fqcm_allocate": ([_vp, _vp, _vp, _i, _i, _i, ctypes.c_uint64, _vp,
                                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64),
                                _vp, _sz, _vp], _i),
+    "bitsmoe_moe_down_workspace_size": ([_i, _i, _i, _i, _i, _i, _psz], _i),
+    "bitsmoe_moe_down": ([_vp, _sz, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz,
+                          _vp], _i),
 }
 FQCM_WS_BYTES = 1024
 for _name, (_args, _res) in _SIGS.items():
@@ -263,3 +266,29 @@ def fqcm_allocate(a, beta, eps, dout, budget_bits, bits=None, ws=None, stream=No
                                       ctypes.byref(used), _ptr(ws), _nbytes(ws),
                                       _stream(stream)))
     return bits, lam.value, used.value
+
+
+def moe_down_workspace_size(T, k, E, dout, din, r_d):
+    out = ctypes.c_size_t(0)
+    _check(_lib.bitsmoe_moe_down_workspace_size(T, k, E, dout, din, r_d, ctypes.byref(out)))
+    return out.value
+
+
+def moe_down(packed_down, phi_t_down, h, ids, g, E, din, r_d, out=None, ws=None, stream=None):
+    """out (T x din float32) = sum_j g[t, j] * down_e(h[t, j]); h: T x k x
+    dout float32, ids: T x k int32, g: T x k float32, phi_t_down: r_d x dout
+    fp16, packed_down: the down blob; all device tensors."""
+    import torch
+    T, k, dout = h.shape
+    if h.dtype != torch.float32 or g.dtype != torch.float32 or ids.dtype != torch.int32:
+        raise ValueError("h and g must be float32, ids int32")
+    h, ids, g = h.contiguous(), ids.contiguous(), g.contiguous()
+    if out is None:
+        out = torch.empty((T, din), dtype=torch.float32, device=h.device)
+    if ws is None:
+        ws = torch.empty(moe_down_workspace_size(T, k, E, dout, din, r_d), dtype=torch.uint8,
+                         device=h.device)
+    _check(_lib.bitsmoe_moe_down(_ptr(packed_down), _nbytes(packed_down), _ptr(phi_t_down),
+                                 _ptr(h), _ptr(ids), _ptr(g), T, k, E, dout, din, r_d, _ptr(out),
+                                 _ptr(ws), _nbytes(ws), _stream(stream)))
+    return out

@@ -1,0 +1,124 @@
+// Down projection and routing-weighted combine.
+//
+// The down projection restated with the two splits of the BitsMoE blog
+// note's Methodology ("first split": a shared basis of the input space;
+// "second split": quantized unit directions with magnitudes).  Its input is
+// the gate/up output h, different for every (token, slot), so z =
+// Phi_down^T h is formed per pair; the pages name only gate and up, and this
+// is the plain extension of the same machinery.
+//
+//  1. k_h_to_f16: h (float32) -> fp16, the activation precision the
+//     projection reads;
+//  2. z = Phi_down^T h16 for the T*k pairs (the spectral projection kernel);
+//  3. y = P_e diag(a_e) z per pair (the expert apply kernel on the down
+//     blob, one pair per row);
+//  4. k_combine: out[t] = sum over slots j, in order, of g[t, j] y[t, j]
+//     (float32); a pair whose id is outside [0, E) contributes nothing.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include "bitsmoe.h"
+#include "common.h"
+
+namespace bitsmoe {
+namespace {
+
+__global__ __launch_bounds__(256) void k_h_to_f16(const float* __restrict__ h,
+                                                  __half* __restrict__ h16, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    h16[i] = __float2half_rn(h[i]);
+}
+
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
+                                                 const int32_t* __restrict__ ids,
+                                                 const float* __restrict__ g, int k, int E,
+                                                 int din, float* __restrict__ out) {
+  const int t = (int)blockIdx.y;
+  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (i >= din) return;
+  float acc = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int e = ids[t * k + j];
+    if (e < 0 || e >= E) continue;
+    acc += g[t * k + j] * y[((size_t)t * k + j) * din + i];
+  }
+  out[(size_t)t * din + i] = acc;
+}
+
+struct DownWs {
+  size_t h16, z, y, total;
+};
+DownWs down_ws(int T, int k, int dout, int din, int rd) {
+  const uint64_t n = (uint64_t)T * k;
+  DownWs w;
+  w.h16 = 0;
+  w.z = (size_t)(((n * dout * 2) + 255) / 256 * 256);
+  w.y = w.z + (size_t)(((n * rd * 4) + 255) / 256 * 256);
+  w.total = w.y + (size_t)(((n * din * 4) + 255) / 256 * 256);
+  return w;
+}
+
+int down_dims(int T, int k, int E, int dout, int din, int rd) {
+  if (T < 1 || k < 1 || k > E) return fail(BITSMOE_EINVAL, "T=%d k=%d E=%d", T, k, E);
+  if (E <= 0 || dout <= 0 || din <= 0 || rd <= 0)
+    return fail(BITSMOE_ESHAPE, "E=%d dout=%d din=%d r_d=%d", E, dout, din, rd);
+  if (dout % 8) return fail(BITSMOE_ESHAPE, "dout=%d is not a multiple of 8", dout);
+  if ((long long)T * k > (1LL << 24) || T > 65535)
+    return fail(BITSMOE_ESHAPE, "T=%d k=%d too large", T, k);
+  return BITSMOE_OK;
+}
+
+}  // namespace
+}  // namespace bitsmoe
+
+using namespace bitsmoe;
+
+extern "C" {
+
+int bitsmoe_moe_down_workspace_size(int T, int k, int E, int dout, int din, int r_d,
+                                    size_t* bytes) {
+  if (!bytes) return fail(BITSMOE_EINVAL, "bytes is null");
+  const int st = down_dims(T, k, E, dout, din, r_d);
+  if (st) return st;
+  *bytes = down_ws(T, k, dout, din, r_d).total;
+  return BITSMOE_OK;
+}
+
+int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi_t_down_f16,
+                     const float* h, const int32_t* ids, const float* g, int T, int k, int E,
+                     int dout, int din, int r_d, float* out, void* ws, size_t ws_bytes,
+                     bitsmoe_stream_t stream) {
+  int st = down_dims(T, k, E, dout, din, r_d);
+  if (st) return st;
+  if (!packed_down || !phi_t_down_f16 || !h || !ids || !g || !out || !ws)
+    return fail(BITSMOE_EINVAL, "null pointer argument");
+  if (((uintptr_t)ws & 255u) || ((uintptr_t)h & 3u) || ((uintptr_t)g & 3u) ||
+      ((uintptr_t)ids & 3u) || ((uintptr_t)out & 3u))
+    return fail(BITSMOE_EINVAL, "misaligned pointer (ws: 256 bytes; h, g, ids, out: 4)");
+  const DownWs w = down_ws(T, k, dout, din, r_d);
+  if (ws_bytes < w.total) return fail(BITSMOE_ENOSPC, "ws_bytes=%zu < %zu", ws_bytes, w.total);
+  const hipStream_t s = (hipStream_t)stream;
+  uint8_t* w8 = (uint8_t*)ws;
+  const size_t n = (size_t)T * k * dout;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_h_to_f16, dim3((unsigned)blocks), dim3(256), 0, s, h,
+                     (__half*)(w8 + w.h16), n);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(BITSMOE_EHIP, "fp16 cast launch: %s", hipGetErrorString(err));
+  float* z = (float*)(w8 + w.z);
+  float* y = (float*)(w8 + w.y);
+  if ((st = bitsmoe_spectral_proj(phi_t_down_f16, w8 + w.h16, z, T * k, dout, r_d, stream)))
+    return st;
+  if ((st = bitsmoe_expert_apply(packed_down, down_bytes, E, din, r_d, z, r_d, ids, T * k, 1, y,
+                                 nullptr, 0, stream)))
+    return st;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((din + 255) / 256), (unsigned)T), dim3(256), 0, s,
+                     y, ids, g, k, E, din, out);
+  err = hipGetLastError();
+  if (err != hipSuccess) return fail(BITSMOE_EHIP, "combine launch: %s", hipGetErrorString(err));
+  return BITSMOE_OK;
+}
+
+}  // extern "C"

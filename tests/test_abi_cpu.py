@@ -223,3 +223,18 @@ def test_fqcm_entry_points_validate_before_launch():
     assert al(ws=None) == bm.EINVAL
     assert al(bits=None) == bm.EINVAL
     assert al(E=0) == bm.ESHAPE
+
+
+def test_down_entry_point_validates_before_launch():
+    L = bm._lib
+    need = bm.moe_down_workspace_size(2, 2, 4, 96, 64, 32)
+    assert need >= 2 * 2 * (96 * 2 + 32 * 4 + 64 * 4)
+    def dn(T=2, k=2, E=4, dout=96, ws=FAKE, ws_bytes=need, h=FAKE):
+        return L.bitsmoe_moe_down(FAKE, 1 << 16, FAKE, h, FAKE, FAKE, T, k, E, dout, 64, 32,
+                                  FAKE, ws, ws_bytes, None)
+    assert dn(ws_bytes=need - 1) == bm.ENOSPC
+    assert dn(dout=90) == bm.ESHAPE
+    assert dn(T=0) == bm.EINVAL
+    assert dn(k=5) == bm.EINVAL
+    assert dn(ws=FAKE + 16) == bm.EINVAL
+    assert dn(h=None) == bm.EINVAL
