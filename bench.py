@@ -369,6 +369,66 @@ def bench_down(args):
     print(json.dumps(res, ensure_ascii=False), flush=True)
 
 
+def bench_ssd(args):
+    """Shared-basis decomposition of one linear type at a layer's full size
+    (ssd_<layer>): a seeded Gaussian dense stack W (E x dout x din float32)
+    resident in HBM, r = din; one call (it synchronizes once per Jacobi
+    sweep) timed on the wall clock."""
+    import time
+
+    import torch
+    import synth
+    from oracle import ssd as ossd
+    from spectral_expert_gemv_amd import bitsmoe
+
+    spec = synth.LAYERS[args.workload[len("ssd_"):]]
+    E, dout, din = spec.E, spec.dout, spec.din
+    rng = np.random.default_rng(2024)
+    W = rng.standard_normal((E, dout, din), dtype=np.float32)
+    dev = torch.device("cuda:0")
+    Wd = torch.from_numpy(W).to(dev)
+    ws = torch.empty(bitsmoe.ssd_workspace_size(E, dout, din, din), dtype=torch.uint8,
+                     device=dev)
+    K = max(1, min(args.steps, 3))
+    if args.warmup:
+        bitsmoe.ssd(Wd, din, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        phi, a, p, s2, sweeps = bitsmoe.ssd(Wd, din, ws=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    # float64 flops: Gram matrix and projection (2 x 2 E dout din^2) and the
+    # rotations (per sweep, n - 1 rounds of 3 x 3 n^2 multiply-adds on G and V)
+    flop = 2 * 2.0 * E * dout * din * din + sweeps * (din - 1) * 9.0 * din * din * 2
+    tfs = flop / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "ssd_ms", "value": round(ms, 2), "unit": "ms/projection", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 2),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "E": E, "dout": dout, "din": din, "r": din,
+                   "jacobi_sweeps": sweeps, "inputs": "seeded N(0,1) dense W, float32"},
+        "roofline": {"bound": "alu", "achieved": round(tfs, 3), "peak": 78.6,
+                     "unit": "TFLOP/s", "frac": round(tfs / 78.6, 5), "traffic": None,
+                     "flop": flop,
+                     "note": "whole call over the float64 flops of the Gram matrix, the "
+                             "projection and the Jacobi rotations, against the fp64 vector "
+                             "peak"},
+    }
+    if not args.no_cpu:
+        ne = max(1, min(E, 16))
+        t0 = time.perf_counter()
+        ossd.ssd(W[:ne].astype(np.float64))
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(el * 1e3 * E / ne, 1), "unit": "ms/projection",
+                               "cores": int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or None,
+                               "kind": "oracle",
+                               "sample": "numpy SVD (LAPACK) of %d of %d experts' stack, "
+                                         "%.2f s, scaled linearly in E" % (ne, E, el)}
+    print(json.dumps(res, ensure_ascii=False), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -381,6 +441,8 @@ def main():
         return bench_fqcm(args)
     if args.workload.startswith("down_"):
         return bench_down(args)
+    if args.workload.startswith("ssd_"):
+        return bench_ssd(args)
     import torch
     import synth
     from spectral_expert_gemv_amd import bitsmoe

@@ -234,6 +234,28 @@ int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi
                      int dout, int din, int r_d, float* out, void* ws, size_t ws_bytes,
                      bitsmoe_stream_t stream);
 
+/* ------------------------------------------------------------------- SSD
+ * Shared-basis spectral decomposition of one linear type (BitsMoE blog note,
+ * Methodology, first and second split): W_cat = [W_1; ...; W_E] =
+ * U Sigma Phi^T, P = U Sigma, W_e = sum_k a_{e,k} p_{e,k} phi_k^T.
+ *   W     : device E*dout*din float32, W_e row-major at W[e*dout*din]
+ *   phi   : device din*r float32 (phi_k = column k), the r leading right
+ *           singular vectors, each signed so that its first largest-magnitude
+ *           entry is positive
+ *   a, p  : device E*r and E*r*dout float32 (p laid out as for bitsmoe_pack;
+ *           a zero column gets p = e_0)
+ *   sigma2: optional HOST array of r float64 squared singular values
+ *   sweeps: optional HOST int, the Jacobi sweeps taken
+ * Float64 Gram matrix and cyclic Jacobi (circle ordering) until the
+ * off-diagonal mass is below (1e-15 ||G||)^2 or max_sweeps sweeps.  ws: device
+ * memory of bitsmoe_ssd_workspace_size() bytes, 256-byte aligned.  The call
+ * synchronizes `stream` (once per sweep and at the end).  din <= 8192,
+ * r <= min(din, E*dout). */
+int bitsmoe_ssd_workspace_size(int E, int dout, int din, int r, size_t* bytes);
+int bitsmoe_ssd(const float* W, int E, int dout, int din, int r, float* phi, float* a, float* p,
+                double* sigma2, int* sweeps, int max_sweeps, void* ws, size_t ws_bytes,
+                bitsmoe_stream_t stream);
+
 /* Zero-fills a workspace with a kernel (no memset node), on `stream`. */
 int bitsmoe_workspace_init(void* ws, size_t ws_bytes, bitsmoe_stream_t stream);
 

@@ -67,6 +67,8 @@ _SIGS = {
     "bitsmoe_moe_down_workspace_size": ([_i, _i, _i, _i, _i, _i, _psz], _i),
     "bitsmoe_moe_down": ([_vp, _sz, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz,
                           _vp], _i),
+    "bitsmoe_ssd_workspace_size": ([_i, _i, _i, _i, _psz], _i),
+    "bitsmoe_ssd": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _pi, _i, _vp, _sz, _vp], _i),
 }
 FQCM_WS_BYTES = 1024
 for _name, (_args, _res) in _SIGS.items():
@@ -292,3 +294,30 @@ def moe_down(packed_down, phi_t_down, h, ids, g, E, din, r_d, out=None, ws=None,
                                  _ptr(h), _ptr(ids), _ptr(g), T, k, E, dout, din, r_d, _ptr(out),
                                  _ptr(ws), _nbytes(ws), _stream(stream)))
     return out
+
+
+def ssd_workspace_size(E, dout, din, r):
+    out = ctypes.c_size_t(0)
+    _check(_lib.bitsmoe_ssd_workspace_size(E, dout, din, r, ctypes.byref(out)))
+    return out.value
+
+
+def ssd(W, r, max_sweeps=30, ws=None, stream=None):
+    """Shared-basis decomposition of W (E x dout x din float32 device tensor).
+    Returns (phi din x r, a E x r, p E x r x dout) device float32 tensors,
+    sigma^2 (numpy float64, r) and the Jacobi sweeps taken."""
+    import torch
+    E, dout, din = W.shape
+    if W.dtype != torch.float32 or not W.is_contiguous():
+        raise ValueError("W must be contiguous float32")
+    phi = torch.empty((din, r), dtype=torch.float32, device=W.device)
+    a = torch.empty((E, r), dtype=torch.float32, device=W.device)
+    p = torch.empty((E, r, dout), dtype=torch.float32, device=W.device)
+    if ws is None:
+        ws = torch.empty(ssd_workspace_size(E, dout, din, r), dtype=torch.uint8, device=W.device)
+    s2 = np.zeros(r, dtype=np.float64)
+    sw = ctypes.c_int(0)
+    _check(_lib.bitsmoe_ssd(_ptr(W), E, dout, din, r, _ptr(phi), _ptr(a), _ptr(p),
+                            s2.ctypes.data, ctypes.byref(sw), int(max_sweeps), _ptr(ws),
+                            _nbytes(ws), _stream(stream)))
+    return phi, a, p, s2, sw.value

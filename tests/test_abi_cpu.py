@@ -238,3 +238,18 @@ def test_down_entry_point_validates_before_launch():
     assert dn(k=5) == bm.EINVAL
     assert dn(ws=FAKE + 16) == bm.EINVAL
     assert dn(h=None) == bm.EINVAL
+
+
+def test_ssd_entry_point_validates_before_launch():
+    L = bm._lib
+    need = bm.ssd_workspace_size(4, 10, 12, 12)
+    assert need >= 2 * 12 * 12 * 8 + 4 * 10 * 12 * 8
+    def sd(E=4, dout=10, din=12, r=12, ws=FAKE, ws_bytes=need, W=FAKE, sweeps=30):
+        return L.bitsmoe_ssd(W, E, dout, din, r, FAKE, FAKE, FAKE, None, None, sweeps, ws,
+                             ws_bytes, None)
+    assert sd(ws_bytes=need - 1) == bm.ENOSPC
+    assert sd(r=13) == bm.ESHAPE
+    assert sd(din=9000, r=12) == bm.ESHAPE
+    assert sd(W=None) == bm.EINVAL
+    assert sd(ws=FAKE + 64) == bm.EINVAL
+    assert sd(sweeps=0) == bm.EINVAL
