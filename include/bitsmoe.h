@@ -200,8 +200,11 @@ int bitsmoe_expert_apply(const void* packed, size_t packed_bytes, int E, int dou
  *                             rows r..2r-1 = Phi_up^T
  *   x_f16 : T*din fp16; ids : T*k int32; h : T*k*dout float32
  *   ws    : device workspace of at least bitsmoe_moe_gateup_workspace_size()
- *           bytes, zero-filled before its first use (bitsmoe_workspace_init);
- *           every call leaves its synchronization words at zero again.
+ *           bytes, zero-filled once before its first use
+ *           (bitsmoe_workspace_init).  The one-launch path (T <= 4) keeps a
+ *           launch counter and cumulative hint counters in it from call to
+ *           call, so a workspace serves one stream: calls that share it must
+ *           not run concurrently.
  */
 int bitsmoe_moe_gateup_workspace_size(int T, int k, int E, int din, int dout, int r,
                                       size_t* bytes);

@@ -12,36 +12,41 @@
 //    XCD b % 8 and takes units b, b + G, ...); with 8 or more pairs every
 //    segment of a pair sits on one XCD, whose L2 then serves the pair's
 //    column metadata to all of them.
-//  * Waves 0-3 of every work-group issue the loads of their contiguous run
-//    of Phi^T rows first (the rows do not depend on anything), compute z for
-//    them (v_dot2_f32_f16, a transposing 4-row reduction) and publish each
-//    value as one 64-bit word (float bits | launch tag << 32, device-coherent
-//    store), wait for their stores and count themselves on one of 64 hint
-//    counters.  A reader can tell a fresh value from a stale one by its tag,
-//    without fences.
-//  * Waves 4-7 meanwhile read the routed id and the two directory records,
-//    issue the slot metadata of both projections and copy the unit's gate
-//    and up segment records into LDS (16-byte global_load_lds); wave 4
-//    publishes both segment descriptors in LDS.
-//  * One wave polls the hint counters; then the work-group copies the
-//    token's 2r tagged words into LDS (coalesced, L2-shared, re-reading
-//    stale words device-coherently).
-//  * Coefficients (waves 4-7): lane l owns slots 8l .. 8l + 7 and the tail
-//    slot 2048 + l of each projection; it forms c = a s z (a z for 16-bit
-//    slots) and a m z, and after block-wide DPP reductions writes the fp16
-//    pair hi + lo of c 2^S into LDS.
-//  * Apply: each wave of a projection takes every 4th 32-slot K step; the
-//    codes of its 16-row tiles are decoded from the plane words straight
-//    into fp16 A operands and multiplied with the coefficient column (B,
-//    token column 0) by v_mfma_f32_16x16x32_f16, hi and lo parts.
-//  * The 4 waves' row sums meet in LDS; wave 0 scales back by 2^-S, adds the
-//    offset sums and writes SiLU(gate) * up for the 32 rows.
+//  * Waves 0-3 of every work-group issue the loads of their run of Phi^T
+//    rows first (nothing they depend on), compute z for them
+//    (v_dot2_f32_f16, a transposing 4-row reduction) and publish each value
+//    as one 64-bit word (float bits | launch tag << 32) into a ring of 8
+//    buffers (the tag picks one), then add one to a hint counter without
+//    waiting for the stores.  The counters are cumulative over launches: after
+//    the launch with tag g their sum is g times the number of producing waves.
+//  * Waves 4-7 meanwhile read the routed id and the two directory records
+//    (scalar loads), issue the raw slot metadata of both projections (16-byte
+//    loads kept in registers) and copy the unit's gate and up segment records
+//    into LDS with 16-byte global_load_lds; wave 4 publishes the descriptors.
+//  * One wave polls the hint counters; then the token's 2r tagged words are
+//    copied into LDS (an L2-shared read; a word whose tag is stale is re-read
+//    device-coherently, bounded).
+//  * Coefficients: waves 4-7 form c = a s z (a z for 16-bit slots) and a m z
+//    for both projections and write c into LDS; then all eight waves split
+//    their projection's c into v = rint(c 2^S) (S from the largest |c| of the
+//    1..8-bit slots, S16 for the 16-bit ones) and store its four balanced
+//    base-256 digit bytes as digit rows.
+//  * Apply: per 64-slot step one v_mfma_i32_16x16x64_i8 per 16-row tile, the
+//    decoded code bytes as A (width 8 as code - 128) and the digit rows as B
+//    columns 0-3, so every product and sum is exact in int32; the 16-bit
+//    group uses v_mfma_f32_16x16x32_f16 with the fp16 hi and lo parts of
+//    v 2^-16 in columns 0 and 1.  Each wave of a projection takes every 4th
+//    step.
+//  * Epilogue: the columns are folded with 2^(8n - S) (2^(16 - S16)), the
+//    four waves' row sums meet in LDS, and wave 0 adds the width-8 offset
+//    correction and the row-independent sum a m z and writes SiLU(gate) * up.
 // Segments whose record exceeds the LDS arena are applied in chunks of K
 // steps.  Work-groups wait for other groups' z, so the host launches at most
 // as many groups as can be resident at once; all waits are bounded (a
-// time-out gives NaN rows, the kernel still exits).  The last group of the
-// grid advances the epoch.  Barriers order LDS only (lds_sync): the
-// staging copies are waited for explicitly where their data is needed.
+// time-out gives NaN rows, the kernel still exits).  Work-group 0 advances
+// the epoch once every producer of the launch has counted itself.  Barriers
+// order LDS only (lds_sync): the staging copies are waited for explicitly
+// where their data is needed.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -410,7 +415,6 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     SlotMeta<kFSper> md0, md1;  // kBoth: gate, up; otherwise md0 is this wave's projection
     bool ok0 = true, ok1 = true;
     uint32_t ns0 = 0, nq0 = 0, ns1 = 0, nq1 = 0;  // n_slot, n_qslot of md0, md1
-    uint32_t e8a0 = 0, e8b0 = 0, e8a1 = 0, e8b1 = 0;  // width-8 slot ranges of md0, md1
     if (pj == 1) {
       // routed id -> both directory records (scalar loads) -> slot metadata,
       // staging copies (waves 4-5 gate, 6-7 up) and the descriptors in LDS
@@ -425,14 +429,11 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         ok1 = PU.ok;
         ns0 = PG.n_slot; nq0 = PG.n_qslot;
         ns1 = PU.n_slot; nq1 = PU.n_qslot;
-        e8a0 = 4u * PG.b5; e8b0 = 4u * PG.b6;
-        e8a1 = 4u * PU.b5; e8b1 = 4u * PU.b6;
         load_meta<kFSper>(PG, lp, md0);
         load_meta<kFSper>(PU, lp, md1);
       } else {
         ok0 = PU.ok;
         ns0 = PU.n_slot; nq0 = PU.n_qslot;
-        e8a0 = 4u * PU.b5; e8b0 = 4u * PU.b6;
         load_meta<kFSper>(PU, lp, md0);
       }
       const SegProj& SP = (wv & 2) ? PU : PG;
@@ -456,7 +457,6 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         const SegProj PG = uniform_seg(L.desc[0]);
         ok0 = PG.ok;
         ns0 = PG.n_slot; nq0 = PG.n_qslot;
-        e8a0 = 4u * PG.b5; e8b0 = 4u * PG.b6;
         load_meta<kFSper>(PG, lp, md0);
       }
     }

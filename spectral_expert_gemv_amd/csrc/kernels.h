@@ -19,9 +19,9 @@ constexpr int kTile = 16;            // tokens per grouped work unit (MFMA N)
 struct GateUpPlan {
   size_t z_off;       // T x 2r float32 (projection launch of the batched path)
   size_t zpart_off;   // T x ceil(2r / 16) float32: max |z| per projection work-group
-  size_t zt_off;      // T x 2r uint64 tagged z (one-launch path)
-  size_t sync_off;    // uint32 epoch, uint32 grid arrival counter (left at 0), then
-                      // 64 hint counters 128 bytes apart (left at 0)
+  size_t zt_off;      // ring of kZRing x T x 2r uint64 tagged z (one-launch path)
+  size_t sync_off;    // uint32 epoch (the last launch's tag), then from byte 128 the
+                      // 64 cumulative hint counters, 128 bytes apart
   size_t route_off;   // route lists (see RouteLists)
   size_t total;
 };
