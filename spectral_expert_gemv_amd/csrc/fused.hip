@@ -401,6 +401,23 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
                              1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  if (pj == 1) {
+    // Warm this XCD's L2 with both directories (128-byte lines; the first
+    // 256 of them): the record loads that follow the routed id then hit L2
+    // instead of queueing behind the Phi^T loads.  One unconditional 4-byte
+    // copy per lane into the digit-table area, which nothing reads before
+    // these copies have been waited for (the coefficient pass waits for all
+    // of the wave's loads first).
+    typedef __attribute__((address_space(1))) void gvoid;
+    const uint32_t nl = ((uint32_t)a.E * kDirRecBytes + 127u) / 128u;  // lines per projection
+    uint32_t j = (uint32_t)threadIdx.x - kFProj;
+    j = j < 2u * nl ? j : 2u * nl - 1u;
+    const uint8_t* line = (j < nl ? a.blob_g : a.blob_u) + kHeaderBytes + 128u * (j < nl ? j : j - nl);
+    __builtin_amdgcn_global_load_lds((gvoid*)line,
+                                     (lds_void*)(reinterpret_cast<uint8_t*>(&L.Lb[0][0][0]) +
+                                                 256 * (wv - kFPW)),
+                                     4, 0, 0);
+  }
   int zt_cached = -1;  // token whose z is in L.Z
   bool zok = true;     // this wave's words of L.Z arrived
   for (; have; u += G, have = u < U) {
