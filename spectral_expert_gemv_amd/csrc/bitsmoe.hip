@@ -356,6 +356,11 @@ int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, i
 
 }  // namespace
 
+int launch_proj_maxima(const void* phi, const void* x, float* z, float* zpart, int T, int din,
+                       int R, hipStream_t st) {
+  return launch_proj(phi, x, z, zpart, T, din, R, st);
+}
+
 int tile_cap(int T, int k, int E) {
   const long long P = (long long)T * k;
   const long long g = P < E ? P : E;
@@ -487,6 +492,7 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     gs.zpart = zpart;
     gs.nzp = (2 * r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
     gs.tcap = tile_cap(T, k, E);
+    gs.single = 0;
     int* rb = (int*)(wsb + plan.route_off);
     gs.rl.ntiles = rb;
     gs.rl.tile = rb + 1;

@@ -10,8 +10,11 @@
 //  1. k_h_to_f16: h (float32) -> fp16, the activation precision the
 //     projection reads;
 //  2. z = Phi_down^T h16 for the T*k pairs (the spectral projection kernel);
-//  3. y = P_e diag(a_e) z per pair (the expert apply kernel on the down
-//     blob, one pair per row);
+//  3. y = P_e diag(a_e) z per pair: the pairs are grouped by expert and
+//     each tile of up to 16 pairs of one expert goes through the grouped MFMA
+//     kernel in its one-projection mode (each pair is one B column with its
+//     own z; the two wave halves take two 32-row segments); beyond the
+//     grouped kernel's limits the per-pair apply kernel;
 //  4. k_combine: out[t] = sum over slots j, in order, of g[t, j] y[t, j]
 //     (float32); a pair whose id is outside [0, E) contributes nothing.
 #include <hip/hip_fp16.h>
@@ -19,6 +22,8 @@
 
 #include "bitsmoe.h"
 #include "common.h"
+#include "format.h"
+#include "kernels.h"
 
 namespace bitsmoe {
 namespace {
@@ -47,15 +52,19 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
 }
 
 struct DownWs {
-  size_t h16, z, y, total;
+  size_t h16, z, y, zpart, route, total;
 };
-DownWs down_ws(int T, int k, int dout, int din, int rd) {
+DownWs down_ws(int T, int k, int E, int dout, int din, int rd) {
   const uint64_t n = (uint64_t)T * k;
+  auto al = [](uint64_t x) { return (size_t)((x + 255) / 256 * 256); };
+  const uint64_t nzp = ((uint64_t)rd + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
   DownWs w;
   w.h16 = 0;
-  w.z = (size_t)(((n * dout * 2) + 255) / 256 * 256);
-  w.y = w.z + (size_t)(((n * rd * 4) + 255) / 256 * 256);
-  w.total = w.y + (size_t)(((n * din * 4) + 255) / 256 * 256);
+  w.z = al(n * dout * 2);
+  w.y = w.z + al(n * rd * 4);
+  w.zpart = w.y + al(n * din * 4);
+  w.route = w.zpart + al(n * nzp * 4);
+  w.total = w.route + al((1 + 3 * (uint64_t)tile_cap(T, k, E) + n) * 4);
   return w;
 }
 
@@ -81,7 +90,7 @@ int bitsmoe_moe_down_workspace_size(int T, int k, int E, int dout, int din, int 
   if (!bytes) return fail(BITSMOE_EINVAL, "bytes is null");
   const int st = down_dims(T, k, E, dout, din, r_d);
   if (st) return st;
-  *bytes = down_ws(T, k, dout, din, r_d).total;
+  *bytes = down_ws(T, k, E, dout, din, r_d).total;
   return BITSMOE_OK;
 }
 
@@ -96,7 +105,7 @@ int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi
   if (((uintptr_t)ws & 255u) || ((uintptr_t)h & 3u) || ((uintptr_t)g & 3u) ||
       ((uintptr_t)ids & 3u) || ((uintptr_t)out & 3u))
     return fail(BITSMOE_EINVAL, "misaligned pointer (ws: 256 bytes; h, g, ids, out: 4)");
-  const DownWs w = down_ws(T, k, dout, din, r_d);
+  const DownWs w = down_ws(T, k, E, dout, din, r_d);
   if (ws_bytes < w.total) return fail(BITSMOE_ENOSPC, "ws_bytes=%zu < %zu", ws_bytes, w.total);
   const hipStream_t s = (hipStream_t)stream;
   uint8_t* w8 = (uint8_t*)ws;
@@ -109,11 +118,53 @@ int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi
   if (err != hipSuccess) return fail(BITSMOE_EHIP, "fp16 cast launch: %s", hipGetErrorString(err));
   float* z = (float*)(w8 + w.z);
   float* y = (float*)(w8 + w.y);
-  if ((st = bitsmoe_spectral_proj(phi_t_down_f16, w8 + w.h16, z, T * k, dout, r_d, stream)))
-    return st;
-  if ((st = bitsmoe_expert_apply(packed_down, down_bytes, E, din, r_d, z, r_d, ids, T * k, 1, y,
-                                 nullptr, 0, stream)))
-    return st;
+  const bool grouped = r_d <= kGroupMaxR && E <= kGroupMaxE && dout <= kGroupMaxDin;
+  if (!grouped) {
+    if ((st = bitsmoe_spectral_proj(phi_t_down_f16, w8 + w.h16, z, T * k, dout, r_d, stream)))
+      return st;
+    if ((st = bitsmoe_expert_apply(packed_down, down_bytes, E, din, r_d, z, r_d, ids, T * k, 1,
+                                   y, nullptr, 0, stream)))
+      return st;
+  } else {
+    if (((uintptr_t)packed_down & 15u) || ((uintptr_t)phi_t_down_f16 & 15u))
+      return fail(BITSMOE_EINVAL, "packed_down and phi_t_down_f16 must be 16-byte aligned");
+    if (down_bytes < kHeaderBytes + (size_t)kDirRecBytes * E)
+      return fail(BITSMOE_ENOSPC, "packed_down: %zu bytes cannot hold header and directory",
+                  down_bytes);
+    // z and, per 16-row block of the projection, the largest |z| the grouped
+    // kernel scales its coefficients by
+    float* zpart = (float*)(w8 + w.zpart);
+    if ((st = launch_proj_maxima(phi_t_down_f16, w8 + w.h16, z, zpart, T * k, dout, r_d, s)))
+      return st;
+    GroupArgs gs;
+    gs.g.blob_g = gs.g.blob_u = (const uint8_t*)packed_down;
+    gs.g.bytes_g = gs.g.bytes_u = (uint64_t)down_bytes;
+    gs.g.E = E;
+    gs.g.dout = din;
+    gs.g.r = r_d;
+    gs.g.ids = ids;
+    gs.g.ktop = k;
+    gs.g.npairs = T * k;
+    gs.g.h = y;
+    gs.g.n_seg = (din + kSegRows - 1) / kSegRows;
+    gs.z = z;
+    gs.zpart = zpart;
+    gs.nzp = (r_d + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
+    gs.tcap = tile_cap(T, k, E);
+    gs.single = 1;
+    int* rb = (int*)(w8 + w.route);
+    gs.rl.ntiles = rb;
+    gs.rl.tile = rb + 1;
+    gs.rl.pairs = rb + 1 + 3 * gs.tcap;
+    launch_route_group(ids, T * k, E, din, y, gs.rl, s);
+    err = hipGetLastError();
+    if (err != hipSuccess)
+      return fail(BITSMOE_EHIP, "route grouping launch: %s", hipGetErrorString(err));
+    launch_gateup_grouped(gs, s);
+    err = hipGetLastError();
+    if (err != hipSuccess)
+      return fail(BITSMOE_EHIP, "grouped apply launch: %s", hipGetErrorString(err));
+  }
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((din + 255) / 256), (unsigned)T), dim3(256), 0, s,
                      y, ids, g, k, E, din, out);
   err = hipGetLastError();

@@ -150,8 +150,14 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   const int R = 2 * a.r;
 
   const int u = blockIdx.x;
-  const int ti = u % s.tcap, sg = u / s.tcap;
-  if (sg >= a.n_seg || ti >= s.rl.ntiles[0]) return;
+  const int ti = u % s.tcap;
+  const bool single = s.single != 0;
+  // single: this half's segment (a half past the last segment repeats it
+  // and writes nothing)
+  const int sg0 = single ? 2 * (u / s.tcap) : u / s.tcap;
+  if (sg0 >= a.n_seg || ti >= s.rl.ntiles[0]) return;
+  const int sgh = single ? sg0 + pj : sg0;
+  const int sg = sgh < a.n_seg ? sgh : a.n_seg - 1;
   const int e = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti]);
   const int p0 = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti + 1]);
   const int nt = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti + 2]);
@@ -168,11 +174,12 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   if (threadIdx.x < (unsigned)nt) L.pair[threadIdx.x] = s.rl.pairs[p0 + threadIdx.x];
   {
     const int n = lp / kGZP, j = lp % kGZP;
-    const int pz0 = pj ? a.r / kProjRowsPerBlock : 0;
-    const int pz1 = pj ? s.nzp : (a.r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
+    const int pz0 = (pj && !single) ? a.r / kProjRowsPerBlock : 0;
+    const int pz1 = (pj || single) ? s.nzp : (a.r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
     float zm = 0.f;
     if (n < nt) {
-      const int t = s.rl.pairs[p0 + n] / a.ktop;
+      const int pr = s.rl.pairs[p0 + n];
+      const int t = single ? pr : pr / a.ktop;  // z row: the pair's own (single) or its token's
       const float* zp = s.zpart + (size_t)t * s.nzp;
       for (int i = pz0 + j; i < pz1; i += kGZP) zm = fmaxf(zm, zp[i]);
     }
@@ -192,7 +199,7 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
 #pragma unroll
   for (int n = 0; n < kTile; ++n) {
     Sn[n] = n < nt ? L.S[pj][n] : 0;
-    zoff[n] = n < nt ? (L.pair[n] / a.ktop) * R + (pj ? a.r : 0) : 0;
+    zoff[n] = n < nt ? (single ? L.pair[n] * a.r : (L.pair[n] / a.ktop) * R + (pj ? a.r : 0)) : 0;
   }
 
   bool good = P.ok;
@@ -273,21 +280,33 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
     const int n = threadIdx.x >> 5, row = threadIdx.x & 31;
     if (n < nt) {
       float ys[2];
-      bool ok = true;
+      uint32_t okq[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         float sum = 0.f, bsum = 0.f;
+        uint32_t okw = 1u;
 #pragma unroll
         for (int w = 0; w < kGPW; ++w) {
           sum += L.u.red[q][w][n][row];
           bsum += L.pbias[q][w][n];
-          ok = ok && L.pok[q][w];
+          okw &= L.pok[q][w];
         }
         ys[q] = ldexpf(sum, -L.S[q][n]) + bsum;
+        okq[q] = okw;
       }
-      const int orow = sg * kSegRows + row;
-      if (orow < a.dout)
-        a.h[(size_t)L.pair[n] * a.dout + orow] = ok ? silu_mul(ys[0], ys[1]) : __builtin_nanf("");
+      if (!single) {
+        const int orow = sg * kSegRows + row;
+        if (orow < a.dout)
+          a.h[(size_t)L.pair[n] * a.dout + orow] =
+              (okq[0] & okq[1]) ? silu_mul(ys[0], ys[1]) : __builtin_nanf("");
+      } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int orow = (sg0 + q) * kSegRows + row;
+          if (sg0 + q < a.n_seg && orow < a.dout)
+            a.h[(size_t)L.pair[n] * a.dout + orow] = okq[q] ? ys[q] : __builtin_nanf("");
+        }
+      }
     }
   }
 }
@@ -312,7 +331,7 @@ int launch_gateup_grouped(const GroupArgs& s, hipStream_t st) {
     (void)hipGetLastError();
     attr_done[dev] = true;
   }
-  const long long blocks = (long long)s.tcap * s.g.n_seg;
+  const long long blocks = (long long)s.tcap * (s.single ? (s.g.n_seg + 1) / 2 : s.g.n_seg);
   hipLaunchKernelGGL(k_gateup_grouped, dim3((unsigned)blocks), dim3(kGThreads), sizeof(GroupLds),
                      st, s);
   return 0;

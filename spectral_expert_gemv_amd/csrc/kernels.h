@@ -70,8 +70,16 @@ struct GroupArgs {
   int nzp;             // projection work-groups (ceil(2r / 16))
   RouteLists rl;
   int tcap;            // tiles the grid is sized for
+  // 0: gate and up (waves 0-3 / 4-7), SiLU * mul into h.  1: one projection
+  // (blob_g == blob_u) with z per pair (row p of z, nzp maxima per pair):
+  // the two wave halves take segments 2 s and 2 s + 1, y goes to h.
+  int single;
 };
 size_t grouped_lds_bytes();
+// z = Phi^T x and, when zpart is not null (din <= kGroupMaxDin), the largest
+// |z| of every 16-row block of the projection per token.
+int launch_proj_maxima(const void* phi, const void* x, float* z, float* zpart, int T, int din,
+                       int R, hipStream_t st);
 int launch_route_group(const int32_t* ids, int P, int E, int dout, float* h,
                        const RouteLists& rl, hipStream_t st);
 int launch_gateup_grouped(const GroupArgs& s, hipStream_t st);
