@@ -399,8 +399,10 @@ def bench_ssd(args):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / K
     # float64 flops: Gram matrix and projection (2 x 2 E dout din^2) and the
-    # rotations (per sweep, n - 1 rounds of 3 x 3 n^2 multiply-adds on G and V)
-    flop = 2 * 2.0 * E * dout * din * din + sweeps * (din - 1) * 9.0 * din * din * 2
+    # rotations (per round 9 din^2: two 2 x 2 rotations of every element of
+    # G, 6 flops, and one of every element of V, 3 flops; din - 1 rounds a
+    # sweep)
+    flop = 2 * 2.0 * E * dout * din * din + sweeps * (din - 1) * 9.0 * din * din
     tfs = flop / (ms * 1e-3) / 1e12
     res = {
         "metric": "ssd_ms", "value": round(ms, 2), "unit": "ms/projection", "n_gpus": 1,

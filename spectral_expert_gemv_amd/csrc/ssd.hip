@@ -12,7 +12,8 @@
 //    and its eigenvalues the squared singular values;
 //  * cyclic Jacobi with the round-robin (circle) ordering: in each of the
 //    n - 1 rounds of a sweep the n / 2 disjoint pairs rotate at once
-//    (angles from the round's start; columns of G and V, then rows of G);
+//    (angles from the round's start, then one pass that maps every 2 x 2
+//    block of G by both of its pairs' rotations and rotates V's columns);
 //    sweeps stop when the off-diagonal mass falls below (1e-15 ||G||)^2;
 //  * rank the eigenvalues (descending, ties by index), Phi = the leading r
 //    eigenvectors, each signed so that its largest-magnitude entry (first
@@ -138,31 +139,59 @@ __global__ void k_jacobi_angles(const double* G, int n, int n0, int t, double* c
   cs[4 * i + 3] = s;
 }
 
-// Columns p, q of M (rows x n0, row-major): M <- M J.
-__global__ void k_jacobi_cols(double* M, int rows, int n0, int npairs, const double* cs) {
+// One round's rotations in one pass (after k_jacobi_angles): thread
+// (i, j) < npairs^2 maps the 2 x 2 block of G at rows {p_i, q_i} and columns
+// {p_j, q_j} to J_i^T B J_j (the disjoint rotations of a round commute, so
+// this equals all column rotations followed by all row rotations); the
+// remaining n0 * npairs threads rotate columns p, q of one row of V.
+__global__ void k_jacobi_round(double* G, double* V, int n0, int npairs, const double* cs) {
   const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= (size_t)rows * npairs) return;
-  const int row = (int)(id / npairs), i = (int)(id % npairs);
+  const size_t nb = (size_t)npairs * npairs;
+  if (id < nb) {
+    const int i = (int)(id / npairs), j = (int)(id % npairs);  // neighbours: consecutive j
+    const int pi = (int)cs[4 * i], qi = (int)cs[4 * i + 1];
+    const int pjx = (int)cs[4 * j], qjx = (int)cs[4 * j + 1];
+    if (qi >= n0 || qjx >= n0) {
+      // a padding index: rotate only the real side (its partner index has
+      // c = 1, s = 0, so the block reduces to one row or column pair)
+      if (qi < n0 && pjx < n0 && qjx >= n0) {
+        const double ci = cs[4 * i + 2], si = cs[4 * i + 3];
+        const double a = G[(size_t)pi * n0 + pjx], b = G[(size_t)qi * n0 + pjx];
+        G[(size_t)pi * n0 + pjx] = ci * a - si * b;
+        G[(size_t)qi * n0 + pjx] = si * a + ci * b;
+      } else if (qjx < n0 && pi < n0 && qi >= n0) {
+        const double cj = cs[4 * j + 2], sj = cs[4 * j + 3];
+        const double a = G[(size_t)pi * n0 + pjx], b = G[(size_t)pi * n0 + qjx];
+        G[(size_t)pi * n0 + pjx] = cj * a - sj * b;
+        G[(size_t)pi * n0 + qjx] = sj * a + cj * b;
+      }
+      return;
+    }
+    const double ci = cs[4 * i + 2], si = cs[4 * i + 3];
+    const double cj = cs[4 * j + 2], sj = cs[4 * j + 3];
+    double* rp = G + (size_t)pi * n0;
+    double* rq = G + (size_t)qi * n0;
+    const double b00 = rp[pjx], b01 = rp[qjx], b10 = rq[pjx], b11 = rq[qjx];
+    // columns: B J_j
+    const double c00 = cj * b00 - sj * b01, c01 = sj * b00 + cj * b01;
+    const double c10 = cj * b10 - sj * b11, c11 = sj * b10 + cj * b11;
+    // rows: J_i^T (B J_j)
+    rp[pjx] = ci * c00 - si * c10;
+    rp[qjx] = ci * c01 - si * c11;
+    rq[pjx] = si * c00 + ci * c10;
+    rq[qjx] = si * c01 + ci * c11;
+    return;
+  }
+  const size_t v = id - nb;
+  if (v >= (size_t)n0 * npairs) return;
+  const int row = (int)(v / npairs), i = (int)(v % npairs);
   const int p = (int)cs[4 * i], q = (int)cs[4 * i + 1];
   if (q >= n0) return;
   const double c = cs[4 * i + 2], s = cs[4 * i + 3];
-  double* r = M + (size_t)row * n0;
+  double* r = V + (size_t)row * n0;
   const double mp = r[p], mq = r[q];
   r[p] = c * mp - s * mq;
   r[q] = s * mp + c * mq;
-}
-
-// Rows p, q of G: G <- J^T G.
-__global__ void k_jacobi_rows(double* G, int n0, int npairs, const double* cs) {
-  const size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= (size_t)n0 * npairs) return;
-  const int i = (int)(id / n0), col = (int)(id % n0);  // neighbours: consecutive columns
-  const int p = (int)cs[4 * i], q = (int)cs[4 * i + 1];
-  if (q >= n0) return;
-  const double c = cs[4 * i + 2], s = cs[4 * i + 3];
-  const double gp = G[(size_t)p * n0 + col], gq = G[(size_t)q * n0 + col];
-  G[(size_t)p * n0 + col] = c * gp - s * gq;
-  G[(size_t)q * n0 + col] = s * gp + c * gq;
 }
 
 // out[0] = off-diagonal sum of squares, out[1] = total sum of squares (one
@@ -336,7 +365,8 @@ int bitsmoe_ssd(const float* W, int E, int dout, int din, int r, float* phi, flo
   // cyclic Jacobi, circle ordering over an even index count
   const int n = din + (din & 1), npairs = n / 2;
   const unsigned gp = (unsigned)((npairs + 255) / 256);
-  const unsigned gc = (unsigned)(((size_t)din * npairs + 255) / 256);
+  const unsigned gr =
+      (unsigned)((((size_t)npairs * npairs + (size_t)din * npairs) + 255) / 256);
   int sw = 0;
   for (; sw < max_sweeps; ++sw) {
     hipLaunchKernelGGL(k_jacobi_norms, dim3(1), dim3(1024), 0, s, G, din, nrm);
@@ -348,9 +378,7 @@ int bitsmoe_ssd(const float* W, int E, int dout, int din, int r, float* phi, flo
     if (!(hn[0] > 1e-30 * hn[1])) break;  // off-diagonal below (1e-15 ||G||)^2
     for (int t = 0; t < n - 1; ++t) {
       hipLaunchKernelGGL(k_jacobi_angles, dim3(gp), dim3(256), 0, s, G, n, din, t, cs);
-      hipLaunchKernelGGL(k_jacobi_cols, dim3(gc), dim3(256), 0, s, G, din, din, npairs, cs);
-      hipLaunchKernelGGL(k_jacobi_rows, dim3(gc), dim3(256), 0, s, G, din, npairs, cs);
-      hipLaunchKernelGGL(k_jacobi_cols, dim3(gc), dim3(256), 0, s, V, din, din, npairs, cs);
+      hipLaunchKernelGGL(k_jacobi_round, dim3(gr), dim3(256), 0, s, G, V, din, npairs, cs);
     }
     if ((st = hip_ok(hipGetLastError(), "rotation launch"))) return st;
   }
