@@ -32,7 +32,7 @@ KERNEL_TWO_LAUNCHES = "k_proj_rows + k_route_group + k_gateup_grouped (timed tog
 # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counter runs, scaled by
 # the same counters on a plain copy of known size; None until measured for
 # the current kernel.
-TRAFFIC = {"qwen3_30b_a3b_t1": 26188555}
+TRAFFIC = {"qwen3_30b_a3b_t1": 26315709}
 
 
 def parse():
