@@ -361,6 +361,27 @@ int launch_proj_maxima(const void* phi, const void* x, float* z, float* zpart, i
   return launch_proj(phi, x, z, zpart, T, din, R, st);
 }
 
+// Per-tile coefficient tables: hi and lo rows (with 256 slots of slack for
+// the last row's 16-byte copies), the chunk sums and the flags.
+size_t group_coef_bytes(int tcap, int r) {
+  const size_t rpad = (size_t)group_rpad(r), nck = rpad / 256;
+  const size_t rows = (size_t)tcap * 2 * kTile;
+  return 2 * align_up(rows * rpad * 2 + 512, 256) + align_up((size_t)tcap * 2 * nck * kTile * 4, 256) +
+         align_up((size_t)tcap * 2 * 4, 256);
+}
+
+void group_coef_tables(GroupArgs& gs, uint8_t* base, int r) {
+  const size_t rpad = (size_t)group_rpad(r), nck = rpad / 256;
+  const size_t rows = (size_t)gs.tcap * 2 * kTile;
+  const size_t hb = align_up(rows * rpad * 2 + 512, 256);
+  gs.thi = (_Float16*)base;
+  gs.tlo = (_Float16*)(base + hb);
+  gs.tbias = (float*)(base + 2 * hb);
+  gs.tbad = (uint32_t*)(base + 2 * hb + align_up((size_t)gs.tcap * 2 * nck * kTile * 4, 256));
+  gs.rpad = (int)rpad;
+  gs.nck = (int)nck;
+}
+
 int tile_cap(int T, int k, int E) {
   const long long P = (long long)T * k;
   const long long g = P < E ? P : E;
@@ -377,7 +398,8 @@ GateUpPlan gateup_plan(int T, int k, int E, int r) {
   p.zt_off = align_up(p.zpart_off + (size_t)T * nzp * sizeof(float), 256);
   p.sync_off = align_up(p.zt_off + (size_t)kZRing * T * 2 * r * sizeof(uint64_t), 256);
   p.route_off = align_up(p.sync_off + 128 + 64 * 128, 256);
-  p.total = align_up(p.route_off + (1 + 3 * (size_t)tile_cap(T, k, E) + P) * sizeof(int), 256);
+  p.coef_off = align_up(p.route_off + (1 + 3 * (size_t)tile_cap(T, k, E) + P) * sizeof(int), 256);
+  p.total = p.coef_off + group_coef_bytes(tile_cap(T, k, E), r);
   return p;
 }
 
@@ -497,8 +519,12 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     gs.rl.ntiles = rb;
     gs.rl.tile = rb + 1;
     gs.rl.pairs = rb + 1 + 3 * gs.tcap;
+    group_coef_tables(gs, wsb + plan.coef_off, r);
     launch_route_group(ids, T * k, E, dout, h, gs.rl, s);
     if ((st = launch_status("route grouping launch"))) return st;
+    if ((st = bitsmoe_workspace_init(gs.tbad, (size_t)gs.tcap * 2 * 4, stream))) return st;
+    launch_group_coef(gs, s);
+    if ((st = launch_status("tile coefficient launch"))) return st;
     launch_gateup_grouped(gs, s);
     return launch_status("grouped gate/up launch");
   }

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
 }
 
 struct DownWs {
-  size_t h16, z, y, zpart, route, total;
+  size_t h16, z, y, zpart, route, coef, total;
 };
 DownWs down_ws(int T, int k, int E, int dout, int din, int rd) {
   const uint64_t n = (uint64_t)T * k;
@@ -64,7 +64,8 @@ DownWs down_ws(int T, int k, int E, int dout, int din, int rd) {
   w.y = w.z + al(n * rd * 4);
   w.zpart = w.y + al(n * din * 4);
   w.route = w.zpart + al(n * nzp * 4);
-  w.total = w.route + al((1 + 3 * (uint64_t)tile_cap(T, k, E) + n) * 4);
+  w.coef = w.route + al((1 + 3 * (uint64_t)tile_cap(T, k, E) + n) * 4);
+  w.total = w.coef + group_coef_bytes(tile_cap(T, k, E), rd);
   return w;
 }
 
@@ -156,10 +157,16 @@ int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi
     gs.rl.ntiles = rb;
     gs.rl.tile = rb + 1;
     gs.rl.pairs = rb + 1 + 3 * gs.tcap;
+    group_coef_tables(gs, w8 + w.coef, r_d);
     launch_route_group(ids, T * k, E, din, y, gs.rl, s);
     err = hipGetLastError();
     if (err != hipSuccess)
       return fail(BITSMOE_EHIP, "route grouping launch: %s", hipGetErrorString(err));
+    if ((st = bitsmoe_workspace_init(gs.tbad, (size_t)gs.tcap * 2 * 4, stream))) return st;
+    launch_group_coef(gs, s);
+    err = hipGetLastError();
+    if (err != hipSuccess)
+      return fail(BITSMOE_EHIP, "tile coefficient launch: %s", hipGetErrorString(err));
     launch_gateup_grouped(gs, s);
     err = hipGetLastError();
     if (err != hipSuccess)

@@ -15,15 +15,22 @@
 // result), cut into tiles of at most 16 pairs.  Pairs whose id lies outside
 // [0, E) get NaN rows.
 //
+// k_group_coef: the coefficients of every tile, once per tile instead of
+// once per row segment: c = a s z_t[k] (a z for 16-bit slots) of each of the
+// tile's tokens as the fp16 hi + lo parts of c 2^S_t, S_t from the expert's
+// bound max |a s| (directory) and the token's max |z| (partial maxima written
+// by the projection launch), and the row-independent sums a m z per 256-slot
+// chunk, into tables in the workspace.
+//
 // k_gateup_grouped: one 512-lane work-group per (tile, 32-row segment) unit,
 // both projections (waves 0-3 gate, 4-7 up); unit u = segment * tcap + tile
-// runs on XCD u % 8, so every segment of a tile shares one L2.  The segment
-// records are staged in LDS once; the tile's coefficients are formed 256
-// slots at a time: c = a s z_t[k] (a z for 16-bit slots) gathered from the
-// projection's z rows, as fp16 hi + lo parts of c 2^S_t, where S_t follows
-// from the expert's bound max |a s| (directory) and the token's max |z|
-// (partial maxima written by the projection launch).  The apply is the same
-// MFMA K-step loop as the one-launch kernel with up to 16 token columns.
+// runs on XCD u % 8, so every segment of a tile shares one L2 (and reads the
+// tile's coefficient tables from it).  The segment records are staged in
+// LDS once; each 256-slot chunk of the tile's coefficients is copied into
+// LDS with 16-byte loads.  The apply is the same MFMA K-step loop as the
+// one-launch kernel with up to 16 token columns.  A one-projection mode
+// (the down projection) gives each pair its own z and lets the two wave
+// halves take two segments.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
@@ -138,6 +145,82 @@ __device__ __forceinline__ void stage_chunk(uint32_t* arena, const SegProj& p, i
   stage16(arena, p.planes + (size_t)sg * p.seg_words + w0, (w1 - w0) / 4u, lp, lane, nl);
 }
 
+// Coefficients of every tile, once (not once per row segment): one
+// 256-lane work-group per (256-slot chunk, tile, projection).  Lane l takes
+// slot 256 chunk + l of the tile's expert and forms, for each of the tile's
+// tokens, c = a s z[k] (a z for 16-bit slots) and a m z[k], writes the fp16
+// hi and lo parts of c 2^S_n and the chunk's row-independent sums.  The
+// scale S_n follows from the expert's bound and the token's max |z| exactly
+// as the apply kernel forms it.
+__global__ __launch_bounds__(256) void k_group_coef(GroupArgs s) {
+  const GateUpArgs& a = s.g;
+  const int ck = (int)blockIdx.x, ti = (int)blockIdx.y, pj = (int)blockIdx.z;
+  if (ti >= s.rl.ntiles[0]) return;
+  const bool single = s.single != 0;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int e = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti]);
+  const int p0 = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti + 1]);
+  const int nt = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti + 2]);
+  const uint8_t* blob = pj ? a.blob_u : a.blob_g;
+  const SegProj P = uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
+                                         load_rec_s(blob, e, a.E), load_hdr(blob), a.E, a.dout,
+                                         a.r));
+  __shared__ int S[kTile];
+  __shared__ int zoff[kTile];
+  __shared__ float bred[4][kTile];
+  __shared__ uint32_t bad[4];
+  {
+    const int n = threadIdx.x / kGZP, j = threadIdx.x % kGZP;
+    const int pz0 = (pj && !single) ? a.r / kProjRowsPerBlock : 0;
+    const int pz1 = (pj || single) ? s.nzp : (a.r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
+    float zm = 0.f;
+    int pr = 0;
+    if (n < nt) {
+      pr = s.rl.pairs[p0 + n];
+      const int t = single ? pr : pr / a.ktop;
+      const float* zp = s.zpart + (size_t)t * s.nzp;
+      for (int i = pz0 + j; i < pz1; i += kGZP) zm = fmaxf(zm, zp[i]);
+    }
+#pragma unroll
+    for (int off = kGZP / 2; off > 0; off >>= 1) zm = fmaxf(zm, __shfl_xor(zm, off, kWave));
+    if (j == 0 && n < nt) {
+      S[n] = coef_shift(P.cmax, zm);
+      zoff[n] = single ? pr * a.r : (pr / a.ktop) * (2 * a.r) + (pj ? a.r : 0);
+    }
+  }
+  __syncthreads();
+  const uint32_t sl = 256u * (uint32_t)ck + threadIdx.x;
+  const bool live = sl < P.n_slot;
+  uint32_t k = live ? P.kidx[sl] : 0u;
+  bool good = k < (uint32_t)a.r;
+  k = good ? k : 0u;
+  const float av = live ? P.A[sl] : 0.f;
+  const bool isq = sl < P.n_qslot;
+  const float sv = (live && isq) ? __half2float(__ushort_as_half(P.S[sl])) : 1.f;
+  const float mv = (live && isq) ? __half2float(__ushort_as_half(P.M[sl])) : 0.f;
+  const size_t row0 = (size_t)(ti * 2 + pj) * kTile;
+  for (int n = 0; n < nt; ++n) {
+    const float az = av * (live ? s.z[zoff[n] + k] : 0.f);
+    _Float16 hi, lo;
+    split_coef(az * sv, S[n], hi, lo);
+    s.thi[(row0 + n) * s.rpad + sl] = hi;
+    s.tlo[(row0 + n) * s.rpad + sl] = lo;
+    const float bw = wave_sum(az * mv);
+    if (lane == 0) bred[wv][n] = bw;
+  }
+  const bool wok = __all(good);
+  if (lane == 0) bad[wv] = wok ? 0u : 1u;
+  __syncthreads();
+  if ((int)threadIdx.x < nt) {
+    const int n = threadIdx.x;
+    s.tbias[((size_t)(ti * 2 + pj) * s.nck + ck) * kTile + n] =
+        (bred[0][n] + bred[1][n]) + (bred[2][n] + bred[3][n]);
+  }
+  if (threadIdx.x == 0 && (bad[0] | bad[1] | bad[2] | bad[3]))
+    atomicOr(&s.tbad[ti * 2 + pj], 1u);
+}
+
 __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   extern __shared__ __align__(16) uint8_t lds_raw[];
   GroupLds& L = *reinterpret_cast<GroupLds*>(lds_raw);
@@ -147,7 +230,6 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   const int pj = wv >= kGPW ? 1 : 0;  // waves 0-3 gate, 4-7 up
   const int wp = wv & (kGPW - 1);
   const int lp = (int)threadIdx.x & (kGProj - 1);
-  const int R = 2 * a.r;
 
   const int u = blockIdx.x;
   const int ti = u % s.tcap;
@@ -194,19 +276,9 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   }
   __syncthreads();
   const int nch = __builtin_amdgcn_readfirstlane(max(L.nch[0], L.nch[1]));  // uniform
-  int Sn[kTile];
-  int zoff[kTile];  // z row of token n, this projection
-#pragma unroll
-  for (int n = 0; n < kTile; ++n) {
-    Sn[n] = n < nt ? L.S[pj][n] : 0;
-    zoff[n] = n < nt ? (single ? L.pair[n] * a.r : (L.pair[n] / a.ktop) * R + (pj ? a.r : 0)) : 0;
-  }
-
   bool good = P.ok;
-  float bias[kTile];
-#pragma unroll
-  for (int n = 0; n < kTile; ++n) bias[n] = 0.f;
   f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const size_t trow = (size_t)(ti * 2 + (single ? 0 : pj)) * kTile;
   uint32_t b0 = 0;
   for (int ch = 0; ch < max(nch, 1); ++ch) {
     if (ch > 0) {
@@ -220,27 +292,22 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
     for (int cc = 0; cc < ncc; ++cc) {
       const uint32_t cb0 = b0 + 64u * cc;
       const uint32_t s0 = 4u * cb0;
-      const uint32_t sl = s0 + (uint32_t)lp;
-      const bool live = sl < 4u * b1;  // padding slots have a = 0
       if (cc > 0) __syncthreads();     // the previous coefficient chunk is read
-      uint32_t k = live ? P.kidx[sl] : 0u;
-      good &= k < (uint32_t)a.r;
-      k = k < (uint32_t)a.r ? k : 0u;
-      const float av = live ? P.A[sl] : 0.f;
-      const bool isq = sl < P.n_qslot;
-      const float sv = (live && isq) ? __half2float(__ushort_as_half(P.S[sl])) : 1.f;
-      const float mv = (live && isq) ? __half2float(__ushort_as_half(P.M[sl])) : 0.f;
-      float zv[kTile];
+      // the tile's coefficients of slots s0 .. s0 + 255 (k_group_coef):
+      // 16-byte copies, rows of the present tokens only
+      {
+        const int q = lp >> 5, c = lp & 31;  // 8 lanes groups x 32 16-byte pieces of a row
 #pragma unroll
-      for (int n = 0; n < kTile; ++n) zv[n] = (live && n < nt) ? s.z[zoff[n] + k] : 0.f;
-#pragma unroll
-      for (int n = 0; n < kTile; ++n) {
-        const float az = av * zv[n];
-        bias[n] += az * mv;
-        _Float16 hi, lo;
-        split_coef(az * sv, Sn[n], hi, lo);
-        L.u.c.hi[pj][n * kGCStride + lp] = hi;
-        L.u.c.lo[pj][n * kGCStride + lp] = lo;
+        for (int h = 0; h < 4; ++h) {
+          const int n = q + 8 * (h & 1);
+          const bool lo_part = h >= 2;
+          if (n < nt) {
+            const _Float16* src = (lo_part ? s.tlo : s.thi) + (trow + n) * s.rpad + s0 + 8 * c;
+            const uint4 v = *reinterpret_cast<const uint4*>(src);
+            _Float16* dst = (lo_part ? &L.u.c.lo[pj][0] : &L.u.c.hi[pj][0]) + n * kGCStride + 8 * c;
+            *reinterpret_cast<uint4*>(dst) = v;
+          }
+        }
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -265,14 +332,17 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
         L.u.red[pj][wp][n][16 + 4 * kg + i] = acc1[i];
       }
     }
-#pragma unroll
-    for (int n2 = 0; n2 < kTile; ++n2) {
-      if (n2 < nt) {
-        const float bw = wave_sum(bias[n2]);
-        if (lane == 0) L.pbias[pj][wp][n2] = bw;
-      }
+    // the row-independent sums of the tile's chunks (wave 0 of each half),
+    // the column-index check from the coefficient pass
+    if (wp == 0 && lane < nt) {
+      const float* tb = s.tbias + (size_t)(ti * 2 + (single ? 0 : pj)) * s.nck * kTile + lane;
+      float bsum = 0.f;
+      for (int c = 0; c < s.nck; ++c) bsum += tb[(size_t)c * kTile];
+      L.pbias[pj][0][lane] = bsum;
+    } else if (lane < nt) {
+      L.pbias[pj][wp][lane] = 0.f;
     }
-    const bool wok = __all(good);
+    const bool wok = __all(good) && s.tbad[ti * 2 + (single ? 0 : pj)] == 0u;
     if (lane == 0) L.pok[pj][wp] = wok;
   }
   __syncthreads();
@@ -319,6 +389,12 @@ int launch_route_group(const int32_t* ids, int P, int E, int dout, float* h,
                        const RouteLists& rl, hipStream_t st) {
   hipLaunchKernelGGL(k_route_group, dim3(1), dim3(kRThreads), (size_t)2 * E * sizeof(uint32_t),
                      st, ids, P, E, dout, h, rl);
+  return 0;
+}
+
+int launch_group_coef(const GroupArgs& s, hipStream_t st) {
+  hipLaunchKernelGGL(k_group_coef, dim3((unsigned)s.nck, (unsigned)s.tcap, s.single ? 1u : 2u),
+                     dim3(256), 0, st, s);
   return 0;
 }
 

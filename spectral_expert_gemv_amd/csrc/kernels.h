@@ -23,6 +23,7 @@ struct GateUpPlan {
   size_t sync_off;    // uint32 epoch (the last launch's tag), then from byte 128 the
                       // 64 cumulative hint counters, 128 bytes apart
   size_t route_off;   // route lists (see RouteLists)
+  size_t coef_off;    // per-tile coefficient tables (batched path, see GroupArgs)
   size_t total;
 };
 GateUpPlan gateup_plan(int T, int k, int E, int r);
@@ -74,7 +75,23 @@ struct GroupArgs {
   // (blob_g == blob_u) with z per pair (row p of z, nzp maxima per pair):
   // the two wave halves take segments 2 s and 2 s + 1, y goes to h.
   int single;
+  // per-tile coefficient tables (k_group_coef): fp16 hi and lo parts of
+  // c 2^S of token column n and slot s at [((tile * 2 + proj) * kTile + n) *
+  // rpad + s]; the row-independent sums per 256-slot chunk at
+  // [((tile * 2 + proj) * nck + chunk) * kTile + n]; a flag per (tile, proj)
+  // set when a column index is out of range
+  _Float16* thi;
+  _Float16* tlo;
+  float* tbias;
+  uint32_t* tbad;
+  int rpad, nck;
 };
+// slots of a tile's coefficient rows: the largest slot count an expert can
+// have (r plus group padding), rounded up to whole 256-slot chunks
+inline int group_rpad(int r) { return (r + 7 * 31 + 255) / 256 * 256; }
+int launch_group_coef(const GroupArgs& s, hipStream_t st);
+size_t group_coef_bytes(int tcap, int r);                // workspace of the tables
+void group_coef_tables(GroupArgs& gs, uint8_t* base, int r);  // sets thi .. nck (needs tcap)
 size_t grouped_lds_bytes();
 // z = Phi^T x and, when zpart is not null (din <= kGroupMaxDin), the largest
 // |z| of every 16-row block of the projection per token.
