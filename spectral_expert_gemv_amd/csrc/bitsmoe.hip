@@ -96,6 +96,65 @@ __device__ __forceinline__ void pstep(float (&v)[kPRW * kPT], bool up) {
   }
 }
 
+// Batched projection on the matrix cores (T >= 16, din a multiple of 32):
+// z^T = Phi^T x^T as a dense contraction over din.  Work-group (b, c): rows
+// 16 b .. 16 b + 15 of Phi^T and tokens 64 c .. 64 c + 63, one 16 x 16
+// v_mfma_f32_16x16x32_f16 block per wave; both operands are read from
+// global memory in 16-byte pieces (Phi^T rows and x rows are contiguous
+// along din), four K steps in flight.  fp16 products are exact in fp32; the
+// sums are fp32.  zpart gets the largest |z| of the 16 rows per token.
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_proj_mfma(const uint4* __restrict__ phi_t,
+                                                   const uint4* __restrict__ x,
+                                                   float* __restrict__ z,
+                                                   float* __restrict__ zpart, int T, int din8,
+                                                   int R, int nzp) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int row0 = (int)blockIdx.x * 16;
+  const int tok0 = ((int)blockIdx.y * 4 + wv) * 16;
+  if (tok0 >= T) return;  // whole wave: nothing below needs the others
+  const int m = lane & 15, kg = lane >> 4;
+  const int ra = min(row0 + m, R - 1), tb = min(tok0 + m, T - 1);
+  const uint4* pa = phi_t + (size_t)ra * din8 + kg;
+  const uint4* pb = x + (size_t)tb * din8 + kg;
+  f4v acc = {0.f, 0.f, 0.f, 0.f};
+  const int nk = din8 / 4;  // K steps of 32
+  int k = 0;
+  for (; k + 4 <= nk; k += 4) {
+    uint4 av[4], bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      av[j] = pa[4 * (k + j)];
+      bv[j] = pb[4 * (k + j)];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8v*>(&av[j]),
+                                                   *reinterpret_cast<const h8v*>(&bv[j]), acc,
+                                                   0, 0, 0);
+  }
+  for (; k < nk; ++k) {
+    const uint4 av = pa[4 * k], bv = pb[4 * k];
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8v*>(&av),
+                                                 *reinterpret_cast<const h8v*>(&bv), acc, 0, 0,
+                                                 0);
+  }
+  // acc[i] = z of row row0 + 4 kg + i, token tok0 + m
+  const int tok = tok0 + m;
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = row0 + 4 * kg + i;
+    if (tok < T && row < R) z[(size_t)tok * R + row] = acc[i];
+    mx = fmaxf(mx, row < R ? fabsf(acc[i]) : 0.f);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  if (zpart && kg == 0 && tok < T) zpart[(size_t)tok * nzp + blockIdx.x] = mx;
+}
+
 template <int U>
 __global__ __launch_bounds__(kProjWaves * kWave) void k_proj_rows(
     const uint4* __restrict__ phi_t, const uint4* __restrict__ x, float* __restrict__ z,
@@ -335,6 +394,12 @@ int proj_args(const void* phi, const void* x, const float* z, int T, int din, in
 int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, int din, int R,
                 hipStream_t s) {
   const int din8 = din / 8;
+  if (T >= 16 && din % 32 == 0) {
+    const int nzp = (R + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
+    hipLaunchKernelGGL(k_proj_mfma, dim3((unsigned)nzp, (unsigned)((T + 63) / 64)), dim3(256), 0,
+                       s, (const uint4*)phi, (const uint4*)x, z, zpart, T, din8, R, nzp);
+    return launch_status("spectral projection launch");
+  }
   const dim3 grid_rows((R + kProjWaves * kPRW - 1) / (kProjWaves * kPRW));
   const dim3 block(kProjWaves * kWave);
   const uint4* p4 = (const uint4*)phi;
@@ -520,9 +585,8 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     gs.rl.tile = rb + 1;
     gs.rl.pairs = rb + 1 + 3 * gs.tcap;
     group_coef_tables(gs, wsb + plan.coef_off, r);
-    launch_route_group(ids, T * k, E, dout, h, gs.rl, s);
+    launch_route_group(ids, T * k, E, dout, h, gs.rl, s, gs.tbad, gs.tcap * 2);
     if ((st = launch_status("route grouping launch"))) return st;
-    if ((st = bitsmoe_workspace_init(gs.tbad, (size_t)gs.tcap * 2 * 4, stream))) return st;
     launch_group_coef(gs, s);
     if ((st = launch_status("tile coefficient launch"))) return st;
     launch_gateup_grouped(gs, s);

@@ -158,11 +158,10 @@ int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi
     gs.rl.tile = rb + 1;
     gs.rl.pairs = rb + 1 + 3 * gs.tcap;
     group_coef_tables(gs, w8 + w.coef, r_d);
-    launch_route_group(ids, T * k, E, din, y, gs.rl, s);
+    launch_route_group(ids, T * k, E, din, y, gs.rl, s, gs.tbad, gs.tcap * 2);
     err = hipGetLastError();
     if (err != hipSuccess)
       return fail(BITSMOE_EHIP, "route grouping launch: %s", hipGetErrorString(err));
-    if ((st = bitsmoe_workspace_init(gs.tbad, (size_t)gs.tcap * 2 * 4, stream))) return st;
     launch_group_coef(gs, s);
     err = hipGetLastError();
     if (err != hipSuccess)

@@ -67,11 +67,14 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* buf, uint32
 __global__ __launch_bounds__(kRThreads) void k_route_group(const int32_t* __restrict__ ids,
                                                            int P, int E, int dout,
                                                            float* __restrict__ h,
-                                                           RouteLists rl) {
+                                                           RouteLists rl,
+                                                           uint32_t* __restrict__ zero,
+                                                           int nzero) {
   extern __shared__ uint32_t cnt[];  // E counters, then E cursors
   uint32_t* cur = cnt + E;
   __shared__ uint32_t buf[kRThreads];
   const int tid = threadIdx.x;
+  for (int i = tid; i < nzero; i += kRThreads) zero[i] = 0u;  // the tiles' index flags
   for (int i = tid; i < E; i += kRThreads) cnt[i] = 0;
   __syncthreads();
   for (int p = tid; p < P; p += kRThreads) {
@@ -386,9 +389,9 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
 size_t grouped_lds_bytes() { return sizeof(GroupLds); }
 
 int launch_route_group(const int32_t* ids, int P, int E, int dout, float* h,
-                       const RouteLists& rl, hipStream_t st) {
+                       const RouteLists& rl, hipStream_t st, uint32_t* zero, int nzero) {
   hipLaunchKernelGGL(k_route_group, dim3(1), dim3(kRThreads), (size_t)2 * E * sizeof(uint32_t),
-                     st, ids, P, E, dout, h, rl);
+                     st, ids, P, E, dout, h, rl, zero, nzero);
   return 0;
 }
 

@@ -97,8 +97,10 @@ size_t grouped_lds_bytes();
 // |z| of every 16-row block of the projection per token.
 int launch_proj_maxima(const void* phi, const void* x, float* z, float* zpart, int T, int din,
                        int R, hipStream_t st);
+// also zero-fills zero[0, nzero) (the coefficient tables' flags)
 int launch_route_group(const int32_t* ids, int P, int E, int dout, float* h,
-                       const RouteLists& rl, hipStream_t st);
+                       const RouteLists& rl, hipStream_t st, uint32_t* zero = nullptr,
+                       int nzero = 0);
 int launch_gateup_grouped(const GroupArgs& s, hipStream_t st);
 
 }  // namespace bitsmoe
