@@ -419,9 +419,17 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
                                      4, 0, 0);
   }
   int zt_cached = -1;  // token whose z is in L.Z
+  // pair whose digit tables, scales and offset sums are in LDS: the units
+  // of a work-group (b, b + G, ...) share one pair whenever the grid is a
+  // multiple of the pair count, and then the coefficient pass runs once
+  // (long slot lists, where a work-group has many units)
+  int coef_pair = -1;
   bool zok = true;     // this wave's words of L.Z arrived
   for (; have; u += G, have = u < U) {
     const int pair = u % np;
+    // (the r <= 2048 instantiation keeps its one-unit code unchanged: there
+    // the extra branches cost more than they save)
+    const bool reuse = kFSper > 9 && pair == coef_pair;  // uniform
     const int sg = u / np;
     const int t = pair / a.ktop;
     // kBoth: waves 4-7 form the coefficients of both projections; otherwise
@@ -446,12 +454,14 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         ok1 = PU.ok;
         ns0 = PG.n_slot; nq0 = PG.n_qslot;
         ns1 = PU.n_slot; nq1 = PU.n_qslot;
-        load_meta<kFSper>(PG, lp, md0);
-        load_meta<kFSper>(PU, lp, md1);
+        if (!reuse) {
+          load_meta<kFSper>(PG, lp, md0);
+          load_meta<kFSper>(PU, lp, md1);
+        }
       } else {
         ok0 = PU.ok;
         ns0 = PU.n_slot; nq0 = PU.n_qslot;
-        load_meta<kFSper>(PU, lp, md0);
+        if (!reuse) load_meta<kFSper>(PU, lp, md0);
       }
       const SegProj& SP = (wv & 2) ? PU : PG;
       stage_chunk(&L.W[(wv >> 1) & 1][0], SP, sg, 0, chunk_end(SP, 0, kFMaxW),
@@ -474,7 +484,7 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
         const SegProj PG = uniform_seg(L.desc[0]);
         ok0 = PG.ok;
         ns0 = PG.n_slot; nq0 = PG.n_qslot;
-        load_meta<kFSper>(PG, lp, md0);
+        if (!reuse) load_meta<kFSper>(PG, lp, md0);
       }
     }
     if (t != zt_cached) {
@@ -487,6 +497,8 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
       lds_sync();                  // L.Z complete
       zt_cached = t;
     }
+    SegProj P;  // this wave's projection
+    if (!reuse) {
     // ---- coefficients ----
     // (kBoth: waves 4-7 do projection 0 = gate from md0 and 1 = up from md1;
     // otherwise every wave does its own projection pj from md0).  All the
@@ -562,7 +574,7 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     lds_sync();
     // this wave's projection (wave 4 published the descriptors before any
     // barrier of this unit that came before this one)
-    const SegProj P = uniform_seg(L.desc[pj]);
+    P = uniform_seg(L.desc[pj]);
     {
       float cq[kFSper];
       if (kBoth) {
@@ -619,8 +631,11 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
       corr = wave_sum_dpp(corr);
       if (lane == 0) L.pcorr[pj][wp] = ldexpf(128.f * corr, -S);
     }
+    }  // !reuse
+    coef_pair = pair;
     __builtin_amdgcn_s_waitcnt(0);
     lds_sync();
+    if (reuse) P = uniform_seg(L.desc[pj]);  // published by wave 4 before this barrier
     const int nch = __builtin_amdgcn_readfirstlane(max(L.nch[0], L.nch[1]));  // uniform
     // ---- apply ----
     i32x4 acc_0 = {0, 0, 0, 0}, acc_1 = {0, 0, 0, 0};  // column n: digit n
