@@ -26,8 +26,12 @@
 // both projections (waves 0-3 gate, 4-7 up); unit u = segment * tcap + tile
 // runs on XCD u % 8, so every segment of a tile shares one L2 (and reads the
 // tile's coefficient tables from it).  The segment records are staged in
-// LDS once; each 256-slot chunk of the tile's coefficients is copied into
-// LDS with 16-byte loads.  The apply is the same MFMA K-step loop as the
+// LDS in chunks of at most 7168 words per projection; the tile's
+// coefficients go through LDS in 128-slot chunks, each loaded into
+// registers (16 bytes a lane) while the previous chunk's products run.  The
+// work-group's LDS stays under half of a CU's, so two units share a CU and
+// each one's chain of dependent loads overlaps the other's products.  The
+// apply is the same MFMA K-step loop as the
 // one-launch kernel with up to 16 token columns.  A one-projection mode
 // (the down projection) gives each pair its own z and lets the two wave
 // halves take two segments.
@@ -120,8 +124,8 @@ constexpr int kGWaves = 8;
 constexpr int kGThreads = kGWaves * kWave;  // 512
 constexpr int kGProj = 256;                 // lanes per projection
 constexpr int kGPW = kGWaves / 2;           // waves per projection
-constexpr int kGMaxW = 12288;               // plane words per projection per chunk
-constexpr int kGCS = kGProj;                // slots per coefficient chunk (one per lane)
+constexpr int kGMaxW = 7168;                // plane words per projection per chunk
+constexpr int kGCS = 128;                   // slots per coefficient chunk of the apply
 constexpr int kGCStride = kGCS + 8;         // fp16 per token row (bank spread)
 constexpr int kGZP = 16;                    // lanes per token for the partial maxima
 
@@ -139,7 +143,9 @@ struct __align__(16) GroupLds {
   int pair[kTile];
   uint32_t pok[2][kGPW];
   int nch[2];
+  int ncc[2][2];  // [plane chunk parity][projection]: coefficient chunks
 };
+static_assert(sizeof(GroupLds) <= 80 * 1024, "two work-groups per CU (160 KB of LDS)");
 
 __device__ __forceinline__ void stage_chunk(uint32_t* arena, const SegProj& p, int sg,
                                             uint32_t b0, uint32_t b1, int lp, int lane, int nl) {
@@ -254,6 +260,26 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   uint32_t b1 = chunk_end(P, 0, kGMaxW);
   stage_chunk(&L.W[pj][0], P, sg, 0, b1, lp, lane, kGProj);
 
+  // The tile's coefficients (k_group_coef) pass through registers: lane lp
+  // holds the 16-byte piece 8 (lp % 16) .. + 7 of row lp / 16 of the hi and
+  // lo tables; the next 128-slot chunk is loaded while the products of the
+  // current one run.  Rows past the tile's tokens load the last token's row
+  // (same cache lines) and are not stored.
+  const size_t trow = (size_t)(ti * 2 + (single ? 0 : pj)) * kTile;
+  static_assert(kGProj == kTile * kGCS / 8, "one 16-byte piece per lane");
+  const int cq = lp / (kGCS / 8), c8 = 8 * (lp % (kGCS / 8));
+  const bool cA = cq < nt;
+  const size_t oA = (trow + (size_t)min(cq, nt - 1)) * s.rpad + c8;
+  _Float16* const dA = &L.u.c.hi[pj][0] + cq * kGCStride + c8;
+  _Float16* const dAl = &L.u.c.lo[pj][0] + cq * kGCStride + c8;
+  uint4 chA, clA;
+#define GROUPED_COEF_FETCH(s0)                                             \
+  do {                                                                     \
+    chA = *reinterpret_cast<const uint4*>(s.thi + oA + (s0));             \
+    clA = *reinterpret_cast<const uint4*>(s.tlo + oA + (s0));             \
+  } while (0)
+  GROUPED_COEF_FETCH(0u);
+
   // tokens of the tile and their coefficient scales: lanes (n, j) of the
   // projection take partial maxima j, j + 16, ... of token n
   if (threadIdx.x < (unsigned)nt) L.pair[threadIdx.x] = s.rl.pairs[p0 + threadIdx.x];
@@ -272,51 +298,63 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
     for (int off = kGZP / 2; off > 0; off >>= 1) zm = fmaxf(zm, __shfl_xor(zm, off, kWave));
     if (j == 0 && n < nt) L.S[pj][n] = coef_shift(P.cmax, zm);
   }
+  // Coefficient chunks of kGCS slots (kGCS / 4 blocks, kGCS / 32 K steps)
+  // inside each plane chunk.  The two projections' plane chunks end at
+  // different blocks, so their counts of coefficient chunks may differ; the
+  // barriers are shared, so the work-group runs the larger count (published
+  // through L.ncc, one slot per chunk parity) and a half past its own count
+  // only takes part in the barriers.
+  constexpr uint32_t kCB = kGCS / 4;
+  auto n_coef_chunks = [](uint32_t c0, uint32_t c1) {
+    return max((int)((c1 - c0 + kCB - 1) / kCB), 1);
+  };
   {
     int nc = 0;
     for (uint32_t b = 0; b < P.n_blk; b = chunk_end(P, b, kGMaxW)) ++nc;
-    if (threadIdx.x == (unsigned)(pj * kGProj)) L.nch[pj] = nc;
+    if (threadIdx.x == (unsigned)(pj * kGProj)) {
+      L.nch[pj] = nc;
+      L.ncc[0][pj] = n_coef_chunks(0u, b1);
+    }
   }
+  // the first plane chunk's staged words have landed (waited for here, once,
+  // so that no later LDS read is made to wait for the coefficient loads)
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int nch = __builtin_amdgcn_readfirstlane(max(L.nch[0], L.nch[1]));  // uniform
   bool good = P.ok;
   f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const size_t trow = (size_t)(ti * 2 + (single ? 0 : pj)) * kTile;
   uint32_t b0 = 0;
   for (int ch = 0; ch < max(nch, 1); ++ch) {
     if (ch > 0) {
-      __syncthreads();  // every wave is done with the previous chunk
-      b1 = chunk_end(P, b0, kGMaxW);
+      const uint32_t b1n = chunk_end(P, b0, kGMaxW);
+      if (threadIdx.x == (unsigned)(pj * kGProj)) L.ncc[ch & 1][pj] = n_coef_chunks(b0, b1n);
+      lds_sync();  // every wave is done with the previous chunk; L.ncc is set
+      b1 = b1n;
       stage_chunk(&L.W[pj][0], P, sg, b0, b1, lp, lane, kGProj);
+      __builtin_amdgcn_s_waitcnt(0);  // the staged words have landed
     }
-    // coefficient chunks of 256 slots (64 blocks) inside the plane chunk
     const uint32_t kbe = (b1 + kBlkPerK - 1) / kBlkPerK;
-    const int ncc = max((int)((b1 - b0 + 63u) / 64u), 1);
-    for (int cc = 0; cc < ncc; ++cc) {
-      const uint32_t cb0 = b0 + 64u * cc;
+    const int ncc = n_coef_chunks(b0, b1);  // this half's
+    const int nccw = __builtin_amdgcn_readfirstlane(max(L.ncc[ch & 1][0], L.ncc[ch & 1][1]));
+    for (int cc = 0; cc < nccw; ++cc) {
+      const uint32_t cb0 = b0 + kCB * cc;
       const uint32_t s0 = 4u * cb0;
-      if (cc > 0) __syncthreads();     // the previous coefficient chunk is read
-      // the tile's coefficients of slots s0 .. s0 + 255 (k_group_coef):
-      // 16-byte copies, rows of the present tokens only
-      {
-        const int q = lp >> 5, c = lp & 31;  // 8 lanes groups x 32 16-byte pieces of a row
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const int n = q + 8 * (h & 1);
-          const bool lo_part = h >= 2;
-          if (n < nt) {
-            const _Float16* src = (lo_part ? s.tlo : s.thi) + (trow + n) * s.rpad + s0 + 8 * c;
-            const uint4 v = *reinterpret_cast<const uint4*>(src);
-            _Float16* dst = (lo_part ? &L.u.c.lo[pj][0] : &L.u.c.hi[pj][0]) + n * kGCStride + 8 * c;
-            *reinterpret_cast<uint4*>(dst) = v;
-          }
+      const bool mine = cc < ncc;
+      if (cc > 0) lds_sync();  // the previous coefficient chunk is read
+      if (mine) {
+        if (cA) {
+          *reinterpret_cast<uint4*>(dA) = chA;
+          *reinterpret_cast<uint4*>(dAl) = clA;
         }
+        if (cc + 1 < ncc)
+          GROUPED_COEF_FETCH(s0 + (uint32_t)kGCS);
+        else if (ch + 1 < nch)
+          GROUPED_COEF_FETCH(4u * b1);
       }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      lds_sync();
       const uint32_t kb0 = cb0 / kBlkPerK;
-      const uint32_t kb1 = min(kb0 + 8u, kbe);
-      if (b1 > cb0) {
+      const uint32_t kb1 = min(kb0 + kCB / kBlkPerK, kbe);
+      if (mine && b1 > cb0) {
         const uint32_t* base = &L.W[pj][0] - block_word(P, b0);
         mfma_ksteps(P, base, &L.u.c.hi[pj][0], &L.u.c.lo[pj][0], kGCStride, s0,
                     nt, kb0, kb1, wp, lane, acc0, acc1);
@@ -324,6 +362,7 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
     }
     b0 = b1;
   }
+#undef GROUPED_COEF_FETCH
   __syncthreads();  // coefficient tables are reused as row-sum buffers
   // ---- row sums of the 4 waves per token, SiLU * mul ----
   {
