@@ -98,57 +98,85 @@ __device__ __forceinline__ void pstep(float (&v)[kPRW * kPT], bool up) {
 
 // Batched projection on the matrix cores (T >= 16, din a multiple of 32):
 // z^T = Phi^T x^T as a dense contraction over din.  Work-group (b, c): rows
-// 16 b .. 16 b + 15 of Phi^T and tokens 64 c .. 64 c + 63, one 16 x 16
-// v_mfma_f32_16x16x32_f16 block per wave; both operands are read from
-// global memory in 16-byte pieces (Phi^T rows and x rows are contiguous
-// along din), four K steps in flight.  fp16 products are exact in fp32; the
-// sums are fp32.  zpart gets the largest |z| of the 16 rows per token.
+// 16 b .. 16 b + 15 of Phi^T and tokens 64 c .. 64 c + 63 (four 16-token
+// blocks).  Wave w takes the K steps (32 of din each) k = w, w + 8, ...: it
+// loads the Phi^T piece of a step once and applies it to every token block
+// present with v_mfma_f32_16x16x32_f16, four steps' loads in flight, so the
+// work-group keeps 8 waves' worth of Phi^T reads outstanding.  Both operands
+// are read from global memory in 16-byte pieces (Phi^T rows and x rows are
+// contiguous along din).  The 8 partial sums are added through LDS in wave
+// order.  fp16 products are exact in fp32; the sums are fp32.  zpart gets
+// the largest |z| of the 16 rows per token.
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
-__global__ __launch_bounds__(256) void k_proj_mfma(const uint4* __restrict__ phi_t,
-                                                   const uint4* __restrict__ x,
-                                                   float* __restrict__ z,
-                                                   float* __restrict__ zpart, int T, int din8,
-                                                   int R, int nzp) {
+constexpr int kPMWaves = 8;   // waves of a projection work-group (K split)
+constexpr int kPMBlocks = 4;  // 16-token blocks of a work-group
+
+__device__ __forceinline__ f4v mfma16(const uint4& a, const uint4& b, f4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8v*>(&a),
+                                                *reinterpret_cast<const h8v*>(&b), c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kPMWaves * kWave) void k_proj_mfma(const uint4* __restrict__ phi_t,
+                                                               const uint4* __restrict__ x,
+                                                               float* __restrict__ z,
+                                                               float* __restrict__ zpart, int T,
+                                                               int din8, int R, int nzp) {
+  __shared__ f4v part[kPMWaves][kPMBlocks][kWave];
   const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row0 = (int)blockIdx.x * 16;
-  const int tok0 = ((int)blockIdx.y * 4 + wv) * 16;
-  if (tok0 >= T) return;  // whole wave: nothing below needs the others
+  const int tok0 = (int)blockIdx.y * 16 * kPMBlocks;
+  const int nb = min(kPMBlocks, (T - tok0 + 15) / 16);  // token blocks present (>= 1)
   const int m = lane & 15, kg = lane >> 4;
-  const int ra = min(row0 + m, R - 1), tb = min(tok0 + m, T - 1);
-  const uint4* pa = phi_t + (size_t)ra * din8 + kg;
-  const uint4* pb = x + (size_t)tb * din8 + kg;
-  f4v acc = {0.f, 0.f, 0.f, 0.f};
+  const uint4* pa = phi_t + (size_t)min(row0 + m, R - 1) * din8 + kg;
+  const uint4* pb[kPMBlocks];
+#pragma unroll
+  for (int b = 0; b < kPMBlocks; ++b)
+    pb[b] = x + (size_t)min(tok0 + 16 * b + m, T - 1) * din8 + kg;
+  f4v acc[kPMBlocks];
+#pragma unroll
+  for (int b = 0; b < kPMBlocks; ++b) acc[b] = f4v{0.f, 0.f, 0.f, 0.f};
   const int nk = din8 / 4;  // K steps of 32
-  int k = 0;
-  for (; k + 4 <= nk; k += 4) {
-    uint4 av[4], bv[4];
+  int k = wv;
+  for (; k + 3 * kPMWaves < nk; k += 4 * kPMWaves) {
+    uint4 av[4], bv[4][kPMBlocks];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      av[j] = pa[4 * (k + j)];
-      bv[j] = pb[4 * (k + j)];
+      av[j] = pa[4 * (k + j * kPMWaves)];
+#pragma unroll
+      for (int b = 0; b < kPMBlocks; ++b)
+        if (b < nb) bv[j][b] = pb[b][4 * (k + j * kPMWaves)];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8v*>(&av[j]),
-                                                   *reinterpret_cast<const h8v*>(&bv[j]), acc,
-                                                   0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < kPMBlocks; ++b)
+        if (b < nb) acc[b] = mfma16(av[j], bv[j][b], acc[b]);
   }
-  for (; k < nk; ++k) {
-    const uint4 av = pa[4 * k], bv = pb[4 * k];
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8v*>(&av),
-                                                 *reinterpret_cast<const h8v*>(&bv), acc, 0, 0,
-                                                 0);
+  for (; k < nk; k += kPMWaves) {
+    const uint4 av = pa[4 * k];
+#pragma unroll
+    for (int b = 0; b < kPMBlocks; ++b)
+      if (b < nb) acc[b] = mfma16(av, pb[b][4 * k], acc[b]);
   }
-  // acc[i] = z of row row0 + 4 kg + i, token tok0 + m
-  const int tok = tok0 + m;
+#pragma unroll
+  for (int b = 0; b < kPMBlocks; ++b)
+    if (b < nb) part[wv][b][lane] = acc[b];
+  __syncthreads();
+  // wave b < nb sums block b: s[i] = z of row row0 + 4 kg + i, token
+  // tok0 + 16 b + m
+  if (wv >= nb) return;
+  f4v sum = part[0][wv][lane];
+#pragma unroll
+  for (int w = 1; w < kPMWaves; ++w) sum += part[w][wv][lane];
+  const int tok = tok0 + 16 * wv + m;
   float mx = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = row0 + 4 * kg + i;
-    if (tok < T && row < R) z[(size_t)tok * R + row] = acc[i];
-    mx = fmaxf(mx, row < R ? fabsf(acc[i]) : 0.f);
+    if (tok < T && row < R) z[(size_t)tok * R + row] = sum[i];
+    mx = fmaxf(mx, row < R ? fabsf(sum[i]) : 0.f);
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
   mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
@@ -396,7 +424,8 @@ int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, i
   const int din8 = din / 8;
   if (T >= 16 && din % 32 == 0) {
     const int nzp = (R + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
-    hipLaunchKernelGGL(k_proj_mfma, dim3((unsigned)nzp, (unsigned)((T + 63) / 64)), dim3(256), 0,
+    hipLaunchKernelGGL(k_proj_mfma, dim3((unsigned)nzp, (unsigned)((T + 16 * kPMBlocks - 1) / (16 * kPMBlocks))),
+                       dim3(kPMWaves * kWave), 0,
                        s, (const uint4*)phi, (const uint4*)x, z, zpart, T, din8, R, nzp);
     return launch_status("spectral projection launch");
   }
