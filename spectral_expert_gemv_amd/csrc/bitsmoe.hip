@@ -14,6 +14,7 @@
 #include "device_common.h"
 #include "format.h"
 #include "kernels.h"
+#include "route.h"
 
 namespace bitsmoe {
 namespace {
@@ -106,7 +107,9 @@ __device__ __forceinline__ void pstep(float (&v)[kPRW * kPT], bool up) {
 // are read from global memory in 16-byte pieces (Phi^T rows and x rows are
 // contiguous along din).  The 8 partial sums are added through LDS in wave
 // order.  fp16 products are exact in fp32; the sums are fp32.  zpart gets
-// the largest |z| of the 16 rows per token.
+// the largest |z| of the 16 rows per token.  With a route job, one more
+// column of work-groups is launched and its first one groups the pairs by
+// expert (route.h) while the others project.
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kPMWaves = 8;   // waves of a projection work-group (K split)
@@ -121,8 +124,20 @@ __global__ __launch_bounds__(kPMWaves * kWave) void k_proj_mfma(const uint4* __r
                                                                const uint4* __restrict__ x,
                                                                float* __restrict__ z,
                                                                float* __restrict__ zpart, int T,
-                                                               int din8, int R, int nzp) {
-  __shared__ f4v part[kPMWaves][kPMBlocks][kWave];
+                                                               int din8, int R, int nzp,
+                                                               RouteJob rj) {
+  __shared__ union {
+    f4v part[kPMWaves][kPMBlocks][kWave];
+    struct {
+      uint32_t cnt[2 * kRouteFuseMaxE];
+      uint32_t buf[kPMWaves * kWave];
+    } r;
+  } L;
+  if (rj.ids && (int)blockIdx.x == nzp) {
+    if (blockIdx.y == 0) route_lists<kPMWaves * kWave>(rj, L.r.cnt, L.r.buf);
+    return;
+  }
+  f4v(&part)[kPMWaves][kPMBlocks][kWave] = L.part;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row0 = (int)blockIdx.x * 16;
@@ -418,15 +433,24 @@ int proj_args(const void* phi, const void* x, const float* z, int T, int din, in
 }
 
 // z = Phi^T x; zpart (may be null; din <= 4096 only) gets max |z| per
-// 16-row work-group and token.
+// 16-row work-group and token.  A route job (may be null) runs in the same
+// launch when the projection takes the matrix-core kernel and E <=
+// kRouteFuseMaxE; *routed tells whether it did.
 int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, int din, int R,
-                hipStream_t s) {
+                hipStream_t s, const RouteJob* route = nullptr, bool* routed = nullptr) {
   const int din8 = din / 8;
+  if (routed) *routed = false;
   if (T >= 16 && din % 32 == 0) {
     const int nzp = (R + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
-    hipLaunchKernelGGL(k_proj_mfma, dim3((unsigned)nzp, (unsigned)((T + 16 * kPMBlocks - 1) / (16 * kPMBlocks))),
-                       dim3(kPMWaves * kWave), 0,
-                       s, (const uint4*)phi, (const uint4*)x, z, zpart, T, din8, R, nzp);
+    RouteJob rj{};
+    const bool fuse = route && route->E <= kRouteFuseMaxE;
+    if (fuse) rj = *route;
+    hipLaunchKernelGGL(k_proj_mfma,
+                       dim3((unsigned)(nzp + (fuse ? 1 : 0)),
+                            (unsigned)((T + 16 * kPMBlocks - 1) / (16 * kPMBlocks))),
+                       dim3(kPMWaves * kWave), 0, s, (const uint4*)phi, (const uint4*)x, z, zpart,
+                       T, din8, R, nzp, rj);
+    if (routed) *routed = fuse;
     return launch_status("spectral projection launch");
   }
   const dim3 grid_rows((R + kProjWaves * kPRW - 1) / (kProjWaves * kPRW));
@@ -598,8 +622,9 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   }
   const bool grouped = r <= kGroupMaxR && E <= kGroupMaxE && din <= kGroupMaxDin;
   float* zpart = grouped ? (float*)(wsb + plan.zpart_off) : nullptr;
-  if ((st = launch_proj(phi_t_gateup_f16, x_f16, z, zpart, T, din, 2 * r, s))) return st;
-  if (grouped) {
+  if (!grouped) {
+    if ((st = launch_proj(phi_t_gateup_f16, x_f16, z, zpart, T, din, 2 * r, s))) return st;
+  } else {
     // batched tokens: pairs grouped by expert, each expert's planes read and
     // unpacked once per tile of up to 16 tokens
     GroupArgs gs;
@@ -614,8 +639,14 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     gs.rl.tile = rb + 1;
     gs.rl.pairs = rb + 1 + 3 * gs.tcap;
     group_coef_tables(gs, wsb + plan.coef_off, r);
-    launch_route_group(ids, T * k, E, dout, h, gs.rl, s, gs.tbad, gs.tcap * 2);
-    if ((st = launch_status("route grouping launch"))) return st;
+    const RouteJob rj{ids, T * k, E, dout, h, gs.rl, gs.tbad, gs.tcap * 2};
+    bool routed = false;
+    if ((st = launch_proj(phi_t_gateup_f16, x_f16, z, zpart, T, din, 2 * r, s, &rj, &routed)))
+      return st;
+    if (!routed) {
+      launch_route_group(ids, T * k, E, dout, h, gs.rl, s, gs.tbad, gs.tcap * 2);
+      if ((st = launch_status("route grouping launch"))) return st;
+    }
     launch_group_coef(gs, s);
     if ((st = launch_status("tile coefficient launch"))) return st;
     launch_gateup_grouped(gs, s);

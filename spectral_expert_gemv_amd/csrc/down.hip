@@ -24,13 +24,24 @@
 #include "common.h"
 #include "format.h"
 #include "kernels.h"
+#include "route.h"
 
 namespace bitsmoe {
 namespace {
 
+// With a route job, the last work-group groups the pairs by expert
+// (route.h) instead of converting.
 __global__ __launch_bounds__(256) void k_h_to_f16(const float* __restrict__ h,
-                                                  __half* __restrict__ h16, size_t n) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
+                                                  __half* __restrict__ h16, size_t n,
+                                                  RouteJob rj) {
+  __shared__ uint32_t cnt[2 * kRouteFuseMaxE];
+  __shared__ uint32_t buf[256];
+  const unsigned nconv = gridDim.x - (rj.ids ? 1u : 0u);
+  if (blockIdx.x >= nconv) {
+    route_lists<256>(rj, cnt, buf);
+    return;
+  }
+  const size_t stride = (size_t)nconv * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
     h16[i] = __float2half_rn(h[i]);
 }
@@ -111,33 +122,19 @@ int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi
   const hipStream_t s = (hipStream_t)stream;
   uint8_t* w8 = (uint8_t*)ws;
   const size_t n = (size_t)T * k * dout;
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_h_to_f16, dim3((unsigned)blocks), dim3(256), 0, s, h,
-                     (__half*)(w8 + w.h16), n);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return fail(BITSMOE_EHIP, "fp16 cast launch: %s", hipGetErrorString(err));
   float* z = (float*)(w8 + w.z);
   float* y = (float*)(w8 + w.y);
   const bool grouped = r_d <= kGroupMaxR && E <= kGroupMaxE && dout <= kGroupMaxDin;
-  if (!grouped) {
-    if ((st = bitsmoe_spectral_proj(phi_t_down_f16, w8 + w.h16, z, T * k, dout, r_d, stream)))
-      return st;
-    if ((st = bitsmoe_expert_apply(packed_down, down_bytes, E, din, r_d, z, r_d, ids, T * k, 1,
-                                   y, nullptr, 0, stream)))
-      return st;
-  } else {
-    if (((uintptr_t)packed_down & 15u) || ((uintptr_t)phi_t_down_f16 & 15u))
-      return fail(BITSMOE_EINVAL, "packed_down and phi_t_down_f16 must be 16-byte aligned");
-    if (down_bytes < kHeaderBytes + (size_t)kDirRecBytes * E)
-      return fail(BITSMOE_ENOSPC, "packed_down: %zu bytes cannot hold header and directory",
-                  down_bytes);
-    // z and, per 16-row block of the projection, the largest |z| the grouped
-    // kernel scales its coefficients by
-    float* zpart = (float*)(w8 + w.zpart);
-    if ((st = launch_proj_maxima(phi_t_down_f16, w8 + w.h16, z, zpart, T * k, dout, r_d, s)))
-      return st;
-    GroupArgs gs;
+  if (grouped && (((uintptr_t)packed_down & 15u) || ((uintptr_t)phi_t_down_f16 & 15u)))
+    return fail(BITSMOE_EINVAL, "packed_down and phi_t_down_f16 must be 16-byte aligned");
+  if (grouped && down_bytes < kHeaderBytes + (size_t)kDirRecBytes * E)
+    return fail(BITSMOE_ENOSPC, "packed_down: %zu bytes cannot hold header and directory",
+                down_bytes);
+  // the grouped path's pair lists: grouped in the cast launch when E is small
+  GroupArgs gs;
+  RouteJob rj{};
+  float* const zpart = (float*)(w8 + w.zpart);
+  if (grouped) {
     gs.g.blob_g = gs.g.blob_u = (const uint8_t*)packed_down;
     gs.g.bytes_g = gs.g.bytes_u = (uint64_t)down_bytes;
     gs.g.E = E;
@@ -158,10 +155,31 @@ int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi
     gs.rl.tile = rb + 1;
     gs.rl.pairs = rb + 1 + 3 * gs.tcap;
     group_coef_tables(gs, w8 + w.coef, r_d);
-    launch_route_group(ids, T * k, E, din, y, gs.rl, s, gs.tbad, gs.tcap * 2);
-    err = hipGetLastError();
-    if (err != hipSuccess)
-      return fail(BITSMOE_EHIP, "route grouping launch: %s", hipGetErrorString(err));
+    if (E <= kRouteFuseMaxE) rj = RouteJob{ids, T * k, E, din, y, gs.rl, gs.tbad, gs.tcap * 2};
+  }
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_h_to_f16, dim3((unsigned)blocks + (rj.ids ? 1u : 0u)), dim3(256), 0, s, h,
+                     (__half*)(w8 + w.h16), n, rj);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return fail(BITSMOE_EHIP, "fp16 cast launch: %s", hipGetErrorString(err));
+  if (!grouped) {
+    if ((st = bitsmoe_spectral_proj(phi_t_down_f16, w8 + w.h16, z, T * k, dout, r_d, stream)))
+      return st;
+    if ((st = bitsmoe_expert_apply(packed_down, down_bytes, E, din, r_d, z, r_d, ids, T * k, 1,
+                                   y, nullptr, 0, stream)))
+      return st;
+  } else {
+    // z and, per 16-row block of the projection, the largest |z| the grouped
+    // kernel scales its coefficients by
+    if ((st = launch_proj_maxima(phi_t_down_f16, w8 + w.h16, z, zpart, T * k, dout, r_d, s)))
+      return st;
+    if (!rj.ids) {
+      launch_route_group(ids, T * k, E, din, y, gs.rl, s, gs.tbad, gs.tcap * 2);
+      err = hipGetLastError();
+      if (err != hipSuccess)
+        return fail(BITSMOE_EHIP, "route grouping launch: %s", hipGetErrorString(err));
+    }
     launch_group_coef(gs, s);
     err = hipGetLastError();
     if (err != hipSuccess)

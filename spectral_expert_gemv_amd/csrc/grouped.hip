@@ -9,11 +9,9 @@
 // from HBM and unpacked once per tile of up to 16 routed tokens instead of
 // once per token, and the tokens become the N columns of the MFMA.
 //
-// k_route_group (one work-group): counting sort of the T*k pairs by expert
-// id -- LDS histogram, block scan, scatter -- into per-expert pair lists
-// (experts ascending; the order of pairs inside a list does not affect any
-// result), cut into tiles of at most 16 pairs.  Pairs whose id lies outside
-// [0, E) get NaN rows.
+// k_route_group (one work-group): the counting sort of the T*k pairs by
+// expert id into tiles of at most 16 pairs (route.h), for expert counts
+// beyond what the work-group added to the projection launch handles.
 //
 // k_group_coef: the coefficients of every tile, once per tile instead of
 // once per row segment: c = a s z_t[k] (a z for 16-bit slots) of each of the
@@ -41,6 +39,7 @@
 #include "device_common.h"
 #include "format.h"
 #include "kernels.h"
+#include "route.h"
 #include "seg_common.h"
 
 namespace bitsmoe {
@@ -51,72 +50,10 @@ using namespace seg;
 // ------------------------------------------------------------ route groups
 constexpr int kRThreads = 1024;
 
-// Exclusive block scan of one value per thread; total gets the sum.
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* buf, uint32_t& total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int d = 1; d < kRThreads; d <<= 1) {
-    const uint32_t a = tid >= d ? buf[tid - d] : 0u;
-    __syncthreads();
-    buf[tid] += a;
-    __syncthreads();
-  }
-  total = buf[kRThreads - 1];
-  const uint32_t incl = buf[tid];
-  __syncthreads();
-  return incl - v;
-}
-
-__global__ __launch_bounds__(kRThreads) void k_route_group(const int32_t* __restrict__ ids,
-                                                           int P, int E, int dout,
-                                                           float* __restrict__ h,
-                                                           RouteLists rl,
-                                                           uint32_t* __restrict__ zero,
-                                                           int nzero) {
+__global__ __launch_bounds__(kRThreads) void k_route_group(RouteJob j) {
   extern __shared__ uint32_t cnt[];  // E counters, then E cursors
-  uint32_t* cur = cnt + E;
   __shared__ uint32_t buf[kRThreads];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < nzero; i += kRThreads) zero[i] = 0u;  // the tiles' index flags
-  for (int i = tid; i < E; i += kRThreads) cnt[i] = 0;
-  __syncthreads();
-  for (int p = tid; p < P; p += kRThreads) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1u);
-  }
-  __syncthreads();
-  // each thread owns a contiguous run of experts
-  const int per = (E + kRThreads - 1) / kRThreads;
-  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-  uint32_t sum = 0, nt = 0;
-  for (int e = e0; e < e1; ++e) {
-    sum += cnt[e];
-    nt += (cnt[e] + kTile - 1) / kTile;
-  }
-  uint32_t total_pairs, total_tiles;
-  uint32_t off = block_scan(sum, buf, total_pairs);
-  uint32_t ti = block_scan(nt, buf, total_tiles);
-  for (int e = e0; e < e1; ++e) {
-    const uint32_t c = cnt[e];
-    cur[e] = off;
-    for (uint32_t i = 0; i < c; i += kTile, ++ti) {
-      rl.tile[3 * ti] = e;
-      rl.tile[3 * ti + 1] = (int)(off + i);
-      rl.tile[3 * ti + 2] = (int)min((uint32_t)kTile, c - i);
-    }
-    off += c;
-  }
-  if (tid == 0) rl.ntiles[0] = (int)total_tiles;
-  __syncthreads();
-  for (int p = tid; p < P; p += kRThreads) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) {
-      rl.pairs[atomicAdd(&cur[e], 1u)] = p;
-    } else {
-      for (int i = 0; i < dout; ++i) h[(size_t)p * dout + i] = __builtin_nanf("");
-    }
-  }
+  route_lists<kRThreads>(j, cnt, buf);
 }
 
 // ------------------------------------------------------- grouped gate/up
@@ -429,8 +366,9 @@ size_t grouped_lds_bytes() { return sizeof(GroupLds); }
 
 int launch_route_group(const int32_t* ids, int P, int E, int dout, float* h,
                        const RouteLists& rl, hipStream_t st, uint32_t* zero, int nzero) {
+  const RouteJob j{ids, P, E, dout, h, rl, zero, nzero};
   hipLaunchKernelGGL(k_route_group, dim3(1), dim3(kRThreads), (size_t)2 * E * sizeof(uint32_t),
-                     st, ids, P, E, dout, h, rl, zero, nzero);
+                     st, j);
   return 0;
 }
 

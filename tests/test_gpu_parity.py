@@ -225,11 +225,14 @@ def test_edges_zero_expert_k1_duplicates(bm, T):
     _check_h(got, pairs_ref(Lz, x, ids))
 
 
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("T", [4, 8, 16])
 def test_bad_expert_id_and_blob_mismatch_give_nan(bm, T):
+    # T = 4: one launch; T = 8: separate route launch; T = 16: the route
+    # work-group inside the matrix-core projection launch
     L, dev = device_layer("tiny")
     spec = L.spec
-    x, ids = synth.make_batch(synth.workload("tiny_t8"), L)
+    wl = synth.workload("tiny_t8" if T <= 8 else "tiny_t64")
+    x, ids = synth.make_batch(wl, L)
     x, ids = x[:T], ids[:T].copy()
     ids[3, 1] = spec.E          # out of range
     ids[T - 3, 0] = -1
@@ -243,7 +246,8 @@ def test_bad_expert_id_and_blob_mismatch_give_nan(bm, T):
     dout_call = spec.dout - 1
     h = torch.zeros((T, k, dout_call), dtype=torch.float32, device="cuda")
     ws = dev.workspace(T, k)
-    good_ids = _cuda(synth.make_batch(synth.workload("tiny_t8"), L)[1][:T])
+    good_ids = _cuda(synth.make_batch(wl, L)[1][:T])
+    assert good_ids.shape == (T, k)
     bm._check(bm._lib.bitsmoe_moe_gateup(
         dev.blob_gate.data_ptr(), dev.blob_gate.numel(), dev.blob_up.data_ptr(),
         dev.blob_up.numel(), dev.phi_t.data_ptr(), _cuda(x).data_ptr(),
