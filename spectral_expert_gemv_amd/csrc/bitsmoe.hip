@@ -198,12 +198,32 @@ __global__ __launch_bounds__(kPMWaves * kWave) void k_proj_mfma(const uint4* __r
   if (zpart && kg == 0 && tok < T) zpart[(size_t)tok * nzp + blockIdx.x] = mx;
 }
 
-template <int U>
+// F32: x holds float32 values, rounded to fp16 (to nearest even) while they
+// are staged, so z is the projection of fp16(x) exactly as with an fp16 x.
+// With a route job, the last work-group groups the pairs by expert
+// (route.h) instead of projecting.
+template <int U, bool F32>
 __global__ __launch_bounds__(kProjWaves * kWave) void k_proj_rows(
-    const uint4* __restrict__ phi_t, const uint4* __restrict__ x, float* __restrict__ z,
-    float* __restrict__ zpart, int T, int din8, int R) {
-  __shared__ __align__(16) uint4 xs[kPT][kPMaxU * kWave];
+    const uint4* __restrict__ phi_t, const void* __restrict__ xin, float* __restrict__ z,
+    float* __restrict__ zpart, int T, int din8, int R, RouteJob rj) {
+  __shared__ union {
+    uint4 xs[kPT][kPMaxU * kWave];
+    struct {
+      uint32_t cnt[2 * kRouteFuseMaxE];
+      uint32_t buf[kProjWaves * kWave];
+    } r;
+  } L;
   __shared__ float wmx[kProjWaves][kPT];
+  // projection work-groups: the row stride of zpart (the route work-group,
+  // if any, is the last one and writes no maxima)
+  const unsigned nproj = gridDim.x - (rj.ids ? 1u : 0u);
+  if (blockIdx.x >= nproj) {
+    route_lists<kProjWaves * kWave>(rj, L.r.cnt, L.r.buf);
+    return;
+  }
+  uint4(&xs)[kPT][kPMaxU * kWave] = L.xs;
+  const uint4* __restrict__ x = static_cast<const uint4*>(xin);
+  const float* __restrict__ xf = static_cast<const float*>(xin);
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * kProjWaves + wv) * kPRW;
@@ -220,11 +240,32 @@ __global__ __launch_bounds__(kProjWaves * kWave) void k_proj_rows(
   for (int t0 = 0; t0 < T; t0 += kPT) {
     __syncthreads();  // the previous batch has been read
     for (int tt = 0; tt < kPT && t0 + tt < T; ++tt) {
-      const uint4* src = x + (size_t)(t0 + tt) * din8;
-      uint8_t* dst = reinterpret_cast<uint8_t*>(&xs[tt][0]);
-      for (int i = threadIdx.x; i < din8; i += kProjWaves * kWave)
-        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + i),
-                                         (lds_void_t*)(dst + 16 * (size_t)(i - lane)), 16, 0, 0);
+      if constexpr (F32) {
+        const float4* src = reinterpret_cast<const float4*>(xf + (size_t)(t0 + tt) * din8 * 8);
+        for (int i = threadIdx.x; i < din8; i += kProjWaves * kWave) {
+          const float4 a = src[2 * i], b = src[2 * i + 1];
+          union {
+            _Float16 h[8];
+            uint4 u;
+          } c;
+          c.h[0] = (_Float16)a.x;
+          c.h[1] = (_Float16)a.y;
+          c.h[2] = (_Float16)a.z;
+          c.h[3] = (_Float16)a.w;
+          c.h[4] = (_Float16)b.x;
+          c.h[5] = (_Float16)b.y;
+          c.h[6] = (_Float16)b.z;
+          c.h[7] = (_Float16)b.w;
+          xs[tt][i] = c.u;
+        }
+      } else {
+        const uint4* src = x + (size_t)(t0 + tt) * din8;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(&xs[tt][0]);
+        for (int i = threadIdx.x; i < din8; i += kProjWaves * kWave)
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + i),
+                                           (lds_void_t*)(dst + 16 * (size_t)(i - lane)), 16, 0,
+                                           0);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -262,7 +303,7 @@ __global__ __launch_bounds__(kProjWaves * kWave) void k_proj_rows(
       const int tt = threadIdx.x;
       if (tt < kPT && t0 + tt < T) {
         const float mm = fmaxf(fmaxf(wmx[0][tt], wmx[1][tt]), fmaxf(wmx[2][tt], wmx[3][tt]));
-        zpart[(size_t)(t0 + tt) * gridDim.x + blockIdx.x] = mm;
+        zpart[(size_t)(t0 + tt) * nproj + blockIdx.x] = mm;
       }
     }
   }
@@ -437,9 +478,12 @@ int proj_args(const void* phi, const void* x, const float* z, int T, int din, in
 // launch when the projection takes the matrix-core kernel and E <=
 // kRouteFuseMaxE; *routed tells whether it did.
 int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, int din, int R,
-                hipStream_t s, const RouteJob* route = nullptr, bool* routed = nullptr) {
+                hipStream_t s, const RouteJob* route = nullptr, bool* routed = nullptr,
+                bool x_f32 = false) {
   const int din8 = din / 8;
   if (routed) *routed = false;
+  if (x_f32 && ((T >= 16 && din % 32 == 0) || din8 > kPMaxU * kWave || ((uintptr_t)x & 15u)))
+    return fail(BITSMOE_EINVAL, "float32 x needs T < 16 or din %% 32 != 0, din <= 4096, 16-byte x");
   if (T >= 16 && din % 32 == 0) {
     const int nzp = (R + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
     RouteJob rj{};
@@ -453,19 +497,28 @@ int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, i
     if (routed) *routed = fuse;
     return launch_status("spectral projection launch");
   }
-  const dim3 grid_rows((R + kProjWaves * kPRW - 1) / (kProjWaves * kPRW));
-  const dim3 block(kProjWaves * kWave);
   const uint4* p4 = (const uint4*)phi;
   const uint4* x4 = (const uint4*)x;
-  if (din8 <= kWave)
-    hipLaunchKernelGGL(k_proj_rows<1>, grid_rows, block, 0, s, p4, x4, z, zpart, T, din8, R);
-  else if (din8 <= 2 * kWave)
-    hipLaunchKernelGGL(k_proj_rows<2>, grid_rows, block, 0, s, p4, x4, z, zpart, T, din8, R);
-  else if (din8 <= 4 * kWave)
-    hipLaunchKernelGGL(k_proj_rows<4>, grid_rows, block, 0, s, p4, x4, z, zpart, T, din8, R);
-  else if (din8 <= kPMaxU * kWave)
-    hipLaunchKernelGGL(k_proj_rows<8>, grid_rows, block, 0, s, p4, x4, z, zpart, T, din8, R);
-  else
+  const dim3 block(kProjWaves * kWave);
+  if (din8 <= kPMaxU * kWave) {
+    RouteJob rj{};
+    const bool fuse = route && route->E <= kRouteFuseMaxE;
+    if (fuse) rj = *route;
+    const dim3 grid((R + kProjWaves * kPRW - 1) / (kProjWaves * kPRW) + (fuse ? 1 : 0));
+#define PROJ_ROWS(U)                                                                         \
+  hipLaunchKernelGGL((x_f32 ? k_proj_rows<U, true> : k_proj_rows<U, false>), grid, block, 0, s, \
+                     p4, x, z, zpart, T, din8, R, rj)
+    if (din8 <= kWave)
+      PROJ_ROWS(1);
+    else if (din8 <= 2 * kWave)
+      PROJ_ROWS(2);
+    else if (din8 <= 4 * kWave)
+      PROJ_ROWS(4);
+    else
+      PROJ_ROWS(8);
+#undef PROJ_ROWS
+    if (routed) *routed = fuse;
+  } else
     hipLaunchKernelGGL(k_proj_gemv, dim3((R + kProjWaves - 1) / kProjWaves), block, 0, s, p4,
                        x4, z, T, din8, R);
   return launch_status("spectral projection launch");
@@ -475,8 +528,8 @@ int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, i
 }  // namespace
 
 int launch_proj_maxima(const void* phi, const void* x, float* z, float* zpart, int T, int din,
-                       int R, hipStream_t st) {
-  return launch_proj(phi, x, z, zpart, T, din, R, st);
+                       int R, hipStream_t st, const RouteJob* route, bool* routed, bool x_f32) {
+  return launch_proj(phi, x, z, zpart, T, din, R, st, route, routed, x_f32);
 }
 
 // Per-tile coefficient tables: hi and lo rows (with 256 slots of slack for

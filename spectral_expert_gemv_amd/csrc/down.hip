@@ -157,12 +157,20 @@ int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi
     group_coef_tables(gs, w8 + w.coef, r_d);
     if (E <= kRouteFuseMaxE) rj = RouteJob{ids, T * k, E, din, y, gs.rl, gs.tbad, gs.tcap * 2};
   }
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_h_to_f16, dim3((unsigned)blocks + (rj.ids ? 1u : 0u)), dim3(256), 0, s, h,
-                     (__half*)(w8 + w.h16), n, rj);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return fail(BITSMOE_EHIP, "fp16 cast launch: %s", hipGetErrorString(err));
+  // few pairs: the row projection reads float32 h itself (rounding to fp16
+  // as it stages), so no cast launch
+  const bool direct = grouped && !((long long)T * k >= 16 && dout % 32 == 0) && dout <= 4096 &&
+                      ((uintptr_t)h & 15u) == 0;
+  hipError_t err = hipSuccess;
+  if (!direct) {
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_h_to_f16, dim3((unsigned)blocks + (rj.ids ? 1u : 0u)), dim3(256), 0, s,
+                       h, (__half*)(w8 + w.h16), n, rj);
+    err = hipGetLastError();
+    if (err != hipSuccess)
+      return fail(BITSMOE_EHIP, "fp16 cast launch: %s", hipGetErrorString(err));
+  }
   if (!grouped) {
     if ((st = bitsmoe_spectral_proj(phi_t_down_f16, w8 + w.h16, z, T * k, dout, r_d, stream)))
       return st;
@@ -172,9 +180,17 @@ int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi
   } else {
     // z and, per 16-row block of the projection, the largest |z| the grouped
     // kernel scales its coefficients by
-    if ((st = launch_proj_maxima(phi_t_down_f16, w8 + w.h16, z, zpart, T * k, dout, r_d, s)))
+    bool routed = rj.ids != nullptr;  // done by the cast launch
+    if (direct) {
+      const RouteJob rjd{ids, T * k, E, din, y, gs.rl, gs.tbad, gs.tcap * 2};
+      if ((st = launch_proj_maxima(phi_t_down_f16, h, z, zpart, T * k, dout, r_d, s, &rjd,
+                                   &routed, true)))
+        return st;
+    } else if ((st = launch_proj_maxima(phi_t_down_f16, w8 + w.h16, z, zpart, T * k, dout, r_d,
+                                        s))) {
       return st;
-    if (!rj.ids) {
+    }
+    if (!routed) {
       launch_route_group(ids, T * k, E, din, y, gs.rl, s, gs.tbad, gs.tcap * 2);
       err = hipGetLastError();
       if (err != hipSuccess)

@@ -94,9 +94,15 @@ size_t group_coef_bytes(int tcap, int r);                // workspace of the tab
 void group_coef_tables(GroupArgs& gs, uint8_t* base, int r);  // sets thi .. nck (needs tcap)
 size_t grouped_lds_bytes();
 // z = Phi^T x and, when zpart is not null (din <= kGroupMaxDin), the largest
-// |z| of every 16-row block of the projection per token.
+// |z| of every 16-row block of the projection per token.  A route job (may
+// be null) runs inside the launch when the kernel taken can host it (E <=
+// kRouteFuseMaxE); *routed tells whether it did.  x_f32: x is float32,
+// rounded to fp16 as it is staged (T < 16 or din % 32 != 0, din <= 4096,
+// x 16-byte aligned; otherwise an error).
+struct RouteJob;
 int launch_proj_maxima(const void* phi, const void* x, float* z, float* zpart, int T, int din,
-                       int R, hipStream_t st);
+                       int R, hipStream_t st, const RouteJob* route = nullptr,
+                       bool* routed = nullptr, bool x_f32 = false);
 // also zero-fills zero[0, nzero) (the coefficient tables' flags)
 int launch_route_group(const int32_t* ids, int P, int E, int dout, float* h,
                        const RouteLists& rl, hipStream_t st, uint32_t* zero = nullptr,

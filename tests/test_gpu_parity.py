@@ -227,8 +227,8 @@ def test_edges_zero_expert_k1_duplicates(bm, T):
 
 @pytest.mark.parametrize("T", [4, 8, 16])
 def test_bad_expert_id_and_blob_mismatch_give_nan(bm, T):
-    # T = 4: one launch; T = 8: separate route launch; T = 16: the route
-    # work-group inside the matrix-core projection launch
+    # T = 4: one launch; T = 8 and 16: the route work-group inside the row
+    # and the matrix-core projection launch
     L, dev = device_layer("tiny")
     spec = L.spec
     wl = synth.workload("tiny_t8" if T <= 8 else "tiny_t64")
@@ -255,3 +255,24 @@ def test_bad_expert_id_and_blob_mismatch_give_nan(bm, T):
         ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     assert torch.isnan(h).all()
+
+
+@pytest.mark.parametrize("T", [8, 16])
+def test_many_experts_separate_route_launch(bm, T):
+    # more than 1024 experts: the pairs are grouped by their own launch (the
+    # projection launches host the route work-group up to 1024 experts);
+    # T = 8 follows the row projection, T = 16 the matrix-core one
+    from spectral_expert_gemv_amd import DeviceLayer
+    from synth.configs import LayerSpec, Workload
+    spec = LayerSpec("many_experts", E=1040, din=64, dout=32, r=32, k=2, decay=0.5,
+                     ln_sigma=0.3, bits="uniform", outlier_frac=0.0, outlier_scale=1.0,
+                     phi_fp16=False)
+    L = synth.make_layer(spec, cache=False)
+    dev = DeviceLayer.from_synth(L)
+    x, ids = synth.make_batch(Workload("many_experts_t16", spec, 16, ("uniform",)), L)
+    x, ids = x[:T], ids[:T].copy()
+    ids[1, 0] = spec.E + 5          # out of range
+    got = _run_gateup(dev, x, ids)
+    assert np.all(np.isnan(got[1, 0]))
+    ok = [(t, s) for t in range(T) for s in range(2) if (t, s) != (1, 0)]
+    _check_h(got, pairs_ref(L, x, ids, pairs=ok))
