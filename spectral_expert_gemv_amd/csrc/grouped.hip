@@ -146,14 +146,21 @@ __global__ __launch_bounds__(256) void k_group_coef(GroupArgs s) {
   const float sv = (live && isq) ? __half2float(__ushort_as_half(P.S[sl])) : 1.f;
   const float mv = (live && isq) ? __half2float(__ushort_as_half(P.M[sl])) : 0.f;
   const size_t row0 = (size_t)(ti * 2 + pj) * kTile;
-  for (int n = 0; n < nt; ++n) {
-    const float az = av * (live ? s.z[zoff[n] + k] : 0.f);
-    _Float16 hi, lo;
-    split_coef(az * sv, S[n], hi, lo);
-    s.thi[(row0 + n) * s.rpad + sl] = hi;
-    s.tlo[(row0 + n) * s.rpad + sl] = lo;
-    const float bw = wave_sum(az * mv);
-    if (lane == 0) bred[wv][n] = bw;
+  // the tile's z values of this slot, all loaded before any is used
+  float zv[kTile];
+#pragma unroll
+  for (int n = 0; n < kTile; ++n) zv[n] = (live && n < nt) ? s.z[zoff[n] + k] : 0.f;
+#pragma unroll
+  for (int n = 0; n < kTile; ++n) {
+    if (n < nt) {  // uniform
+      const float az = av * zv[n];
+      _Float16 hi, lo;
+      split_coef(az * sv, S[n], hi, lo);
+      s.thi[(row0 + n) * s.rpad + sl] = hi;
+      s.tlo[(row0 + n) * s.rpad + sl] = lo;
+      const float bw = wave_sum(az * mv);
+      if (lane == 0) bred[wv][n] = bw;
+    }
   }
   const bool wok = __all(good);
   if (lane == 0) bad[wv] = wok ? 0u : 1u;
