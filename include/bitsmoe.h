@@ -34,8 +34,10 @@
  *   - Device-side faults the host cannot see (a blob whose header does not
  *     match the dimensions passed, an expert id outside [0, E)) never cause
  *     an out-of-bounds access: the affected output rows are written as NaN.
- *   - Stateless and re-entrant; calls that share a workspace must not
- *     overlap in time.
+ *   - The library keeps no state between calls except what the caller's
+ *     workspace holds (bitsmoe_moe_gateup keeps a launch counter there) and
+ *     the test hook's wait limit; entry points are re-entrant, and calls that
+ *     share a workspace must not overlap in time.
  */
 #ifndef BITSMOE_H
 #define BITSMOE_H
@@ -202,9 +204,10 @@ int bitsmoe_expert_apply(const void* packed, size_t packed_bytes, int E, int dou
  *   ws    : device workspace of at least bitsmoe_moe_gateup_workspace_size()
  *           bytes, zero-filled once before its first use
  *           (bitsmoe_workspace_init).  The one-launch path (T <= 4) keeps a
- *           launch counter and cumulative hint counters in it from call to
- *           call, so a workspace serves one stream: calls that share it must
- *           not run concurrently.
+ *           launch counter and cumulative hint counters in its first 8448
+ *           bytes from call to call (at that fixed place whatever T is, so
+ *           one workspace, sized for the largest T, may serve calls of any T
+ *           in turn); calls that share a workspace must not run concurrently.
  */
 int bitsmoe_moe_gateup_workspace_size(int T, int k, int E, int din, int dout, int r,
                                       size_t* bytes);
@@ -263,6 +266,14 @@ int bitsmoe_ssd(const float* W, int E, int dout, int din, int r, float* phi, flo
 int bitsmoe_workspace_init(void* ws, size_t ws_bytes, bitsmoe_stream_t stream);
 
 /* ---------------------------------------------------------------- testing
+ * bitsmoe_debug_set_wait_limit: sets the bound on the one-launch gate/up
+ * kernel's waits for z produced by its other work-groups (default 2^20
+ * re-reads; 0 gives up at once, so every row of the launch becomes NaN and
+ * every work-group still exits) and returns the previous bound.  Process-wide;
+ * for tests of the give-up path. */
+uint32_t bitsmoe_debug_set_wait_limit(uint32_t spins);
+
+/*
  * Codes of expert e as the device unpack routine decodes them, in k order:
  * codes[k*dout + i] = q (1..8-bit columns), the fp16 bit pattern (16-bit
  * columns), 0 (0-bit columns).  codes: device buffer of r*dout uint16. */

@@ -57,6 +57,7 @@ _SIGS = {
                             _vp, _vp, _sz, _vp], _i),
     "bitsmoe_workspace_init": ([_vp, _sz, _vp], _i),
     "bitsmoe_dump_codes": ([_vp, _sz, _i, _i, _i, _i, _vp, _vp], _i),
+    "bitsmoe_debug_set_wait_limit": ([ctypes.c_uint32], ctypes.c_uint32),
     "bitsmoe_pack_device_workspace_size": ([_i, _i, _i, _vp, _psz], _i),
     "bitsmoe_pack_device": ([_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp], _i),
     "bitsmoe_fqcm_distortion": ([_vp, _i, _i, _i, _vp, _vp], _i),
@@ -183,6 +184,12 @@ def moe_gateup(packed_gate, packed_up, phi_t_gateup, x, ids, E, dout, r, h, ws, 
 
 def workspace_init(ws, stream=None):
     _check(_lib.bitsmoe_workspace_init(_ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def debug_set_wait_limit(spins):
+    """Sets the bound on the one-launch gate/up kernel's waits for z (0: give
+    up at once, every row NaN); returns the previous bound.  Test hook."""
+    return int(_lib.bitsmoe_debug_set_wait_limit(int(spins)))
 
 
 def dump_codes(packed, E, dout, r, e, codes, stream=None):

@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "bitsmoe.h"
 #include "common.h"
 #include "device_common.h"
@@ -18,6 +20,10 @@
 
 namespace bitsmoe {
 namespace {
+
+// Bound on the waits of the one-launch kernels (polls of the hint counters
+// and re-reads of stale z words); a test hook can lower it.
+std::atomic<uint32_t> g_wait_limit{kSpinDefault};
 
 // ---------------------------------------------------------------------------
 // Shared projection for din > 4096: one wave per basis vector n.  Lanes
@@ -564,11 +570,11 @@ GateUpPlan gateup_plan(int T, int k, int E, int r) {
   GateUpPlan p;
   const size_t P = (size_t)T * k;
   const size_t nzp = ((size_t)2 * r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
-  p.z_off = 0;
-  p.zpart_off = align_up((size_t)T * 2 * r * sizeof(float), 256);
+  p.sync_off = 0;
+  p.z_off = align_up(kSyncBytes, 256);
+  p.zpart_off = align_up(p.z_off + (size_t)T * 2 * r * sizeof(float), 256);
   p.zt_off = align_up(p.zpart_off + (size_t)T * nzp * sizeof(float), 256);
-  p.sync_off = align_up(p.zt_off + (size_t)kZRing * T * 2 * r * sizeof(uint64_t), 256);
-  p.route_off = align_up(p.sync_off + 128 + 64 * 128, 256);
+  p.route_off = align_up(p.zt_off + (size_t)kZRing * T * 2 * r * sizeof(uint64_t), 256);
   p.coef_off = align_up(p.route_off + (1 + 3 * (size_t)tile_cap(T, k, E) + P) * sizeof(int), 256);
   p.total = p.coef_off + group_coef_bytes(tile_cap(T, k, E), r);
   return p;
@@ -659,7 +665,10 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   // One launch when every work-group can be resident at once (the groups
   // wait for each other's z); otherwise z first, then the expert kernels.
   const int fgrid = fused_grid();
-  if (T <= kFusedMaxTokens && r <= kFusedMaxR && fgrid > 0) {
+  const int ugrid = unit_grid();
+  const bool unit = T <= kFusedMaxTokens && r <= kUnitMaxR && ugrid > 0 &&
+                    (long long)T * k * a.n_seg <= ugrid;
+  if (unit || (T <= kFusedMaxTokens && r <= kFusedMaxR && fgrid > 0)) {
     FusedArgs fa;
     fa.g = a;
     fa.phi_t = (const uint4*)phi_t_gateup_f16;
@@ -669,8 +678,12 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     fa.zt = (uint64_t*)(wsb + plan.zt_off);
     fa.epoch = (uint32_t*)(wsb + plan.sync_off);
     fa.hint = fa.epoch + 32;
-    fa.grid = fgrid;
-    launch_gateup_fused(fa, s);
+    fa.grid = unit ? ugrid : fgrid;
+    fa.spin = g_wait_limit.load(std::memory_order_relaxed);
+    if (unit)
+      launch_gateup_unit(fa, s);
+    else
+      launch_gateup_fused(fa, s);
     return launch_status("one-launch gate/up");
   }
   const bool grouped = r <= kGroupMaxR && E <= kGroupMaxE && din <= kGroupMaxDin;
@@ -722,6 +735,10 @@ int bitsmoe_workspace_init(void* ws, size_t ws_bytes, bitsmoe_stream_t stream) {
   hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      (uint4*)ws, n16, (uint8_t*)ws + n16 * 16, ntail);
   return launch_status("workspace fill launch");
+}
+
+uint32_t bitsmoe_debug_set_wait_limit(uint32_t spins) {
+  return g_wait_limit.exchange(spins);
 }
 
 int bitsmoe_dump_codes(const void* packed, size_t packed_bytes, int E, int dout, int r, int e,

@@ -54,11 +54,14 @@
 #include "format.h"
 #include "kernels.h"
 #include "seg_common.h"
+#include "slotmeta.h"
+#include "zx.h"
 
 namespace bitsmoe {
 namespace {
 
 using namespace seg;
+using namespace zx;
 
 constexpr int kFWaves = 8;
 constexpr int kFThreads = kFWaves * kWave;  // 512
@@ -67,10 +70,6 @@ constexpr int kFPW = kFWaves / 2;           // waves per projection
 constexpr int kFMaxW = 10240;               // plane words per projection per chunk
 constexpr int kFMaxS = 4320;                // slots per projection (r <= 4096, padded)
 // slots per lane of the coefficient pass: 9 covers r <= 2048, 17 r <= 4096
-constexpr int kFPre = 4;                    // Phi^T rows a wave loads up front
-constexpr uint32_t kFSpin = 1u << 20;
-constexpr int kFHint = 64;         // hint counters (one per 64th of the producing waves)
-constexpr int kFHintStride = 32;   // u32 between counters (one 128-byte line each)
 
 constexpr int kFZ = 2 * kFusedMaxR;         // z values of one token (gate, up)
 constexpr int kFZPer = kFZ / kFThreads;     // tagged z words per lane
@@ -89,265 +88,6 @@ struct __align__(16) FusedLds {
   uint32_t zok[kFWaves];  // each wave's staged z words arrived
   SegProj desc[2];  // the unit's gate and up descriptors (written by wave 4)
 };
-
-__device__ __forceinline__ float fdot8(uint4 a, uint4 b, float acc) {
-  const h2* ha = reinterpret_cast<const h2*>(&a);
-  const h2* hb = reinterpret_cast<const h2*>(&b);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(ha[i], hb[i], acc, false);
-  return acc;
-}
-
-// This lane's partial dot product of one Phi^T row (p: this lane's 4 16-byte
-// units of the first 2048 inputs) with token tt's x, over all din inputs.
-__device__ __forceinline__ float zpart(const FusedArgs& s, const uint4* prow, const uint4 (&p)[4],
-                                       const uint4 (&xv)[4], int tt, int lane) {
-  const uint4* xt = s.x + (size_t)tt * s.din8;
-  float acc = 0.f;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = lane + u * kWave;
-    if (i < s.din8) acc = fdot8(p[u], tt == 0 ? xv[u] : xt[i], acc);
-  }
-  for (int i0 = 4 * kWave; i0 < s.din8; i0 += 4 * kWave) {  // din > 2048
-    uint4 q4[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + lane + u * kWave;
-      q4[u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + lane + u * kWave;
-      if (i < s.din8) acc = fdot8(q4[u], xt[i], acc);
-    }
-  }
-  return acc;
-}
-
-__device__ __forceinline__ void publish_z(uint64_t* zt, int r, int tt, int n, float v,
-                                          uint32_t tag) {
-  const uint64_t w = ((uint64_t)tag << 32) | __float_as_uint(v);
-  __hip_atomic_store(&zt[(size_t)tt * 2 * r + n], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// One transposing exchange of a kFPre-value reduction: lanes with bit O set
-// keep the upper half of the values, the others the lower half.
-template <int O>
-__device__ __forceinline__ void tstep(float (&v)[kFPre], bool up) {
-#pragma unroll
-  for (int i = 0; i < O; ++i) {
-    const float send = up ? v[i] : v[i + O];
-    const float keep = up ? v[i + O] : v[i];
-    v[i] = keep + __shfl_xor(send, O, kWave);
-  }
-}
-
-// Waves 0-3 of work-group b own z rows [n0, n0 + nrw) of every token.  The
-// loads of the first kFPre Phi^T rows and of x go out first, in straight-line
-// code (so that they stay together and ahead of anything that depends on a
-// load); z_finish then reduces the kFPre partial sums together (2 transposing
-// exchanges leave row lane & 3 in every lane, 4 more finish the sum), lane i
-// publishes row i, and rows beyond the first kFPre follow one at a time.
-struct PhiRegs {
-  uint4 pv[kFPre][4];
-  uint4 xv[4];
-};
-
-__device__ __forceinline__ void phi_issue(const FusedArgs& s, int n0, int nrw, int lane,
-                                          PhiRegs& q) {
-  const int R = 2 * s.g.r;
-#pragma unroll
-  for (int j = 0; j < kFPre; ++j) {
-    const int n = (j < nrw && n0 + j < R) ? n0 + j : 0;
-    const uint4* prow = s.phi_t + (size_t)n * s.din8;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + u * kWave;
-      q.pv[j][u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = lane + u * kWave;
-    q.xv[u] = i < s.din8 ? s.x[i] : make_uint4(0, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void z_finish(const FusedArgs& s, uint64_t* zt, int n0, int nrw,
-                                         int lane, uint32_t tag, const PhiRegs& q) {
-  static_assert(kFPre == 4, "the transposing reduction is written for 4 rows");
-  const int R = 2 * s.g.r;
-  // (T >= 1: a do-while leaves no path on which the x and Phi^T loads are
-  // still outstanding when the hint increment is issued, which would make the
-  // compiler wait for every store first)
-  int tt = 0;
-  do {
-    float v[kFPre];
-#pragma unroll
-    for (int j = 0; j < kFPre; ++j) {
-      const int n = (j < nrw && n0 + j < R) ? n0 + j : 0;
-      v[j] = zpart(s, s.phi_t + (size_t)n * s.din8, q.pv[j], q.xv, tt, lane);
-    }
-    tstep<2>(v, (lane & 2) != 0);
-    tstep<1>(v, (lane & 1) != 0);
-    float z = v[0];
-#pragma unroll
-    for (int off = 4; off < kWave; off <<= 1) z += __shfl_xor(z, off, kWave);
-    const int j = lane & 3;
-    if (lane < kFPre && j < nrw && n0 + j < R) publish_z(zt, s.g.r, tt, n0 + j, z, tag);
-  } while (++tt < s.T);
-  for (int j = kFPre; j < nrw && n0 + j < R; ++j) {  // rows beyond the first kFPre
-    const int n = n0 + j;
-    const uint4* prow = s.phi_t + (size_t)n * s.din8;
-    uint4 p0[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + u * kWave;
-      p0[u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
-    }
-    for (int tt = 0; tt < s.T; ++tt) {
-      const float z = wave_sum(zpart(s, prow, p0, q.xv, tt, lane));
-      if (lane == 0) publish_z(zt, s.g.r, tt, n, z, tag);
-    }
-  }
-}
-
-// Bounded wait until the hint counters say that every producing wave of this
-// launch has published: the counters are never reset, so after the launch
-// with tag g their sum is g times the number of producing waves (modulo
-// 2^32).  Lane i reads counter i; 64 counters on separate lines keep the
-// producers' increments from contending.  Only a hint: the tags decide.
-__device__ __forceinline__ void wait_hint(const uint32_t* hint, uint32_t target) {
-  const int lane = threadIdx.x & (kWave - 1);
-  uint32_t spins = 0;
-  while (true) {
-    const uint32_t c =
-        __hip_atomic_load(hint + kFHintStride * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t tot = wave_sum_u32_dpp(c);  // modulo 2^32, like the target
-    if ((int32_t)(tot - target) >= 0 || ++spins >= kFSpin / 64) break;
-    __builtin_amdgcn_s_sleep(4);
-  }
-}
-
-// The token's 2r tagged z words, copied into LDS as floats by all lanes with
-// coalesced loads.  The first read is an ordinary (L2-cached) load, issued
-// once the hint counters say that every producer's z stores have completed,
-// so the work-groups of one XCD share one fetch; words whose tag is not
-// there (a line the L2 kept from an older launch) are re-read with
-// device-coherent loads until it is (bounded wait).  Returns false on a
-// time-out.
-__device__ __forceinline__ bool stage_z(const uint64_t* src, int R, uint32_t tag, float* Z) {
-  uint64_t zw[kFZPer];
-#pragma unroll
-  for (int j = 0; j < kFZPer; ++j) {
-    const int i = (int)threadIdx.x + kFThreads * j;
-    zw[j] = i < R ? src[i] : ((uint64_t)tag << 32);
-  }
-  uint32_t spins = 0;
-  while (true) {
-    bool ready = true;
-#pragma unroll
-    for (int j = 0; j < kFZPer; ++j) ready &= (uint32_t)(zw[j] >> 32) == tag;
-    if (__all(ready) || spins >= kFSpin) break;
-    __builtin_amdgcn_s_sleep(2);
-#pragma unroll
-    for (int j = 0; j < kFZPer; ++j) {
-      const int i = (int)threadIdx.x + kFThreads * j;
-      if ((uint32_t)(zw[j] >> 32) != tag)
-        zw[j] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    ++spins;
-  }
-#pragma unroll
-  for (int j = 0; j < kFZPer; ++j) {
-    const int i = (int)threadIdx.x + kFThreads * j;
-    if (i < R) Z[i] = __uint_as_float((uint32_t)zw[j]);
-  }
-  return spins < kFSpin;
-}
-
-// Slot metadata of one lane: kFSper = 8 V + 1 slots, the 8 V contiguous
-// slots 8 V lp .. 8 V lp + 8 V - 1 (read with 16-byte loads) and the tail
-// slot 2048 V + lp (n_slot <= r + 7 * 31 < 2048 V + 256).  The raw loaded
-// words are kept as they are and unpacked only where the coefficients are
-// formed, so that nothing before that point waits for these loads.
-template <int kFSper>
-struct SlotMeta {
-  static constexpr int V = (kFSper - 1) / 8;
-  uint4 kq[V], a0[V], a1[V], sq[V], mq[V];  // kidx, a (2 x 4), s, m of 8 slots each
-  uint32_t kt, at, st, mt;                  // the tail slot
-};
-template <int kFSper>
-__device__ __forceinline__ uint32_t meta_slot(int lp, int i) {
-  constexpr int V = SlotMeta<kFSper>::V;
-  return i < 8 * V ? (uint32_t)(8 * V * lp + i) : (uint32_t)(2048 * V + lp);
-}
-// Every load is issued unconditionally (an index past the array is replaced
-// by 0, inside the expert block) and through a global address (the
-// descriptor's pointers are global ones); a load inside a branch, or a flat
-// load (which also counts on the LDS counter), would make the wave wait for
-// all of its outstanding loads right there.  A 16-byte vector that starts
-// inside an array ends at most 28 bytes past it, still inside the expert
-// block (the next array, or the planes and the block's 16-byte tail).
-template <int kFSper>
-__device__ __forceinline__ void load_meta(const SegProj& p, int lp, SlotMeta<kFSper>& md) {
-  constexpr int V = SlotMeta<kFSper>::V;
-  static_assert(kFSper == 8 * V + 1, "8 V contiguous slots and one tail slot");
-  const uint32_t s0 = 8u * V * (uint32_t)lp;
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const uint32_t sv = s0 + 8u * v;
-    const uint32_t iq = sv < p.n_slot ? sv : 0u, ia = sv + 4 < p.n_slot ? sv + 4 : 0u;
-    const uint32_t is = sv < p.n_qslot ? sv : 0u;
-    md.kq[v] = ld16(p.kidx + iq);
-    md.a0[v] = ld16(p.A + iq);
-    md.a1[v] = ld16(p.A + ia);
-    md.sq[v] = ld16(p.S + is);
-    md.mq[v] = ld16(p.M + is);
-  }
-  const uint32_t sl = 2048u * V + (uint32_t)lp;
-  const uint32_t ic = sl < p.n_slot ? sl : 0u, iq = sl < p.n_qslot ? sl : 0u;
-  // 16-bit values through the aligned 32-bit word that holds them (the half
-  // is picked where they are used)
-  md.kt = *(const gu32*)(p.kidx + (ic & ~1u));
-  md.at = *(const gu32*)(p.A + ic);
-  md.st = *(const gu32*)(p.S + (iq & ~1u));
-  md.mt = *(const gu32*)(p.M + (iq & ~1u));
-}
-// Slot i of the lane (see SlotMeta): component index k, magnitude a and
-// fp16 s, m as floats; slots past the arrays give k = 0, a = 0, s = 1, m = 0.
-template <int kFSper>
-__device__ __forceinline__ void meta_get(const SlotMeta<kFSper>& md, int lp, int i,
-                                         uint32_t n_slot, uint32_t n_qslot, uint32_t& k,
-                                         float& a, float& sv, float& mv) {
-  constexpr int V = SlotMeta<kFSper>::V;
-  const uint32_t sl = meta_slot<kFSper>(lp, i);
-  uint32_t kk, aa, ss, mm;
-  if (i < 8 * V) {
-    const int v = i >> 3, j = i & 7;
-    const uint32_t kw[4] = {md.kq[v].x, md.kq[v].y, md.kq[v].z, md.kq[v].w};
-    const uint32_t sw[4] = {md.sq[v].x, md.sq[v].y, md.sq[v].z, md.sq[v].w};
-    const uint32_t mw[4] = {md.mq[v].x, md.mq[v].y, md.mq[v].z, md.mq[v].w};
-    const uint32_t aw[8] = {md.a0[v].x, md.a0[v].y, md.a0[v].z, md.a0[v].w,
-                            md.a1[v].x, md.a1[v].y, md.a1[v].z, md.a1[v].w};
-    const uint32_t sh = 16 * (j & 1);
-    kk = (kw[j >> 1] >> sh) & 0xFFFFu;
-    ss = (sw[j >> 1] >> sh) & 0xFFFFu;
-    mm = (mw[j >> 1] >> sh) & 0xFFFFu;
-    aa = aw[j];
-  } else {
-    const uint32_t sh = 16 * (sl & 1);  // the tail slot's half of the loaded words
-    kk = (md.kt >> sh) & 0xFFFFu;
-    aa = md.at;
-    ss = (md.st >> sh) & 0xFFFFu;
-    mm = (md.mt >> sh) & 0xFFFFu;
-  }
-  k = sl < n_slot ? kk : 0u;
-  a = sl < n_slot ? __uint_as_float(aa) : 0.f;
-  sv = sl < n_qslot ? __half2float(__ushort_as_half((unsigned short)ss)) : 1.f;
-  mv = sl < n_qslot ? __half2float(__ushort_as_half((unsigned short)mm)) : 0.f;
-}
 
 // Stage chunk [b0, b1) of segment sg of projection p into arena (nl lanes).
 __device__ __forceinline__ void stage_chunk(uint32_t* arena, const SegProj& p, int sg,
@@ -396,9 +136,7 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     z_finish(s, zt, n0, nrw, lane, tag, phr);
     // (the hint may run ahead of the z stores: a reader that comes too early
     // finds old tags and re-reads those words)
-    if (lane == 0)
-      __hip_atomic_fetch_add(s.hint + kFHintStride * (((int)blockIdx.x * kFPW + wp) & (kFHint - 1)),
-                             1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    hint_add(s, (int)blockIdx.x * kFPW + wp, lane);
   }
 
   if (pj == 1) {
@@ -489,9 +227,10 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     }
     if (t != zt_cached) {
       // one wave polls the hint counters (the first time only), the rest wait
-      if (zt_cached < 0 && wv == 0) wait_hint(s.hint, tag * (uint32_t)nzw);
+      if (zt_cached < 0 && wv == 0) wait_hint(s.hint, tag * (uint32_t)nzw, s.spin);
       lds_sync();
-      zok = stage_z(zt + (size_t)t * R, R, tag, &L.Z[0]);
+      float zmx;
+      zok = stage_z<kFThreads, kFZPer>(zt + (size_t)t * R, R, tag, &L.Z[0], s.spin, zmx);
       zok = __all(zok);
       if (lane == 0) L.zok[wv] = zok;  // every wave's words: combined in the epilogue
       lds_sync();                  // L.Z complete
@@ -710,8 +449,10 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
   // Work-group 0 advances the epoch once every producing wave has counted
   // itself: by then every work-group has read the old epoch (its tag is in
   // its registers), and the next launch reads the new one.
+  // (Waited for with the default bound also when a test lowered the
+  // launch's bound.)
   if (blockIdx.x == 0 && wv == 0) {
-    if (zt_cached < 0) wait_hint(s.hint, tag * (uint32_t)nzw);
+    wait_hint(s.hint, tag * (uint32_t)nzw, max(s.spin, kSpinDefault));
     if (lane == 0) __hip_atomic_store(s.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

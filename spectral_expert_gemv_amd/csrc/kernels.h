@@ -8,20 +8,27 @@ namespace bitsmoe {
 
 constexpr int kFusedMaxTokens = 4;   // one-launch path: T <= this
 constexpr int kFusedMaxR = 4096;     //   and r <= this
+constexpr int kUnitMaxR = 2048;      // one-unit-per-work-group kernel: r <= this
 constexpr int kZRing = 8;            // tagged z buffers of the one-launch path (by launch)
+constexpr size_t kSyncBytes = 128 + 64 * 128;  // epoch line + 64 hint counter lines
+constexpr uint32_t kSpinDefault = 1u << 20;    // bound on the one-launch kernels' waits
 constexpr int kGroupMaxR = 4096;     // grouped path: r <= this
 constexpr int kGroupMaxE = 16384;    //   and E <= this (route histogram in LDS)
 constexpr int kGroupMaxDin = 4096;   //   and din <= this (row-blocked projection)
 constexpr int kProjRowsPerBlock = 16;  // Phi^T rows per work-group of the projection
 constexpr int kTile = 16;            // tokens per grouped work unit (MFMA N)
 
-// Workspace layout of one gate/up call (offsets in bytes from ws).
+// Workspace layout of one gate/up call (offsets in bytes from ws).  The sync
+// words come first, at an offset that depends on nothing, so one workspace
+// can serve calls of different shapes in turn: no other part of a call's
+// layout ever overlaps them.
 struct GateUpPlan {
+  size_t sync_off;    // = 0: uint32 epoch (the last one-launch call's tag), then
+                      // from byte 128 the 64 cumulative hint counters, 128 bytes
+                      // apart (kSyncBytes in all)
   size_t z_off;       // T x 2r float32 (projection launch of the batched path)
   size_t zpart_off;   // T x ceil(2r / 16) float32: max |z| per projection work-group
   size_t zt_off;      // ring of kZRing x T x 2r uint64 tagged z (one-launch path)
-  size_t sync_off;    // uint32 epoch (the last launch's tag), then from byte 128 the
-                      // 64 cumulative hint counters, 128 bytes apart
   size_t route_off;   // route lists (see RouteLists)
   size_t coef_off;    // per-tile coefficient tables (batched path, see GroupArgs)
   size_t total;
@@ -52,10 +59,17 @@ struct FusedArgs {
   uint32_t* epoch;     // tag of the previous launch
   uint32_t* hint;      // 64 counters, 32 words apart: producing waves done, cumulative over launches
   int grid;            // multiple of 8, all work-groups resident
+  uint32_t spin;       // bound on the z exchange waits (0: give up at once, rows NaN)
 };
 size_t fused_lds_bytes();
 int fused_grid();  // work-groups of the fused kernel on this device (0: unavailable)
 void launch_gateup_fused(const FusedArgs& s, hipStream_t st);
+// The same path with one (pair, segment) unit per work-group and the unit's
+// codes decoded into registers before z arrives (r <= kUnitMaxR, T <=
+// kFusedMaxTokens, T * k * ceil(dout / 32) <= unit_grid()).
+size_t unit_lds_bytes();
+int unit_grid();  // work-groups of that kernel on this device (0: unavailable)
+void launch_gateup_unit(const FusedArgs& s, hipStream_t st);
 
 // Pairs grouped by expert and cut into tiles of <= kTile pairs (written by
 // the route-grouping launch).

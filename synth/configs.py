@@ -54,6 +54,13 @@ DEEPSEEK_MOE_16B = LayerSpec(
     ln_sigma=0.5, bits={1: 5, 2: 25, 3: 35, 4: 25, 6: 5, 8: 4, 16: 1},
     outlier_frac=0.005, outlier_scale=20.0, phi_fp16=True)
 
+# Test-only shape: r = 2048 with most columns at 8 and 16 bits, so that one
+# unit of the one-launch kernel holds more K steps and plane words than its
+# registers and LDS arena take at once; ragged dout.
+HEAVY = LayerSpec("heavy", E=4, din=2048, dout=200, r=2048, k=2, decay=0.5,
+                  ln_sigma=0.3, bits={16: 60, 8: 30, 1: 10}, outlier_frac=0.0,
+                  outlier_scale=1.0, phi_fp16=True)
+
 # Test-only shape: wide columns (mostly 6- and 8-bit, many fp16) and a ragged
 # dout, so that one 64-row slab of one expert holds more plane masks and
 # fp16 columns than a work-group stages at once.
@@ -62,7 +69,7 @@ WIDE = LayerSpec("wide", E=4, din=3072, dout=4133, r=3072, k=2, decay=0.5,
                  outlier_scale=1.0, phi_fp16=True)
 
 LAYERS: Dict[str, LayerSpec] = {l.name: l for l in
-                                (TINY, QWEN3_30B_A3B, MIXTRAL_8X7B, DEEPSEEK_MOE_16B, WIDE)}
+                                (TINY, QWEN3_30B_A3B, MIXTRAL_8X7B, DEEPSEEK_MOE_16B, WIDE, HEAVY)}
 
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     Workload("tiny_t8", TINY, 8, ("uniform",)),
@@ -72,6 +79,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     Workload("wide_t8", WIDE, 8, ("uniform",)),
     Workload("tiny_t64", TINY, 64, ("zipf", 1.1)),
     Workload("qwen3_30b_a3b_t1", QWEN3_30B_A3B, 1, ("uniform",)),
+    Workload("qwen3_30b_a3b_t4", QWEN3_30B_A3B, 4, ("uniform",)),
+    Workload("heavy_t1", HEAVY, 1, ("uniform",)),
     Workload("qwen3_30b_a3b_t32", QWEN3_30B_A3B, 32, ("zipf", 1.1)),
     Workload("mixtral_8x7b_t1", MIXTRAL_8X7B, 1, ("uniform",)),
     Workload("mixtral_8x7b_t8", MIXTRAL_8X7B, 8, ("uniform",)),

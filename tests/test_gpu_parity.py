@@ -142,8 +142,8 @@ def _check_h(got, href):
 
 @pytest.mark.parametrize("wl_name,steps", [("tiny_t1", 3), ("tiny_t4", 3), ("tiny_t8", 3),
                                            ("tiny_t64", 2), ("qwen3_30b_a3b_t1", 3),
-                                           ("qwen3_30b_a3b_t32", 1), ("wide_t2", 2),
-                                           ("wide_t8", 1)])
+                                           ("qwen3_30b_a3b_t4", 1), ("qwen3_30b_a3b_t32", 1),
+                                           ("wide_t2", 2), ("wide_t8", 1), ("heavy_t1", 2)])
 def test_gateup_full(bm, wl_name, steps):
     wl = synth.workload(wl_name)
     L, dev = device_layer(wl.layer.name)
@@ -276,3 +276,81 @@ def test_many_experts_separate_route_launch(bm, T):
     assert np.all(np.isnan(got[1, 0]))
     ok = [(t, s) for t in range(T) for s in range(2) if (t, s) != (1, 0)]
     _check_h(got, pairs_ref(L, x, ids, pairs=ok))
+
+
+# ------------------------------------------------- workspace and waits
+
+def _gateup_raw(bm, dev, x, ids, E, dout, h, ws):
+    T, k = ids.shape
+    bm._check(bm._lib.bitsmoe_moe_gateup(
+        dev.blob_gate.data_ptr(), dev.blob_gate.numel(), dev.blob_up.data_ptr(),
+        dev.blob_up.numel(), dev.phi_t.data_ptr(), x.data_ptr(), ids.data_ptr(), T, k, E,
+        dev.din, dout, dev.r, h.data_ptr(), ws.data_ptr(), ws.numel(),
+        torch.cuda.current_stream().cuda_stream))
+
+
+def test_workspace_reused_across_token_counts(bm):
+    """One workspace serves calls of different T in turn: T = 1 (the
+    one-unit-per-work-group kernel) and T = 4 (the chunked one-launch kernel)
+    alternate for 12 calls, more than the 8-buffer ring of tagged z, and every
+    call matches the oracle on a sample of pairs."""
+    L, dev = device_layer("qwen3_30b_a3b")
+    spec = L.spec
+    ws = dev.workspace(4, spec.k)  # sized for the larger T
+    for call in range(12):
+        T = 1 if call % 2 == 0 else 4
+        wl = synth.workload("qwen3_30b_a3b_t1" if T == 1 else "qwen3_30b_a3b_t4")
+        x, ids = synth.make_batch(wl, L, step=100 + call)
+        _say("reuse call %d T=%d" % (call, T))
+        h = dev.gateup(_cuda(x), _cuda(ids), ws=ws)
+        torch.cuda.synchronize()
+        got = h.cpu().numpy()
+        assert np.all(np.isfinite(got)), call
+        pairs = [(0, 0), (T - 1, spec.k - 1)]
+        _check_h(got, pairs_ref(L, x, ids, pairs=pairs))
+
+
+@pytest.mark.parametrize("wl_name", ["tiny_t1", "wide_t2", "tiny_t8"])
+def test_blob_expert_count_mismatch_gives_nan(bm, wl_name):
+    """A call that passes more experts than the blobs' headers hold: every
+    directory record fails its check, every row is NaN and nothing is read
+    outside the blobs (T = 1: one unit per work-group; T = 2 on the wide
+    layer: the chunked one-launch kernel; T = 8: the batched path)."""
+    wl = synth.workload(wl_name)
+    L, dev = device_layer(wl.layer.name)
+    spec = L.spec
+    x, ids = synth.make_batch(wl, L)
+    E_call = spec.E + 4
+    assert dev.blob_gate.numel() >= 128 + 64 * E_call
+    T, k = ids.shape
+    h = torch.zeros((T, k, spec.dout), dtype=torch.float32, device="cuda")
+    n = bm.moe_gateup_workspace_size(T, k, E_call, spec.din, spec.dout, spec.r)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    bm.workspace_init(ws)
+    _gateup_raw(bm, dev, _cuda(x), _cuda(ids), E_call, spec.dout, h, ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(h).all()
+
+
+@pytest.mark.parametrize("wl_name", ["tiny_t1", "wide_t2"])
+def test_wait_limit_zero_gives_nan_rows_then_recovers(bm, wl_name):
+    """With the wait bound set to 0 by the host, every wait of the one-launch
+    kernels gives up at once: the launch completes and every row is NaN.
+    With the bound restored, the next calls on the same workspace are exact
+    again (the launch counter advanced normally)."""
+    wl = synth.workload(wl_name)
+    L, dev = device_layer(wl.layer.name)
+    x, ids = synth.make_batch(wl, L)
+    T, k = ids.shape
+    ws = dev.workspace(T, k)
+    prev = bm.debug_set_wait_limit(0)
+    try:
+        h = dev.gateup(_cuda(x), _cuda(ids), ws=ws)
+        torch.cuda.synchronize()
+        assert torch.isnan(h).all()
+    finally:
+        assert bm.debug_set_wait_limit(prev) == 0
+    for _ in range(2):
+        got = dev.gateup(_cuda(x), _cuda(ids), ws=ws)
+        torch.cuda.synchronize()
+        _check_h(got.cpu().numpy(), pairs_ref(L, x, ids))
