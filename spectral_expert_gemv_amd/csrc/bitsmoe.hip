@@ -665,10 +665,7 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   // One launch when every work-group can be resident at once (the groups
   // wait for each other's z); otherwise z first, then the expert kernels.
   const int fgrid = fused_grid();
-  const int ugrid = unit_grid();
-  const bool unit = T <= kFusedMaxTokens && r <= kUnitMaxR && ugrid > 0 &&
-                    (long long)T * k * a.n_seg <= ugrid;
-  if (unit || (T <= kFusedMaxTokens && r <= kFusedMaxR && fgrid > 0)) {
+  if (T <= kFusedMaxTokens && r <= kFusedMaxR && fgrid > 0) {
     FusedArgs fa;
     fa.g = a;
     fa.phi_t = (const uint4*)phi_t_gateup_f16;
@@ -678,12 +675,9 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     fa.zt = (uint64_t*)(wsb + plan.zt_off);
     fa.epoch = (uint32_t*)(wsb + plan.sync_off);
     fa.hint = fa.epoch + 32;
-    fa.grid = unit ? ugrid : fgrid;
+    fa.grid = fgrid;
     fa.spin = g_wait_limit.load(std::memory_order_relaxed);
-    if (unit)
-      launch_gateup_unit(fa, s);
-    else
-      launch_gateup_fused(fa, s);
+    launch_gateup_fused(fa, s);
     return launch_status("one-launch gate/up");
   }
   const bool grouped = r <= kGroupMaxR && E <= kGroupMaxE && din <= kGroupMaxDin;

@@ -8,7 +8,6 @@ namespace bitsmoe {
 
 constexpr int kFusedMaxTokens = 4;   // one-launch path: T <= this
 constexpr int kFusedMaxR = 4096;     //   and r <= this
-constexpr int kUnitMaxR = 2048;      // one-unit-per-work-group kernel: r <= this
 constexpr int kZRing = 8;            // tagged z buffers of the one-launch path (by launch)
 constexpr size_t kSyncBytes = 128 + 64 * 128;  // epoch line + 64 hint counter lines
 constexpr uint32_t kSpinDefault = 1u << 20;    // bound on the one-launch kernels' waits
@@ -64,12 +63,6 @@ struct FusedArgs {
 size_t fused_lds_bytes();
 int fused_grid();  // work-groups of the fused kernel on this device (0: unavailable)
 void launch_gateup_fused(const FusedArgs& s, hipStream_t st);
-// The same path with one (pair, segment) unit per work-group and the unit's
-// codes decoded into registers before z arrives (r <= kUnitMaxR, T <=
-// kFusedMaxTokens, T * k * ceil(dout / 32) <= unit_grid()).
-size_t unit_lds_bytes();
-int unit_grid();  // work-groups of that kernel on this device (0: unavailable)
-void launch_gateup_unit(const FusedArgs& s, hipStream_t st);
 
 // Pairs grouped by expert and cut into tiles of <= kTile pairs (written by
 // the route-grouping launch).

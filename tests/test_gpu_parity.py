@@ -290,9 +290,8 @@ def _gateup_raw(bm, dev, x, ids, E, dout, h, ws):
 
 
 def test_workspace_reused_across_token_counts(bm):
-    """One workspace serves calls of different T in turn: T = 1 (the
-    one-unit-per-work-group kernel) and T = 4 (the chunked one-launch kernel)
-    alternate for 12 calls, more than the 8-buffer ring of tagged z, and every
+    """One workspace serves calls of different T in turn: T = 1 and T = 4
+    (both on the one-launch kernel, with z rings of different sizes) alternate for 12 calls, more than the 8-buffer ring of tagged z, and every
     call matches the oracle on a sample of pairs."""
     L, dev = device_layer("qwen3_30b_a3b")
     spec = L.spec
@@ -314,8 +313,8 @@ def test_workspace_reused_across_token_counts(bm):
 def test_blob_expert_count_mismatch_gives_nan(bm, wl_name):
     """A call that passes more experts than the blobs' headers hold: every
     directory record fails its check, every row is NaN and nothing is read
-    outside the blobs (T = 1: one unit per work-group; T = 2 on the wide
-    layer: the chunked one-launch kernel; T = 8: the batched path)."""
+    outside the blobs (T = 1 and T = 2: the one-launch kernel; T = 8: the
+    batched path)."""
     wl = synth.workload(wl_name)
     L, dev = device_layer(wl.layer.name)
     spec = L.spec
