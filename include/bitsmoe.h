@@ -25,7 +25,8 @@
  *   - Return value: BITSMOE_OK (0) or a negative status; bitsmoe_strerror()
  *     names it and bitsmoe_last_error_detail() gives a thread-local message.
  *   - Ownership: the caller allocates and frees every buffer.  The library
- *     allocates no device memory and never synchronizes.
+ *     allocates no device memory (bitsmoe_moe_gateup_noalloc's static array
+ *     is part of the loaded code object) and never synchronizes.
  *   - Device pointers must be 16-byte aligned (ids: 4-byte aligned).
  *   - Device calls enqueue work on `stream` (0 = null stream) and return at
  *     once; inputs must stay valid until the stream reaches the work.  Host
@@ -35,9 +36,10 @@
  *     match the dimensions passed, an expert id outside [0, E)) never cause
  *     an out-of-bounds access: the affected output rows are written as NaN.
  *   - The library keeps no state between calls except what the caller's
- *     workspace holds (bitsmoe_moe_gateup keeps a launch counter there) and
- *     the test hook's wait limit; entry points are re-entrant, and calls that
- *     share a workspace must not overlap in time.
+ *     workspace holds (bitsmoe_moe_gateup keeps a launch counter there), the
+ *     static workspace of bitsmoe_moe_gateup_noalloc and the test hook's
+ *     wait limit; entry points are re-entrant, and calls that share a
+ *     workspace must not overlap in time.
  */
 #ifndef BITSMOE_H
 #define BITSMOE_H
@@ -217,6 +219,27 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes,
                        const int32_t* ids, int T, int k, int E, int din, int dout,
                        int r, float* h, void* ws, size_t ws_bytes,
                        bitsmoe_stream_t stream);
+
+/* ------------------------------------------------- gate/up, no allocation
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): bitsmoe_moe_gateup
+ * with the same arguments, meanings and results, minus the workspace.  The
+ * workspace is a static array of BITSMOE_GATEUP_NOALLOC_MAX_WS bytes in the
+ * library's device code, one per device, which the device keeps until the
+ * process ends; the first call on a device zero-fills it on `stream`.
+ *   - A call whose bitsmoe_moe_gateup_workspace_size() exceeds that size
+ *     returns BITSMOE_ENOSPC and enqueues nothing.
+ *   - Calls no hipMalloc, hipFree or other allocating routine.
+ *   - Every call on one device shares that array: calls that overlap in
+ *     time on one device (other streams, other threads) race and must not
+ *     be made; calls in order on one stream are fine.
+ */
+#define BITSMOE_GATEUP_NOALLOC_MAX_WS ((size_t)64 << 20)
+int bitsmoe_moe_gateup_noalloc(const void* packed_gate, size_t gate_bytes,
+                               const void* packed_up, size_t up_bytes,
+                               const void* phi_t_gateup_f16, const void* x_f16,
+                               const int32_t* ids, int T, int k, int E, int din,
+                               int dout, int r, float* h, bitsmoe_stream_t stream);
 
 /* ---------------------------------------------------------- down + combine
  * out[t*din + i] = sum over slots j (ascending) of g[t*k + j] * y_{t,j}[i],

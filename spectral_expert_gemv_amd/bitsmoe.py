@@ -55,6 +55,8 @@ _SIGS = {
     "bitsmoe_moe_gateup_workspace_size": ([_i, _i, _i, _i, _i, _i, _psz], _i),
     "bitsmoe_moe_gateup": ([_vp, _sz, _vp, _sz, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                             _vp, _vp, _sz, _vp], _i),
+    "bitsmoe_moe_gateup_noalloc": ([_vp, _sz, _vp, _sz, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                    _i, _vp, _vp], _i),
     "bitsmoe_workspace_init": ([_vp, _sz, _vp], _i),
     "bitsmoe_dump_codes": ([_vp, _sz, _i, _i, _i, _i, _vp, _vp], _i),
     "bitsmoe_debug_set_wait_limit": ([ctypes.c_uint32], ctypes.c_uint32),
@@ -180,6 +182,22 @@ def moe_gateup(packed_gate, packed_up, phi_t_gateup, x, ids, E, dout, r, h, ws, 
                                    _nbytes(packed_up), _ptr(phi_t_gateup), _ptr(x), _ptr(ids),
                                    T, k, E, din, dout, r, _ptr(h), _ptr(ws), _nbytes(ws),
                                    _stream(stream)))
+
+
+# bytes of the static workspace behind moe_gateup_noalloc
+GATEUP_NOALLOC_MAX_WS = 64 << 20
+
+
+def moe_gateup_noalloc(packed_gate, packed_up, phi_t_gateup, x, ids, E, dout, r, h,
+                       stream=None):
+    """moe_gateup on the library's static per-device workspace (no workspace
+    argument; calls that overlap in time on one device race)."""
+    T, k = ids.shape
+    din = x.shape[1]
+    _check(_lib.bitsmoe_moe_gateup_noalloc(_ptr(packed_gate), _nbytes(packed_gate),
+                                           _ptr(packed_up), _nbytes(packed_up),
+                                           _ptr(phi_t_gateup), _ptr(x), _ptr(ids), T, k, E,
+                                           din, dout, r, _ptr(h), _stream(stream)))
 
 
 def workspace_init(ws, stream=None):

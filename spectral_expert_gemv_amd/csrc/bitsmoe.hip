@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "bitsmoe.h"
 #include "common.h"
@@ -627,24 +628,45 @@ int bitsmoe_moe_gateup_workspace_size(int T, int k, int E, int din, int dout, in
   return BITSMOE_OK;
 }
 
-int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* packed_up,
-                       size_t up_bytes, const void* phi_t_gateup_f16, const void* x_f16,
-                       const int32_t* ids, int T, int k, int E, int din, int dout, int r,
-                       float* h, void* ws, size_t ws_bytes, bitsmoe_stream_t stream) {
+}  // extern "C"
+
+namespace {
+// Host checks of a gate/up call.  static_ws: the workspace is the library's
+// static array (ws is not checked; ws_bytes is its size).
+int gateup_checks(const void* packed_gate, size_t gate_bytes, const void* packed_up,
+                  size_t up_bytes, const void* phi_t_gateup_f16, const void* x_f16,
+                  const int32_t* ids, int T, int k, int E, int din, int dout, int r,
+                  const float* h, const void* ws, size_t ws_bytes, bool static_ws) {
   int st = check_layer_dims(E, dout, r);
   if (st) return st;
   if ((st = check_blob_arg(packed_gate, gate_bytes, E, "packed_gate"))) return st;
   if ((st = check_blob_arg(packed_up, up_bytes, E, "packed_up"))) return st;
-  if (!ids || !h || !ws) return fail(BITSMOE_EINVAL, "null pointer argument");
-  if (!aligned16(h) || !aligned16(ws) || ((uintptr_t)ids & 3u))
+  if (!ids || !h || (!static_ws && !ws)) return fail(BITSMOE_EINVAL, "null pointer argument");
+  if (!aligned16(h) || (!static_ws && !aligned16(ws)) || ((uintptr_t)ids & 3u))
     return fail(BITSMOE_EINVAL, "misaligned h, ws or ids");
   if (k < 1 || k > E) return fail(BITSMOE_EINVAL, "k=%d E=%d", k, E);
-  if ((st = proj_args(phi_t_gateup_f16, x_f16, (const float*)ws, T, din, 2 * r))) return st;
+  if ((st = proj_args(phi_t_gateup_f16, x_f16, h, T, din, 2 * r))) return st;
   if ((long long)T * k > (1LL << 24))
     return fail(BITSMOE_ESHAPE, "T*k=%lld too large", (long long)T * k);
   size_t need = 0;
   bitsmoe_moe_gateup_workspace_size(T, k, E, din, dout, r, &need);
-  if (ws_bytes < need) return fail(BITSMOE_ENOSPC, "ws_bytes=%zu < %zu", ws_bytes, need);
+  if (ws_bytes < need)
+    return fail(BITSMOE_ENOSPC, static_ws ? "needs %zu bytes of workspace, above the %zu of "
+                "the static one: use bitsmoe_moe_gateup with a workspace" : "ws_bytes=%zu < %zu",
+                static_ws ? need : ws_bytes, static_ws ? ws_bytes : need);
+  return BITSMOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* packed_up,
+                       size_t up_bytes, const void* phi_t_gateup_f16, const void* x_f16,
+                       const int32_t* ids, int T, int k, int E, int din, int dout, int r,
+                       float* h, void* ws, size_t ws_bytes, bitsmoe_stream_t stream) {
+  int st = gateup_checks(packed_gate, gate_bytes, packed_up, up_bytes, phi_t_gateup_f16, x_f16,
+                         ids, T, k, E, din, dout, r, h, ws, ws_bytes, false);
+  if (st) return st;
   const GateUpPlan plan = gateup_plan(T, k, E, r);
   hipStream_t s = (hipStream_t)stream;
   uint8_t* wsb = (uint8_t*)ws;
@@ -729,6 +751,62 @@ int bitsmoe_workspace_init(void* ws, size_t ws_bytes, bitsmoe_stream_t stream) {
   hipLaunchKernelGGL(k_zero_fill, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      (uint4*)ws, n16, (uint8_t*)ws + n16 * 16, ntail);
   return launch_status("workspace fill launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free gate/up: the workspace is this file-scope array, one copy
+// per device, kept (with the one-launch kernel's counters in its first bytes)
+// until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host it only names the symbol): it uses the device address
+// hipGetSymbolAddress returns, looked up once per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = BITSMOE_GATEUP_NOALLOC_MAX_WS;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDevices];
+
+// Device address of this device's scratch array.  The first call on a device
+// looks it up and zero-fills it on `s` (work enqueued after it on any stream
+// of that device must come after that fill, as with bitsmoe_workspace_init).
+int scratch_for_current_device(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BITSMOE_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchMaxDevices)
+    return fail(BITSMOE_EHIP, "device %d outside [0,%d)", dev, kScratchMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(BITSMOE_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    const int st = bitsmoe_workspace_init(p, kScratchBytes, (bitsmoe_stream_t)s);
+    if (st) return st;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BITSMOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int bitsmoe_moe_gateup_noalloc(const void* packed_gate, size_t gate_bytes, const void* packed_up,
+                               size_t up_bytes, const void* phi_t_gateup_f16, const void* x_f16,
+                               const int32_t* ids, int T, int k, int E, int din, int dout, int r,
+                               float* h, bitsmoe_stream_t stream) {
+  int st = gateup_checks(packed_gate, gate_bytes, packed_up, up_bytes, phi_t_gateup_f16, x_f16,
+                         ids, T, k, E, din, dout, r, h, nullptr, kScratchBytes, true);
+  if (st) return st;
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device((hipStream_t)stream, &ws))) return st;
+  return bitsmoe_moe_gateup(packed_gate, gate_bytes, packed_up, up_bytes, phi_t_gateup_f16,
+                            x_f16, ids, T, k, E, din, dout, r, h, ws, kScratchBytes, stream);
 }
 
 uint32_t bitsmoe_debug_set_wait_limit(uint32_t spins) {

@@ -36,6 +36,9 @@ def test_exports_every_declared_symbol():
     for name in decl:
         assert hasattr(lib, name), name
     assert set(decl) == set(bm.EXPORTS)
+    hdr = open(os.path.join(ROOT, "include", "bitsmoe.h")).read()
+    m = re.search(r"#define BITSMOE_GATEUP_NOALLOC_MAX_WS \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == bm.GATEUP_NOALLOC_MAX_WS
 
 
 def test_strerror_and_version():
@@ -175,6 +178,19 @@ def test_device_entry_points_validate_before_launch():
     assert gu(k=0) == bm.EINVAL
     assert gu(h=None) == bm.EINVAL
     assert gu(ws=FAKE + 8) == bm.EINVAL
+    # gate/up on the static workspace: the same checks, and a call needing
+    # more workspace than the static array holds is refused before any HIP call
+    def gun(T=8, k=2, E=4, din=64, dout=96, r=64, h=FAKE):
+        return L.bitsmoe_moe_gateup_noalloc(FAKE, 1 << 20, FAKE, 1 << 20, FAKE, FAKE, FAKE, T, k,
+                                            E, din, dout, r, h, None)
+    assert bm.moe_gateup_workspace_size(256, 8, 128, 2048, 768, 2048) > bm.GATEUP_NOALLOC_MAX_WS
+    assert gun(T=256, k=8, E=128, din=2048, dout=768, r=2048) == bm.ENOSPC
+    assert b"static" in bm._lib.bitsmoe_last_error_detail()
+    assert gun(T=0) == bm.EINVAL
+    assert gun(k=5) == bm.EINVAL
+    assert gun(din=60) == bm.ESHAPE
+    assert gun(h=None) == bm.EINVAL
+    assert gun(h=FAKE + 4) == bm.EINVAL
     # code dump
     assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 4, FAKE, None) == bm.EINVAL
     assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 0, None, None) == bm.EINVAL
