@@ -297,11 +297,29 @@ int bitsmoe_workspace_init(void* ws, size_t ws_bytes, bitsmoe_stream_t stream);
 uint32_t bitsmoe_debug_set_wait_limit(uint32_t spins);
 
 /*
- * Codes of expert e as the device unpack routine decodes them, in k order:
- * codes[k*dout + i] = q (1..8-bit columns), the fp16 bit pattern (16-bit
- * columns), 0 (0-bit columns).  codes: device buffer of r*dout uint16. */
+ * Codes of expert e as one of the device decoders produces them, in k order
+ * ("execution": the width-grouped plane layout read back), for bit-exact
+ * tests of the decode each kernel actually runs.  codes: device buffer of
+ * r*dout uint16, 16-byte aligned; 0-bit columns are 0; a directory record
+ * that fails its check gives 0xFFFF everywhere.  codes[k*dout + i] is
+ *   path BITSMOE_DUMP_I8  : the int8 A-operand byte of the one-launch
+ *                           kernel's apply (q for 1..6-bit columns, q ^ 0x80
+ *                           for 8-bit ones), the fp16 bit pattern of 16-bit
+ *                           columns;
+ *   path BITSMOE_DUMP_F16 : the fp16 A operand of the batched kernel's apply
+ *                           (the fp16 bit pattern of q, or of the stored
+ *                           value for 16-bit columns);
+ *   path BITSMOE_DUMP_LANE: q (1..8-bit), the fp16 bit pattern (16-bit), as
+ *                           read by the lane-per-row kernel of
+ *                           bitsmoe_expert_apply and of gate/up beyond the
+ *                           MFMA kernels' limits.
+ * A path outside these returns BITSMOE_EINVAL. */
+#define BITSMOE_DUMP_I8   0
+#define BITSMOE_DUMP_F16  1
+#define BITSMOE_DUMP_LANE 2
 int bitsmoe_dump_codes(const void* packed, size_t packed_bytes, int E, int dout,
-                       int r, int e, uint16_t* codes, bitsmoe_stream_t stream);
+                       int r, int e, int path, uint16_t* codes,
+                       bitsmoe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -237,28 +237,34 @@ def _plane_codes(words: np.ndarray, w: int, nb: int, n_seg: int) -> np.ndarray:
     return Q.reshape(4 * nb, n_seg * 32)
 
 
-def unpack(blob) -> dict:
+def unpack(blob, experts=None) -> dict:
     """Read codes back: returns dict with per-expert arrays in k order.
 
     'q'   E x r x dout uint16 (codes; fp16 bit patterns for b = 16; 0 for b = 0)
     's','m' E x r float16, 'a' E x r float32 (0 for b = 0), 'bits' E x r uint8,
     'cmax' E float32 (the directory's coefficient bound)
+    experts: None for all, else a list of expert ids; row i of every array
+    then belongs to experts[i].
     """
     H = read_header(blob)
     if H["magic"] != MAGIC or H["version"] != VERSION:
-        raise ValueError("not a v2 BMOE blob")
+        raise ValueError("not a v%d BMOE blob" % VERSION)
     if zlib.crc32(memoryview(blob)[HEADER_BYTES:H["total_bytes"]]) & 0xFFFFFFFF != H["crc32"]:
         raise ValueError("CRC mismatch")
     E, r, dout, dp, ns = H["E"], H["r"], H["dout"], H["dout_pad"], H["n_seg"]
-    q = np.zeros((E, r, dout), dtype=np.uint16)
-    s = np.ones((E, r), dtype=np.float16)
-    m = np.zeros((E, r), dtype=np.float16)
-    a = np.zeros((E, r), dtype=np.float32)
-    bits = np.zeros((E, r), dtype=np.uint8)
-    cmax = np.zeros(E, dtype=np.float32)
+    sel = list(range(E)) if experts is None else [int(e) for e in experts]
+    if any(e < 0 or e >= E for e in sel):
+        raise ValueError("expert id outside [0, %d)" % E)
+    n = len(sel)
+    q = np.zeros((n, r, dout), dtype=np.uint16)
+    s = np.ones((n, r), dtype=np.float16)
+    m = np.zeros((n, r), dtype=np.float16)
+    a = np.zeros((n, r), dtype=np.float32)
+    bits = np.zeros((n, r), dtype=np.uint8)
+    cmax = np.zeros(n, dtype=np.float32)
     buf = np.frombuffer(blob, dtype=np.uint8)
-    for e in range(E):
-        D = read_dir(blob, e)
+    for e, ex in enumerate(sel):
+        D = read_dir(blob, ex)
         cmax[e] = D["cmax"]
         L = _block_layout(list(D["count"]), ns)
         base = D["block_offset"]

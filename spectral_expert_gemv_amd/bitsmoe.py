@@ -58,7 +58,7 @@ _SIGS = {
     "bitsmoe_moe_gateup_noalloc": ([_vp, _sz, _vp, _sz, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                     _i, _vp, _vp], _i),
     "bitsmoe_workspace_init": ([_vp, _sz, _vp], _i),
-    "bitsmoe_dump_codes": ([_vp, _sz, _i, _i, _i, _i, _vp, _vp], _i),
+    "bitsmoe_dump_codes": ([_vp, _sz, _i, _i, _i, _i, _i, _vp, _vp], _i),
     "bitsmoe_debug_set_wait_limit": ([ctypes.c_uint32], ctypes.c_uint32),
     "bitsmoe_pack_device_workspace_size": ([_i, _i, _i, _vp, _psz], _i),
     "bitsmoe_pack_device": ([_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp], _i),
@@ -210,9 +210,15 @@ def debug_set_wait_limit(spins):
     return int(_lib.bitsmoe_debug_set_wait_limit(int(spins)))
 
 
-def dump_codes(packed, E, dout, r, e, codes, stream=None):
-    _check(_lib.bitsmoe_dump_codes(_ptr(packed), _nbytes(packed), E, dout, r, e, _ptr(codes),
-                                   _stream(stream)))
+DUMP_I8, DUMP_F16, DUMP_LANE = 0, 1, 2
+
+
+def dump_codes(packed, E, dout, r, e, codes, path=DUMP_LANE, stream=None):
+    """Codes of expert e as decoder `path` builds them (DUMP_I8: int8 operand
+    bytes of the one-launch kernel; DUMP_F16: fp16 operands of the batched
+    kernel; DUMP_LANE: codes of the lane-per-row kernel)."""
+    _check(_lib.bitsmoe_dump_codes(_ptr(packed), _nbytes(packed), E, dout, r, e, path,
+                                   _ptr(codes), _stream(stream)))
 
 
 def pack_device_workspace_size(E, dout, r, bits):

@@ -11,6 +11,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "bitsmoe.h"
 #include "common.h"
@@ -18,6 +19,7 @@
 #include "format.h"
 #include "kernels.h"
 #include "route.h"
+#include "seg_common.h"
 
 namespace bitsmoe {
 namespace {
@@ -400,8 +402,9 @@ __global__ __launch_bounds__(kGateUp ? 128 : 64) void k_expert_seg(
         (ok && s_ok[lane]) ? silu_mul(y, s_y[lane]) : __builtin_nanf("");
 }
 
-// grid (ceil(n_seg / 2)); block 64: codes of expert e in k order (0-bit
-// columns are left as the caller's zero fill; padding slots are skipped).
+// grid (ceil(n_seg / 2)); block 64: codes of expert e in k order as the
+// lane-per-row decoder of k_expert_seg reads them (0-bit columns are left as
+// the caller's zero fill; padding slots are skipped).
 __global__ __launch_bounds__(64) void k_dump_codes(const uint8_t* __restrict__ blob,
                                                    uint64_t blob_bytes, int E, int dout, int r,
                                                    int e, uint16_t* __restrict__ codes) {
@@ -433,6 +436,107 @@ __global__ __launch_bounds__(64) void k_dump_codes(const uint8_t* __restrict__ b
       }
     }
   }
+}
+
+// Codes as the MFMA kernels' operand builders produce them.  grid (n_seg);
+// block 64 (one wave per 32-row segment, read straight from the blob).
+//  kPath 0: the one-launch kernel's int8 apply: a_i8<W> for widths 1..8 (the
+//           A byte: the code, width 8: code ^ 0x80), a_tiles_f16 for 16-bit
+//           slots, in that kernel's 64-slot steps (the last, odd K32 step
+//           of a group taken as a half step);
+//  kPath 1: the batched kernel's fp16 apply: a_tiles_uniform<W> (fp16 of the
+//           code through codes_to_f16) and a_tiles_f16, in 32-slot steps.
+// Each lane scatters the operand elements it holds to codes[k * dout + row]
+// (k = the slot's component index); padding slots are skipped.
+template <int kPath>
+__global__ __launch_bounds__(64) void k_dump_operands(const uint8_t* __restrict__ blob,
+                                                      uint64_t blob_bytes, int E, int dout, int r,
+                                                      int e, uint16_t* __restrict__ codes) {
+  using namespace seg;
+  const int lane = threadIdx.x, seg_i = blockIdx.x;
+  const DirRec d = load_rec_s(blob, e, E);
+  const SegProj p = uniform_seg(make_seg(blob, blob_bytes, e, d, load_hdr(blob), E, dout, r));
+  if (!p.ok) {
+    const int orow = seg_i * kSegRows + (lane & 31);
+    if (orow < dout)
+      for (int k = lane >> 5; k < r; k += 2) codes[(size_t)k * dout + orow] = 0xFFFFu;
+    return;
+  }
+  // (generic pointers into the blob, as the kernels' LDS copies are read)
+  const uint32_t* base = (const uint32_t*)(p.planes + (size_t)seg_i * p.seg_words);
+  const gu16* kidx = p.kidx;
+  const int m = lane & 15, q = lane >> 4;
+  const uint32_t gb[kNumGroups + 1] = {0u, p.b1, p.b2, p.b3, p.b4, p.b5, p.b6, p.n_blk};
+  const uint32_t gw[kNumGroups] = {0u, p.w1, p.w2, p.w3, p.w4, p.w5, p.w6};
+  // element (block blk of the segment's block list, slot u, row 16 tile + m)
+  auto put = [&](int g, uint32_t blk, int u, int tile, uint32_t v) {
+    if (4u * (blk - gb[g]) + (uint32_t)u >= d.count[g]) return;  // padding slot
+    const uint32_t k = kidx[4u * blk + (uint32_t)u];
+    const int orow = seg_i * kSegRows + 16 * tile + m;
+    if (k < (uint32_t)r && orow < dout) codes[(size_t)k * dout + orow] = (uint16_t)v;
+  };
+  // fp16 operands of K32 step kb: this lane's blocks 8 kb + 2 q + t, element
+  // 4 t + u of tile `tile`
+  auto put_h8 = [&](int g, uint32_t kb, const h8& a0, const h8& a1) {
+    const uint4 v0 = __builtin_bit_cast(uint4, a0), v1 = __builtin_bit_cast(uint4, a1);
+    const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t blk = 8u * kb + 2u * (uint32_t)q + (uint32_t)(j >> 2);
+      put(g, blk, j & 3, 0, (w0[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      put(g, blk, j & 3, 1, (w1[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+    }
+  };
+  auto f16_steps = [&](int g, auto wc) {
+    constexpr int W = decltype(wc)::value;
+    constexpr uint32_t bw = 4u * (uint32_t)W;
+    for (uint32_t kb = gb[g] / kBlkPerK; kb < gb[g + 1] / kBlkPerK; ++kb) {
+      const uint32_t* rec0 = base + gw[g] + (kBlkPerK * kb - gb[g]) * bw + 2u * bw * (uint32_t)q;
+      h8 a0, a1;
+      if constexpr (W == 16)
+        a_tiles_f16(rec0, m, a0, a1);
+      else
+        a_tiles_uniform<W>(rec0, m, a0, a1);
+      put_h8(g, kb, a0, a1);
+    }
+  };
+  auto i8_steps = [&](int g, auto wc) {
+    constexpr int W = decltype(wc)::value;
+    const uint32_t s = gb[g] / kBlkPerK, e_ = gb[g + 1] / kBlkPerK;
+    for (uint32_t k = s; k < e_; k += 2) {
+      if (!(q < 2 || k + 1 < e_)) continue;  // upper half of a trailing half step
+      const uint32_t* rec = base + gw[g] + (8u * k + 4u * (uint32_t)q - gb[g]) * 4u * W;
+      for (int tile = 0; tile < 2; ++tile) {
+        const i32x4 a = a_i8<W>(rec, m, tile);
+        for (int dd = 0; dd < 4; ++dd)
+          for (int u = 0; u < 4; ++u)
+            put(g, 8u * k + 4u * (uint32_t)q + (uint32_t)dd, u, tile,
+                ((uint32_t)a[dd] >> (8 * u)) & 0xFFu);
+      }
+    }
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I6 = std::integral_constant<int, 6>;
+  using I8 = std::integral_constant<int, 8>;
+  using I16 = std::integral_constant<int, 16>;
+  if constexpr (kPath == 0) {
+    i8_steps(0, I1{});
+    i8_steps(1, I2{});
+    i8_steps(2, I3{});
+    i8_steps(3, I4{});
+    i8_steps(4, I6{});
+    i8_steps(5, I8{});
+  } else {
+    f16_steps(0, I1{});
+    f16_steps(1, I2{});
+    f16_steps(2, I3{});
+    f16_steps(3, I4{});
+    f16_steps(4, I6{});
+    f16_steps(5, I8{});
+  }
+  f16_steps(6, I16{});
 }
 
 __global__ __launch_bounds__(256) void k_zero_fill(uint4* __restrict__ p, size_t n16,
@@ -814,17 +918,27 @@ uint32_t bitsmoe_debug_set_wait_limit(uint32_t spins) {
 }
 
 int bitsmoe_dump_codes(const void* packed, size_t packed_bytes, int E, int dout, int r, int e,
-                       uint16_t* codes, bitsmoe_stream_t stream) {
+                       int path, uint16_t* codes, bitsmoe_stream_t stream) {
   int st = check_layer_dims(E, dout, r);
   if (st) return st;
   if ((st = check_blob_arg(packed, packed_bytes, E, "packed"))) return st;
   if (!codes) return fail(BITSMOE_EINVAL, "codes is null");
   if (!aligned16(codes)) return fail(BITSMOE_EINVAL, "codes is not 16-byte aligned");
   if (e < 0 || e >= E) return fail(BITSMOE_EINVAL, "e=%d outside [0,%d)", e, E);
+  if (path < 0 || path > 2) return fail(BITSMOE_EINVAL, "path=%d outside [0,2]", path);
   hipStream_t s = (hipStream_t)stream;
   if ((st = bitsmoe_workspace_init(codes, (size_t)r * dout * 2, stream))) return st;
-  hipLaunchKernelGGL(k_dump_codes, dim3((dout + 2 * kSegRows - 1) / (2 * kSegRows)), dim3(64), 0, s,
-                     (const uint8_t*)packed, (uint64_t)packed_bytes, E, dout, r, e, codes);
+  const int n_seg = (dout + kSegRows - 1) / kSegRows;
+  const uint8_t* b = (const uint8_t*)packed;
+  if (path == 0)
+    hipLaunchKernelGGL(k_dump_operands<0>, dim3(n_seg), dim3(64), 0, s, b,
+                       (uint64_t)packed_bytes, E, dout, r, e, codes);
+  else if (path == 1)
+    hipLaunchKernelGGL(k_dump_operands<1>, dim3(n_seg), dim3(64), 0, s, b,
+                       (uint64_t)packed_bytes, E, dout, r, e, codes);
+  else
+    hipLaunchKernelGGL(k_dump_codes, dim3((n_seg + 1) / 2), dim3(64), 0, s, b,
+                       (uint64_t)packed_bytes, E, dout, r, e, codes);
   return launch_status("code dump launch");
 }
 

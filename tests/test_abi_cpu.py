@@ -192,8 +192,10 @@ def test_device_entry_points_validate_before_launch():
     assert gun(h=None) == bm.EINVAL
     assert gun(h=FAKE + 4) == bm.EINVAL
     # code dump
-    assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 4, FAKE, None) == bm.EINVAL
-    assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 0, None, None) == bm.EINVAL
+    assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 4, 0, FAKE, None) == bm.EINVAL
+    assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 0, 0, None, None) == bm.EINVAL
+    assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 0, 3, FAKE, None) == bm.EINVAL
+    assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 0, -1, FAKE, None) == bm.EINVAL
     assert L.bitsmoe_workspace_init(None, 16, None) == bm.EINVAL
     assert bm._lib.bitsmoe_last_error_detail()
 

@@ -62,19 +62,47 @@ def _run_gateup(dev, x, ids):
 
 # ------------------------------------------------------------------ codes
 
-@pytest.mark.parametrize("name,experts", [("tiny", None), ("qwen3_30b_a3b", [0, 17, 127])])
+def _expected_operands(bm, q, bits, path):
+    """What decoder `path` must produce from codes q (r x dout, the oracle
+    unpacker's) of columns of widths bits (r): DUMP_I8 takes the int8 operand
+    byte (code - 128 for 8-bit columns, i.e. the code with its top bit
+    flipped), DUMP_F16 the fp16 bit pattern of the code; 16-bit columns keep
+    their stored fp16 bits and 0-bit columns are 0 on every path."""
+    out = q.copy()
+    if path == bm.DUMP_I8:
+        w8 = bits == 8
+        out[w8] = q[w8] ^ 0x80
+    elif path == bm.DUMP_F16:
+        small = (bits > 0) & (bits < 16)
+        out[small] = q[small].astype(np.float16).view(np.uint16)
+    return out
+
+
+@pytest.mark.parametrize("name,experts", [("tiny", None), ("wide", None), ("heavy", None),
+                                          ("qwen3_30b_a3b", [0, 17, 127]),
+                                          ("mixtral_8x7b", [3])])
 def test_codes_bit_exact(bm, name, experts):
+    """Every decoder the kernels run, read back through the kernels' own
+    operand builders, equals the oracle unpacker's codes bit for bit: every
+    width group, every row of every segment (ragged dout on wide and heavy),
+    all experts of the small layers."""
     L, dev = device_layer(name)
     spec = L.spec
-    for proj, blob in (("gate", dev.blob_gate), ("up", dev.blob_up)):
-        ref = fmt.unpack(dev.host_blobs[0 if proj == "gate" else 1].tobytes())["q"]
+    sel = list(range(spec.E)) if experts is None else experts
+    for pj, (proj, blob) in enumerate((("gate", dev.blob_gate), ("up", dev.blob_up))):
+        ref = fmt.unpack(dev.host_blobs[pj].tobytes(), experts=sel)
         codes = torch.empty((spec.r, spec.dout), dtype=torch.int16, device="cuda")
-        for e in (range(spec.E) if experts is None else experts):
-            _say("codes %s %s e=%d" % (name, proj, e))
-            bm.dump_codes(blob, spec.E, spec.dout, spec.r, e, codes)
-            torch.cuda.synchronize()
-            got = codes.cpu().numpy().view(np.uint16)
-            assert np.array_equal(got, ref[e]), (proj, e)
+        for i, e in enumerate(sel):
+            for path in (bm.DUMP_I8, bm.DUMP_F16, bm.DUMP_LANE):
+                _say("codes %s %s e=%d path=%d" % (name, proj, e, path))
+                bm.dump_codes(blob, spec.E, spec.dout, spec.r, e, codes, path=path)
+                torch.cuda.synchronize()
+                got = codes.cpu().numpy().view(np.uint16)
+                want = _expected_operands(bm, ref["q"][i], ref["bits"][i], path)
+                assert np.array_equal(got, want), (proj, e, path,
+                                                   int(np.count_nonzero(got != want)))
+    if name == "tiny":  # every width group, each one K32 step (a half int8 step)
+        assert set(np.unique(L.bits["up"]).tolist()) == {0, 1, 2, 3, 4, 6, 8, 16}
 
 
 def test_codes_match_oracle_quantizer(bm):

@@ -112,6 +112,22 @@ def test_round_trip_all_widths(dout):
         assert np.all(out["a"][e][~nz] == 0)
 
 
+def test_unpack_subset_of_experts():
+    """unpack(blob, experts) gives the same rows as the full unpack, in the
+    order asked for, and refuses ids outside [0, E)."""
+    E, r, dout = 4, 24, 70
+    rng = np.random.default_rng(7)
+    bits = rng.choice([0, 1, 2, 3, 4, 6, 8, 16], size=(E, r))
+    p, a, bits = _random_layer(E, r, dout, bits, 7)
+    blob = fmt.pack(p, a, bits)
+    full = fmt.unpack(blob)
+    sub = fmt.unpack(blob, experts=[2, 0])
+    for key in ("q", "s", "m", "a", "bits", "cmax"):
+        assert np.array_equal(sub[key], full[key][[2, 0]]), key
+    with pytest.raises(ValueError):
+        fmt.unpack(blob, experts=[4])
+
+
 def test_header_alignment_and_crc():
     p, a, bits = _random_layer(3, 16, 96, np.random.default_rng(5).choice(
         [0, 1, 2, 3, 4, 6, 8, 16], size=(3, 16)), 5)
