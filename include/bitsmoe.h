@@ -150,22 +150,31 @@ int bitsmoe_pack_device(int E, int dout, int r, const float* p, const float* a,
  *   outside [0, E) are skipped).  Async on `stream`.
  * bitsmoe_fqcm_allocate: widths bits[e*r + k] (device uint8) minimising
  *   sum L(b) with L(b) = ((a*a)*beta)*eps(b) (float64) subject to
- *   sum dout*b <= budget_bits, by the Lagrangian relaxation: each column
- *   minimises L(b) + lam*(dout*b) (ties to the narrower width) at the
- *   smallest double lam >= 0 whose total fits (bisection over the bit
- *   patterns of doubles).  The result is an exact optimum for the bits it
- *   uses (*used_bits <= budget_bits); *lambda gets lam.  ws: device memory
- *   of BITSMOE_FQCM_WS_BYTES bytes, 8-byte aligned.  The call synchronizes
- *   `stream` once per bisection step (at most 65 steps).
+ *   sum dout*b <= budget_bits: the integer program's exact minimum (ties to
+ *   the narrower width, then to the fewest bits; float64 sums, so two
+ *   allocations whose losses differ only by rounding may be taken either
+ *   way).  Steps: the Lagrangian relaxation (each column minimises
+ *   L(b) + lam*(dout*b), ties to the narrower width, at the smallest double
+ *   lam >= 0 whose total fits: bisection over the bit patterns of doubles),
+ *   then an exact step over the columns whose reduced cost at lam is within
+ *   the gap to the dual bound.  *used_bits <= budget_bits gets the bits
+ *   used, *lambda lam, *lp_gap the loss minus the dual bound
+ *   D(lam) = sum_c min_b (L_c(b) + lam*dout*b) - lam*dout*floor(budget/dout)
+ *   (0 when the Lagrangian widths use the whole budget; any pointer may be
+ *   NULL).  BITSMOE_ENOSPC when more than 65536 alternatives, or more than
+ *   2^28 column x unit states, fall within that gap (not seen on the
+ *   synthetic layers).  ws: device memory of BITSMOE_FQCM_WS_BYTES bytes,
+ *   8-byte aligned.  The call synchronizes `stream` once per bisection step
+ *   (at most 65 + 64 steps) and runs the exact step on the host.
  */
-#define BITSMOE_FQCM_WS_BYTES 1024
+#define BITSMOE_FQCM_WS_BYTES ((size_t)1024 + 65536 * 24)
 int bitsmoe_fqcm_distortion(const float* p, int E, int r, int dout, double* eps,
                             bitsmoe_stream_t stream);
 int bitsmoe_fqcm_beta(const float* z, int z_stride, const int32_t* ids, const float* g, int T,
                       int k, int E, int r, double* beta, bitsmoe_stream_t stream);
 int bitsmoe_fqcm_allocate(const float* a, const double* beta, const double* eps, int E, int r,
                           int dout, uint64_t budget_bits, uint8_t* bits, double* lambda,
-                          uint64_t* used_bits, void* ws, size_t ws_bytes,
+                          uint64_t* used_bits, double* lp_gap, void* ws, size_t ws_bytes,
                           bitsmoe_stream_t stream);
 
 /* Host-side check of a blob in host memory: magic, version, sizes, CRC and

@@ -18,23 +18,26 @@ Readings used here (the pages leave these steps open):
     ((a * a) * beta) * eps in float64.
   * Budget: sum over columns of dout * b <= budget bits (the pages count a
     wider code by its m = dout extra bits per unit of width; metadata and
-    group padding are not counted).
-  * Solver: the Lagrangian relaxation of that integer program.  For a
-    multiplier lam >= 0 each column takes the width minimising
-    L(b) + lam * (dout * b) (float64, ties to the narrower width); the total
-    is non-increasing in lam, and the result is the allocation at the
-    smallest float64 lam whose total fits the budget (bisection over the
-    ordered bit patterns of non-negative doubles).  Such an allocation is an
-    exact optimum of the integer program for the bits it uses (every other
-    allocation that uses no more bits has a loss at least as large); what it
-    leaves unused is below the next step of the hull.
+    group padding are not counted), i.e. sum of b <= floor(budget / dout)
+    budget units.
+  * Solver: the integer program itself, solved exactly (allocate): a plain
+    dynamic program over the columns in order and the budget units used so
+    far, float64 sums, ties to the narrower width at each column and, among
+    equal totals, to the fewest units.  Any solver giving the same minimum
+    is equivalent; this one is here because a reader can check it by eye.
+  * The Lagrangian relaxation (lagrangian, lp_bound) is kept for the
+    multiplier the library reports and for the dual bound: for a multiplier
+    lam >= 0 each column takes the width minimising L(b) + lam * (dout * b)
+    (float64, ties to the narrower width), lam is the smallest float64 whose
+    total fits (bisection over the ordered bit patterns of non-negative
+    doubles), and D(lam) = sum over columns of that minimum - lam * dout *
+    floor(budget / dout) is a lower bound on every allocation's loss.
 
 Pinned by tests/test_oracle_fqcm.py: closed forms of eps (dropped column,
 exact two-level columns, fp16-exact columns), brute-force beta loops,
-brute-force enumeration of every allocation on tiny instances (optimality for
-the bits used), an exact dynamic program on small instances (never better
-than the optimum, equal where the budget falls on the hull), and planted
-mistakes.
+brute-force enumeration of every allocation on tiny instances (the dynamic
+program's minimum is the brute-force minimum), a hand-built instance where
+the Lagrangian result is not optimal, the dual bound, and planted mistakes.
 """
 import numpy as np
 
@@ -96,8 +99,9 @@ def _bits_used(idx: np.ndarray, dout: int) -> int:
     return int(np.array(WIDTHS, dtype=np.int64)[idx].sum()) * int(dout)
 
 
-def allocate(a: np.ndarray, bet: np.ndarray, eps: np.ndarray, dout: int, budget_bits: int):
-    """Returns (bits uint8 like a, lam float64, bits used)."""
+def lagrangian(a: np.ndarray, bet: np.ndarray, eps: np.ndarray, dout: int, budget_bits: int):
+    """Lagrangian relaxation: returns (bits uint8 like a, lam float64, bits
+    used) at the smallest lam whose allocation fits."""
     L = losses(a, bet, eps)
     widths = np.array(WIDTHS, dtype=np.uint8)
     idx0 = choose(L, dout, 0.0)
@@ -116,6 +120,49 @@ def allocate(a: np.ndarray, bet: np.ndarray, eps: np.ndarray, dout: int, budget_
     lam = float(np.uint64(hi).view(np.float64))
     idx = choose(L, dout, lam)
     return widths[idx], lam, _bits_used(idx, dout)
+
+
+def lp_bound(a, bet, eps, dout: int, budget_bits: int, lam: float) -> float:
+    """Dual bound D(lam) <= the loss of every allocation within the budget."""
+    L = losses(a, bet, eps).reshape(-1, len(WIDTHS))
+    cost = L + np.float64(lam) * (np.float64(dout) * np.array(WIDTHS, dtype=np.float64))
+    return float(cost.min(axis=1).sum()) - float(lam) * float(dout) * float(budget_bits // dout)
+
+
+def allocate(a: np.ndarray, bet: np.ndarray, eps: np.ndarray, dout: int, budget_bits: int):
+    """Minimum-loss widths within the budget.  Returns (bits uint8 like a,
+    bits used).
+
+    best[u] holds the least loss of the columns so far using exactly u units
+    (inf where no choice reaches u); column c moves it to min over widths w
+    of best[u - w] + L_c(w).  The answer is the least best[u] over u <= the
+    budget units, read back through the recorded choices."""
+    L = losses(a, bet, eps).reshape(-1, len(WIDTHS))
+    n = L.shape[0]
+    W = np.array(WIDTHS, dtype=np.int64)
+    U = int(min(budget_bits // dout, int(W[-1]) * n))
+    best = np.full(U + 1, np.inf)
+    best[0] = 0.0
+    pick = np.zeros((n, U + 1), dtype=np.uint8)
+    for c in range(n):
+        new = np.full(U + 1, np.inf)
+        for i, w in enumerate(W):          # narrower widths first: they keep ties
+            if w > U:
+                break
+            cand = np.full(U + 1, np.inf)
+            cand[w:] = best[:U + 1 - w] + L[c, i]
+            better = cand < new
+            new[better] = cand[better]
+            pick[c, better] = i
+        best = new
+    u = int(np.argmin(best))                # first minimum: the fewest units
+    idx = np.zeros(n, dtype=np.int64)
+    for c in range(n - 1, -1, -1):
+        idx[c] = pick[c, u]
+        u -= int(W[idx[c]])
+    assert u == 0
+    bits = W[idx].astype(np.uint8).reshape(np.shape(a))
+    return bits, int(W[idx].sum()) * int(dout)
 
 
 def total_loss(a, bet, eps, bits) -> float:

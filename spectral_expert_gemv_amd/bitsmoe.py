@@ -66,14 +66,14 @@ _SIGS = {
     "bitsmoe_fqcm_beta": ([_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _vp], _i),
     "bitsmoe_fqcm_allocate": ([_vp, _vp, _vp, _i, _i, _i, ctypes.c_uint64, _vp,
                                ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_uint64),
-                               _vp, _sz, _vp], _i),
+                               ctypes.POINTER(ctypes.c_double), _vp, _sz, _vp], _i),
     "bitsmoe_moe_down_workspace_size": ([_i, _i, _i, _i, _i, _i, _psz], _i),
     "bitsmoe_moe_down": ([_vp, _sz, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _sz,
                           _vp], _i),
     "bitsmoe_ssd_workspace_size": ([_i, _i, _i, _i, _psz], _i),
     "bitsmoe_ssd": ([_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _pi, _i, _vp, _sz, _vp], _i),
 }
-FQCM_WS_BYTES = 1024
+FQCM_WS_BYTES = 1024 + 65536 * 24
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
     _f.argtypes = _args
@@ -284,8 +284,9 @@ def fqcm_beta(z, ids, g, E, beta=None, stream=None):
 
 
 def fqcm_allocate(a, beta, eps, dout, budget_bits, bits=None, ws=None, stream=None):
-    """Widths under the bit budget; returns (bits uint8 device tensor E x r,
-    lam, bits used)."""
+    """Least-loss widths within the bit budget; returns (bits uint8 device
+    tensor E x r, the Lagrangian multiplier lam, bits used, loss minus the
+    dual bound at lam)."""
     import torch
     E, r = a.shape
     if bits is None:
@@ -294,11 +295,12 @@ def fqcm_allocate(a, beta, eps, dout, budget_bits, bits=None, ws=None, stream=No
         ws = torch.empty(FQCM_WS_BYTES, dtype=torch.uint8, device=a.device)
     lam = ctypes.c_double(0.0)
     used = ctypes.c_uint64(0)
+    gap = ctypes.c_double(0.0)
     _check(_lib.bitsmoe_fqcm_allocate(_ptr(a), _ptr(beta), _ptr(eps), E, r, dout,
                                       int(budget_bits), _ptr(bits), ctypes.byref(lam),
-                                      ctypes.byref(used), _ptr(ws), _nbytes(ws),
-                                      _stream(stream)))
-    return bits, lam.value, used.value
+                                      ctypes.byref(used), ctypes.byref(gap), _ptr(ws),
+                                      _nbytes(ws), _stream(stream)))
+    return bits, lam.value, used.value, gap.value
 
 
 def moe_down_workspace_size(T, k, E, dout, din, r_d):

@@ -236,7 +236,10 @@ def test_fqcm_entry_points_validate_before_launch():
     used = ctypes.c_uint64()
     def al(ws_bytes=bm.FQCM_WS_BYTES, ws=FAKE, bits=FAKE, E=2):
         return L.bitsmoe_fqcm_allocate(FAKE, FAKE, FAKE, E, 3, 4, 100, bits, ctypes.byref(lam),
-                                       ctypes.byref(used), ws, ws_bytes, None)
+                                       ctypes.byref(used), None, ws, ws_bytes, None)
+    hdr = open(os.path.join(ROOT, "include", "bitsmoe.h")).read()
+    m = re.search(r"#define BITSMOE_FQCM_WS_BYTES \(\(size_t\)(\d+) \+ (\d+) \* (\d+)\)", hdr)
+    assert m and int(m.group(1)) + int(m.group(2)) * int(m.group(3)) == bm.FQCM_WS_BYTES
     assert al(ws_bytes=bm.FQCM_WS_BYTES - 1) == bm.ENOSPC
     assert al(ws=None) == bm.EINVAL
     assert al(bits=None) == bm.EINVAL

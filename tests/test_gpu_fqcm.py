@@ -6,9 +6,11 @@ Bars:
   the same float64 operations); only the order of the float64 sums differs:
   |d eps| <= 1e-12 * eps(0) per column.
 * beta: the same float64 operations in the same pair order: bit-exact.
-* allocation: given the same a, beta, eps both sides take every decision in
-  float64 with the same expressions: widths, lam and the bits used are
-  bit-exact.
+* allocation: the integer program's minimum (the oracle's dynamic program
+  over budget units): the widths and bits used bit-exact, except that two
+  allocations whose float64 losses agree to 1e-12 (sums in another order)
+  may be taken either way; the Lagrangian multiplier lam bit-exact (same
+  float64 expressions); lp_gap = loss - the oracle's dual bound at lam.
 """
 import sys
 
@@ -118,19 +120,60 @@ def _alloc_inputs(E, r, seed):
     return a, bet, eps
 
 
-@pytest.mark.parametrize("E,r,dout", [(1, 5, 7), (3, 40, 96), (128, 2048, 768)])
-def test_allocation_matches_oracle_bit_exact(bm, E, r, dout):
+def _check_alloc(bm, a, bet, eps, dout, budget, got_bits, used, gap):
+    rb, rused = fqcm.allocate(a, bet, eps, dout, budget)
+    loss = fqcm.total_loss(a, bet, eps, got_bits)
+    rloss = fqcm.total_loss(a, bet, eps, rb)
+    assert used <= budget and used == int(got_bits.astype(np.int64).sum()) * dout
+    if not np.array_equal(got_bits, rb):
+        # only a float64 near tie may differ
+        assert abs(loss - rloss) <= 1e-12 * max(rloss, 1e-300), (loss, rloss)
+    else:
+        assert used == rused
+    return loss
+
+
+@pytest.mark.parametrize("E,r,dout", [(1, 5, 7), (3, 40, 96), (8, 256, 64)])
+def test_allocation_matches_oracle(bm, E, r, dout):
     a, bet, eps = _alloc_inputs(E, r, E * r)
     full = 16 * dout * E * r
     ad, bd, ed = _cuda(a), _cuda(bet), _cuda(eps)
     for frac in (0.0, 0.01, 0.15, 0.3, 0.6, 1.0):
-        budget = int(frac * full)
+        budget = int(frac * full) + (dout // 3 if 0 < frac < 1 else 0)
         _say("allocate E=%d r=%d budget=%d" % (E, r, budget))
-        bits, lam, used = bm.fqcm_allocate(ad, bd, ed, dout, budget)
-        rb, rlam, rused = fqcm.allocate(a, bet, eps, dout, budget)
-        assert lam == rlam and used == rused, (lam, rlam, used, rused)
-        assert np.array_equal(bits.cpu().numpy(), rb)
-        assert used <= budget
+        bits, lam, used, gap = bm.fqcm_allocate(ad, bd, ed, dout, budget)
+        bits = bits.cpu().numpy()
+        _, rlam, _ = fqcm.lagrangian(a, bet, eps, dout, budget)
+        assert lam == rlam, (lam, rlam)
+        loss = _check_alloc(bm, a, bet, eps, dout, budget, bits, used, gap)
+        bound = fqcm.lp_bound(a, bet, eps, dout, budget, lam)
+        assert gap >= 0.0 and abs((loss - bound) - gap) <= 1e-9 * loss + 1e-300, (gap, loss, bound)
+
+
+def test_allocation_full_size_against_lagrangian_and_bound(bm):
+    """Qwen3-shaped gate projection (262 144 columns): too large for the
+    oracle's dynamic program, so the checks are the Lagrangian multiplier
+    (bit-exact), a loss never above the Lagrangian widths', the bits within
+    the budget, and lp_gap = loss - the oracle's dual bound (printed)."""
+    E, r, dout = 128, 2048, 768
+    a, bet, eps = _alloc_inputs(E, r, E * r)
+    full = 16 * dout * E * r
+    ad, bd, ed = _cuda(a), _cuda(bet), _cuda(eps)
+    for frac in (0.01, 0.15, 0.3, 0.6):
+        budget = int(frac * full) + 101
+        bits, lam, used, gap = bm.fqcm_allocate(ad, bd, ed, dout, budget)
+        bits = bits.cpu().numpy()
+        lb, rlam, lused = fqcm.lagrangian(a, bet, eps, dout, budget)
+        assert lam == rlam
+        loss = fqcm.total_loss(a, bet, eps, bits)
+        lag = fqcm.total_loss(a, bet, eps, lb)
+        bound = fqcm.lp_bound(a, bet, eps, dout, budget, lam)
+        assert used <= budget and used == int(bits.astype(np.int64).sum()) * dout
+        assert used >= lused and loss <= lag * (1 + 1e-12)
+        assert gap >= 0.0 and abs((loss - bound) - gap) <= 1e-9 * loss
+        _say("full size frac=%.2f: loss %.9e, Lagrangian %.9e, LP bound %.9e, gap %.3e "
+             "(%.2e of the loss), units left %d" % (frac, loss, lag, bound, gap, gap / loss,
+                                                   (budget - used) // dout))
 
 
 def test_fqcm_chain_feeds_the_device_packer(bm):
@@ -148,15 +191,15 @@ def test_fqcm_chain_feeds_the_device_packer(bm):
     eps = bm.fqcm_distortion(pd)
     bet = bm.fqcm_beta(_cuda(z), _cuda(ids), _cuda(g), spec.E)
     budget = int(L.bits["gate"].astype(np.int64).sum()) * spec.dout
-    bits, lam, used = bm.fqcm_allocate(ad, bet, eps, spec.dout, budget)
+    bits, lam, used, gap = bm.fqcm_allocate(ad, bet, eps, spec.dout, budget)
     bits = bits.cpu().numpy()
     assert used <= budget and used == int(bits.astype(np.int64).sum()) * spec.dout
     assert set(np.unique(bits)) <= set(fqcm.WIDTHS)
     blob = bm.pack_device(pd, ad, bits).cpu().numpy()
     assert bm.blob_check(blob) == (spec.E, spec.dout, spec.r)
     # the oracle, from the same z, routing and p, gives the same widths
-    rb, rlam, rused = fqcm.allocate(a, fqcm.beta(z, ids, g, spec.E),
-                                    fqcm.distortion(P.reshape(-1, spec.dout)).reshape(
-                                        spec.E, spec.r, 8), spec.dout, budget)
+    rb, rused = fqcm.allocate(a, fqcm.beta(z, ids, g, spec.E),
+                              fqcm.distortion(P.reshape(-1, spec.dout)).reshape(
+                                  spec.E, spec.r, 8), spec.dout, budget)
     agree = np.mean(rb == bits)
     assert agree >= 0.98, agree   # float64 sums in another order may move a near tie

@@ -6,11 +6,13 @@
   represents exactly give 0 (two-level columns at b = 1, fp16 values at 16).
 * beta: the one-hot routing matrix form G^T (z * z), a different order of
   summation; linearity in the routing weights; unrouted experts stay 0.
-* allocation: brute force over every allocation of tiny instances (the
-  result is optimal for the bits it uses); an exact dynamic program over
-  the budget on small instances (never better than the optimum at the bits
-  used, never worse than the Lagrangian at the full budget); the end points
-  of the budget.
+* allocation (the integer program's minimum within the budget): brute force
+  over every allocation of tiny instances gives the same minimum loss (and
+  the same widths where that minimum is unique); a hand-built instance whose
+  Lagrangian result leaves a unit unused that the optimum spends; the dual
+  bound D(lam) is never above it; at a budget the Lagrangian result uses up,
+  both agree; the end points of the budget.
+* Lagrangian: optimal for the bits it uses (brute force).
 """
 import itertools
 import json
@@ -88,71 +90,106 @@ def _tiny(n, seed, dout=6):
     return a, bet, eps, dout
 
 
-def _brute_best(L, dout, budget):
-    best = math.inf
+def _brute(L, dout, budget):
+    """(least loss, its allocations) over every allocation within budget;
+    losses summed in column order, as float64."""
+    best, arg = math.inf, []
     for combo in itertools.product(range(len(W)), repeat=L.shape[0]):
-        used = int(W[list(combo)].sum()) * dout
-        if used <= budget:
-            best = min(best, float(sum(L[i, c] for i, c in enumerate(combo))))
-    return best
+        if int(W[list(combo)].sum()) * dout > budget:
+            continue
+        v = 0.0
+        for i, c in enumerate(combo):
+            v += float(L[i, c])
+        if v < best * (1 - 1e-12):
+            best, arg = v, [combo]
+        elif v <= best * (1 + 1e-12):
+            arg.append(combo)
+    return best, arg
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
-def test_allocation_is_optimal_for_the_bits_it_uses(seed):
+def test_lagrangian_is_optimal_for_the_bits_it_uses(seed):
     a, bet, eps, dout = _tiny(4, seed)
     L = fqcm.losses(a, bet, eps)
     for budget in (0, dout, 5 * dout, 11 * dout, 23 * dout, 40 * dout, 64 * dout):
-        bits, lam, used = fqcm.allocate(a, bet, eps, dout, budget)
+        bits, lam, used = fqcm.lagrangian(a, bet, eps, dout, budget)
         assert used <= budget and used == int(bits.astype(np.int64).sum()) * dout
         got = fqcm.total_loss(a, bet, eps, bits)
-        best = _brute_best(L, dout, used)
+        best, _ = _brute(L, dout, used)
         assert got <= best * (1 + 1e-12) + 1e-300, (seed, budget, got, best)
 
 
-def _dp_best(L, dout, budget):
-    """Exact multiple-choice knapsack over budget units of dout bits."""
-    units = budget // dout
-    cur = np.zeros(units + 1)
-    for i in range(L.shape[0]):
-        nxt = np.full(units + 1, np.inf)
-        for c, w in enumerate(W):
-            if w <= units:
-                cand = np.full(units + 1, np.inf)
-                cand[w:] = cur[:units + 1 - w] + L[i, c]
-                nxt = np.minimum(nxt, cand)
-        cur = np.minimum.accumulate(nxt)
-    return float(cur[units])
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 6])
+def test_allocation_is_the_brute_force_minimum(seed):
+    a, bet, eps, dout = _tiny(4, seed)
+    L = fqcm.losses(a, bet, eps)
+    for units in (0, 1, 2, 3, 5, 7, 11, 13, 19, 23, 31, 40, 64):
+        budget = units * dout + (seed % 3)      # a remainder below one unit
+        bits, used = fqcm.allocate(a, bet, eps, dout, budget)
+        assert used <= budget and used == int(bits.astype(np.int64).sum()) * dout
+        got = fqcm.total_loss(a, bet, eps, bits)
+        best, arg = _brute(L, dout, budget)
+        assert abs(got - best) <= 1e-12 * best + 1e-300, (seed, units, got, best)
+        if len(arg) == 1:
+            assert np.array_equal(bits, W[list(arg[0])]), (seed, units)
+
+
+def test_allocation_spends_what_the_lagrangian_leaves():
+    """Three columns, 3 budget units (dout = 1, a = beta = 1, so L = eps):
+    A drops 10 at width 2, B drops 9 at width 2, C drops 4 at width 1.  The
+    multiplier that first fits (4.5) takes A alone (2 units, loss 13); the
+    optimum adds C in the unit left over (loss 9)."""
+    eps = np.array([[10, 10, 0, 0, 0, 0, 0, 0],
+                    [9, 9, 0, 0, 0, 0, 0, 0],
+                    [4, 0, 0, 0, 0, 0, 0, 0]], dtype=np.float64)
+    a = np.ones(3, np.float32)
+    bet = np.ones(3)
+    bits, lam, used = fqcm.lagrangian(a, bet, eps, 1, 3)
+    assert list(bits) == [2, 0, 0] and lam == 4.5 and used == 2
+    assert fqcm.total_loss(a, bet, eps, bits) == 13.0
+    bits, used = fqcm.allocate(a, bet, eps, 1, 3)
+    assert list(bits) == [2, 0, 1] and used == 3
+    assert fqcm.total_loss(a, bet, eps, bits) == 9.0
+    assert fqcm.lp_bound(a, bet, eps, 1, 3, 4.5) <= 9.0
 
 
 @pytest.mark.parametrize("seed", [4, 5])
-def test_allocation_against_exact_dynamic_program(seed):
+def test_allocation_against_lagrangian_and_dual_bound(seed):
     a, bet, eps, dout = _tiny(12, seed)
-    L = fqcm.losses(a, bet, eps)
     for units in (3, 17, 40, 77, 150):
         budget = units * dout
-        bits, lam, used = fqcm.allocate(a, bet, eps, dout, budget)
+        bits, used = fqcm.allocate(a, bet, eps, dout, budget)
         got = fqcm.total_loss(a, bet, eps, bits)
-        assert _dp_best(L, dout, budget) <= got * (1 + 1e-12)
-        assert abs(_dp_best(L, dout, used) - got) <= 1e-12 * got
+        lb, lam, lused = fqcm.lagrangian(a, bet, eps, dout, budget)
+        lag = fqcm.total_loss(a, bet, eps, lb)
+        assert got <= lag * (1 + 1e-12)                 # never worse than the relaxation
+        for f in (0.0, 0.5, 1.0, 2.0):                   # weak duality
+            assert fqcm.lp_bound(a, bet, eps, dout, budget, f * lam) <= got * (1 + 1e-12)
+        # at the bits the Lagrangian result uses, it is optimal: equal losses
+        b2, u2 = fqcm.allocate(a, bet, eps, dout, lused)
+        assert abs(fqcm.total_loss(a, bet, eps, b2) - lag) <= 1e-12 * lag
 
 
 def test_allocation_end_points():
     a, bet, eps, dout = _tiny(6, 9)
-    bits, lam, used = fqcm.allocate(a, bet, eps, dout, 0)
+    bits, used = fqcm.allocate(a, bet, eps, dout, 0)
     assert np.all(bits == 0) and used == 0
-    bits, lam, used = fqcm.allocate(a, bet, eps, dout, 10 ** 9)
-    assert lam == 0.0
+    bits, used = fqcm.allocate(a, bet, eps, dout, dout - 1)   # less than one unit
+    assert np.all(bits == 0) and used == 0
+    bits, used = fqcm.allocate(a, bet, eps, dout, 10 ** 9)
     L = fqcm.losses(a, bet, eps)
     assert np.array_equal(bits, W[np.argmin(L, axis=1)])
+    bits, lam, used = fqcm.lagrangian(a, bet, eps, dout, 10 ** 9)
+    assert lam == 0.0 and np.array_equal(bits, W[np.argmin(L, axis=1)])
     # an expert that calibration never routes to gets no bits
     bet0 = bet.copy()
     bet0[2] = 0.0
-    bits, lam, used = fqcm.allocate(a, bet0, eps, dout, 30 * dout)
+    bits, used = fqcm.allocate(a, bet0, eps, dout, 30 * dout)
     assert bits[2] == 0
     # more budget never raises the loss
     prev = math.inf
     for units in range(0, 60, 3):
-        b, _, _ = fqcm.allocate(a, bet, eps, dout, units * dout)
+        b, _ = fqcm.allocate(a, bet, eps, dout, units * dout)
         cur = fqcm.total_loss(a, bet, eps, b)
         assert cur <= prev * (1 + 1e-12)
         prev = cur

@@ -147,15 +147,29 @@ def _distortion_m_minus(P):
     return res
 
 
+_orig_lagrangian = fqcm.lagrangian
+
+
 def _allocate_over_budget(a, bet, eps, dout, budget):
-    bits, lam, used = _orig_allocate(a, bet, eps, dout, budget)
-    if lam > 0:       # the last multiplier that did not fit
+    # the last multiplier that did not fit: one step of the hull too many
+    bits, lam, used = _orig_lagrangian(a, bet, eps, dout, budget)
+    if lam > 0:
         L = _orig_losses(a, bet, eps)
         lam2 = float(np.nextafter(lam, 0.0))
         idx = fqcm.choose(L, dout, lam2)
         bits = np.array(fqcm.WIDTHS, np.uint8)[idx]
         used = int(bits.astype(np.int64).sum()) * dout
-    return bits, lam, used
+    return bits, used
+
+
+def _allocate_is_lagrangian(a, bet, eps, dout, budget):
+    bits, lam, used = _orig_lagrangian(a, bet, eps, dout, budget)
+    return bits, used
+
+
+def _allocate_dp_off_by_one_unit(a, bet, eps, dout, budget):
+    # the dynamic program run with one budget unit too few
+    return _orig_allocate(a, bet, eps, dout, max(budget - dout, 0))
 
 
 def test_fqcm_loss_without_a_squared_caught(monkeypatch):
@@ -173,9 +187,12 @@ def test_fqcm_distortion_sign_caught(monkeypatch):
     assert _fails(T_f.test_eps_from_hand_derived_cases)
 
 
-def test_fqcm_allocation_over_budget_caught(monkeypatch):
-    monkeypatch.setattr(fqcm, "allocate", _allocate_over_budget)
-    assert any(_fails(T_f.test_allocation_is_optimal_for_the_bits_it_uses, s) for s in range(4))
+@pytest.mark.parametrize("bad", [_allocate_over_budget, _allocate_is_lagrangian,
+                                 _allocate_dp_off_by_one_unit])
+def test_fqcm_allocation_slips_caught(monkeypatch, bad):
+    monkeypatch.setattr(fqcm, "allocate", bad)
+    assert any(_fails(T_f.test_allocation_is_the_brute_force_minimum, s) for s in range(4))
+    assert _fails(T_f.test_allocation_spends_what_the_lagrangian_leaves)
 
 
 _orig_down = path.moe_down
