@@ -77,32 +77,56 @@ def step_bytes(spec, per_e_g, per_e_u, ids):
     return phi + experts + xh, phi, experts
 
 
-def cpu_baseline(layer, batches, seconds):
-    """The oracle on the host cores: tokens processed within ~`seconds`."""
-    from tests.oracle_ref import pairs_ref
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-        cores = max(blas) if blas else 1
-    except Exception:  # pragma: no cover
-        cores = 1
-    tok = 0
-    t0 = time.perf_counter()
-    i = 0
-    while True:
-        x, ids = batches[i % len(batches)]
-        pairs_ref(layer, x, ids)
-        tok += x.shape[0]
-        i += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": el / tok * 1e6, "unit": "µs/token", "cores": int(cores), "kind": "oracle",
-            "tokens_per_s": tok / el,
-            "sample": "%d batch(es), %d token(s) of the same workload through the float64 "
-                      "oracle (dequantize routed experts, z = Phi^T x, ordered k sum, SiLU*mul); "
-                      "numpy, BLAS threads = %d, other work single-threaded; %.1f s"
-                      % (i, tok, cores, el)}
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(layer, batches, seconds):
+    """The plain C oracle (oracle/ref_decode.c) on the host cores: z = Phi^T x,
+    every routed expert's codes read back from its bit planes, the ordered
+    k sums and SiLU*mul, all in float64, from blobs written by the oracle's
+    own packer.  A token sample sized to ~`seconds` of work is timed with 1
+    thread and with every core the process may use, 3 runs each (median)."""
+    from oracle import build_ref, fmt, ref_c
+    if not os.path.exists(ref_c.LIB_PATH):
+        build_ref.build()
+    spec = layer.spec
+    blobs = [np.frombuffer(fmt.pack(layer.p[p], layer.a[p], layer.bits[p]), np.uint8)
+             for p in ("gate", "up")]
+    phi_t = np.ascontiguousarray(np.concatenate([np.asarray(layer.phi["gate"], np.float16).T,
+                                                 np.asarray(layer.phi["up"], np.float16).T]))
+    x = np.concatenate([b[0] for b in batches])
+    ids = np.concatenate([b[1] for b in batches])
+    cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():   # the host's share for this job
+        cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
+
+    def run(n, threads):
+        t0 = time.perf_counter()
+        ref_c.gateup(blobs[0], blobs[1], phi_t, x[:n], ids[:n], spec.E, spec.dout, spec.r,
+                     threads=threads)
+        return time.perf_counter() - t0
+
+    t1 = run(1, 1)
+    # 3 single-thread and 3 all-core runs of n tokens within ~seconds
+    n = int(max(1, min(len(x), seconds / (3.0 * t1 * (1.0 + 1.0 / cores)))))
+    one = sorted(run(n, 1) for _ in range(3))[1]
+    allc = sorted(run(n, cores) for _ in range(3))[1]
+    return {"value": round(allc / n * 1e6, 1), "unit": "µs/token", "cores": int(cores),
+            "kind": "oracle", "tokens_per_s": round(n / allc, 2),
+            "one_core": {"value": round(one / n * 1e6, 1), "unit": "µs/token", "cores": 1},
+            "cpu_model": _cpu_model(),
+            "sample": "%d token(s) of the same workload (routed experts decoded from the "
+                      "packed planes each time) through the plain C float64 oracle "
+                      "(gcc -O2, OpenMP over tokens and pairs); median of 3 runs on %d "
+                      "threads and of 3 on 1 thread" % (n, cores)}
 
 
 def bench_pack(args):
@@ -585,7 +609,7 @@ def main():
                      "kernel": KERNEL_ONE_LAUNCH if T <= 4 else KERNEL_TWO_LAUNCHES},
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(L, host_batches[:4], args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(L, host_batches, args.cpu_seconds)
     print(json.dumps(out, ensure_ascii=False), flush=True)
     if args.copy_calib_mib > 0:
         n = args.copy_calib_mib << 20
