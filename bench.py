@@ -30,9 +30,29 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_ONE_LAUNCH = "k_gateup_fused (z, expert apply and SiLU*mul in one launch)"
 KERNEL_TWO_LAUNCHES = "k_proj_rows + k_route_group + k_gateup_grouped (timed together)"
 # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counter runs, scaled by
-# the same counters on a plain copy of known size; None until measured for
-# the current kernel.
-TRAFFIC = {"qwen3_30b_a3b_t1": 26315709}
+# the same counters on a plain copy of known size, with the hash of the
+# kernel sources they were taken on: reported only while the sources still
+# hash the same (None once a kernel has changed since).
+TRAFFIC = {"qwen3_30b_a3b_t1": (26326560, "9e1fb6eaa28b5e4d")}
+
+
+def kernel_source_hash():
+    """First 16 hex digits of the SHA-256 of the library's sources (csrc/,
+    in name order)."""
+    import hashlib
+    d = os.path.join(ROOT, "spectral_expert_gemv_amd", "csrc")
+    hs = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            hs.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                hs.update(f.read())
+    return hs.hexdigest()[:16]
+
+
+def traffic_for(workload):
+    t = TRAFFIC.get(workload)
+    return t[0] if t and t[1] == kernel_source_hash() else None
 
 
 def parse():
@@ -530,37 +550,52 @@ def main():
                 step(start + i, stream.cuda_stream)
         return g
 
-    def run(nsteps, graph_full, graph_rem):
+    def run(nsteps, start, graph_full, graph_rem):
         if args.no_graph:
             with torch.cuda.stream(stream):
                 for i in range(nsteps):
-                    step(i, stream)
+                    step(start + i, stream)
             return
         for _ in range(nsteps // S):
             graph_full.replay()
         if nsteps % S:
             graph_rem.replay()
 
+    # W warm-up steps from index 0, then LOOPS timed loops of exactly K
+    # steps, each continuing the rotation where the last one stopped (loop j
+    # starts at W + j K), so no timed loop starts on copies just touched;
+    # the value is the median loop.
+    LOOPS = 5
     K, W = args.steps, args.warmup
+    starts = [W + j * K for j in range(LOOPS)]
     g_full = None if args.no_graph else make_graph(S, 0)
-    g_rem = None if args.no_graph else make_graph(K % S, 0)
+    g_rems = [None if args.no_graph else make_graph(K % S, st) for st in starts]
     g_wrem = None if args.no_graph else make_graph(W % S, 0)
     with torch.cuda.stream(stream):
-        run(W, g_full, g_wrem)
+        run(W, 0, g_full, g_wrem)
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        run(K, g_full, g_rem)
-        ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
+    loop_ms = []
+    for j in range(LOOPS):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            run(K, starts[j], g_full, g_rems[j])
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        loop_ms.append(ev0.elapsed_time(ev1))
+    jm = sorted(range(LOOPS), key=lambda j: loop_ms[j])[LOOPS // 2]
+    ms = loop_ms[jm]
     ms_per_step = ms / K
     us_per_token = ms_per_step * 1000.0 / T
 
     # algorithmic bytes averaged over the steps timed (step i uses batch i % NB)
-    avg_bytes = sum(sb[i % len(sb)][0] for i in range(K)) / K
+    if args.no_graph:
+        idx = [starts[jm] + i for i in range(K)]
+    else:
+        idx = list(range(S)) * (K // S) + [starts[jm] + i for i in range(K % S)]
+    avg_bytes = sum(sb[i % len(sb)][0] for i in idx) / K
     achieved = avg_bytes / (ms_per_step * 1e-3) / 1e9
 
     # The timed region is back-to-back launches of the step's kernel(s) on
@@ -599,10 +634,12 @@ def main():
                    "batches": len(batches), "graph_steps": S,
                    "inputs": "fp16 Phi and x, packed 0..16-bit directions, fp32 h"},
         "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "timed_loops_us_per_token": [round(m * 1000.0 / K / T, 4) for m in loop_ms],
         "warm_mall_us_per_token": None if warm_us is None else round(warm_us, 4),
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": TRAFFIC.get(wl.name), "bytes_per_launch": round(kern_bytes),
+                     "traffic": traffic_for(wl.name), "kernel_source_hash": kernel_source_hash(),
+                     "bytes_per_launch": round(kern_bytes),
                      "phi_bytes": sb[0][1],
                      "expert_bytes_avg": round(sum(s[2] for s in sb) / len(sb)),
                      "launch_us_avg": round(kern_us, 3),
