@@ -68,11 +68,20 @@ WIDE = LayerSpec("wide", E=4, din=3072, dout=4133, r=3072, k=2, decay=0.5,
                  ln_sigma=0.3, bits={4: 10, 6: 30, 8: 50, 16: 10}, outlier_frac=0.0,
                  outlier_scale=1.0, phi_fp16=True)
 
+# Test-only shape beyond the matrix-core kernels' limits (r and din above
+# 4096): gate/up runs the projection and the lane-per-row expert kernel.
+BEYOND = LayerSpec("beyond", E=2, din=4112, dout=40, r=4112, k=2, decay=0.5,
+                   ln_sigma=0.3, bits="uniform", outlier_frac=0.0, outlier_scale=1.0,
+                   phi_fp16=True)
+
 LAYERS: Dict[str, LayerSpec] = {l.name: l for l in
-                                (TINY, QWEN3_30B_A3B, MIXTRAL_8X7B, DEEPSEEK_MOE_16B, WIDE, HEAVY)}
+                                (TINY, QWEN3_30B_A3B, MIXTRAL_8X7B, DEEPSEEK_MOE_16B, WIDE, HEAVY,
+                                 BEYOND)}
 
 WORKLOADS: Dict[str, Workload] = {w.name: w for w in (
     Workload("tiny_t8", TINY, 8, ("uniform",)),
+    Workload("beyond_t1", BEYOND, 1, ("uniform",)),
+    Workload("beyond_t8", BEYOND, 8, ("uniform",)),
     Workload("tiny_t1", TINY, 1, ("uniform",)),
     Workload("tiny_t4", TINY, 4, ("uniform",)),
     Workload("wide_t2", WIDE, 2, ("uniform",)),

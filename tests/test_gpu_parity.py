@@ -156,6 +156,45 @@ def test_expert_apply_tiny(bm):
             assert max_rel_err(got[t, s], ref) <= Y_TOL, (proj, t, s)
 
 
+def test_expert_apply_qwen_shape(bm):
+    """bitsmoe_expert_apply alone (the lane-per-row kernel) on the Qwen3-shaped
+    layer: 2 tokens x 8 experts, every row of each pair against the oracle."""
+    wl = synth.workload("qwen3_30b_a3b_t1")
+    L, dev = device_layer("qwen3_30b_a3b")
+    x, ids = synth.make_batch(wl, L, T=2, step=7)
+    _, yg, yu = pairs_ref(L, x, ids, want_y=True)
+    zr = z_ref(L, x)
+    spec = L.spec
+    for proj, blob, yref in (("gate", dev.blob_gate, yg), ("up", dev.blob_up, yu)):
+        z = _cuda(zr[proj].astype(np.float32))
+        y = torch.empty((x.shape[0], spec.k, spec.dout), dtype=torch.float32, device="cuda")
+        _say("expert apply qwen %s" % proj)
+        bm.expert_apply(blob, spec.E, spec.dout, spec.r, z, _cuda(ids), y)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()
+        for (t, s), ref in yref.items():
+            assert max_rel_err(got[t, s], ref) <= Y_TOL, (proj, t, s)
+
+
+@pytest.mark.parametrize("wl_name", ["beyond_t1", "beyond_t8"])
+def test_gateup_beyond_matrix_core_limits(bm, wl_name):
+    """r = din = 4112 (above 4096): neither the one-launch nor the grouped
+    kernel takes the call; the projection and the lane-per-row expert kernel
+    (k_expert_seg) do, for one token and for eight.  Every pair against the
+    oracle, with one id outside [0, E) giving a NaN row."""
+    wl = synth.workload(wl_name)
+    L, dev = device_layer(wl.layer.name)
+    x, ids = synth.make_batch(wl, L)
+    _say("beyond %s" % wl_name)
+    got = _run_gateup(dev, x, ids)
+    _check_h(got, pairs_ref(L, x, ids))
+    bad = ids.copy()
+    bad[0, 1] = L.spec.E
+    got = _run_gateup(dev, x, bad)
+    assert np.all(np.isnan(got[0, 1]))
+    assert np.all(np.isfinite(got[0, 0]))
+
+
 # ------------------------------------------------------------------ gate/up
 
 def _check_h(got, href):
