@@ -88,15 +88,18 @@ __device__ __forceinline__ SegProj make_seg(const uint8_t* blob, uint64_t bytes,
                                             int r) {
   SegProj p;
   p.ok = check_dir(h, d, bytes, e, E, dout, r);
-  // A record that fails the check is not used for any address: every array
-  // then points at the blob base (its 128-byte header covers the 16-byte
-  // loads issued at index 0) and every count is 0.
+  // A record that fails the check gives counts of 0 (no loop reads an
+  // array) and a block at the blob base: kidx is then the blob base, and the
+  // one reader that loads without looking at the counts (load_meta) takes
+  // every array from there (the 128-byte header covers its loads at index
+  // 0).  The other arrays' offsets are taken unchecked here, so that forming
+  // them does not wait for the check.
   const uint64_t blk = reinterpret_cast<uint64_t>(blob) + (p.ok ? d.block_offset : 0);
   p.kidx = (const gu16*)blk;
-  p.A = (const gf32*)(blk + (p.ok ? d.a_off : 0u));
-  p.S = (const gu16*)(blk + (p.ok ? d.s_off : 0u));
-  p.M = (const gu16*)(blk + (p.ok ? d.m_off : 0u));
-  p.planes = (const gu32*)(blk + (p.ok ? d.planes_off : 0u));
+  p.A = (const gf32*)(blk + d.a_off);
+  p.S = (const gu16*)(blk + d.s_off);
+  p.M = (const gu16*)(blk + d.m_off);
+  p.planes = (const gu32*)(blk + d.planes_off);
   const SlotGeo geo = slot_geo(d.count);
   uint32_t nb[kNumGroups];
 #pragma unroll

@@ -39,10 +39,15 @@ __device__ __forceinline__ uint32_t meta_slot(int lp, int i) {
 // all of its outstanding loads right there.  A 16-byte vector that starts
 // inside an array ends at most 28 bytes past it, still inside the expert
 // block (the next array, or the planes and the block's 16-byte tail).
+// A descriptor whose record failed its check has counts of 0, so every index
+// is 0, and its arrays are all taken from kidx, the blob base then.
 template <int kFSper>
 __device__ __forceinline__ void load_meta(const SegProj& p, int lp, SlotMeta<kFSper>& md) {
   constexpr int V = SlotMeta<kFSper>::V;
   static_assert(kFSper == 8 * V + 1, "8 V contiguous slots and one tail slot");
+  const gf32* A = p.ok ? p.A : (const gf32*)p.kidx;
+  const gu16* S = p.ok ? p.S : p.kidx;
+  const gu16* M = p.ok ? p.M : p.kidx;
   const uint32_t s0 = 8u * V * (uint32_t)lp;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
@@ -50,19 +55,19 @@ __device__ __forceinline__ void load_meta(const SegProj& p, int lp, SlotMeta<kFS
     const uint32_t iq = sv < p.n_slot ? sv : 0u, ia = sv + 4 < p.n_slot ? sv + 4 : 0u;
     const uint32_t is = sv < p.n_qslot ? sv : 0u;
     md.kq[v] = ld16(p.kidx + iq);
-    md.a0[v] = ld16(p.A + iq);
-    md.a1[v] = ld16(p.A + ia);
-    md.sq[v] = ld16(p.S + is);
-    md.mq[v] = ld16(p.M + is);
+    md.a0[v] = ld16(A + iq);
+    md.a1[v] = ld16(A + ia);
+    md.sq[v] = ld16(S + is);
+    md.mq[v] = ld16(M + is);
   }
   const uint32_t sl = 2048u * V + (uint32_t)lp;
   const uint32_t ic = sl < p.n_slot ? sl : 0u, iq = sl < p.n_qslot ? sl : 0u;
   // 16-bit values through the aligned 32-bit word that holds them (the half
   // is picked where they are used)
   md.kt = *(const gu32*)(p.kidx + (ic & ~1u));
-  md.at = *(const gu32*)(p.A + ic);
-  md.st = *(const gu32*)(p.S + (iq & ~1u));
-  md.mt = *(const gu32*)(p.M + (iq & ~1u));
+  md.at = *(const gu32*)(A + ic);
+  md.st = *(const gu32*)(S + (iq & ~1u));
+  md.mt = *(const gu32*)(M + (iq & ~1u));
 }
 // Slot i of the lane (see SlotMeta): component index k, magnitude a and
 // fp16 s, m as floats; slots past the arrays give k = 0, a = 0, s = 1, m = 0.
