@@ -209,13 +209,23 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   // lo tables; the next 128-slot chunk is loaded while the products of the
   // current one run.  Rows past the tile's tokens load the last token's row
   // (same cache lines) and are not stored.
+  //
+  // Chunk length: the LDS table holds kTile rows of kGCS slots, so a tile of
+  // nt <= ntp tokens (ntp a power of two) takes chunks of cs = kGCS kTile /
+  // ntp slots in ntp rows of stride cs + 8: fewer chunks, barriers and
+  // coefficient round trips for the small tiles that dominate decode-sized
+  // batches.
   const size_t trow = (size_t)(ti * 2 + (single ? 0 : pj)) * kTile;
   static_assert(kGProj == kTile * kGCS / 8, "one 16-byte piece per lane");
-  const int cq = lp / (kGCS / 8), c8 = 8 * (lp % (kGCS / 8));
+  const int ntp = nt <= 1 ? 1 : (nt <= 2 ? 2 : (nt <= 4 ? 4 : (nt <= 8 ? 8 : 16)));
+  const uint32_t cs = (uint32_t)(kGCS * kTile / ntp);  // slots per coefficient chunk
+  const int cstr = (int)cs + 8;                          // fp16 per token row in LDS
+  const int ppr = (int)cs / 8;                           // 16-byte pieces per row
+  const int cq = lp / ppr, c8 = 8 * (lp % ppr);
   const bool cA = cq < nt;
   const size_t oA = (trow + (size_t)min(cq, nt - 1)) * s.rpad + c8;
-  _Float16* const dA = &L.u.c.hi[pj][0] + cq * kGCStride + c8;
-  _Float16* const dAl = &L.u.c.lo[pj][0] + cq * kGCStride + c8;
+  _Float16* const dA = &L.u.c.hi[pj][0] + cq * cstr + c8;
+  _Float16* const dAl = &L.u.c.lo[pj][0] + cq * cstr + c8;
   uint4 chA, clA;
 #define GROUPED_COEF_FETCH(s0)                                             \
   do {                                                                     \
@@ -248,8 +258,8 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   // barriers are shared, so the work-group runs the larger count (published
   // through L.ncc, one slot per chunk parity) and a half past its own count
   // only takes part in the barriers.
-  constexpr uint32_t kCB = kGCS / 4;
-  auto n_coef_chunks = [](uint32_t c0, uint32_t c1) {
+  const uint32_t kCB = cs / 4;  // blocks per coefficient chunk
+  auto n_coef_chunks = [kCB](uint32_t c0, uint32_t c1) {
     return max((int)((c1 - c0 + kCB - 1) / kCB), 1);
   };
   {
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
           *reinterpret_cast<uint4*>(dAl) = clA;
         }
         if (cc + 1 < ncc)
-          GROUPED_COEF_FETCH(s0 + (uint32_t)kGCS);
+          GROUPED_COEF_FETCH(s0 + cs);
         else if (ch + 1 < nch)
           GROUPED_COEF_FETCH(4u * b1);
       }
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
       const uint32_t kb1 = min(kb0 + kCB / kBlkPerK, kbe);
       if (mine && b1 > cb0) {
         const uint32_t* base = &L.W[pj][0] - block_word(P, b0);
-        mfma_ksteps(P, base, &L.u.c.hi[pj][0], &L.u.c.lo[pj][0], kGCStride, s0,
+        mfma_ksteps(P, base, &L.u.c.hi[pj][0], &L.u.c.lo[pj][0], cstr, s0,
                     nt, kb0, kb1, wp, lane, acc0, acc1);
       }
     }
