@@ -21,9 +21,10 @@
 // chunk, into tables in the workspace.
 //
 // k_gateup_grouped: one 512-lane work-group per (tile, 32-row segment) unit,
-// both projections (waves 0-3 gate, 4-7 up); unit u = segment * tcap + tile
-// runs on XCD u % 8, so every segment of a tile shares one L2 (and reads the
-// tile's coefficient tables from it).  The segment records are staged in
+// both projections (waves 0-3 gate, 4-7 up); the units fill the first
+// ntiles x segments blocks of the grid (unit u: tile u % ntiles, segment
+// u / ntiles), the grid's other blocks, sized for the largest tile count,
+// exit at once.  The segment records are staged in
 // LDS in chunks of at most 7168 words per projection; the tile's
 // coefficients go through LDS in 128-slot chunks, each loaded into
 // registers (16 bytes a lane) while the previous chunk's products run.  The
@@ -184,13 +185,20 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   const int wp = wv & (kGPW - 1);
   const int lp = (int)threadIdx.x & (kGProj - 1);
 
+  // The units fill the first ntiles x segments blocks (tile = b % ntiles):
+  // the grid is sized for tcap tiles, and blocks past the units exit at
+  // once, after every unit has been dispatched, so no launch slot sits
+  // behind a block without work.
+  typedef __attribute__((address_space(4))) const int CI32;
+  const int ntl = *(CI32*)s.rl.ntiles;  // written by the route step before this launch
   const int u = blockIdx.x;
-  const int ti = u % s.tcap;
   const bool single = s.single != 0;
+  const int nsu = single ? (a.n_seg + 1) / 2 : a.n_seg;  // segment units per tile
+  if (ntl <= 0 || u >= ntl * nsu) return;
+  const int ti = u % ntl;
   // single: this half's segment (a half past the last segment repeats it
   // and writes nothing)
-  const int sg0 = single ? 2 * (u / s.tcap) : u / s.tcap;
-  if (sg0 >= a.n_seg || ti >= s.rl.ntiles[0]) return;
+  const int sg0 = single ? 2 * (u / ntl) : u / ntl;
   const int sgh = single ? sg0 + pj : sg0;
   const int sg = sgh < a.n_seg ? sgh : a.n_seg - 1;
   const int e = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti]);
