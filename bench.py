@@ -27,6 +27,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/token + % HBM roofline, spectral MoE gate/up layer, Qwen3-30B-A3B shape, batch 1"
 HBM_PEAK_GBS = 8000.0
+KERNEL_ONE_TOKEN = ("k_gateup_one (z, every routed expert's coefficients, expert apply and "
+                    "SiLU*mul in one launch)")
 KERNEL_ONE_LAUNCH = "k_gateup_fused (z, expert apply and SiLU*mul in one launch)"
 KERNEL_TWO_LAUNCHES = "k_proj_rows + k_route_group + k_gateup_grouped (timed together)"
 # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counter runs, scaled by
@@ -643,7 +645,8 @@ def main():
                      "phi_bytes": sb[0][1],
                      "expert_bytes_avg": round(sum(s[2] for s in sb) / len(sb)),
                      "launch_us_avg": round(kern_us, 3),
-                     "kernel": KERNEL_ONE_LAUNCH if T <= 4 else KERNEL_TWO_LAUNCHES},
+                     "kernel": (KERNEL_ONE_TOKEN if T == 1 and spec.r <= 2048 else
+                                KERNEL_ONE_LAUNCH if T <= 4 else KERNEL_TWO_LAUNCHES)},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(L, host_batches, args.cpu_seconds)

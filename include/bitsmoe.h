@@ -61,7 +61,7 @@ typedef struct ihipStream_t* bitsmoe_stream_t; /* same type as hipStream_t */
 #define BITSMOE_EFORMAT  -5  /* blob magic, version, CRC or directory invalid */
 #define BITSMOE_EHIP     -6  /* HIP runtime or launch error */
 
-#define BITSMOE_FORMAT_VERSION 3
+#define BITSMOE_FORMAT_VERSION 4
 
 /* Library version (major*10000 + minor*100 + patch). */
 int bitsmoe_version(void);
@@ -80,17 +80,24 @@ const char* bitsmoe_last_error_detail(void);
  *   m = fp16_rne(min p) (-0 below +0); q_i = clamp(nearbyint((p_i - m) / s),
  *   0, 2^b - 1)
  *   with ties to even.  16 bits: fp16_rne(p_i).  0 bits: no entry.
- * Blob layout (format v3, little-endian, offsets from the blob base):
- *   header 128 B: "BMOE", u32 version(=3), E, dout, r, dout_pad
+ * Blob layout (format v4, little-endian, offsets from the blob base):
+ *   header 128 B: "BMOE", u32 version(=4), E, dout, r, dout_pad
  *     (=32*ceil(dout/32)), n_seg (=dout_pad/32), header_bytes(=128);
  *     u64 total_bytes at 32, u64 dir_offset(=128) at 40, u32 CRC-32 (IEEE)
- *     of [128, total) at 48.
+ *     of [128, total) at 48, u64 slot_index_offset (=align256(128 + 64 E))
+ *     at 56.
  *   directory: E records of 64 B: u64 block_offset; u32 n_nz, n_q, n_16,
  *     seg_words (u32 words of one 32-row segment record), a_off, s_off,
  *     m_off, planes_off; f32 cmax (largest |a|*s over 1..8-bit columns,
  *     |a| over 16-bit ones); u32 block_bytes; u16 count[7] of widths
  *     1,2,3,4,6,8,16 at 48 (offsets relative to the expert block).
- *   expert block (256-aligned, back to back): slots ordered by width group
+ *   slot index at slot_index_offset: per expert, at stride align16(2 r),
+ *     u16[r]: entry k is the slot of component k in the expert's slot
+ *     order, 0xFFFF for a 0-bit component (the inverse of kidx; it lets the
+ *     producer of z_k place the coefficient a_k s_k z_k of every routed
+ *     expert directly).
+ *   expert block (256-aligned, back to back from
+ *     align256(slot_index_offset + E align16(2 r))): slots ordered by width group
  *     1,2,3,4,6,8,16, ascending k inside a group, each group padded with
  *     zero slots to a multiple of 32 (so a 32-slot step has one width);
  *     0-bit columns have no slot.  n_slot slots, n_qslot of width <= 8:

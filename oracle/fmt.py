@@ -1,4 +1,4 @@
-"""Independent writer and reader of the packed spectral-expert blob (format v3).
+"""Independent writer and reader of the packed spectral-expert blob (format v4).
 
 Test infrastructure: only the tests, the smoke check and the benchmark's CPU
 baseline use this module; the HIP library never imports it.
@@ -12,10 +12,11 @@ bytes from its own C++ code, and the tests compare the two.
 Layout (little-endian; offsets in bytes from the blob base):
 
 Header, 128 bytes
-  0 'BMOE' | 4 u32 version=3 | 8 u32 E | 12 u32 dout | 16 u32 r
+  0 'BMOE' | 4 u32 version=4 | 8 u32 E | 12 u32 dout | 16 u32 r
   20 u32 dout_pad = 32*ceil(dout/32) | 24 u32 n_seg = dout_pad/32
   28 u32 header_bytes=128 | 32 u64 total_bytes | 40 u64 dir_offset=128
-  48 u32 CRC-32 (IEEE, as zlib) of bytes [128, total_bytes) | rest zero
+  48 u32 CRC-32 (IEEE, as zlib) of bytes [128, total_bytes)
+  56 u64 ctab_offset = align256(128 + 64 E) | rest zero
 Directory, E records of 64 bytes at dir_offset
   0 u64 block_offset | 8 u32 n_nz | 12 u32 n_q | 16 u32 n_16
   20 u32 seg_words (u32 words of one 32-row segment record)
@@ -24,7 +25,17 @@ Directory, E records of 64 bytes at dir_offset
   48 u16 count of columns of width 1,2,3,4,6,8,16 (7 values) | 62 u16 0
   cmax = max over the expert's stored columns of |a_k| * s_k (1..8 bits,
   float32 product) or |a_k| (16 bits); 0 when the expert stores none.
-Expert block (first at align256(128 + 64 E), blocks back to back)
+Component table at ctab_offset: for expert e, at e * stride, with
+  R2 = align16(2 r), stride = 3 R2 + align16(4 r) + 16:
+  0      u16 slot[r]: slot of component k in expert e's slot order (below),
+         0xFFFF when component k has width 0
+  R2     f16 s[r], 2 R2: f16 m[r]: scale and offset of 1..8-bit components
+         (0 for 16-bit and 0-bit ones)
+  3 R2   f32 a[r] (0 for 0-bit components)
+  3 R2 + align16(4 r): f32 cmax (as in the directory), then 12 zero bytes
+  (the same values as the expert block's slot arrays, in component order)
+Expert block (first at align256(ctab_offset + E stride), blocks back to
+back)
   slot order: width groups 1,2,3,4,6,8,16; inside a group the columns in
   ascending k, then zero slots up to a multiple of 32 (nb_w = 8 ceil(n_w /
   32) blocks of 4 slots per group, so that a 32-slot step never mixes
@@ -55,7 +66,7 @@ import numpy as np
 from .quantize import quantize_expert
 
 MAGIC = b"BMOE"
-VERSION = 3
+VERSION = 4
 HEADER_BYTES = 128
 DIR_REC = 64
 SEG_ROWS = 32
@@ -64,6 +75,17 @@ GROUP_WIDTHS = (1, 2, 3, 4, 6, 8, 16)
 
 def _al(x: int, a: int) -> int:
     return (x + a - 1) // a * a
+
+
+def ctab_offset(E: int) -> int:
+    return _al(HEADER_BYTES + DIR_REC * E, 256)
+
+
+def ctab_layout(r: int) -> dict:
+    """Byte offsets of the component table's arrays inside one expert's entry."""
+    r2 = _al(2 * r, 16)
+    return dict(slot=0, s=r2, m=2 * r2, a=3 * r2, cmax=3 * r2 + _al(4 * r, 16),
+                stride=3 * r2 + _al(4 * r, 16) + 16)
 
 
 def plane_bit(rho, u):
@@ -140,7 +162,8 @@ def pack(p: np.ndarray, a: np.ndarray, bits: np.ndarray) -> bytes:
     for e in range(E):
         cnt = [int(np.count_nonzero(bits[e] == w)) for w in GROUP_WIDTHS]
         lays.append(_block_layout(cnt, n_seg))
-    first = _al(HEADER_BYTES + DIR_REC * E, 256)
+    CT = ctab_layout(r)
+    first = _al(ctab_offset(E) + E * CT["stride"], 256)
     offs = []
     pos = first
     for L in lays:
@@ -153,6 +176,7 @@ def pack(p: np.ndarray, a: np.ndarray, bits: np.ndarray) -> bytes:
         base = offs[e]
         slots = _slots(bits[e])
         real = slots >= 0
+
         ks = np.where(real, slots, 0)
         qe = quantize_expert(p[e], bits[e])
         a_s = np.where(real, a[e][ks], np.float32(0)).astype("<f4")
@@ -171,6 +195,23 @@ def pack(p: np.ndarray, a: np.ndarray, bits: np.ndarray) -> bytes:
                          L["a_off"], L["s_off"], L["m_off"], L["p_off"],
                          float(cmax), L["nbytes"])
         struct.pack_into("<7H", buf, HEADER_BYTES + DIR_REC * e + 48, *L["cnt"])
+        # component table: the stored slots' values in component order
+        cslot = np.full(r, 0xFFFF, dtype="<u2")
+        cs = np.zeros(r, dtype="<f2")
+        cm = np.zeros(r, dtype="<f2")
+        ca = np.zeros(r, dtype="<f4")
+        sl_real = np.nonzero(real)[0]
+        cslot[slots[sl_real]] = sl_real
+        ca[slots[sl_real]] = a_s[sl_real]
+        q_real = sl_real[sl_real < qs]
+        cs[slots[q_real]] = s_s[q_real]
+        cm[slots[q_real]] = m_s[q_real]
+        co = ctab_offset(E) + e * CT["stride"]
+        buf[co + CT["slot"]:co + CT["slot"] + 2 * r] = cslot.tobytes()
+        buf[co + CT["s"]:co + CT["s"] + 2 * r] = cs.tobytes()
+        buf[co + CT["m"]:co + CT["m"] + 2 * r] = cm.tobytes()
+        buf[co + CT["a"]:co + CT["a"] + 4 * r] = ca.tobytes()
+        struct.pack_into("<f", buf, co + CT["cmax"], float(cmax))
         n_slot = L["n_slot"]
         buf[base:base + 2 * n_slot] = ks.astype("<u2").tobytes()
         buf[base + L["a_off"]:base + L["a_off"] + 4 * n_slot] = a_s.tobytes()
@@ -193,6 +234,7 @@ def pack(p: np.ndarray, a: np.ndarray, bits: np.ndarray) -> bytes:
     struct.pack_into("<4sIIIIIII", buf, 0, MAGIC, VERSION, E, dout, r,
                      dout_pad, n_seg, HEADER_BYTES)
     struct.pack_into("<QQ", buf, 32, total, HEADER_BYTES)
+    struct.pack_into("<Q", buf, 56, ctab_offset(E))
     struct.pack_into("<I", buf, 48, zlib.crc32(memoryview(buf)[HEADER_BYTES:]) & 0xFFFFFFFF)
     return bytes(buf)
 
@@ -202,9 +244,25 @@ def read_header(blob) -> dict:
     magic, ver, E, dout, r, dout_pad, n_seg, hb = struct.unpack_from("<4sIIIIIII", mv, 0)
     total, dir_off = struct.unpack_from("<QQ", mv, 32)
     crc, = struct.unpack_from("<I", mv, 48)
+    cto, = struct.unpack_from("<Q", mv, 56)
     return dict(magic=magic, version=ver, E=E, dout=dout, r=r, dout_pad=dout_pad,
                 n_seg=n_seg, header_bytes=hb, total_bytes=total,
-                dir_offset=dir_off, crc32=crc)
+                dir_offset=dir_off, crc32=crc, ctab_offset=cto)
+
+
+def read_ctab(blob, e: int) -> dict:
+    """Expert e's component table: 'slot' int64 (-1 for width 0), 's', 'm'
+    float16, 'a' float32 (component order) and 'cmax' float32."""
+    H = read_header(blob)
+    CT = ctab_layout(H["r"])
+    r = H["r"]
+    o = H["ctab_offset"] + e * CT["stride"]
+    slot = np.frombuffer(blob, dtype="<u2", count=r, offset=o + CT["slot"]).astype(np.int64)
+    return dict(slot=np.where(slot == 0xFFFF, -1, slot),
+                s=np.frombuffer(blob, dtype="<f2", count=r, offset=o + CT["s"]),
+                m=np.frombuffer(blob, dtype="<f2", count=r, offset=o + CT["m"]),
+                a=np.frombuffer(blob, dtype="<f4", count=r, offset=o + CT["a"]),
+                cmax=np.frombuffer(blob, dtype="<f4", count=1, offset=o + CT["cmax"])[0])
 
 
 def read_dir(blob, e: int) -> dict:
@@ -249,6 +307,9 @@ def unpack(blob, experts=None) -> dict:
     H = read_header(blob)
     if H["magic"] != MAGIC or H["version"] != VERSION:
         raise ValueError("not a v%d BMOE blob" % VERSION)
+    if H["ctab_offset"] != ctab_offset(H["E"]):
+        raise ValueError("component table offset %d, expected %d" % (H["ctab_offset"],
+                                                                     ctab_offset(H["E"])))
     if zlib.crc32(memoryview(blob)[HEADER_BYTES:H["total_bytes"]]) & 0xFFFFFFFF != H["crc32"]:
         raise ValueError("CRC mismatch")
     E, r, dout, dp, ns = H["E"], H["r"], H["dout"], H["dout_pad"], H["n_seg"]
@@ -275,12 +336,23 @@ def unpack(blob, experts=None) -> dict:
         m_s = buf[base + D["m_off"]:base + D["m_off"] + 2 * qs].view("<f2")
         planes = buf[base + D["p_off"]:base + D["p_off"] + 4 * ns * L["seg_words"]]
         planes = planes.view("<u4").reshape(ns, L["seg_words"])
+        CTe = read_ctab(blob, ex)
+        sidx = CTe["slot"]
+        if np.count_nonzero(sidx >= 0) != D["n_nz"]:
+            raise ValueError("expert %d: component table has extra entries" % ex)
         col = 0
         sl = 0
         for w, c, nb in zip(GROUP_WIDTHS, D["count"], L["nb"]):
             if nb == 0:
                 continue
             ks = kidx[sl:sl + c]
+            if not np.array_equal(sidx[ks], np.arange(sl, sl + c)) or \
+                    not np.array_equal(CTe["a"][ks].view("<u4"), a_s[sl:sl + c].view("<u4")):
+                raise ValueError("expert %d: component table does not match its columns" % ex)
+            if w != 16 and not (np.array_equal(CTe["s"][ks].view("<u2"), s_s[sl:sl + c].view("<u2"))
+                                and np.array_equal(CTe["m"][ks].view("<u2"),
+                                                   m_s[sl:sl + c].view("<u2"))):
+                raise ValueError("expert %d: component table does not match its columns" % ex)
             bits[e, ks] = w
             a[e, ks] = a_s[sl:sl + c]
             if w != 16:

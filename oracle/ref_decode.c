@@ -61,7 +61,7 @@ typedef struct {
 } Expert;
 
 static int locate(const uint8_t* blob, size_t nbytes, int E, int dout, int r, int e, Expert* x) {
-  if (nbytes < kHeader || memcmp(blob, "BMOE", 4) != 0 || rd32(blob + 4) != 3) return -1;
+  if (nbytes < kHeader || memcmp(blob, "BMOE", 4) != 0 || rd32(blob + 4) != 4) return -1;
   if ((int)rd32(blob + 8) != E || (int)rd32(blob + 12) != dout || (int)rd32(blob + 16) != r)
     return -1;
   if (e < 0 || e >= E) return -1;

@@ -20,7 +20,7 @@ OUT = os.path.join(PKG, "libbitsmoe.so")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["common.cpp", "pack.cpp"]
-HIP_SOURCES = ["bitsmoe.hip", "fused.hip", "grouped.hip", "pack_gpu.hip", "fqcm.hip", "down.hip", "ssd.hip"]
+HIP_SOURCES = ["bitsmoe.hip", "fused.hip", "one.hip", "grouped.hip", "pack_gpu.hip", "fqcm.hip", "down.hip", "ssd.hip"]
 
 HIP_FLAGS = [
     "-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",

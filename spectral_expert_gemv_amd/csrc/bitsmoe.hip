@@ -558,11 +558,12 @@ int launch_status(const char* what) {
   return BITSMOE_OK;
 }
 
-int check_blob_arg(const void* blob, size_t bytes, int E, const char* name) {
+int check_blob_arg(const void* blob, size_t bytes, int E, int r, const char* name) {
   if (!blob) return fail(BITSMOE_EINVAL, "%s is null", name);
   if (!aligned16(blob)) return fail(BITSMOE_EINVAL, "%s is not 16-byte aligned", name);
-  if (bytes < kHeaderBytes + (size_t)kDirRecBytes * E)
-    return fail(BITSMOE_ENOSPC, "%s: %zu bytes cannot hold header and directory", name, bytes);
+  if (bytes < first_block_offset((uint64_t)E, (uint64_t)r))
+    return fail(BITSMOE_ENOSPC, "%s: %zu bytes cannot hold header, directory and slot index",
+                name, bytes);
   return BITSMOE_OK;
 }
 
@@ -679,7 +680,11 @@ GateUpPlan gateup_plan(int T, int k, int E, int r) {
   p.z_off = align_up(kSyncBytes, 256);
   p.zpart_off = align_up(p.z_off + (size_t)T * 2 * r * sizeof(float), 256);
   p.zt_off = align_up(p.zpart_off + (size_t)T * nzp * sizeof(float), 256);
-  p.route_off = align_up(p.zt_off + (size_t)kZRing * T * 2 * r * sizeof(uint64_t), 256);
+  p.cw_off = align_up(p.zt_off + (size_t)kZRing * T * 2 * r * sizeof(uint64_t), 256);
+  const size_t ncw = T == 1 && k <= kOneMaxK && r <= kOneMaxR
+                         ? (size_t)kZRing * k * 2 * ((size_t)kOneSlots + r) * sizeof(uint64_t)
+                         : 0;
+  p.route_off = align_up(p.cw_off + ncw, 256);
   p.coef_off = align_up(p.route_off + (1 + 3 * (size_t)tile_cap(T, k, E) + P) * sizeof(int), 256);
   p.total = p.coef_off + group_coef_bytes(tile_cap(T, k, E), r);
   return p;
@@ -705,7 +710,7 @@ int bitsmoe_expert_apply(const void* packed, size_t packed_bytes, int E, int dou
   (void)ws_bytes;
   int st = check_layer_dims(E, dout, r);
   if (st) return st;
-  if ((st = check_blob_arg(packed, packed_bytes, E, "packed"))) return st;
+  if ((st = check_blob_arg(packed, packed_bytes, E, r, "packed"))) return st;
   if (!z || !ids || !y) return fail(BITSMOE_EINVAL, "null pointer argument");
   if (!aligned16(z) || !aligned16(y) || ((uintptr_t)ids & 3u))
     return fail(BITSMOE_EINVAL, "misaligned z, y or ids");
@@ -743,8 +748,8 @@ int gateup_checks(const void* packed_gate, size_t gate_bytes, const void* packed
                   const float* h, const void* ws, size_t ws_bytes, bool static_ws) {
   int st = check_layer_dims(E, dout, r);
   if (st) return st;
-  if ((st = check_blob_arg(packed_gate, gate_bytes, E, "packed_gate"))) return st;
-  if ((st = check_blob_arg(packed_up, up_bytes, E, "packed_up"))) return st;
+  if ((st = check_blob_arg(packed_gate, gate_bytes, E, r, "packed_gate"))) return st;
+  if ((st = check_blob_arg(packed_up, up_bytes, E, r, "packed_up"))) return st;
   if (!ids || !h || (!static_ws && !ws)) return fail(BITSMOE_EINVAL, "null pointer argument");
   if (!aligned16(h) || (!static_ws && !aligned16(ws)) || ((uintptr_t)ids & 3u))
     return fail(BITSMOE_EINVAL, "misaligned h, ws or ids");
@@ -791,7 +796,13 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
   // One launch when every work-group can be resident at once (the groups
   // wait for each other's z); otherwise z first, then the expert kernels.
   const int fgrid = fused_grid();
-  if (T <= kFusedMaxTokens && r <= kFusedMaxR && fgrid > 0) {
+  // (both one-launch kernels add 4 per work-group to the shared hint
+  // counters, so they must use the same grid)
+  const int ogrid = one_grid();
+  const bool one = T == 1 && k <= kOneMaxK && r <= kOneMaxR && r % 4 == 0 &&
+                   din <= kOneMaxDin && ogrid > 0 && ogrid == fgrid && 2 * r <= 32 * ogrid &&
+                   (long long)k * a.n_seg <= ogrid;
+  if (one || (T <= kFusedMaxTokens && r <= kFusedMaxR && fgrid > 0)) {
     FusedArgs fa;
     fa.g = a;
     fa.phi_t = (const uint4*)phi_t_gateup_f16;
@@ -799,11 +810,16 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     fa.din8 = din / 8;
     fa.T = T;
     fa.zt = (uint64_t*)(wsb + plan.zt_off);
+    fa.cw = (uint64_t*)(wsb + plan.cw_off);
+    fa.bw = fa.cw + (size_t)kZRing * k * 2 * kOneSlots;
     fa.epoch = (uint32_t*)(wsb + plan.sync_off);
     fa.hint = fa.epoch + 32;
     fa.grid = fgrid;
     fa.spin = g_wait_limit.load(std::memory_order_relaxed);
-    launch_gateup_fused(fa, s);
+    if (one)
+      launch_gateup_one(fa, s);
+    else
+      launch_gateup_fused(fa, s);
     return launch_status("one-launch gate/up");
   }
   const bool grouped = r <= kGroupMaxR && E <= kGroupMaxE && din <= kGroupMaxDin;
@@ -921,7 +937,7 @@ int bitsmoe_dump_codes(const void* packed, size_t packed_bytes, int E, int dout,
                        int path, uint16_t* codes, bitsmoe_stream_t stream) {
   int st = check_layer_dims(E, dout, r);
   if (st) return st;
-  if ((st = check_blob_arg(packed, packed_bytes, E, "packed"))) return st;
+  if ((st = check_blob_arg(packed, packed_bytes, E, r, "packed"))) return st;
   if (!codes) return fail(BITSMOE_EINVAL, "codes is null");
   if (!aligned16(codes)) return fail(BITSMOE_EINVAL, "codes is not 16-byte aligned");
   if (e < 0 || e >= E) return fail(BITSMOE_EINVAL, "e=%d outside [0,%d)", e, E);

@@ -1,4 +1,4 @@
-// Packed blob format v2: constants and the directory record shared by the
+// Packed blob format v4: constants and the directory record shared by the
 // host packer, the host checker and the device kernels.  The layout is
 // documented in include/bitsmoe.h.
 #pragma once
@@ -13,7 +13,7 @@
 namespace bitsmoe {
 
 constexpr uint32_t kMagic = 0x454F4D42u;  // bytes 'B','M','O','E'
-constexpr uint32_t kVersion = 3;
+constexpr uint32_t kVersion = 4;
 constexpr int kSegRows = 32;                        // rows of one segment record
 constexpr uint32_t kHeaderBytes = 128;
 constexpr uint32_t kDirRecBytes = 64;
@@ -25,7 +25,8 @@ struct Header {
   uint32_t magic, version, E, dout, r, dout_pad, n_seg, header_bytes;
   uint64_t total_bytes, dir_offset;
   uint32_t crc32, reserved0;
-  uint32_t pad[18];
+  uint64_t ctab_offset;  // the component table (see ctab_offset())
+  uint32_t pad[16];
 };
 static_assert(sizeof(Header) == 128, "header is 128 bytes");
 
@@ -42,6 +43,32 @@ static_assert(sizeof(DirRec) == 64, "directory record is 64 bytes");
 
 BM_HD constexpr inline uint64_t align_up(uint64_t x, uint64_t a) {
   return (x + a - 1) / a * a;
+}
+
+// Component table: after the directory, for every expert the values of its
+// components in component (k) order, so that whoever holds z_k can form
+// the coefficient of every routed expert without a directory lookup:
+//   u16 slot[r]  slot of component k in the expert's slot order, kNoSlot
+//                for a 0-bit component
+//   f16 s[r], f16 m[r]  scale and offset of a 1..8-bit component (0 for 16-
+//                and 0-bit components: s == 0 marks a 16-bit one)
+//   f32 a[r]     magnitude (0 for a 0-bit component)
+//   f32 cmax     the directory's coefficient bound, then 12 zero bytes
+// each array padded to 16 bytes; the expert blocks follow.  Its place
+// depends only on E and r.
+constexpr uint16_t kNoSlot = 0xFFFFu;
+BM_HD constexpr inline uint64_t ctab_offset(uint64_t E) {
+  return align_up(kHeaderBytes + (uint64_t)kDirRecBytes * E, 256);
+}
+BM_HD constexpr inline uint64_t ctab_s_off(uint64_t r) { return align_up(2 * r, 16); }
+BM_HD constexpr inline uint64_t ctab_m_off(uint64_t r) { return 2 * align_up(2 * r, 16); }
+BM_HD constexpr inline uint64_t ctab_a_off(uint64_t r) { return 3 * align_up(2 * r, 16); }
+BM_HD constexpr inline uint64_t ctab_cmax_off(uint64_t r) {
+  return 3 * align_up(2 * r, 16) + align_up(4 * r, 16);
+}
+BM_HD constexpr inline uint64_t ctab_stride(uint64_t r) { return ctab_cmax_off(r) + 16; }
+BM_HD constexpr inline uint64_t first_block_offset(uint64_t E, uint64_t r) {
+  return align_up(ctab_offset(E) + E * ctab_stride(r), 256);
 }
 
 constexpr uint32_t kGroupSlots = 32;  // width groups are padded to a multiple of this

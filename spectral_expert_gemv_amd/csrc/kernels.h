@@ -28,6 +28,7 @@ struct GateUpPlan {
   size_t z_off;       // T x 2r float32 (projection launch of the batched path)
   size_t zpart_off;   // T x ceil(2r / 16) float32: max |z| per projection work-group
   size_t zt_off;      // ring of kZRing x T x 2r uint64 tagged z (one-launch path)
+  size_t cw_off;      // one-token kernel (T = 1): the rings of FusedArgs::cw and bw
   size_t route_off;   // route lists (see RouteLists)
   size_t coef_off;    // per-tile coefficient tables (batched path, see GroupArgs)
   size_t total;
@@ -59,10 +60,26 @@ struct FusedArgs {
   uint32_t* hint;      // 64 counters, 32 words apart: producing waves done, cumulative over launches
   int grid;            // multiple of 8, all work-groups resident
   uint32_t spin;       // bound on the z exchange waits (0: give up at once, rows NaN)
+  // one-token kernel: kZRing launch buffers (the tag picks one) of tagged
+  // coefficient words, pairs x 2 x kOneSlots (slot order), and of tagged
+  // row-independent partial sums, pairs x 2 x r
+  uint64_t* cw;
+  uint64_t* bw;
 };
 size_t fused_lds_bytes();
 int fused_grid();  // work-groups of the fused kernel on this device (0: unavailable)
 void launch_gateup_fused(const FusedArgs& s, hipStream_t st);
+
+// One-token kernel (T = 1, r <= kOneMaxR, din <= kOneMaxDin, 2r <= 32 grid,
+// pairs * segments <= grid): one
+// unit per work-group, codes decoded before z arrives; same arguments, tags,
+// ring and hint counters as the fused kernel (so one workspace serves both).
+constexpr int kOneMaxR = 2048;
+constexpr int kOneMaxDin = 2048;
+constexpr int kOneMaxK = 16;        // routed slots (4 lanes of a producing wave each)
+constexpr int kOneSlots = 2304;     // slots of one projection (r + 7 * 31, rounded up)
+int one_grid();  // work-groups of the one-token kernel (0: unavailable)
+void launch_gateup_one(const FusedArgs& s, hipStream_t st);
 
 // Pairs grouped by expert and cut into tiles of <= kTile pairs (written by
 // the route-grouping launch).

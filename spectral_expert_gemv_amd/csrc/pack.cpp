@@ -151,7 +151,7 @@ int pack_plan(int E, int dout, int r, const uint8_t* bits, std::vector<DirRec>& 
   if (!bits) return fail(BITSMOE_EINVAL, "bits is null");
   const uint32_t n_seg = (uint32_t)(align_up(dout, kSegRows) / kSegRows);
   dirs.resize(E);
-  uint64_t pos = align_up(kHeaderBytes + (uint64_t)kDirRecBytes * E, 256);
+  uint64_t pos = first_block_offset((uint64_t)E, (uint64_t)r);
   const uint8_t* lut = group_lut().g;
   for (int e = 0; e < E; ++e) {
     uint32_t c[kNumGroups + 2] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
@@ -223,7 +223,45 @@ std::vector<int> pack_slot_columns(const uint8_t* bits_e, int r) {
   return cols;
 }
 
+void pack_ctab_slots(int E, int r, const uint8_t* bits, uint8_t* dst) {
+  const uint64_t stride = ctab_stride((uint64_t)r);
+  memset(dst, 0, (size_t)(E * stride));
+  for (int e = 0; e < E; ++e) {
+    uint16_t* slot = (uint16_t*)(dst + (size_t)e * stride);
+    for (int k = 0; k < r; ++k) slot[k] = kNoSlot;
+    const std::vector<int> cols = pack_slot_columns(bits + (size_t)e * r, r);
+    for (size_t sl = 0; sl < cols.size(); ++sl)
+      if (cols[sl] >= 0) slot[cols[sl]] = (uint16_t)sl;
+  }
+}
+
 namespace {
+
+// s, m, a and cmax of one expert's component table, read back from its
+// block's slot arrays (the slot array is already in place).
+void fill_ctab_values(const DirRec& d, const uint8_t* blk, int r, uint8_t* ct) {
+  const SlotGeo geo = slot_geo(d.count);
+  const uint16_t* kidx = (const uint16_t*)blk;
+  const uint32_t* A = (const uint32_t*)(blk + d.a_off);
+  const uint16_t* S = (const uint16_t*)(blk + d.s_off);
+  const uint16_t* M = (const uint16_t*)(blk + d.m_off);
+  uint16_t* cs = (uint16_t*)(ct + ctab_s_off(r));
+  uint16_t* cm = (uint16_t*)(ct + ctab_m_off(r));
+  uint32_t* ca = (uint32_t*)(ct + ctab_a_off(r));
+  uint32_t sl = 0;
+  for (int g = 0; g < kNumGroups; ++g) {
+    for (uint32_t u = 0; u < d.count[g]; ++u) {
+      const uint32_t q = sl + u, k = kidx[q];
+      ca[k] = A[q];
+      if (g < kNumQGroups) {
+        cs[k] = S[q];
+        cm[k] = M[q];
+      }
+    }
+    sl += 4u * geo.nb[g];
+  }
+  memcpy(ct + ctab_cmax_off(r), &d.cmax, 4);
+}
 
 void fill_block(DirRec& d, int e, int dout, int r, uint32_t n_seg, const float* p,
                 const float* a, const uint8_t* bits, uint8_t* blk) {
@@ -326,14 +364,18 @@ int bitsmoe_pack(int E, int dout, int r, const float* p, const float* a,
   }
   uint8_t* blob = (uint8_t*)out;
   memset(blob, 0, total);
+  pack_ctab_slots(E, r, bits, blob + ctab_offset((uint64_t)E));
   const uint32_t n_seg = (uint32_t)(align_up(dout, kSegRows) / kSegRows);
   unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
   nt = std::min<unsigned>(nt, (unsigned)E);
   std::vector<std::thread> pool;
   for (unsigned w = 0; w < nt; ++w) {
     pool.emplace_back([&, w]() {
-      for (int e = (int)w; e < E; e += (int)nt)
+      for (int e = (int)w; e < E; e += (int)nt) {
         fill_block(dirs[e], e, dout, r, n_seg, p, a, bits, blob + dirs[e].block_offset);
+        fill_ctab_values(dirs[e], blob + dirs[e].block_offset, r,
+                         blob + ctab_offset((uint64_t)E) + (size_t)e * ctab_stride((uint64_t)r));
+      }
     });
   }
   for (auto& t : pool) t.join();
@@ -350,6 +392,7 @@ int bitsmoe_pack(int E, int dout, int r, const float* p, const float* a,
   h.header_bytes = kHeaderBytes;
   h.total_bytes = total;
   h.dir_offset = kHeaderBytes;
+  h.ctab_offset = ctab_offset((uint64_t)E);
   h.crc32 = crc32_ieee(blob + kHeaderBytes, total - kHeaderBytes);
   memcpy(blob, &h, sizeof(h));
   return BITSMOE_OK;
@@ -364,18 +407,20 @@ int bitsmoe_blob_check(const void* blob_v, size_t bytes, int* E_out, int* dout_o
   memcpy(&h, blob, sizeof(h));
   if (h.magic != kMagic) return fail(BITSMOE_EFORMAT, "bad magic");
   if (h.version != kVersion) return fail(BITSMOE_EFORMAT, "unsupported version %u", h.version);
-  if (h.header_bytes != kHeaderBytes || h.dir_offset != kHeaderBytes)
-    return fail(BITSMOE_EFORMAT, "bad header size or directory offset");
+  if (h.header_bytes != kHeaderBytes || h.dir_offset != kHeaderBytes ||
+      h.ctab_offset != ctab_offset(h.E))
+    return fail(BITSMOE_EFORMAT, "bad header size, directory or component table offset");
   if (check_dims((int)h.E, (int)h.dout, (int)h.r) || h.E > (1u << 20))
     return fail(BITSMOE_EFORMAT, "bad dimensions in header");
   if (h.dout_pad != align_up(h.dout, kSegRows) || h.n_seg != h.dout_pad / kSegRows)
     return fail(BITSMOE_EFORMAT, "bad dout_pad / n_seg");
-  if (h.total_bytes > bytes || h.total_bytes < kHeaderBytes + (uint64_t)kDirRecBytes * h.E)
+  if (h.total_bytes > bytes || h.total_bytes < first_block_offset(h.E, h.r))
     return fail(BITSMOE_EFORMAT, "total_bytes %llu inconsistent with buffer %zu",
                 (unsigned long long)h.total_bytes, bytes);
   if (crc32_ieee(blob + kHeaderBytes, h.total_bytes - kHeaderBytes) != h.crc32)
     return fail(BITSMOE_EFORMAT, "CRC mismatch");
-  uint64_t pos = align_up(kHeaderBytes + (uint64_t)kDirRecBytes * h.E, 256);
+  uint64_t pos = first_block_offset(h.E, h.r);
+  const uint64_t cstride = ctab_stride(h.r);
   for (uint32_t e = 0; e < h.E; ++e) {
     DirRec d;
     memcpy(&d, blob + kHeaderBytes + (size_t)kDirRecBytes * e, sizeof(d));
@@ -389,9 +434,25 @@ int bitsmoe_blob_check(const void* blob_v, size_t bytes, int* E_out, int* dout_o
     pos += d.block_bytes;
     if (pos > h.total_bytes) return fail(BITSMOE_EFORMAT, "block %u beyond total_bytes", e);
     const uint16_t* kidx = (const uint16_t*)(blob + d.block_offset);
-    const uint32_t n_slot = slot_geo(d.count).n_slot;
-    for (uint32_t c2 = 0; c2 < n_slot; ++c2)
+    const SlotGeo geo = slot_geo(d.count);
+    for (uint32_t c2 = 0; c2 < geo.n_slot; ++c2)
       if (kidx[c2] >= h.r) return fail(BITSMOE_EFORMAT, "expert %u column index out of range", e);
+    // the component table is the stored columns' values in component
+    // order: every stored slot maps back, nothing else is indexed, and the
+    // other bytes are zero
+    std::vector<uint8_t> want((size_t)cstride, 0);
+    {
+      uint16_t* ws = (uint16_t*)want.data();
+      for (uint32_t k = 0; k < h.r; ++k) ws[k] = kNoSlot;
+      uint32_t sl = 0;
+      for (int g = 0; g < kNumGroups; ++g) {
+        for (uint32_t u = 0; u < d.count[g]; ++u) ws[kidx[sl + u]] = (uint16_t)(sl + u);
+        sl += 4u * geo.nb[g];
+      }
+      fill_ctab_values(d, blob + d.block_offset, (int)h.r, want.data());
+    }
+    if (memcmp(want.data(), blob + h.ctab_offset + cstride * e, (size_t)cstride) != 0)
+      return fail(BITSMOE_EFORMAT, "expert %u component table does not match its block", e);
   }
   if (pos != h.total_bytes) return fail(BITSMOE_EFORMAT, "total_bytes does not match blocks");
   if (E_out) *E_out = (int)h.E;

@@ -232,6 +232,40 @@ __global__ __launch_bounds__(kPkWaves * 64) void k_pack_blocks(
 
 // Register value of the CRC over each 4 KiB chunk of data[0, n) from a
 // start value of 0 (n and the chunk starts are multiples of 16).
+// The component table's values (s, m, a, cmax) of expert blockIdx.y, copied
+// from its block's slot arrays once k_pack_blocks has written them (the
+// slot array of the table is already in place): one thread per slot.
+__global__ __launch_bounds__(256) void k_pack_ctab(uint8_t* __restrict__ blob, int E, int r) {
+  const int e = (int)blockIdx.y;
+  const DirRec* dir = reinterpret_cast<const DirRec*>(blob + kHeaderBytes) + e;
+  uint16_t cnt[kNumGroups];
+#pragma unroll
+  for (int g = 0; g < kNumGroups; ++g) cnt[g] = dir->count[g];
+  const SlotGeo geo = slot_geo(cnt);
+  uint8_t* ct = blob + ctab_offset((uint64_t)E) + (size_t)e * ctab_stride((uint64_t)r);
+  const uint32_t q = blockIdx.x * blockDim.x + threadIdx.x;
+  if (q == 0) *reinterpret_cast<float*>(ct + ctab_cmax_off(r)) = dir->cmax;
+  if (q >= geo.n_slot) return;
+  uint32_t gs = 0;
+  int g = 0;
+  while (g < kNumGroups - 1 && q >= gs + 4u * geo.nb[g]) {
+    gs += 4u * geo.nb[g];
+    ++g;
+  }
+  if (q - gs >= cnt[g]) return;  // a padding slot
+  const uint8_t* blk = blob + dir->block_offset;
+  const uint32_t k = reinterpret_cast<const uint16_t*>(blk)[q];
+  if (k >= (uint32_t)r) return;
+  reinterpret_cast<uint32_t*>(ct + ctab_a_off(r))[k] =
+      reinterpret_cast<const uint32_t*>(blk + dir->a_off)[q];
+  if (g < kNumQGroups) {
+    reinterpret_cast<uint16_t*>(ct + ctab_s_off(r))[k] =
+        reinterpret_cast<const uint16_t*>(blk + dir->s_off)[q];
+    reinterpret_cast<uint16_t*>(ct + ctab_m_off(r))[k] =
+        reinterpret_cast<const uint16_t*>(blk + dir->m_off)[q];
+  }
+}
+
 __global__ __launch_bounds__(256) void k_crc_chunks(const uint8_t* __restrict__ data, uint64_t n,
                                                     uint32_t* __restrict__ out) {
   __shared__ uint32_t T[4][256];
@@ -364,6 +398,12 @@ int bitsmoe_pack_device(int E, int dout, int r, const float* p, const float* a,
                                       hipMemcpyHostToDevice, s),
                        "directory copy")))
     return st;
+  std::vector<uint8_t> ctab((size_t)E * ctab_stride((uint64_t)r));
+  pack_ctab_slots(E, r, bits, ctab.data());
+  if ((st = hip_status(hipMemcpyAsync(blob + ctab_offset((uint64_t)E), ctab.data(), ctab.size(),
+                                      hipMemcpyHostToDevice, s),
+                       "component table copy")))
+    return st;
   if ((st = hip_status(hipMemcpyAsync(w8 + wl.slot_base, slot_base.data(), 4ull * (E + 1),
                                       hipMemcpyHostToDevice, s),
                        "slot table copy")))
@@ -378,6 +418,9 @@ int bitsmoe_pack_device(int E, int dout, int r, const float* p, const float* a,
                      (const uint32_t*)(w8 + wl.slot_base), (const int32_t*)(w8 + wl.cols), E,
                      dout, r, n_seg, (uint32_t*)w8);
   if ((st = hip_status(hipGetLastError(), "pack launch"))) return st;
+  hipLaunchKernelGGL(k_pack_ctab, dim3((4u * max_blk + 255u) / 256u, (unsigned)E), dim3(256), 0,
+                     s, blob, E, r);
+  if ((st = hip_status(hipGetLastError(), "component table launch"))) return st;
   const uint64_t nbody = total - kHeaderBytes;
   const uint64_t nchunks = (nbody + kCrcChunk - 1) / kCrcChunk;
   hipLaunchKernelGGL(k_crc_chunks, dim3((unsigned)((nchunks + 255) / 256)), dim3(256), 0, s,
@@ -421,6 +464,7 @@ int bitsmoe_pack_device(int E, int dout, int r, const float* p, const float* a,
   h.header_bytes = kHeaderBytes;
   h.total_bytes = total;
   h.dir_offset = kHeaderBytes;
+  h.ctab_offset = ctab_offset((uint64_t)E);
   h.crc32 = reg ^ 0xFFFFFFFFu;
   if ((st = hip_status(hipMemcpyAsync(blob, &h, sizeof(h), hipMemcpyHostToDevice, s),
                        "header copy")) ||

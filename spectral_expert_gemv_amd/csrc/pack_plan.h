@@ -20,4 +20,9 @@ int pack_plan(int E, int dout, int r, const uint8_t* bits, std::vector<DirRec>& 
 // multiple of 32 slots.
 std::vector<int> pack_slot_columns(const uint8_t* bits_e, int r);
 
+// The slot arrays of the component table of every expert (E *
+// ctab_stride(r) bytes, the blob's bytes from ctab_offset(E)): slot of
+// component k, kNoSlot for a 0-bit component.  Everything else zero.
+void pack_ctab_slots(int E, int r, const uint8_t* bits, uint8_t* dst);
+
 }  // namespace bitsmoe

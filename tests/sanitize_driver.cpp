@@ -93,7 +93,7 @@ int main(int argc, char** argv) {
   // compare it with the call's r.  dout (12) flipped by 32 rows, across a
   // segment: a change inside the last segment's padding is consistent too.
   const int fields[][2] = {{0, 1},  {4, 1},  {8, 1},  {12, 32}, {20, 1}, {24, 1},
-                           {28, 1}, {32, 1}, {40, 1}, {48, 1}};
+                           {28, 1}, {32, 1}, {40, 1}, {48, 1}, {56, 16}};
   for (const auto& fm : fields) {
     blob[fm[0]] ^= (uint8_t)fm[1];
     EXPECT(bitsmoe_blob_check(blob.data(), blob.size(), 0, 0, 0) != BITSMOE_OK, "header field");
@@ -121,6 +121,33 @@ int main(int argc, char** argv) {
       c[off0 + 1] = 0xFF;
       reseal(c);
       EXPECT(bitsmoe_blob_check(c.data(), c.size(), 0, 0, 0) == BITSMOE_EFORMAT, "kidx range");
+    }
+  }
+
+  // the component -> slot index, changed and re-sealed: an entry moved to
+  // another slot, and a dropped component given a slot
+  {
+    const size_t io = (128 + 64 * (size_t)E + 255) / 256 * 256;
+    uint16_t* idx0 = nullptr;
+    std::vector<uint8_t> c = blob;
+    idx0 = (uint16_t*)(c.data() + io);
+    int k_stored = -1, k_dropped = -1;
+    for (int k = 0; k < r; ++k) {
+      if (idx0[k] != 0xFFFF && k_stored < 0) k_stored = k;
+      if (idx0[k] == 0xFFFF && k_dropped < 0) k_dropped = k;
+    }
+    if (k_stored >= 0) {
+      idx0[k_stored] ^= 1;
+      reseal(c);
+      EXPECT(bitsmoe_blob_check(c.data(), c.size(), 0, 0, 0) == BITSMOE_EFORMAT, "slot index");
+    }
+    if (k_dropped >= 0) {
+      c = blob;
+      idx0 = (uint16_t*)(c.data() + io);
+      idx0[k_dropped] = 0;
+      reseal(c);
+      EXPECT(bitsmoe_blob_check(c.data(), c.size(), 0, 0, 0) == BITSMOE_EFORMAT,
+             "slot index extra");
     }
   }
 

@@ -181,7 +181,7 @@ def test_device_entry_points_validate_before_launch():
     # gate/up on the static workspace: the same checks, and a call needing
     # more workspace than the static array holds is refused before any HIP call
     def gun(T=8, k=2, E=4, din=64, dout=96, r=64, h=FAKE):
-        return L.bitsmoe_moe_gateup_noalloc(FAKE, 1 << 20, FAKE, 1 << 20, FAKE, FAKE, FAKE, T, k,
+        return L.bitsmoe_moe_gateup_noalloc(FAKE, 1 << 26, FAKE, 1 << 26, FAKE, FAKE, FAKE, T, k,
                                             E, din, dout, r, h, None)
     assert bm.moe_gateup_workspace_size(256, 8, 128, 2048, 768, 2048) > bm.GATEUP_NOALLOC_MAX_WS
     assert gun(T=256, k=8, E=128, din=2048, dout=768, r=2048) == bm.ENOSPC

@@ -25,12 +25,23 @@ def test_hand_built_planes():
     bits = np.array([[2, 0, 1]], np.uint8)
     blob = fmt.pack(p, a, bits)
     H = fmt.read_header(blob)
-    assert H["magic"] == b"BMOE" and H["version"] == 3
+    assert H["magic"] == b"BMOE" and H["version"] == 4
     assert H["dout_pad"] == 32 and H["n_seg"] == 1
     base, n_nz, n_q, n_16, seg_words = struct.unpack_from("<QIIII", blob, 128)
     # each used group padded to 32 slots = 8 blocks: 4 * 8 * (1 + 2) words
     assert (n_nz, n_q, n_16, seg_words) == (2, 2, 0, 96)
-    assert base == 256  # align256(128 + 64)
+    # the component table sits at align256(128 + 64) = 256: slots column 0
+    # -> 32 (the width-2 group starts after the 32 slots of the width-1
+    # group), column 1 dropped, column 2 -> slot 0; then s, m (16 bytes
+    # each) and a (16 bytes) in component order, then cmax
+    assert H["ctab_offset"] == 256
+    assert struct.unpack_from("<3H", blob, 256) == (32, 0xFFFF, 0)
+    assert blob[256 + 6:256 + 16] == bytes(10)
+    assert struct.unpack_from("<3e", blob, 256 + 16) == (0.333251953125, 0.0, 0.25)
+    assert struct.unpack_from("<3e", blob, 256 + 32) == (-0.5, 0.0, 0.25)
+    assert struct.unpack_from("<3f", blob, 256 + 48) == (2.0, 0.0, 0.5)
+    assert struct.unpack_from("<f", blob, 256 + 64)[0] == np.float32(2.0) * np.float32(0.333251953125)
+    assert base == 512  # align256(256 + 3 * 16 + 16 + 16)
     cnt = struct.unpack_from("<7H", blob, 128 + 48)
     assert cnt == (1, 1, 0, 0, 0, 0, 0)
     # width group 1 first (column 2 + 31 padding slots), then width 2 (column 0)
