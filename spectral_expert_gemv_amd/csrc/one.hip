@@ -81,11 +81,15 @@ struct __align__(16) OneLds {
   uint32_t W[2][kOArena + 16];    // planes of the unit's segment, gate and up
   int8_t Dg[2][kDigits][kOQ];     // digit rows of the 1..8-bit slots (by slot)
   _Float16 H[2][2][kO16];         // hi, lo rows of the 16-bit slots (by slot - n_qslot)
-  float red[2][kOPW][kSegRows];
+  uint32_t st[2][kOPW * kONSMax];  // step entries of each projection: slot0 | nslot << 16
+  int32_t acc[2][kSegRows][kDigits];  // digit columns of each projection, summed over waves
+  float acc16[2][kSegRows];         // fp16 columns (hi + lo), summed over waves
   float bias[2][kOPW];
   uint32_t ok[kOWaves];
+  uint32_t nst[2];                  // K steps of each projection (0: bad record)
+  uint32_t bnd[2][kOPW + 1];        // wave w of a projection applies steps bnd[w] .. bnd[w + 1] - 1
+  float xb;                         // ||x||_2 (the bound of every |z_k|)
   SegProj desc[2];
-  uint32_t cnt[2][kNumGroups + 1];  // per-width column counts of the unit's expert
 };
 
 // K step i of a projection (uniform): its group g, first slot, slots (64 or
@@ -271,6 +275,49 @@ __device__ __forceinline__ void apply_step(bool f16, const u32x4& a0, const u32x
   }
 }
 
+// This wave's K steps of width group G (steps [lo, hi) that lie in the
+// group): decode of the step's planes (from the LDS arena when staged, else
+// from global memory), B rows from the digit rows, one MFMA per tile.
+template <int G>
+__device__ __forceinline__ void apply_group(const OneLds& L, int pj, const StepTab& tb,
+                                            uint32_t lo, uint32_t hi, uint32_t staged,
+                                            const gu32* gpl, uint32_t nq, int lane,
+                                            i32x4& ai0, i32x4& ai1, f4& af0, f4& af1) {
+  constexpr bool kQ = G < kNumQGroups;
+  constexpr uint32_t kW = G == 0 ? 1 : G == 1 ? 2 : G == 2 ? 3 : G == 3 ? 4 : G == 4 ? 6 : G == 5 ? 8 : 16;
+  constexpr uint32_t kBps = kQ ? 2u * kBlkPerK : (uint32_t)kBlkPerK;  // blocks per step
+  const uint32_t o0 = tb.off[G], o1 = min(tb.off[G + 1], hi);
+  const uint32_t gb0 = tb.gb[G], gb1 = tb.gb[G + 1], gw0 = tb.gw[G];
+#pragma unroll 1
+  for (uint32_t i = max(o0, lo); i < o1; ++i) {
+    const uint32_t b0 = gb0 + (i - o0) * kBps;
+    const uint32_t nb = min(gb1 - b0, kBps);
+    const uint32_t w0 = gw0 + (b0 - gb0) * 4u * kW, nw = nb * 4u * kW;
+    u32x4 x0, x1;
+    if (w0 + nw <= staged) {
+      if constexpr (kQ)
+        decode_w<(int)kW>(&L.W[pj][w0], nb < kBps, lane, x0, x1);
+      else
+        decode_f16(&L.W[pj][w0], lane, x0, x1);
+    } else {
+      decode_step(gpl + w0, G, 4u * nb, lane, x0, x1);
+    }
+    apply_step(!kQ, x0, x1, b_rows(L, pj, !kQ, 4u * b0, nq, lane), ai0, ai1, af0, af1);
+  }
+}
+
+// One transposing exchange of an N-value reduction: lanes with bit O set
+// keep the upper half of the values (O .. 2 O - 1), the others the lower half.
+template <int O, int N>
+__device__ __forceinline__ void tstep_n(float (&v)[N], bool up) {
+#pragma unroll
+  for (int i = 0; i < O; ++i) {
+    const float send = up ? v[i] : v[i + O];
+    const float keep = up ? v[i + O] : v[i];
+    v[i] = keep + __shfl_xor(send, O, kWave);
+  }
+}
+
 // ||x||_2 of the token (lane l holds 16-byte units l, l + 64, l + 128, l +
 // 192 of x, zero past din): the bound on every |z_k| that fixes the
 // coefficient scale.  Producers and consumers both call it; it is not
@@ -339,64 +386,77 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
   // otherwise be waited for before them.
   uint32_t tag;
   if (wv < kOPW) {
-    // ---- z for four rows and the coefficients of those components ----
-    // this wave's Phi^T rows and x (only the nrw rows it owns are loaded)
-    PhiRegs phr;
-#pragma unroll
-    for (int j = 0; j < kPre; ++j) {
-      const bool own = j < nrw && n0 + j < R;  // uniform
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = lane + u * kWave;
-        phr.pv[j][u] = own && i < s.din8 ? ld16(s.phi_t + (size_t)(n0 + j) * s.din8 + i)
-                                         : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + u * kWave;
-      phr.xv[u] = i < s.din8 ? ld16(s.x + i) : make_uint4(0, 0, 0, 0);
-    }
-    asm volatile("" ::: "memory");
-    tag = *(CU32*)s.epoch + 1u;
+    // ---- z for up to four rows and the coefficients of those components
+    // (one body per rows-per-wave count NR, so no work is spent on rows the
+    // wave does not own) ----
+    float z = 0.f, xb = 0.f, cs = 0.f, cm = 0.f, ca = 0.f, cmax = 0.f;
+    uint32_t cslot = kNoSlot;
+    HdrF hd;
     const int pj = n0 >= a.r ? 1 : 0;     // this wave's projection
     const uint8_t* blob = pj ? a.blob_u : a.blob_g;
-    const HdrF hd = load_hdr(blob);
     const int p = lane >> 2, jr = lane & 3;
     const int k = n0 - pj * a.r + jr;     // this lane's component
     const bool live = p < np && jr < nrw && n0 < R;
     const bool eok = ep >= 0 && ep < a.E;
-    const uint8_t* ct = blob + ctab_offset((uint64_t)a.E) +
-                        (size_t)(eok ? ep : 0) * ctab_stride((uint64_t)a.r);
-    // component table entries (global loads, issued behind the Phi^T loads)
-    uint32_t cslot = kNoSlot;
-    float cs = 0.f, cm = 0.f, ca = 0.f, cmax = 0.f;
-    if (live) {
-      const uint32_t kc = (uint32_t)k < (uint32_t)a.r ? (uint32_t)k : 0u;
-      cslot = *(cg16*)(ct + 2u * kc);
-      cs = __half2float(__ushort_as_half(*(cg16*)(ct + ctab_s_off(a.r) + 2u * kc)));
-      cm = __half2float(__ushort_as_half(*(cg16*)(ct + ctab_m_off(a.r) + 2u * kc)));
-      ca = __uint_as_float(*(cg32*)(ct + ctab_a_off(a.r) + 4u * kc));
-      cmax = __uint_as_float(*(cg32*)(ct + ctab_cmax_off(a.r)));
-    }
-    // z of rows n0 + (lane & 3): the partial dot products of the four rows
-    // are reduced together (two transposing exchanges leave row lane & 3 in
-    // every lane, four more finish the sum); the units past din and the rows
-    // past nrw are zero
-    float v4[kPre];
+    auto produce = [&](auto nr_c) {
+      constexpr int NR = decltype(nr_c)::value;
+      // x first (its norm is formed while the Phi^T rows stream in), then
+      // this wave's NR rows of Phi^T
+      uint4 xv[4], pv[NR][4];
 #pragma unroll
-    for (int j = 0; j < kPre; ++j) {
-      float acc = 0.f;
+      for (int u = 0; u < 4; ++u) {
+        const int i = lane + u * kWave;
+        xv[u] = i < s.din8 ? ld16(s.x + i) : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc = fdot8(phr.pv[j][u], phr.xv[u], acc);
-      v4[j] = acc;
-    }
-    tstep<2>(v4, (lane & 2) != 0);
-    tstep<1>(v4, (lane & 1) != 0);
-    float z = v4[0];
+      for (int j = 0; j < NR; ++j) {
+        const bool own = n0 + j < R;  // uniform
 #pragma unroll
-    for (int off = 4; off < kWave; off <<= 1) z += __shfl_xor(z, off, kWave);
-    const float xb = x_bound(phr.xv[0], phr.xv[1], phr.xv[2], phr.xv[3]);
+        for (int u = 0; u < 4; ++u) {
+          const int i = lane + u * kWave;
+          pv[j][u] = own && i < s.din8 ? ld16(s.phi_t + (size_t)(n0 + j) * s.din8 + i)
+                                       : make_uint4(0, 0, 0, 0);
+        }
+      }
+      asm volatile("" ::: "memory");
+      tag = *(CU32*)s.epoch + 1u;
+      hd = load_hdr(blob);
+      const uint8_t* ct = blob + ctab_offset((uint64_t)a.E) +
+                          (size_t)(eok ? ep : 0) * ctab_stride((uint64_t)a.r);
+      // component table entries (global loads, issued behind the Phi^T loads)
+      if (live) {
+        const uint32_t kc = (uint32_t)k < (uint32_t)a.r ? (uint32_t)k : 0u;
+        cslot = *(cg16*)(ct + 2u * kc);
+        cs = __half2float(__ushort_as_half(*(cg16*)(ct + ctab_s_off(a.r) + 2u * kc)));
+        cm = __half2float(__ushort_as_half(*(cg16*)(ct + ctab_m_off(a.r) + 2u * kc)));
+        ca = __uint_as_float(*(cg32*)(ct + ctab_a_off(a.r) + 4u * kc));
+        cmax = __uint_as_float(*(cg32*)(ct + ctab_cmax_off(a.r)));
+      }
+      xb = x_bound(xv[0], xv[1], xv[2], xv[3]);
+      // z of row n0 + (lane & (NR - 1)): the NR partial dot products are
+      // reduced together (log2 NR transposing exchanges leave row lane &
+      // (NR - 1) in every lane, the remaining exchanges finish the sum)
+      float v[NR];
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = fdot8(pv[j][u], xv[u], acc);
+        v[j] = acc;
+      }
+      if constexpr (NR == 4) tstep_n<2, NR>(v, (lane & 2) != 0);
+      if constexpr (NR >= 2) tstep_n<1, NR>(v, (lane & 1) != 0);
+      z = v[0];
+#pragma unroll
+      for (int off = NR; off < kWave; off <<= 1) z += __shfl_xor(z, off, kWave);
+    };
+    if (nrw == 1)
+      produce(std::integral_constant<int, 1>{});
+    else if (nrw == 2)
+      produce(std::integral_constant<int, 2>{});
+    else
+      produce(std::integral_constant<int, 4>{});
+    if (wv == 0 && lane == 0) L.xb = xb;  // (every wave finds the same value)
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every load of this wave is in
     const bool hok = hd.magic == kMagic && hd.version == kVersion && hd.E == (uint32_t)a.E &&
                      hd.dout == (uint32_t)a.dout && hd.r == (uint32_t)a.r;
@@ -467,10 +527,82 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
       const uint32_t nw = min(SP.seg_words, (uint32_t)kOArena);
       stage16(&L.W[pj][0], SP.planes + (size_t)sg * SP.seg_words, nw / 4u, lq, lane, 256);
     }
-    if ((wv & 3) == 0 && lane == 0) {
-      L.desc[pj] = SP;
+    if ((wv & 3) == 0) {
+      if (lane == 0) L.desc[pj] = SP;
+      // (the column sums start at zero)
+      for (int i = lane; i < kSegRows * (kDigits + 1); i += kWave) {
+        if (i < kSegRows * kDigits)
+          (&L.acc[pj][0][0])[i] = 0;
+        else
+          L.acc16[pj][i - kSegRows * kDigits] = 0.f;
+      }
+    } else if ((wv & 3) == 1) {
+      // the projection's K steps, one entry per step (slot0 | nslot << 16),
+      // and their split over the projection's eight waves: contiguous
+      // ranges of about equal cost, a step costing (in halves) 6 for its
+      // loads, digit rows and product plus its width per 32 slots of
+      // decode (8 for a 16-bit step); steps past kOPW * kONSMax are left
+      // out (their records give NaN rows)
+      const StepTab tb = step_tab(SP);
+      const uint32_t nst = SP.ok ? tb.off[kNumGroups] : 0u;
+      const uint32_t ns = min(nst, (uint32_t)(kOPW * kONSMax));
+      uint32_t c[2] = {0u, 0u};
 #pragma unroll
-      for (int g = 0; g < kNumGroups; ++g) L.cnt[pj][g] = SP.ok ? rd.count[g] : 0u;
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t i = (uint32_t)lane + kWave * h;
+        if (i < ns) {
+          const StepInfo si = step_info(tb, i);
+          L.st[pj][i] = si.slot0 | (si.nslot << 16);
+          c[h] = si.g == kNumGroups - 1 ? 8u : 6u + (uint32_t)group_width(si.g) * (si.nslot / 32u);
+        }
+      }
+      // inclusive prefix sums of the costs in step order
+      uint32_t q0 = c[0], q1 = c[1];
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t t0 = __shfl_up(q0, d, kWave), t1 = __shfl_up(q1, d, kWave);
+        if (lane >= d) {
+          q0 += t0;
+          q1 += t1;
+        }
+      }
+      q1 += (uint32_t)__shfl(q0, kWave - 1, kWave);
+      const uint32_t tot = max((uint32_t)__shfl(q1, kWave - 1, kWave), 1u);
+      // step i goes to wave floor(8 (cost before i + half its cost) / total)
+      const uint32_t w0 = min((8u * (2u * (q0 - c[0]) + c[0])) / (2u * tot), (uint32_t)kOPW - 1);
+      const uint32_t w1 = min((8u * (2u * (q1 - c[1]) + c[1])) / (2u * tot), (uint32_t)kOPW - 1);
+      uint32_t bnd[kOPW + 1];
+      bool fits = true;
+      bnd[0] = 0u;
+#pragma unroll
+      for (int w = 1; w <= kOPW; ++w) {
+        bnd[w] = w == kOPW ? ns
+                           : (uint32_t)__popcll(__ballot((uint32_t)lane < ns && w0 < (uint32_t)w)) +
+                                 (uint32_t)__popcll(__ballot((uint32_t)lane + kWave < ns &&
+                                                             w1 < (uint32_t)w));
+        fits = fits && bnd[w] - bnd[w - 1] <= (uint32_t)kONSMax;
+      }
+      if (lane == 0) {
+        L.nst[pj] = nst;
+#pragma unroll
+        for (int w = 0; w <= kOPW; ++w)  // (equal counts where a range would be too long)
+          L.bnd[pj][w] = fits ? bnd[w] : ((uint32_t)w * ns + kOPW - 1) / kOPW;
+      }
+    } else if ((wv & 3) == 2 && sg == 0 && SP.ok) {
+      // the group padding slots of this pair's projection (each group's
+      // slots past its stored columns) get tagged zero words, so that every
+      // slot of a step has a word of this launch: the pair's segment-0
+      // work-group writes them
+      uint64_t* const cwb =
+          s.cw + ((size_t)(tag % kZRing) * np * 2 + (size_t)pair * 2 + pj) * kOneSlots;
+      const uint32_t gb[kNumGroups + 1] = {0u, SP.b1, SP.b2, SP.b3, SP.b4, SP.b5, SP.b6, SP.n_blk};
+#pragma unroll
+      for (int g = 0; g < kNumGroups; ++g) {
+        const uint32_t q1 = min(4u * gb[g + 1], (uint32_t)kOneSlots);
+        for (uint32_t q = 4u * gb[g] + rd.count[g] + (uint32_t)lane; q < q1; q += kWave)
+          __hip_atomic_store(cwb + q, (uint64_t)tag << 32, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
   } else {
@@ -490,53 +622,31 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
     const SegProj P = uniform_seg(L.desc[pj]);
     const uint32_t staged = P.ok ? min(P.seg_words, (uint32_t)kOArena) : 0u;
     const uint32_t nq = P.n_qslot, s8a = 4u * P.b5, s8b = 4u * P.b6;  // width-8 slots
-    const StepTab tb = step_tab(P);
-    const uint32_t nst = tb.off[kNumGroups];
-    // (nst <= 70 for r <= 2048, so nmine <= kONSMax; the clamp keeps a
-    // wave's step table inside its LDS area whatever the record says)
-    const uint32_t nall = nst > (uint32_t)wp ? (nst - (uint32_t)wp + kOPW - 1) / kOPW : 0u;
-    const uint32_t nmine = min(nall, (uint32_t)kONSMax);
+    const uint32_t nst = __builtin_amdgcn_readfirstlane(L.nst[pj]);
+    // this wave's steps: a contiguous range of at most kONSMax (nst <= 70
+    // for r <= 2048; a longer record gives NaN rows)
+    const uint32_t sb0 = __builtin_amdgcn_readfirstlane(L.bnd[pj][wp]);
+    const uint32_t nmine =
+        min(__builtin_amdgcn_readfirstlane(L.bnd[pj][wp + 1]) - sb0, (uint32_t)kONSMax);
     gu64* const cwp =
         (gu64*)(s.cw + ((size_t)(tag % kZRing) * np * 2 + (size_t)pair * 2 + pj) * kOneSlots);
     gu64* const bwp = (gu64*)(s.bw + ((size_t)(tag % kZRing) * np * 2 + (size_t)pair * 2 + pj) *
                                          a.r);
 
-    // ---- this wave's steps (wp, wp + 4, ...): lane j holds step j's entry
-    // (slot0 | nslot << 16, word0 | g << 24, slots holding a component; the
-    // rest of a step is group padding), read back as uniform values with
-    // v_readlane ----
-    uint32_t e_x = 0, e_y = 0, e_z = 0;
-    if ((uint32_t)lane < nmine) {
-      const StepInfo si = step_info(tb, kOPW * (uint32_t)lane + (uint32_t)wp);
-      uint32_t first = 0, cnt = 0;
-#pragma unroll
-      for (int g = 0; g < kNumGroups; ++g)
-        if (si.g == g) {
-          first = 4u * tb.gb[g];
-          cnt = L.cnt[pj][g];
-        }
-      const uint32_t done = si.slot0 - first;
-      e_x = si.slot0 | (si.nslot << 16);
-      e_y = si.word0 | ((uint32_t)si.g << 24);
-      e_z = cnt > done ? min(cnt - done, si.nslot) : 0u;
-    }
+    // ---- lane j holds the entry of the wave's step j (slot0 | nslot <<
+    // 16), read back as uniform values with v_readlane ----
+    const uint32_t e_x = (uint32_t)lane < nmine ? L.st[pj][sb0 + lane] : 0u;
 #define ST_X(j) ((uint32_t)__builtin_amdgcn_readlane((int)e_x, (j)))
-#define ST_Y(j) ((uint32_t)__builtin_amdgcn_readlane((int)e_y, (j)))
-#define ST_Z(j) ((uint32_t)__builtin_amdgcn_readlane((int)e_z, (j)))
+    // lane l's slot in step j: slot0 + l (lanes past a 32-slot step repeat
+    // its slots; every slot, group padding included, has a word)
+#define SLOT(j) ((ST_X(j) & 0xFFFFu) + ((uint32_t)lane & ((ST_X(j) >> 16) - 1u)))
 
     // ---- loads of this wave's coefficient words and partial sums ----
-    uint32_t sl[kONSMax];  // this lane's slot in step j (0xFFFF: padding or none)
     uint64_t cw[kONSMax];
 #pragma unroll
     for (int j = 0; j < kONSMax; ++j) {
-      sl[j] = 0xFFFFu;
       cw[j] = (uint64_t)tag << 32;
-      if ((uint32_t)j < nmine) {
-        if ((uint32_t)lane < ST_Z(j)) {
-          sl[j] = (ST_X(j) & 0xFFFFu) + (uint32_t)lane;
-          cw[j] = cwp[sl[j]];
-        }
-      }
+      if ((uint32_t)j < nmine) cw[j] = cwp[SLOT(j)];
     }
     const int nw4 = (npp + kOPW - 1) / kOPW;  // partial sums this wave adds
     uint64_t pw[kOPart];
@@ -546,14 +656,7 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
       pw[i] = (uint64_t)tag << 32;
       if (lane + kWave * i < nw4 && q < npp) pw[i] = bwp[q];
     }
-    uint4 xv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + u * kWave;
-      xv[u] = i < s.din8 ? ld16(s.x + i) : make_uint4(0, 0, 0, 0);
-    }
-
-    const int S = coef_scale(P.cmax, x_bound(xv[0], xv[1], xv[2], xv[3]));
+    const int S = coef_scale(P.cmax, L.xb);
 
     // ---- the tags: stale words re-read device-coherently, bounded ----
     uint32_t spins = 0;
@@ -568,7 +671,7 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
 #pragma unroll
       for (int j = 0; j < kONSMax; ++j)
         if ((uint32_t)(cw[j] >> 32) != tag)
-          cw[j] = __hip_atomic_load(cwp + sl[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          cw[j] = __hip_atomic_load(cwp + SLOT(j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
       for (int i = 0; i < kOPart; ++i)
         if ((uint32_t)(pw[i] >> 32) != tag)
@@ -582,19 +685,17 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
     float corr = 0.f;  // sum of rint(c 2^S) over width-8 slots (those enter as code - 128)
 #pragma unroll
     for (int j = 0; j < kONSMax; ++j) {
-      const uint32_t q = sl[j];
       if ((uint32_t)j < nmine) {
-        // (padding lanes of a step write zeros)
-        const uint32_t ex = ST_X(j);
-        const uint32_t q0 = (ex & 0xFFFFu) + (uint32_t)lane;
-        const uint32_t w = (uint32_t)cw[j] & (q != 0xFFFFu ? 0xFFFFFFFFu : 0u);
+        const uint32_t ex = ST_X(j), s0 = ex & 0xFFFFu;  // (uniform)
+        const uint32_t q0 = s0 + (uint32_t)lane;
+        const uint32_t w = (uint32_t)cw[j];
         if ((uint32_t)lane < (ex >> 16)) {
-          if (q0 < nq) {
+          if (s0 < nq) {
             L.Dg[pj][0][q0] = (int8_t)w;
             L.Dg[pj][1][q0] = (int8_t)(w >> 8);
             L.Dg[pj][2][q0] = (int8_t)(w >> 16);
             L.Dg[pj][3][q0] = (int8_t)(w >> 24);
-            if (q0 >= s8a && q0 < s8b) corr += (float)(int)((w ^ 0x80808080u) - 0x80808080u);
+            if (s0 >= s8a && s0 < s8b) corr += (float)(int)((w ^ 0x80808080u) - 0x80808080u);
           } else {
             reinterpret_cast<uint16_t*>(&L.H[pj][0][0])[q0 - nq] = (uint16_t)w;
             reinterpret_cast<uint16_t*>(&L.H[pj][1][0])[q0 - nq] = (uint16_t)(w >> 16);
@@ -612,47 +713,43 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
     // (a step's B operand is read by the wave that wrote its digits: LDS
     // accesses of one wave complete in order)
 
-    // ---- apply: decode each step's A operands and multiply ----
+    // ---- apply: decode each step's A operands and multiply, one loop per
+    // width group (the width a compile-time value) ----
     i32x4 ai0 = {0, 0, 0, 0}, ai1 = {0, 0, 0, 0};  // column n: digit n
     f4 af0 = {0.f, 0.f, 0.f, 0.f}, af1 = {0.f, 0.f, 0.f, 0.f};  // fp16 columns: hi, lo
-#pragma unroll 1
-    for (uint32_t j = 0; j < nmine; ++j) {
-      // (run-time j: the entry comes from LDS-free v_readlane too)
-      const uint32_t ex = (uint32_t)__builtin_amdgcn_readlane((int)e_x, (int)j);
-      const uint32_t ey = (uint32_t)__builtin_amdgcn_readlane((int)e_y, (int)j);
-      const uint32_t s0 = ex & 0xFFFFu, n = ex >> 16;
-      const uint32_t w0 = ey & 0xFFFFFFu, g = ey >> 24;
-      const uint32_t nw = (n / 4u) * 4u * (uint32_t)group_width((int)g);
-      u32x4 x0, x1;
-      if (w0 + nw <= staged)
-        decode_step_lds(&L.W[pj][w0], (int)g, n, lane, x0, x1);
-      else
-        decode_step(P.planes + (size_t)sg * P.seg_words + w0, (int)g, n, lane, x0, x1);
-      const bool f16 = g == kNumGroups - 1;
-      apply_step(f16, x0, x1, b_rows(L, pj, f16, s0, nq, lane), ai0, ai1, af0, af1);
+    {
+      const StepTab tb = step_tab(P);
+      const auto gpl = P.planes + (size_t)sg * P.seg_words;
+      apply_group<0>(L, pj, tb, sb0, sb0 + nmine, staged, gpl, nq, lane, ai0, ai1, af0, af1);
+      apply_group<1>(L, pj, tb, sb0, sb0 + nmine, staged, gpl, nq, lane, ai0, ai1, af0, af1);
+      apply_group<2>(L, pj, tb, sb0, sb0 + nmine, staged, gpl, nq, lane, ai0, ai1, af0, af1);
+      apply_group<3>(L, pj, tb, sb0, sb0 + nmine, staged, gpl, nq, lane, ai0, ai1, af0, af1);
+      apply_group<4>(L, pj, tb, sb0, sb0 + nmine, staged, gpl, nq, lane, ai0, ai1, af0, af1);
+      apply_group<5>(L, pj, tb, sb0, sb0 + nmine, staged, gpl, nq, lane, ai0, ai1, af0, af1);
+      apply_group<6>(L, pj, tb, sb0, sb0 + nmine, staged, gpl, nq, lane, ai0, ai1, af0, af1);
     }
 
 #undef ST_X
-#undef ST_Y
-#undef ST_Z
-    // ---- fold the columns; the eight waves of a projection meet in LDS ----
+#undef SLOT
+    // ---- the eight waves of a projection sum their columns in LDS (exact
+    // for the integer columns: one scale serves the whole projection) ----
     {
       const int n = lane & 15, q = lane >> 4;
+      if (nmine > 0) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const i32x4& ai = t ? ai1 : ai0;
-        const f4& a16 = t ? af1 : af0;
+        for (int t = 0; t < 2; ++t) {
+          const i32x4& ai = t ? ai1 : ai0;
+          const f4& a16 = t ? af1 : af0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = (n < kDigits ? ldexpf((float)ai[i], 8 * n - S) : 0.f) +
-                    (n < 2 ? ldexpf(a16[i], 16 - S) : 0.f);
-          v += dpp_move<0xB1>(v, 0.f);  // quad_perm [1,0,3,2]
-          v += dpp_move<0x4E>(v, 0.f);  // quad_perm [2,3,0,1]
-          if (n == 0) L.red[pj][wp][16 * t + 4 * q + i] = v;
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * t + 4 * q + i;
+            if (n < kDigits) atomicAdd(&L.acc[pj][row][n], ai[i]);
+            if (n < 2) atomicAdd(&L.acc16[pj][row], a16[i]);
+          }
         }
       }
       const float bw = wave_sum_dpp(bias);
-      const bool wok = zok && P.ok && nall <= (uint32_t)kONSMax;
+      const bool wok = zok && P.ok && nst <= (uint32_t)(kOPW * kONSMax);
       if (lane == 0) {
         L.bias[pj][wp] = bw;
         L.ok[wv] = wok ? 1u : 0u;
@@ -660,16 +757,18 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
     }
     lds_sync();
     if (wv == 0 && lane < kSegRows) {
+      // y = sum over digits n of column n 2^(8 n - S) + fp16 columns
+      // 2^(16 - S) + the row-independent part, per projection
       float ys[2];
       uint32_t okw = 1u;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        float sum = 0.f, bsum = 0.f;
+        const int Sq = q == pj ? S : coef_scale(L.desc[q].cmax, L.xb);
+        float sum = ldexpf(L.acc16[q][lane], 16 - Sq), bsum = 0.f;
 #pragma unroll
-        for (int w = 0; w < kOPW; ++w) {
-          sum += L.red[q][w][lane];
-          bsum += L.bias[q][w];
-        }
+        for (int n = 0; n < kDigits; ++n) sum += ldexpf((float)L.acc[q][lane][n], 8 * n - Sq);
+#pragma unroll
+        for (int w = 0; w < kOPW; ++w) bsum += L.bias[q][w];
         ys[q] = sum + bsum;
       }
 #pragma unroll
