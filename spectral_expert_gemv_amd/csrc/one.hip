@@ -81,13 +81,14 @@ struct __align__(16) OneLds {
   uint32_t W[2][kOArena + 16];    // planes of the unit's segment, gate and up
   int8_t Dg[2][kDigits][kOQ];     // digit rows of the 1..8-bit slots (by slot)
   _Float16 H[2][2][kO16];         // hi, lo rows of the 16-bit slots (by slot - n_qslot)
-  uint32_t st[2][kOPW * kONSMax];  // step entries of each projection: slot0 | nslot << 16
   int32_t acc[2][kSegRows][kDigits];  // digit columns of each projection, summed over waves
   float acc16[2][kSegRows];         // fp16 columns (hi + lo), summed over waves
   float bias[2][kOPW];
   uint32_t ok[kOWaves];
   uint32_t nst[2];                  // K steps of each projection (0: bad record)
-  uint32_t bnd[2][kOPW + 1];        // wave w of a projection applies steps bnd[w] .. bnd[w + 1] - 1
+  uint32_t wst[2][kOPW][kONSMax];   // entries (slot0 | nslot << 16) of the steps wave w of a
+                                    // projection applies, in order
+  uint32_t wsb[2][kOPW];            // the first of those steps
   float xb;                         // ||x||_2 (the bound of every |z_k|)
   SegProj desc[2];
 };
@@ -546,13 +547,13 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
       const StepTab tb = step_tab(SP);
       const uint32_t nst = SP.ok ? tb.off[kNumGroups] : 0u;
       const uint32_t ns = min(nst, (uint32_t)(kOPW * kONSMax));
-      uint32_t c[2] = {0u, 0u};
+      uint32_t c[2] = {0u, 0u}, ent[2] = {0u, 0u};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t i = (uint32_t)lane + kWave * h;
         if (i < ns) {
           const StepInfo si = step_info(tb, i);
-          L.st[pj][i] = si.slot0 | (si.nslot << 16);
+          ent[h] = si.slot0 | (si.nslot << 16);
           c[h] = si.g == kNumGroups - 1 ? 8u : 6u + (uint32_t)group_width(si.g) * (si.nslot / 32u);
         }
       }
@@ -582,12 +583,31 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
                                                              w1 < (uint32_t)w));
         fits = fits && bnd[w] - bnd[w - 1] <= (uint32_t)kONSMax;
       }
-      if (lane == 0) {
-        L.nst[pj] = nst;
+      // (equal counts where a range would be too long)
 #pragma unroll
-        for (int w = 0; w <= kOPW; ++w)  // (equal counts where a range would be too long)
-          L.bnd[pj][w] = fits ? bnd[w] : ((uint32_t)w * ns + kOPW - 1) / kOPW;
+      for (int w = 0; w <= kOPW; ++w)
+        bnd[w] = fits ? bnd[w] : ((uint32_t)w * ns + kOPW - 1) / kOPW;
+      // each wave's own list: entry j of wave w is step bnd[w] + j (zero
+      // past the wave's range, and for every wave of an over-long record)
+      for (int i = lane; i < kOPW * kONSMax; i += kWave) (&L.wst[pj][0][0])[i] = 0u;
+      const bool over = nst > (uint32_t)(kOPW * kONSMax);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t i = (uint32_t)lane + kWave * h;
+        uint32_t w = 0, b = 0;
+#pragma unroll
+        for (int v = 1; v < kOPW; ++v)
+          if (i >= bnd[v]) {
+            w = (uint32_t)v;
+            b = bnd[v];
+          }
+        if (i < ns && !over) L.wst[pj][w][i - b] = ent[h];
       }
+      uint32_t bl = 0;
+#pragma unroll
+      for (int v = 1; v < kOPW; ++v) bl = lane == v ? bnd[v] : bl;
+      if (lane < kOPW) L.wsb[pj][lane] = bl;
+      if (lane == 0) L.nst[pj] = nst;
     } else if ((wv & 3) == 2 && sg == 0 && SP.ok) {
       // the group padding slots of this pair's projection (each group's
       // slots past its stored columns) get tagged zero words, so that every
@@ -612,30 +632,20 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
     tag = *(CU32*)s.epoch + 1u;
   }
   lds_barrier();  // staged data and descriptors visible
-  // every wave of the group has read the epoch: count the group on the hint
-  // counters (kOHint waves, as the fused kernel does), after which work-group
-  // 0 may advance the epoch
-  if (wv < kOHint) hint_add(s, (int)blockIdx.x * kOHint + wv, lane);
 
   if (have) {
     const int pj = wv >= kOPW ? 0 : 1;  // waves 8-15 gate, 0-7 up
-    const SegProj P = uniform_seg(L.desc[pj]);
-    const uint32_t staged = P.ok ? min(P.seg_words, (uint32_t)kOArena) : 0u;
-    const uint32_t nq = P.n_qslot, s8a = 4u * P.b5, s8b = 4u * P.b6;  // width-8 slots
-    const uint32_t nst = __builtin_amdgcn_readfirstlane(L.nst[pj]);
-    // this wave's steps: a contiguous range of at most kONSMax (nst <= 70
-    // for r <= 2048; a longer record gives NaN rows)
-    const uint32_t sb0 = __builtin_amdgcn_readfirstlane(L.bnd[pj][wp]);
-    const uint32_t nmine =
-        min(__builtin_amdgcn_readfirstlane(L.bnd[pj][wp + 1]) - sb0, (uint32_t)kONSMax);
+    // this wave's steps (a contiguous range of at most kONSMax; nst <= 70
+    // for r <= 2048, a longer record gives NaN rows): lane j holds the entry
+    // of step j (slot0 | nslot << 16), read back as uniform values with
+    // v_readlane; the coefficient loads go out first
+    const uint32_t e_x = lane < kONSMax ? L.wst[pj][wp][lane] : 0u;
+    const uint32_t nmine = (uint32_t)__popcll(__ballot(e_x != 0u));
     gu64* const cwp =
         (gu64*)(s.cw + ((size_t)(tag % kZRing) * np * 2 + (size_t)pair * 2 + pj) * kOneSlots);
     gu64* const bwp = (gu64*)(s.bw + ((size_t)(tag % kZRing) * np * 2 + (size_t)pair * 2 + pj) *
                                          a.r);
 
-    // ---- lane j holds the entry of the wave's step j (slot0 | nslot <<
-    // 16), read back as uniform values with v_readlane ----
-    const uint32_t e_x = (uint32_t)lane < nmine ? L.st[pj][sb0 + lane] : 0u;
 #define ST_X(j) ((uint32_t)__builtin_amdgcn_readlane((int)e_x, (j)))
     // lane l's slot in step j: slot0 + l (lanes past a 32-slot step repeat
     // its slots; every slot, group padding included, has a word)
@@ -656,6 +666,15 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
       pw[i] = (uint64_t)tag << 32;
       if (lane + kWave * i < nw4 && q < npp) pw[i] = bwp[q];
     }
+    // every wave of the group has read the epoch: count the group on the
+    // hint counters (kOHint waves, as the fused kernel does), after which
+    // work-group 0 may advance the epoch
+    if (wv < kOHint) hint_add(s, (int)blockIdx.x * kOHint + wv, lane);
+    const SegProj P = uniform_seg(L.desc[pj]);
+    const uint32_t staged = P.ok ? min(P.seg_words, (uint32_t)kOArena) : 0u;
+    const uint32_t nq = P.n_qslot, s8a = 4u * P.b5, s8b = 4u * P.b6;  // width-8 slots
+    const uint32_t nst = __builtin_amdgcn_readfirstlane(L.nst[pj]);
+    const uint32_t sb0 = __builtin_amdgcn_readfirstlane(L.wsb[pj][wp]);
     const int S = coef_scale(P.cmax, L.xb);
 
     // ---- the tags: stale words re-read device-coherently, bounded ----
@@ -777,6 +796,8 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
       if (row < a.dout)
         a.h[(size_t)pair * a.dout + row] = okw ? silu_mul(ys[0], ys[1]) : __builtin_nanf("");
     }
+  } else if (wv < kOHint) {
+    hint_add(s, (int)blockIdx.x * kOHint + wv, lane);
   }
 
   // Work-group 0 advances the epoch once every producing wave has counted
