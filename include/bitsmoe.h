@@ -84,20 +84,24 @@ const char* bitsmoe_last_error_detail(void);
  *   header 128 B: "BMOE", u32 version(=4), E, dout, r, dout_pad
  *     (=32*ceil(dout/32)), n_seg (=dout_pad/32), header_bytes(=128);
  *     u64 total_bytes at 32, u64 dir_offset(=128) at 40, u32 CRC-32 (IEEE)
- *     of [128, total) at 48, u64 slot_index_offset (=align256(128 + 64 E))
- *     at 56.
+ *     of [128, total) at 48, u64 ctab_offset (=align256(128 + 64 E)) at 56.
  *   directory: E records of 64 B: u64 block_offset; u32 n_nz, n_q, n_16,
  *     seg_words (u32 words of one 32-row segment record), a_off, s_off,
  *     m_off, planes_off; f32 cmax (largest |a|*s over 1..8-bit columns,
  *     |a| over 16-bit ones); u32 block_bytes; u16 count[7] of widths
  *     1,2,3,4,6,8,16 at 48 (offsets relative to the expert block).
- *   slot index at slot_index_offset: per expert, at stride align16(2 r),
- *     u16[r]: entry k is the slot of component k in the expert's slot
- *     order, 0xFFFF for a 0-bit component (the inverse of kidx; it lets the
- *     producer of z_k place the coefficient a_k s_k z_k of every routed
- *     expert directly).
+ *   component table at ctab_offset: per expert, at stride
+ *     ctab_stride = 3 align16(2 r) + align16(4 r) + 16, the expert's
+ *     components in k order (it lets whoever holds z_k form the coefficient
+ *     of every routed expert without the directory): u16 slot[r] (slot of
+ *     component k in the expert's slot order, 0xFFFF for a 0-bit
+ *     component: the inverse of kidx) @0, f16 s[r] @align16(2 r), f16 m[r]
+ *     @2 align16(2 r) (both 0 for 16- and 0-bit components), f32 a[r]
+ *     @3 align16(2 r) (0 for 0-bit ones), f32 cmax (the directory's) and 12
+ *     zero bytes @3 align16(2 r) + align16(4 r).  bitsmoe_blob_check
+ *     rebuilds every expert's table from its block and compares bytes.
  *   expert block (256-aligned, back to back from
- *     align256(slot_index_offset + E align16(2 r))): slots ordered by width group
+ *     align256(ctab_offset + E ctab_stride)): slots ordered by width group
  *     1,2,3,4,6,8,16, ascending k inside a group, each group padded with
  *     zero slots to a multiple of 32 (so a 32-slot step has one width);
  *     0-bit columns have no slot.  n_slot slots, n_qslot of width <= 8:
@@ -226,6 +230,12 @@ int bitsmoe_expert_apply(const void* packed, size_t packed_bytes, int E, int dou
  *           bytes from call to call (at that fixed place whatever T is, so
  *           one workspace, sized for the largest T, may serve calls of any T
  *           in turn); calls that share a workspace must not run concurrently.
+ * At T = 1 (k <= 16, r <= 2048 and a multiple of 4, din <= 2048) one launch
+ * also forms every routed expert's coefficients next to z.  Their integer
+ * scale comes from the blob's bound cmax and |z_k| <= ||x||_2, which holds
+ * for the unit-norm rows of a basis from a factorization; rows of Phi^T
+ * whose norm exceeds 1.86 can push a coefficient past the scale, and the
+ * affected rows of h are then NaN (never out-of-bounds accesses).
  */
 int bitsmoe_moe_gateup_workspace_size(int T, int k, int E, int din, int dout, int r,
                                       size_t* bytes);
