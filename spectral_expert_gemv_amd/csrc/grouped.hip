@@ -21,17 +21,15 @@
 // chunk, into tables in the workspace.
 //
 // k_gateup_grouped: one 512-lane work-group per (tile, 32-row segment) unit,
-// both projections (waves 0-3 gate, 4-7 up); the units fill the first
-// ntiles x segments blocks of the grid (unit u: tile u % ntiles, segment
-// u / ntiles), the grid's other blocks, sized for the largest tile count,
-// exit at once.  The segment records are staged in
-// LDS in chunks of at most 7168 words per projection; the tile's
-// coefficients go through LDS in 128-slot chunks, each loaded into
-// registers (16 bytes a lane) while the previous chunk's products run.  The
-// work-group's LDS stays under half of a CU's, so two units share a CU and
-// each one's chain of dependent loads overlaps the other's products.  The
-// apply is the same MFMA K-step loop as the
-// one-launch kernel with up to 16 token columns.  A one-projection mode
+// both projections (waves 0-3 gate, 4-7 up).  Tile x + 8 i runs on XCD x
+// with its segment units one after another, so the segments of a tile
+// share one L2 for its coefficient tables; blocks past the tile count exit
+// at once.  The segment records are staged in LDS in chunks of at most
+// 7168 words per projection; each wave reads the B operands of its K steps
+// (16 bytes a lane, two steps ahead) straight from the tile's coefficient
+// tables, so a chunk's steps run without barriers.  The work-group's LDS
+// stays under half of a CU's, so two units share a CU and each one's chain
+// of dependent loads overlaps the other's products.  A one-projection mode
 // (the down projection) gives each pair its own z and lets the two wave
 // halves take two segments.
 #include <hip/hip_fp16.h>
@@ -63,17 +61,11 @@ constexpr int kGThreads = kGWaves * kWave;  // 512
 constexpr int kGProj = 256;                 // lanes per projection
 constexpr int kGPW = kGWaves / 2;           // waves per projection
 constexpr int kGMaxW = 7168;                // plane words per projection per chunk
-constexpr int kGCS = 128;                   // slots per coefficient chunk of the apply
-constexpr int kGCStride = kGCS + 8;         // fp16 per token row (bank spread)
 constexpr int kGZP = 16;                    // lanes per token for the partial maxima
 
 struct __align__(16) GroupLds {
   uint32_t W[2][kGMaxW + 64];
   union {
-    struct {
-      _Float16 hi[2][kTile * kGCStride];
-      _Float16 lo[2][kTile * kGCStride];
-    } c;
     float red[2][kGPW][kTile][kSegRows];
   } u;
   float pbias[2][kGPW][kTile];
@@ -81,7 +73,6 @@ struct __align__(16) GroupLds {
   int pair[kTile];
   uint32_t pok[2][kGPW];
   int nch[2];
-  int ncc[2][2];  // [plane chunk parity][projection]: coefficient chunks
 };
 static_assert(sizeof(GroupLds) <= 80 * 1024, "two work-groups per CU (160 KB of LDS)");
 
@@ -191,14 +182,17 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   // behind a block without work.
   typedef __attribute__((address_space(4))) const int CI32;
   const int ntl = *(CI32*)s.rl.ntiles;  // written by the route step before this launch
-  const int u = blockIdx.x;
   const bool single = s.single != 0;
   const int nsu = single ? (a.n_seg + 1) / 2 : a.n_seg;  // segment units per tile
-  if (ntl <= 0 || u >= ntl * nsu) return;
-  const int ti = u % ntl;
+  // block b runs on XCD b % 8; tile x + 8 i goes to XCD x, its segment units
+  // one after another, so the segments of a tile share one L2 for the
+  // tile's coefficient tables
+  const int xcd = (int)blockIdx.x & 7, jx = (int)blockIdx.x >> 3;
+  const int ti = xcd + 8 * (jx / nsu), su = jx % nsu;
+  if (ntl <= 0 || ti >= ntl) return;
   // single: this half's segment (a half past the last segment repeats it
   // and writes nothing)
-  const int sg0 = single ? 2 * (u / ntl) : u / ntl;
+  const int sg0 = single ? 2 * su : su;
   const int sgh = single ? sg0 + pj : sg0;
   const int sg = sgh < a.n_seg ? sgh : a.n_seg - 1;
   const int e = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti]);
@@ -212,35 +206,13 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   uint32_t b1 = chunk_end(P, 0, kGMaxW);
   stage_chunk(&L.W[pj][0], P, sg, 0, b1, lp, lane, kGProj);
 
-  // The tile's coefficients (k_group_coef) pass through registers: lane lp
-  // holds the 16-byte piece 8 (lp % 16) .. + 7 of row lp / 16 of the hi and
-  // lo tables; the next 128-slot chunk is loaded while the products of the
-  // current one run.  Rows past the tile's tokens load the last token's row
-  // (same cache lines) and are not stored.
-  //
-  // Chunk length: the LDS table holds kTile rows of kGCS slots, so a tile of
-  // nt <= ntp tokens (ntp a power of two) takes chunks of cs = kGCS kTile /
-  // ntp slots in ntp rows of stride cs + 8: fewer chunks, barriers and
-  // coefficient round trips for the small tiles that dominate decode-sized
-  // batches.
+  // The tile's coefficients (k_group_coef) are read straight from the
+  // tables: lane (m, kg) takes token row m (the last token's row past the
+  // tile's tokens: same cache lines, columns never stored), slots 8 kg ..
   const size_t trow = (size_t)(ti * 2 + (single ? 0 : pj)) * kTile;
-  static_assert(kGProj == kTile * kGCS / 8, "one 16-byte piece per lane");
-  const int ntp = nt <= 1 ? 1 : (nt <= 2 ? 2 : (nt <= 4 ? 4 : (nt <= 8 ? 8 : 16)));
-  const uint32_t cs = (uint32_t)(kGCS * kTile / ntp);  // slots per coefficient chunk
-  const int cstr = (int)cs + 8;                          // fp16 per token row in LDS
-  const int ppr = (int)cs / 8;                           // 16-byte pieces per row
-  const int cq = lp / ppr, c8 = 8 * (lp % ppr);
-  const bool cA = cq < nt;
-  const size_t oA = (trow + (size_t)min(cq, nt - 1)) * s.rpad + c8;
-  _Float16* const dA = &L.u.c.hi[pj][0] + cq * cstr + c8;
-  _Float16* const dAl = &L.u.c.lo[pj][0] + cq * cstr + c8;
-  uint4 chA, clA;
-#define GROUPED_COEF_FETCH(s0)                                             \
-  do {                                                                     \
-    chA = *reinterpret_cast<const uint4*>(s.thi + oA + (s0));             \
-    clA = *reinterpret_cast<const uint4*>(s.tlo + oA + (s0));             \
-  } while (0)
-  GROUPED_COEF_FETCH(0u);
+  const size_t boff = (trow + (size_t)min(lane & 15, nt - 1)) * s.rpad + 8u * (uint32_t)(lane >> 4);
+  const _Float16* const bh = s.thi + boff;
+  const _Float16* const bl = s.tlo + boff;
 
   // tokens of the tile and their coefficient scales: lanes (n, j) of the
   // projection take partial maxima j, j + 16, ... of token n
@@ -260,26 +232,16 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
     for (int off = kGZP / 2; off > 0; off >>= 1) zm = fmaxf(zm, __shfl_xor(zm, off, kWave));
     if (j == 0 && n < nt) L.S[pj][n] = coef_shift(P.cmax, zm);
   }
-  // Coefficient chunks of kGCS slots (kGCS / 4 blocks, kGCS / 32 K steps)
-  // inside each plane chunk.  The two projections' plane chunks end at
-  // different blocks, so their counts of coefficient chunks may differ; the
-  // barriers are shared, so the work-group runs the larger count (published
-  // through L.ncc, one slot per chunk parity) and a half past its own count
-  // only takes part in the barriers.
-  const uint32_t kCB = cs / 4;  // blocks per coefficient chunk
-  auto n_coef_chunks = [kCB](uint32_t c0, uint32_t c1) {
-    return max((int)((c1 - c0 + kCB - 1) / kCB), 1);
-  };
+  // Plane chunks of at most kGMaxW words per projection: the two
+  // projections' counts may differ, the barriers are shared, so the
+  // work-group runs the larger count and a half past its own count only
+  // takes part in the barriers.
   {
     int nc = 0;
     for (uint32_t b = 0; b < P.n_blk; b = chunk_end(P, b, kGMaxW)) ++nc;
-    if (threadIdx.x == (unsigned)(pj * kGProj)) {
-      L.nch[pj] = nc;
-      L.ncc[0][pj] = n_coef_chunks(0u, b1);
-    }
+    if (threadIdx.x == (unsigned)(pj * kGProj)) L.nch[pj] = nc;
   }
-  // the first plane chunk's staged words have landed (waited for here, once,
-  // so that no later LDS read is made to wait for the coefficient loads)
+  // the first plane chunk's staged words have landed
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int nch = __builtin_amdgcn_readfirstlane(max(L.nch[0], L.nch[1]));  // uniform
@@ -289,43 +251,20 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   for (int ch = 0; ch < max(nch, 1); ++ch) {
     if (ch > 0) {
       const uint32_t b1n = chunk_end(P, b0, kGMaxW);
-      if (threadIdx.x == (unsigned)(pj * kGProj)) L.ncc[ch & 1][pj] = n_coef_chunks(b0, b1n);
-      lds_sync();  // every wave is done with the previous chunk; L.ncc is set
+      lds_sync();  // every wave is done with the previous chunk
       b1 = b1n;
       stage_chunk(&L.W[pj][0], P, sg, b0, b1, lp, lane, kGProj);
-      __builtin_amdgcn_s_waitcnt(0);  // the staged words have landed
-    }
-    const uint32_t kbe = (b1 + kBlkPerK - 1) / kBlkPerK;
-    const int ncc = n_coef_chunks(b0, b1);  // this half's
-    const int nccw = __builtin_amdgcn_readfirstlane(max(L.ncc[ch & 1][0], L.ncc[ch & 1][1]));
-    for (int cc = 0; cc < nccw; ++cc) {
-      const uint32_t cb0 = b0 + kCB * cc;
-      const uint32_t s0 = 4u * cb0;
-      const bool mine = cc < ncc;
-      if (cc > 0) lds_sync();  // the previous coefficient chunk is read
-      if (mine) {
-        if (cA) {
-          *reinterpret_cast<uint4*>(dA) = chA;
-          *reinterpret_cast<uint4*>(dAl) = clA;
-        }
-        if (cc + 1 < ncc)
-          GROUPED_COEF_FETCH(s0 + cs);
-        else if (ch + 1 < nch)
-          GROUPED_COEF_FETCH(4u * b1);
-      }
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's staged words have landed
       lds_sync();
-      const uint32_t kb0 = cb0 / kBlkPerK;
-      const uint32_t kb1 = min(kb0 + kCB / kBlkPerK, kbe);
-      if (mine && b1 > cb0) {
-        const uint32_t* base = &L.W[pj][0] - block_word(P, b0);
-        mfma_ksteps(P, base, &L.u.c.hi[pj][0], &L.u.c.lo[pj][0], cstr, s0,
-                    nt, kb0, kb1, wp, lane, acc0, acc1);
-      }
+    }
+    if (b1 > b0) {
+      const uint32_t* base = &L.W[pj][0] - block_word(P, b0);
+      mfma_ksteps_gb(P, base, bh, bl, b0 / kBlkPerK, (b1 + kBlkPerK - 1) / kBlkPerK, wp, lane,
+                     acc0, acc1);
     }
     b0 = b1;
   }
-#undef GROUPED_COEF_FETCH
-  __syncthreads();  // coefficient tables are reused as row-sum buffers
+  __syncthreads();
   // ---- row sums of the 4 waves per token, SiLU * mul ----
   {
     const int n = lane & 15, kg = lane >> 4;
@@ -412,7 +351,9 @@ int launch_gateup_grouped(const GroupArgs& s, hipStream_t st) {
     (void)hipGetLastError();
     attr_done[dev] = true;
   }
-  const long long blocks = (long long)s.tcap * (s.single ? (s.g.n_seg + 1) / 2 : s.g.n_seg);
+  // (tile x + 8 i on XCD x: 8 blocks per segment unit and tile octet)
+  const long long blocks =
+      8ll * ((s.tcap + 7) / 8) * (s.single ? (s.g.n_seg + 1) / 2 : s.g.n_seg);
   hipLaunchKernelGGL(k_gateup_grouped, dim3((unsigned)blocks), dim3(kGThreads), sizeof(GroupLds),
                      st, s);
   return 0;

@@ -433,6 +433,77 @@ __device__ __forceinline__ void mfma_ksteps(const SegProj& p, const uint32_t* ba
   group_steps<16>(base, p.b6, p.n_blk, p.w6, kb0, kb1, wp, chi, clo, cstride, s0, nt, m, kg, acc0, acc1);
 }
 
+// The same K steps with the B operand read straight from the tile's
+// coefficient tables in global memory (no LDS copy, no chunk barriers): bh
+// and bl point at this lane's 16-byte piece of step 0 (token row m, slots
+// 8 kg .. + 7), step kb at + 32 kb.  Each step's B is loaded two steps ahead
+// of its products.  Rows past the tile's tokens may hold anything finite:
+// they only feed output columns that are never stored.
+template <int W>
+__device__ __forceinline__ void ksteps_gb(const uint32_t* rec0, uint32_t kfirst, uint32_t kend,
+                                          const _Float16* bh, const _Float16* bl, int m,
+                                          f4& acc0, f4& acc1) {
+  if (kfirst >= kend) return;
+  constexpr uint32_t nw = kPW;
+  const uint32_t rstep = nw * kBlkPerK * 4u * (W == 16 ? 16u : (uint32_t)W);
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  uint4 h0 = *reinterpret_cast<const uint4*>(bh + 32u * kfirst), l0 = *reinterpret_cast<const uint4*>(bl + 32u * kfirst);
+  uint4 h1 = zero, l1 = zero;
+  if (kfirst + nw < kend) {
+    h1 = *reinterpret_cast<const uint4*>(bh + 32u * (kfirst + nw));
+    l1 = *reinterpret_cast<const uint4*>(bl + 32u * (kfirst + nw));
+  }
+#pragma unroll 1
+  for (uint32_t kb = kfirst; kb < kend; kb += nw, rec0 += rstep) {
+    const uint4 vh = h0, vl = l0;
+    h0 = h1;
+    l0 = l1;
+    if (kb + 2u * nw < kend) {
+      h1 = *reinterpret_cast<const uint4*>(bh + 32u * (kb + 2u * nw));
+      l1 = *reinterpret_cast<const uint4*>(bl + 32u * (kb + 2u * nw));
+    }
+    h8 a0, a1;
+    if constexpr (W == 16)
+      a_tiles_f16(rec0, m, a0, a1);
+    else
+      a_tiles_uniform<W>(rec0, m, a0, a1);
+    mfma4(a0, a1, vh, vl, acc0, acc1);
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void group_steps_gb(const uint32_t* base, uint32_t bs, uint32_t be,
+                                               uint32_t ws, uint32_t kb0, uint32_t kb1, int wp,
+                                               const _Float16* bh, const _Float16* bl, int m,
+                                               int kg, f4& acc0, f4& acc1) {
+  const uint32_t ks = max(bs / kBlkPerK, kb0), ke = min(be / kBlkPerK, kb1);
+  const uint32_t kf = ks + ((kb0 + (uint32_t)wp - ks) & (uint32_t)(kPW - 1));
+  if (kf >= ke) return;
+  constexpr uint32_t bw = 4u * (W == 16 ? 16u : (uint32_t)W);  // words per block
+  const uint32_t* rec0 = base + ws + (kBlkPerK * kf - bs) * bw + 2u * bw * (uint32_t)kg;
+  ksteps_gb<W>(rec0, kf, ke, bh, bl, m, acc0, acc1);
+}
+
+// This wave's K steps kb0 + wp, kb0 + wp + 4, ... < kb1 of one segment with
+// B from the coefficient tables (acc0 rows 0-15, acc1 rows 16-31, column n =
+// token n); base: word 0 of the segment record (the staged chunk holds
+// these steps).
+__device__ __forceinline__ void mfma_ksteps_gb(const SegProj& p, const uint32_t* base,
+                                               const _Float16* bh, const _Float16* bl,
+                                               uint32_t kb0, uint32_t kb1, int wp, int lane,
+                                               f4& acc0, f4& acc1) {
+  const int m = lane & 15, kg = lane >> 4;
+  kb0 = rfl(kb0);
+  kb1 = rfl(kb1);
+  group_steps_gb<1>(base, 0u, p.b1, 0u, kb0, kb1, wp, bh, bl, m, kg, acc0, acc1);
+  group_steps_gb<2>(base, p.b1, p.b2, p.w1, kb0, kb1, wp, bh, bl, m, kg, acc0, acc1);
+  group_steps_gb<3>(base, p.b2, p.b3, p.w2, kb0, kb1, wp, bh, bl, m, kg, acc0, acc1);
+  group_steps_gb<4>(base, p.b3, p.b4, p.w3, kb0, kb1, wp, bh, bl, m, kg, acc0, acc1);
+  group_steps_gb<6>(base, p.b4, p.b5, p.w4, kb0, kb1, wp, bh, bl, m, kg, acc0, acc1);
+  group_steps_gb<8>(base, p.b5, p.b6, p.w5, kb0, kb1, wp, bh, bl, m, kg, acc0, acc1);
+  group_steps_gb<16>(base, p.b6, p.n_blk, p.w6, kb0, kb1, wp, bh, bl, m, kg, acc0, acc1);
+}
+
 // ---------------------------------------------------------------------------
 // Integer apply for one token column (the one-launch kernel).
 //
