@@ -685,7 +685,7 @@ GateUpPlan gateup_plan(int T, int k, int E, int r) {
                          ? (size_t)kZRing * k * 2 * ((size_t)kOneSlots + r) * sizeof(uint64_t)
                          : 0;
   p.route_off = align_up(p.cw_off + ncw, 256);
-  p.coef_off = align_up(p.route_off + (1 + 3 * (size_t)tile_cap(T, k, E) + P) * sizeof(int), 256);
+  p.coef_off = align_up(p.route_off + route_ints(tile_cap(T, k, E), P) * sizeof(int), 256);
   p.total = p.coef_off + group_coef_bytes(tile_cap(T, k, E), r);
   return p;
 }
@@ -836,10 +836,7 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     gs.nzp = (2 * r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
     gs.tcap = tile_cap(T, k, E);
     gs.single = 0;
-    int* rb = (int*)(wsb + plan.route_off);
-    gs.rl.ntiles = rb;
-    gs.rl.tile = rb + 1;
-    gs.rl.pairs = rb + 1 + 3 * gs.tcap;
+    route_lists_at(gs.rl, (int*)(wsb + plan.route_off), gs.tcap, (size_t)T * k);
     group_coef_tables(gs, wsb + plan.coef_off, r);
     const RouteJob rj{ids, T * k, E, dout, h, gs.rl, gs.tbad, gs.tcap * 2};
     bool routed = false;

@@ -75,7 +75,7 @@ DownWs down_ws(int T, int k, int E, int dout, int din, int rd) {
   w.y = w.z + al(n * rd * 4);
   w.zpart = w.y + al(n * din * 4);
   w.route = w.zpart + al(n * nzp * 4);
-  w.coef = w.route + al((1 + 3 * (uint64_t)tile_cap(T, k, E) + n) * 4);
+  w.coef = w.route + al(route_ints(tile_cap(T, k, E), (size_t)n) * 4);
   w.total = w.coef + group_coef_bytes(tile_cap(T, k, E), rd);
   return w;
 }
@@ -150,10 +150,7 @@ int bitsmoe_moe_down(const void* packed_down, size_t down_bytes, const void* phi
     gs.nzp = (r_d + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
     gs.tcap = tile_cap(T, k, E);
     gs.single = 1;
-    int* rb = (int*)(w8 + w.route);
-    gs.rl.ntiles = rb;
-    gs.rl.tile = rb + 1;
-    gs.rl.pairs = rb + 1 + 3 * gs.tcap;
+    route_lists_at(gs.rl, (int*)(w8 + w.route), gs.tcap, (size_t)T * k);
     group_coef_tables(gs, w8 + w.coef, r_d);
     if (E <= kRouteFuseMaxE) rj = RouteJob{ids, T * k, E, din, y, gs.rl, gs.tbad, gs.tcap * 2};
   }

@@ -20,11 +20,12 @@
 // by the projection launch), and the row-independent sums a m z per 256-slot
 // chunk, into tables in the workspace.
 //
-// k_gateup_grouped: one 512-lane work-group per (tile, 32-row segment) unit,
-// both projections (waves 0-3 gate, 4-7 up).  Tile x + 8 i runs on XCD x
-// with its segment units one after another, so the segments of a tile
-// share one L2 for its coefficient tables; blocks past the tile count exit
-// at once.  The segment records are staged in LDS in chunks of at most
+// k_gateup_grouped: one 512-lane work-group per (group of up to kSuperTiles
+// tiles of one expert, 32-row segment) unit, both projections (waves 0-3
+// gate, 4-7 up): each K step's planes are decoded once and applied to every
+// tile of the group (up to 16 kSuperTiles token columns).  Group x + 8 i runs on XCD x with its
+// segment units one after another, so the segments of a group share one L2
+// for its coefficient tables; blocks past the group count exit at once.  The segment records are staged in LDS in chunks of at most
 // 7168 words per projection; each wave reads the B operands of its K steps
 // (16 bytes a lane, two steps ahead) straight from the tile's coefficient
 // tables, so a chunk's steps run without barriers.  The work-group's LDS
@@ -69,12 +70,13 @@ struct __align__(16) GroupLds {
     float red[2][kGPW][kTile][kSegRows];
   } u;
   float pbias[2][kGPW][kTile];
-  int S[2][kTile];
-  int pair[kTile];
+  int S[2][kSuperTiles * kTile];
+  int pair[kSuperTiles * kTile];
   uint32_t pok[2][kGPW];
   int nch[2];
 };
 static_assert(sizeof(GroupLds) <= 80 * 1024, "two work-groups per CU (160 KB of LDS)");
+static_assert(kSuperTiles == kMaxNB, "tiles per group");
 
 __device__ __forceinline__ void stage_chunk(uint32_t* arena, const SegProj& p, int sg,
                                             uint32_t b0, uint32_t b1, int lp, int lane, int nl) {
@@ -176,28 +178,33 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   const int wp = wv & (kGPW - 1);
   const int lp = (int)threadIdx.x & (kGProj - 1);
 
-  // The units fill the first ntiles x segments blocks (tile = b % ntiles):
-  // the grid is sized for tcap tiles, and blocks past the units exit at
-  // once, after every unit has been dispatched, so no launch slot sits
-  // behind a block without work.
+  // A unit is (group of up to kSuperTiles consecutive tiles of one expert,
+  // segment): the group's planes are decoded once per K step and applied
+  // to every tile of the group.  Block b runs on XCD b % 8; group x + 8 i
+  // goes to XCD x, its segment units one after another, so the segments of
+  // a group share one L2 for its coefficient tables; blocks past the group
+  // count exit at once.
   typedef __attribute__((address_space(4))) const int CI32;
-  const int ntl = *(CI32*)s.rl.ntiles;  // written by the route step before this launch
+  const int ngr = *(CI32*)s.rl.nstiles;  // written by the route step before this launch
   const bool single = s.single != 0;
-  const int nsu = single ? (a.n_seg + 1) / 2 : a.n_seg;  // segment units per tile
-  // block b runs on XCD b % 8; tile x + 8 i goes to XCD x, its segment units
-  // one after another, so the segments of a tile share one L2 for the
-  // tile's coefficient tables
+  const int nsu = single ? (a.n_seg + 1) / 2 : a.n_seg;  // segment units per group
   const int xcd = (int)blockIdx.x & 7, jx = (int)blockIdx.x >> 3;
-  const int ti = xcd + 8 * (jx / nsu), su = jx % nsu;
-  if (ntl <= 0 || ti >= ntl) return;
+  const int gi = xcd + 8 * (jx / nsu), su = jx % nsu;
+  if (ngr <= 0 || gi >= ngr) return;
   // single: this half's segment (a half past the last segment repeats it
   // and writes nothing)
   const int sg0 = single ? 2 * su : su;
   const int sgh = single ? sg0 + pj : sg0;
   const int sg = sgh < a.n_seg ? sgh : a.n_seg - 1;
-  const int e = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti]);
-  const int p0 = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti + 1]);
-  const int nt = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti + 2]);
+  const int ti0 = __builtin_amdgcn_readfirstlane(s.rl.stile[2 * gi]);
+  const int nb = min(max(__builtin_amdgcn_readfirstlane(s.rl.stile[2 * gi + 1]), 1), kSuperTiles);
+  const int e = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti0]);
+  int p0[kSuperTiles], ntb[kSuperTiles];  // each tile's first pair and pair count (uniform)
+#pragma unroll
+  for (int t = 0; t < kSuperTiles; ++t) {
+    p0[t] = t < nb ? __builtin_amdgcn_readfirstlane(s.rl.tile[3 * (ti0 + t) + 1]) : 0;
+    ntb[t] = t < nb ? __builtin_amdgcn_readfirstlane(s.rl.tile[3 * (ti0 + t) + 2]) : 0;
+  }
 
   const uint8_t* blob = pj ? a.blob_u : a.blob_g;
   const SegProj P = uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
@@ -206,31 +213,42 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   uint32_t b1 = chunk_end(P, 0, kGMaxW);
   stage_chunk(&L.W[pj][0], P, sg, 0, b1, lp, lane, kGProj);
 
-  // The tile's coefficients (k_group_coef) are read straight from the
-  // tables: lane (m, kg) takes token row m (the last token's row past the
-  // tile's tokens: same cache lines, columns never stored), slots 8 kg ..
-  const size_t trow = (size_t)(ti * 2 + (single ? 0 : pj)) * kTile;
-  const size_t boff = (trow + (size_t)min(lane & 15, nt - 1)) * s.rpad + 8u * (uint32_t)(lane >> 4);
-  const _Float16* const bh = s.thi + boff;
-  const _Float16* const bl = s.tlo + boff;
+  // The tiles' coefficients (k_group_coef) are read straight from the
+  // tables: lane (m, kg) takes token row m of each tile (the tile's last
+  // token's row past its tokens: same cache lines, columns never stored),
+  // slots 8 kg ..
+  uint32_t boff[kSuperTiles];
+#pragma unroll
+  for (int t = 0; t < kSuperTiles; ++t) {
+    const int tt = t < nb ? t : 0;
+    const size_t trow = (size_t)((ti0 + tt) * 2 + (single ? 0 : pj)) * kTile;
+    boff[t] = (uint32_t)((trow + (size_t)min(lane & 15, max(ntb[tt], 1) - 1)) * s.rpad) +
+              8u * (uint32_t)(lane >> 4);
+  }
 
-  // tokens of the tile and their coefficient scales: lanes (n, j) of the
+  // tokens of the tiles and their coefficient scales: lanes (n, j) of the
   // projection take partial maxima j, j + 16, ... of token n
-  if (threadIdx.x < (unsigned)nt) L.pair[threadIdx.x] = s.rl.pairs[p0 + threadIdx.x];
   {
     const int n = lp / kGZP, j = lp % kGZP;
     const int pz0 = (pj && !single) ? a.r / kProjRowsPerBlock : 0;
     const int pz1 = (pj || single) ? s.nzp : (a.r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
-    float zm = 0.f;
-    if (n < nt) {
-      const int pr = s.rl.pairs[p0 + n];
-      const int t = single ? pr : pr / a.ktop;  // z row: the pair's own (single) or its token's
-      const float* zp = s.zpart + (size_t)t * s.nzp;
-      for (int i = pz0 + j; i < pz1; i += kGZP) zm = fmaxf(zm, zp[i]);
-    }
 #pragma unroll
-    for (int off = kGZP / 2; off > 0; off >>= 1) zm = fmaxf(zm, __shfl_xor(zm, off, kWave));
-    if (j == 0 && n < nt) L.S[pj][n] = coef_shift(P.cmax, zm);
+    for (int t = 0; t < kSuperTiles; ++t) {
+      if (t < nb) {
+        if (threadIdx.x < (unsigned)ntb[t])
+          L.pair[kTile * t + threadIdx.x] = s.rl.pairs[p0[t] + threadIdx.x];
+        float zm = 0.f;
+        if (n < ntb[t]) {
+          const int pr = s.rl.pairs[p0[t] + n];
+          const int tk = single ? pr : pr / a.ktop;  // z row: the pair's own (single) or its token's
+          const float* zp = s.zpart + (size_t)tk * s.nzp;
+          for (int i = pz0 + j; i < pz1; i += kGZP) zm = fmaxf(zm, zp[i]);
+        }
+#pragma unroll
+        for (int off = kGZP / 2; off > 0; off >>= 1) zm = fmaxf(zm, __shfl_xor(zm, off, kWave));
+        if (j == 0 && n < ntb[t]) L.S[pj][kTile * t + n] = coef_shift(P.cmax, zm);
+      }
+    }
   }
   // Plane chunks of at most kGMaxW words per projection: the two
   // projections' counts may differ, the barriers are shared, so the
@@ -245,8 +263,10 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int nch = __builtin_amdgcn_readfirstlane(max(L.nch[0], L.nch[1]));  // uniform
-  bool good = P.ok;
-  f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const bool good = P.ok;
+  f4 acc0[kSuperTiles], acc1[kSuperTiles];
+#pragma unroll
+  for (int t = 0; t < kSuperTiles; ++t) acc0[t] = acc1[t] = f4{0.f, 0.f, 0.f, 0.f};
   uint32_t b0 = 0;
   for (int ch = 0; ch < max(nch, 1); ++ch) {
     if (ch > 0) {
@@ -259,65 +279,75 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
     }
     if (b1 > b0) {
       const uint32_t* base = &L.W[pj][0] - block_word(P, b0);
-      mfma_ksteps_gb(P, base, bh, bl, b0 / kBlkPerK, (b1 + kBlkPerK - 1) / kBlkPerK, wp, lane,
-                     acc0, acc1);
+      const uint32_t kb0 = b0 / kBlkPerK, kb1 = (b1 + kBlkPerK - 1) / kBlkPerK;
+      if (nb == 1)
+        mfma_ksteps_gb(P, base, s.thi + boff[0], s.tlo + boff[0], kb0, kb1, wp, lane, acc0[0],
+                       acc1[0]);
+      else
+        mfma_ksteps_gbn(P, base, s.thi, s.tlo, boff, nb, kb0, kb1, wp, lane, acc0, acc1);
     }
     b0 = b1;
   }
-  __syncthreads();
-  // ---- row sums of the 4 waves per token, SiLU * mul ----
-  {
-    const int n = lane & 15, kg = lane >> 4;
-    if (n < nt) {
+  // ---- per tile: row sums of the 4 waves per token, SiLU * mul ----
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        L.u.red[pj][wp][n][4 * kg + i] = acc0[i];
-        L.u.red[pj][wp][n][16 + 4 * kg + i] = acc1[i];
-      }
-    }
-    // the row-independent sums of the tile's chunks (wave 0 of each half),
-    // the column-index check from the coefficient pass
-    if (wp == 0 && lane < nt) {
-      const float* tb = s.tbias + (size_t)(ti * 2 + (single ? 0 : pj)) * s.nck * kTile + lane;
-      float bsum = 0.f;
-      for (int c = 0; c < s.nck; ++c) bsum += tb[(size_t)c * kTile];
-      L.pbias[pj][0][lane] = bsum;
-    } else if (lane < nt) {
-      L.pbias[pj][wp][lane] = 0.f;
-    }
-    const bool wok = __all(good) && s.tbad[ti * 2 + (single ? 0 : pj)] == 0u;
-    if (lane == 0) L.pok[pj][wp] = wok;
-  }
-  __syncthreads();
-  {
-    const int n = threadIdx.x >> 5, row = threadIdx.x & 31;
-    if (n < nt) {
-      float ys[2];
-      uint32_t okq[2];
+  for (int t = 0; t < kSuperTiles; ++t) {
+    if (t >= nb) continue;  // (uniform)
+    const int ti = ti0 + t, nt = ntb[t];
+    __syncthreads();  // the previous tile's sums are read
+    {
+      const int n = lane & 15, kg = lane >> 4;
+      if (n < nt) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        float sum = 0.f, bsum = 0.f;
-        uint32_t okw = 1u;
-#pragma unroll
-        for (int w = 0; w < kGPW; ++w) {
-          sum += L.u.red[q][w][n][row];
-          bsum += L.pbias[q][w][n];
-          okw &= L.pok[q][w];
+        for (int i = 0; i < 4; ++i) {
+          L.u.red[pj][wp][n][4 * kg + i] = acc0[t][i];
+          L.u.red[pj][wp][n][16 + 4 * kg + i] = acc1[t][i];
         }
-        ys[q] = ldexpf(sum, -L.S[q][n]) + bsum;
-        okq[q] = okw;
       }
-      if (!single) {
-        const int orow = sg * kSegRows + row;
-        if (orow < a.dout)
-          a.h[(size_t)L.pair[n] * a.dout + orow] =
-              (okq[0] & okq[1]) ? silu_mul(ys[0], ys[1]) : __builtin_nanf("");
-      } else {
+      // the row-independent sums of the tile's chunks (wave 0 of each half),
+      // the column-index check from the coefficient pass
+      if (wp == 0 && lane < nt) {
+        const float* tb = s.tbias + (size_t)(ti * 2 + (single ? 0 : pj)) * s.nck * kTile + lane;
+        float bsum = 0.f;
+        for (int c = 0; c < s.nck; ++c) bsum += tb[(size_t)c * kTile];
+        L.pbias[pj][0][lane] = bsum;
+      } else if (lane < nt) {
+        L.pbias[pj][wp][lane] = 0.f;
+      }
+      const bool wok = __all(good) && s.tbad[ti * 2 + (single ? 0 : pj)] == 0u;
+      if (lane == 0) L.pok[pj][wp] = wok;
+    }
+    __syncthreads();
+    {
+      const int n = threadIdx.x >> 5, row = threadIdx.x & 31;
+      if (n < nt) {
+        float ys[2];
+        uint32_t okq[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          const int orow = (sg0 + q) * kSegRows + row;
-          if (sg0 + q < a.n_seg && orow < a.dout)
-            a.h[(size_t)L.pair[n] * a.dout + orow] = okq[q] ? ys[q] : __builtin_nanf("");
+          float sum = 0.f, bsum = 0.f;
+          uint32_t okw = 1u;
+#pragma unroll
+          for (int w = 0; w < kGPW; ++w) {
+            sum += L.u.red[q][w][n][row];
+            bsum += L.pbias[q][w][n];
+            okw &= L.pok[q][w];
+          }
+          ys[q] = ldexpf(sum, -L.S[q][kTile * t + n]) + bsum;
+          okq[q] = okw;
+        }
+        const int pr = L.pair[kTile * t + n];
+        if (!single) {
+          const int orow = sg * kSegRows + row;
+          if (orow < a.dout)
+            a.h[(size_t)pr * a.dout + orow] =
+                (okq[0] & okq[1]) ? silu_mul(ys[0], ys[1]) : __builtin_nanf("");
+        } else {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int orow = (sg0 + q) * kSegRows + row;
+            if (sg0 + q < a.n_seg && orow < a.dout)
+              a.h[(size_t)pr * a.dout + orow] = okq[q] ? ys[q] : __builtin_nanf("");
+          }
         }
       }
     }
@@ -351,7 +381,8 @@ int launch_gateup_grouped(const GroupArgs& s, hipStream_t st) {
     (void)hipGetLastError();
     attr_done[dev] = true;
   }
-  // (tile x + 8 i on XCD x: 8 blocks per segment unit and tile octet)
+  // (tile group x + 8 i on XCD x: 8 blocks per segment unit and group
+  // octet; there are at most tcap groups)
   const long long blocks =
       8ll * ((s.tcap + 7) / 8) * (s.single ? (s.g.n_seg + 1) / 2 : s.g.n_seg);
   hipLaunchKernelGGL(k_gateup_grouped, dim3((unsigned)blocks), dim3(kGThreads), sizeof(GroupLds),

@@ -87,7 +87,20 @@ struct RouteLists {
   int* ntiles;   // [1]
   int* tile;     // per tile: expert id, first pair index into pairs, pair count (3 ints)
   int* pairs;    // pair indices t * k + slot, grouped by expert
+  int* nstiles;  // [1]
+  int* stile;    // per group of up to kSuperTiles consecutive tiles of one expert:
+                 // first tile, tile count (2 ints)
 };
+constexpr int kSuperTiles = 2;  // tiles of one expert a grouped work-group applies together
+// ints of the route lists for tcap tiles and P pairs, and their places
+inline size_t route_ints(int tcap, size_t P) { return 2 + 5 * (size_t)tcap + P; }
+inline void route_lists_at(RouteLists& rl, int* rb, int tcap, size_t P) {
+  rl.ntiles = rb;
+  rl.tile = rb + 1;
+  rl.pairs = rb + 1 + 3 * (size_t)tcap;
+  rl.nstiles = rl.pairs + P;
+  rl.stile = rl.nstiles + 1;
+}
 struct GroupArgs {
   GateUpArgs g;
   const float* z;      // T x 2r

@@ -11,7 +11,8 @@
 // Counting sort: an LDS histogram of the ids, a block scan of per-thread
 // runs of experts, then a scatter into per-expert pair lists (experts
 // ascending; the order inside a list does not affect any result), cut into
-// tiles.  Pairs whose id lies outside [0, E) get NaN rows in h.
+// tiles, and the tiles of each expert into groups of up to kSuperTiles.
+// Pairs whose id lies outside [0, E) get NaN rows in h.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -66,25 +67,36 @@ __device__ void route_lists(const RouteJob& j, uint32_t* cnt, uint32_t* buf) {
   // each thread owns a contiguous run of experts
   const int per = (j.E + NT - 1) / NT;
   const int e0 = min(j.E, tid * per), e1 = min(j.E, e0 + per);
-  uint32_t sum = 0, nt = 0;
+  uint32_t sum = 0, nt = 0, ns = 0;
   for (int e = e0; e < e1; ++e) {
+    const uint32_t te = (cnt[e] + kTile - 1) / kTile;
     sum += cnt[e];
-    nt += (cnt[e] + kTile - 1) / kTile;
+    nt += te;
+    ns += (te + kSuperTiles - 1) / kSuperTiles;
   }
-  uint32_t total_pairs, total_tiles;
+  uint32_t total_pairs, total_tiles, total_st;
   uint32_t off = route_scan<NT>(sum, buf, total_pairs);
   uint32_t ti = route_scan<NT>(nt, buf, total_tiles);
+  uint32_t si = route_scan<NT>(ns, buf, total_st);
   for (int e = e0; e < e1; ++e) {
-    const uint32_t c = cnt[e];
+    const uint32_t c = cnt[e], t0 = ti;
     cur[e] = off;
     for (uint32_t i = 0; i < c; i += kTile, ++ti) {
       j.rl.tile[3 * ti] = e;
       j.rl.tile[3 * ti + 1] = (int)(off + i);
       j.rl.tile[3 * ti + 2] = (int)min((uint32_t)kTile, c - i);
     }
+    // groups of up to kSuperTiles consecutive tiles of this expert
+    for (uint32_t q = t0; q < ti; q += kSuperTiles, ++si) {
+      j.rl.stile[2 * si] = (int)q;
+      j.rl.stile[2 * si + 1] = (int)min((uint32_t)kSuperTiles, ti - q);
+    }
     off += c;
   }
-  if (tid == 0) j.rl.ntiles[0] = (int)total_tiles;
+  if (tid == 0) {
+    j.rl.ntiles[0] = (int)total_tiles;
+    j.rl.nstiles[0] = (int)total_st;
+  }
   __syncthreads();
   for (int p = tid; p < j.P; p += NT) {
     const int e = j.ids[p];

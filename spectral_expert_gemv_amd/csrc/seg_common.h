@@ -504,6 +504,82 @@ __device__ __forceinline__ void mfma_ksteps_gb(const SegProj& p, const uint32_t*
   group_steps_gb<16>(base, p.b6, p.n_blk, p.w6, kb0, kb1, wp, bh, bl, m, kg, acc0, acc1);
 }
 
+// The same for nb (up to kMaxNB) tiles of one expert: each step's A operands are
+// decoded once and multiplied with every tile's B; tile t's lane piece of
+// step 0 is at thi / tlo + boff[t], step kb at + 32 kb.  Each tile's B of
+// the next step is loaded right after this step's products with it.
+constexpr int kMaxNB = 2;
+
+template <int W>
+__device__ __forceinline__ void ksteps_gbn(const uint32_t* rec0, uint32_t kfirst, uint32_t kend,
+                                           const _Float16* thi, const _Float16* tlo,
+                                           const uint32_t (&boff)[kMaxNB], int nb, int m,
+                                           f4 (&acc0)[kMaxNB], f4 (&acc1)[kMaxNB]) {
+  if (kfirst >= kend) return;
+  constexpr uint32_t nw = kPW;
+  const uint32_t rstep = nw * kBlkPerK * 4u * (W == 16 ? 16u : (uint32_t)W);
+  uint4 vh[kMaxNB], vl[kMaxNB];
+#pragma unroll
+  for (int t = 0; t < kMaxNB; ++t) {
+    vh[t] = vl[t] = make_uint4(0, 0, 0, 0);
+    if (t < nb) {
+      vh[t] = *reinterpret_cast<const uint4*>(thi + boff[t] + 32u * kfirst);
+      vl[t] = *reinterpret_cast<const uint4*>(tlo + boff[t] + 32u * kfirst);
+    }
+  }
+#pragma unroll 1
+  for (uint32_t kb = kfirst; kb < kend; kb += nw, rec0 += rstep) {
+    h8 a0, a1;
+    if constexpr (W == 16)
+      a_tiles_f16(rec0, m, a0, a1);
+    else
+      a_tiles_uniform<W>(rec0, m, a0, a1);
+    const bool more = kb + nw < kend;
+#pragma unroll
+    for (int t = 0; t < kMaxNB; ++t) {
+      if (t < nb) {
+        mfma4(a0, a1, vh[t], vl[t], acc0[t], acc1[t]);
+        if (more) {
+          vh[t] = *reinterpret_cast<const uint4*>(thi + boff[t] + 32u * (kb + nw));
+          vl[t] = *reinterpret_cast<const uint4*>(tlo + boff[t] + 32u * (kb + nw));
+        }
+      }
+    }
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void group_steps_gbn(const uint32_t* base, uint32_t bs, uint32_t be,
+                                                uint32_t ws, uint32_t kb0, uint32_t kb1, int wp,
+                                                const _Float16* thi, const _Float16* tlo,
+                                                const uint32_t (&boff)[kMaxNB], int nb, int m,
+                                                int kg, f4 (&acc0)[kMaxNB], f4 (&acc1)[kMaxNB]) {
+  const uint32_t ks = max(bs / kBlkPerK, kb0), ke = min(be / kBlkPerK, kb1);
+  const uint32_t kf = ks + ((kb0 + (uint32_t)wp - ks) & (uint32_t)(kPW - 1));
+  if (kf >= ke) return;
+  constexpr uint32_t bw = 4u * (W == 16 ? 16u : (uint32_t)W);  // words per block
+  const uint32_t* rec0 = base + ws + (kBlkPerK * kf - bs) * bw + 2u * bw * (uint32_t)kg;
+  ksteps_gbn<W>(rec0, kf, ke, thi, tlo, boff, nb, m, acc0, acc1);
+}
+
+__device__ __forceinline__ void mfma_ksteps_gbn(const SegProj& p, const uint32_t* base,
+                                                const _Float16* thi, const _Float16* tlo,
+                                                const uint32_t (&boff)[kMaxNB], int nb,
+                                                uint32_t kb0, uint32_t kb1, int wp, int lane,
+                                                f4 (&acc0)[kMaxNB], f4 (&acc1)[kMaxNB]) {
+  const int m = lane & 15, kg = lane >> 4;
+  kb0 = rfl(kb0);
+  kb1 = rfl(kb1);
+  group_steps_gbn<1>(base, 0u, p.b1, 0u, kb0, kb1, wp, thi, tlo, boff, nb, m, kg, acc0, acc1);
+  group_steps_gbn<2>(base, p.b1, p.b2, p.w1, kb0, kb1, wp, thi, tlo, boff, nb, m, kg, acc0, acc1);
+  group_steps_gbn<3>(base, p.b2, p.b3, p.w2, kb0, kb1, wp, thi, tlo, boff, nb, m, kg, acc0, acc1);
+  group_steps_gbn<4>(base, p.b3, p.b4, p.w3, kb0, kb1, wp, thi, tlo, boff, nb, m, kg, acc0, acc1);
+  group_steps_gbn<6>(base, p.b4, p.b5, p.w4, kb0, kb1, wp, thi, tlo, boff, nb, m, kg, acc0, acc1);
+  group_steps_gbn<8>(base, p.b5, p.b6, p.w5, kb0, kb1, wp, thi, tlo, boff, nb, m, kg, acc0, acc1);
+  group_steps_gbn<16>(base, p.b6, p.n_blk, p.w6, kb0, kb1, wp, thi, tlo, boff, nb, m, kg, acc0,
+                      acc1);
+}
+
 // ---------------------------------------------------------------------------
 // Integer apply for one token column (the one-launch kernel).
 //
