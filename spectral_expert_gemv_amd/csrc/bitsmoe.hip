@@ -207,6 +207,122 @@ __global__ __launch_bounds__(kPMWaves * kWave) void k_proj_mfma(const uint4* __r
   if (zpart && kg == 0 && tok < T) zpart[(size_t)tok * nzp + blockIdx.x] = mx;
 }
 
+// Batched projection for token counts where z^T = Phi^T x^T is a real dense
+// contraction (T >= 64, din a multiple of 64): work-group (b, c) computes
+// rows 128 b .. + 127 of Phi^T against tokens 64 c .. + 63.  din runs in
+// chunks of 64; each chunk's Phi^T rows (16 KB) and x rows (8 KB) are
+// copied into LDS with 16-byte global_load_lds, double-buffered (the next
+// chunk is copied while this one is multiplied).  The 16-byte pieces of a
+// row are stored with their index xor the row's low three bits, so the
+// sixteen rows one matrix-core read touches spread over the banks.  Wave w
+// takes rows 32 w .. + 31 and all 64 tokens: per 32-wide K step two A
+// pieces, four B pieces and eight v_mfma_f32_16x16x32_f16.  fp16 products
+// are exact in fp32; the sums are fp32 in K order.  zpart gets the largest
+// |z| of each 16 rows per token.  With a route job, one more column of
+// work-groups is launched and its first one groups the pairs by expert.
+constexpr int kQM = 128, kQN = 64, kQK = 64;  // rows, tokens, din per chunk
+constexpr int kQWaves = 4;
+
+__device__ __forceinline__ void proj_stage(uint4* la, uint4* lb, const uint4* phi_t,
+                                           const uint4* x, int row0, int tok0, int R, int T,
+                                           int din8, int ck, int wv, int lane) {
+  typedef __attribute__((address_space(1))) void gvoid;
+  const int j = lane & 7;
+#pragma unroll
+  for (int q = 0; q < kQM / 8 / kQWaves; ++q) {  // 8 rows per copy
+    const int g = wv * (kQM / 8 / kQWaves) + q, r = 8 * g + (lane >> 3);
+    const uint4* src = phi_t + (size_t)min(row0 + r, R - 1) * din8 + 8 * ck + (j ^ (r & 7));
+    __builtin_amdgcn_global_load_lds((gvoid*)src, (lds_void_t*)(la + 64 * g), 16, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < kQN / 8 / kQWaves; ++q) {
+    const int g = wv * (kQN / 8 / kQWaves) + q, t = 8 * g + (lane >> 3);
+    const uint4* src = x + (size_t)min(tok0 + t, T - 1) * din8 + 8 * ck + (j ^ (t & 7));
+    __builtin_amdgcn_global_load_lds((gvoid*)src, (lds_void_t*)(lb + 64 * g), 16, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kQWaves * kWave) void k_proj_gemm(const uint4* __restrict__ phi_t,
+                                                              const uint4* __restrict__ x,
+                                                              float* __restrict__ z,
+                                                              float* __restrict__ zpart, int T,
+                                                              int din8, int R, int nzp,
+                                                              RouteJob rj) {
+  __shared__ union {
+    struct {
+      uint4 a[2][kQM * kQK / 8];
+      uint4 b[2][kQN * kQK / 8];
+    } g;
+    struct {
+      uint32_t cnt[2 * kRouteFuseMaxE];
+      uint32_t buf[kQWaves * kWave];
+    } r;
+  } L;
+  const int nmb = (R + kQM - 1) / kQM;
+  if (rj.ids && (int)blockIdx.x == nmb) {
+    if (blockIdx.y == 0) route_lists<kQWaves * kWave>(rj, L.r.cnt, L.r.buf);
+    return;
+  }
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = (int)blockIdx.x * kQM, tok0 = (int)blockIdx.y * kQN;
+  const int m = lane & 15, kg = lane >> 4;
+  const int nck = din8 / (kQK / 8);
+  f4v acc[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[t][b] = f4v{0.f, 0.f, 0.f, 0.f};
+  proj_stage(L.g.a[0], L.g.b[0], phi_t, x, row0, tok0, R, T, din8, 0, wv, lane);
+  for (int ck = 0; ck < nck; ++ck) {
+    const int cb = ck & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this chunk's copies of this wave are in
+    __syncthreads();                     // ... and every wave's; the other buffer is free
+    if (ck + 1 < nck)
+      proj_stage(L.g.a[cb ^ 1], L.g.b[cb ^ 1], phi_t, x, row0, tok0, R, T, din8, ck + 1, wv,
+                 lane);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = 4 * kk + kg;
+      uint4 av[2], bv[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r = 32 * wv + 16 * t + m;
+        av[t] = L.g.a[cb][8 * r + (c ^ (r & 7))];
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int tt = 16 * b + m;
+        bv[b] = L.g.b[cb][8 * tt + (c ^ (tt & 7))];
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[t][b] = mfma16(av[t], bv[b], acc[t][b]);
+    }
+  }
+  // lane (m, kg) of block (t, b) holds rows 4 kg .. + 3 of the 16-row block
+  // for token 16 b + m
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int rb = row0 + 32 * wv + 16 * t;  // first row of the block
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int tok = tok0 + 16 * b + m;
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rb + 4 * kg + i;
+        if (tok < T && row < R) z[(size_t)tok * R + row] = acc[t][b][i];
+        mx = fmaxf(mx, row < R ? fabsf(acc[t][b][i]) : 0.f);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      if (zpart && kg == 0 && tok < T && rb < R) zpart[(size_t)tok * nzp + rb / 16] = mx;
+    }
+  }
+}
+
 // F32: x holds float32 values, rounded to fp16 (to nearest even) while they
 // are staged, so z is the projection of fp16(x) exactly as with an fp16 x.
 // With a route job, the last work-group groups the pairs by expert
@@ -596,6 +712,19 @@ int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, i
   if (routed) *routed = false;
   if (x_f32 && ((T >= 16 && din % 32 == 0) || din8 > kPMaxU * kWave || ((uintptr_t)x & 15u)))
     return fail(BITSMOE_EINVAL, "float32 x needs T < 16 or din %% 32 != 0, din <= 4096, 16-byte x");
+  if (T >= 64 && din % kQK == 0 && !x_f32) {
+    const int nzp = (R + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
+    RouteJob rj{};
+    const bool fuse = route && route->E <= kRouteFuseMaxE;
+    if (fuse) rj = *route;
+    hipLaunchKernelGGL(k_proj_gemm,
+                       dim3((unsigned)((R + kQM - 1) / kQM + (fuse ? 1 : 0)),
+                            (unsigned)((T + kQN - 1) / kQN)),
+                       dim3(kQWaves * kWave), 0, s, (const uint4*)phi, (const uint4*)x, z, zpart,
+                       T, din8, R, nzp, rj);
+    if (routed) *routed = fuse;
+    return launch_status("spectral projection launch");
+  }
   if (T >= 16 && din % 32 == 0) {
     const int nzp = (R + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
     RouteJob rj{};

@@ -137,6 +137,25 @@ def test_spectral_proj(bm, wl_name):
         assert max_rel_err(got[t], zr) <= Z_TOL, t
 
 
+@pytest.mark.parametrize("wl_name,T", [("tiny_t64", 64), ("deepseek_moe_16b_t512", 100),
+                                        ("deepseek_moe_16b_t512", 512)])
+def test_spectral_proj_batched(bm, wl_name, T):
+    """The tiled matrix-core projection (T >= 64): full and ragged token
+    counts, against the oracle's z token by token."""
+    wl = synth.workload(wl_name)
+    L, dev = device_layer(wl.layer.name)
+    x, _ = synth.make_batch(wl, L)
+    x = np.ascontiguousarray(x[:T])
+    z = torch.empty((T, 2 * L.spec.r), dtype=torch.float32, device="cuda")
+    bm.spectral_proj(dev.phi_t, _cuda(x), z)
+    torch.cuda.synchronize()
+    got = z.cpu().numpy()
+    ref = z_ref(L, x)
+    for t in range(T):
+        zr = np.concatenate([ref["gate"][t], ref["up"][t]])
+        assert max_rel_err(got[t], zr) <= Z_TOL, t
+
+
 # ----------------------------------------------------------- expert apply
 
 def test_expert_apply_tiny(bm):
