@@ -208,38 +208,90 @@ __global__ __launch_bounds__(kPMWaves * kWave) void k_proj_mfma(const uint4* __r
 }
 
 // Batched projection for token counts where z^T = Phi^T x^T is a real dense
-// contraction (T >= 64, din a multiple of 64): work-group (b, c) computes
+// contraction (T >= 64, din a multiple of 128): work-group (b, c) computes
 // rows 128 b .. + 127 of Phi^T against tokens 64 c .. + 63.  din runs in
-// chunks of 64; each chunk's Phi^T rows (16 KB) and x rows (8 KB) are
-// copied into LDS with 16-byte global_load_lds, double-buffered (the next
-// chunk is copied while this one is multiplied).  The 16-byte pieces of a
-// row are stored with their index xor the row's low three bits, so the
+// chunks of 128; each chunk's Phi^T rows (32 KB) and x rows (16 KB) are
+// copied into LDS with 16-byte global_load_lds into one of three buffers,
+// two chunks ahead of the one being multiplied.  The 16-byte pieces of a
+// row are stored with their index xor the row's low four bits, so the
 // sixteen rows one matrix-core read touches spread over the banks.  Wave w
 // takes rows 32 w .. + 31 and all 64 tokens: per 32-wide K step two A
 // pieces, four B pieces and eight v_mfma_f32_16x16x32_f16.  fp16 products
 // are exact in fp32; the sums are fp32 in K order.  zpart gets the largest
 // |z| of each 16 rows per token.  With a route job, one more column of
 // work-groups is launched and its first one groups the pairs by expert.
-constexpr int kQM = 128, kQN = 64, kQK = 64;  // rows, tokens, din per chunk
+constexpr int kQM = 128, kQN = 64, kQK = 128;  // rows, tokens, din per chunk
 constexpr int kQWaves = 4;
+constexpr int kQStages = 3;
+constexpr int kQP = kQK / 8;  // 16-byte pieces per row and chunk
+constexpr int kQCopies = (kQM + kQN) * kQP / kWave / kQWaves;  // copies per wave and chunk
+
+__shared__ __align__(16) uint4 g_qa0[kQM * kQP], g_qa1[kQM * kQP], g_qa2[kQM * kQP];
+__shared__ __align__(16) uint4 g_qb0[kQN * kQP], g_qb1[kQN * kQP], g_qb2[kQN * kQP];
+
+// One 16-byte-per-lane copy from global memory into LDS (lane l writes
+// lds + 16 l).  Issued as a one-instruction asm block: the compiler then
+// does not treat the copy as a pending LDS write, so it inserts no wait for
+// it before the reads of the other buffers; the kernel orders the copies
+// with explicit vmcnt waits and barriers.  (The copy writes no VGPR.)
+__device__ __forceinline__ void lds_copy16(const void* src, const void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)lds;  // the LDS offset (low half of the address)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ void proj_stage(uint4* la, uint4* lb, const uint4* phi_t,
                                            const uint4* x, int row0, int tok0, int R, int T,
                                            int din8, int ck, int wv, int lane) {
-  typedef __attribute__((address_space(1))) void gvoid;
-  const int j = lane & 7;
+  constexpr int kRowsPerCopy = kWave / kQP;  // 4
+  const int j = lane % kQP;
 #pragma unroll
-  for (int q = 0; q < kQM / 8 / kQWaves; ++q) {  // 8 rows per copy
-    const int g = wv * (kQM / 8 / kQWaves) + q, r = 8 * g + (lane >> 3);
-    const uint4* src = phi_t + (size_t)min(row0 + r, R - 1) * din8 + 8 * ck + (j ^ (r & 7));
-    __builtin_amdgcn_global_load_lds((gvoid*)src, (lds_void_t*)(la + 64 * g), 16, 0, 0);
+  for (int q = 0; q < kQM / kRowsPerCopy / kQWaves; ++q) {
+    const int g = wv * (kQM / kRowsPerCopy / kQWaves) + q, r = kRowsPerCopy * g + lane / kQP;
+    lds_copy16(phi_t + (size_t)min(row0 + r, R - 1) * din8 + kQP * ck + (j ^ (r & 15)),
+               la + kWave * g);
   }
 #pragma unroll
-  for (int q = 0; q < kQN / 8 / kQWaves; ++q) {
-    const int g = wv * (kQN / 8 / kQWaves) + q, t = 8 * g + (lane >> 3);
-    const uint4* src = x + (size_t)min(tok0 + t, T - 1) * din8 + 8 * ck + (j ^ (t & 7));
-    __builtin_amdgcn_global_load_lds((gvoid*)src, (lds_void_t*)(lb + 64 * g), 16, 0, 0);
+  for (int q = 0; q < kQN / kRowsPerCopy / kQWaves; ++q) {
+    const int g = wv * (kQN / kRowsPerCopy / kQWaves) + q, t = kRowsPerCopy * g + lane / kQP;
+    lds_copy16(x + (size_t)min(tok0 + t, T - 1) * din8 + kQP * ck + (j ^ (t & 15)),
+               lb + kWave * g);
   }
+}
+
+// The products of one chunk held in buffers (la, lb).
+__device__ __forceinline__ void proj_chunk(const uint4* la, const uint4* lb, int wv, int m,
+                                           int kg, f4v (&acc)[2][4]) {
+#pragma unroll
+  for (int kk = 0; kk < kQP / 4; ++kk) {
+    const int c = 4 * kk + kg;
+    uint4 av[2], bv[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r = 32 * wv + 16 * t + m;
+      av[t] = la[kQP * r + (c ^ (r & 15))];
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int tt = 16 * b + m;
+      bv[b] = lb[kQP * tt + (c ^ (tt & 15))];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[t][b] = mfma16(av[t], bv[b], acc[t][b]);
+  }
+}
+
+// Work-group barrier over LDS only (a fence-based barrier would wait for
+// the copies in flight); the compiler moves no memory access across it.
+__device__ __forceinline__ void proj_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __global__ __launch_bounds__(kQWaves * kWave) void k_proj_gemm(const uint4* __restrict__ phi_t,
@@ -248,59 +300,38 @@ __global__ __launch_bounds__(kQWaves * kWave) void k_proj_gemm(const uint4* __re
                                                               float* __restrict__ zpart, int T,
                                                               int din8, int R, int nzp,
                                                               RouteJob rj) {
-  __shared__ union {
-    struct {
-      uint4 a[2][kQM * kQK / 8];
-      uint4 b[2][kQN * kQK / 8];
-    } g;
-    struct {
-      uint32_t cnt[2 * kRouteFuseMaxE];
-      uint32_t buf[kQWaves * kWave];
-    } r;
-  } L;
   const int nmb = (R + kQM - 1) / kQM;
   if (rj.ids && (int)blockIdx.x == nmb) {
-    if (blockIdx.y == 0) route_lists<kQWaves * kWave>(rj, L.r.cnt, L.r.buf);
+    if (blockIdx.y == 0) {
+      uint32_t* cnt = reinterpret_cast<uint32_t*>(g_qa0);
+      static_assert(sizeof(g_qa0) >= (2 * kRouteFuseMaxE + kQWaves * kWave) * 4, "route LDS");
+      route_lists<kQWaves * kWave>(rj, cnt, cnt + 2 * kRouteFuseMaxE);
+    }
     return;
   }
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row0 = (int)blockIdx.x * kQM, tok0 = (int)blockIdx.y * kQN;
   const int m = lane & 15, kg = lane >> 4;
-  const int nck = din8 / (kQK / 8);
+  const int nck = din8 / kQP;
   f4v acc[2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[t][b] = f4v{0.f, 0.f, 0.f, 0.f};
-  proj_stage(L.g.a[0], L.g.b[0], phi_t, x, row0, tok0, R, T, din8, 0, wv, lane);
-  for (int ck = 0; ck < nck; ++ck) {
-    const int cb = ck & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this chunk's copies of this wave are in
-    __syncthreads();                     // ... and every wave's; the other buffer is free
-    if (ck + 1 < nck)
-      proj_stage(L.g.a[cb ^ 1], L.g.b[cb ^ 1], phi_t, x, row0, tok0, R, T, din8, ck + 1, wv,
-                 lane);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = 4 * kk + kg;
-      uint4 av[2], bv[4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int r = 32 * wv + 16 * t + m;
-        av[t] = L.g.a[cb][8 * r + (c ^ (r & 7))];
-      }
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int tt = 16 * b + m;
-        bv[b] = L.g.b[cb][8 * tt + (c ^ (tt & 7))];
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[t][b] = mfma16(av[t], bv[b], acc[t][b]);
-    }
+  proj_stage(g_qa0, g_qb0, phi_t, x, row0, tok0, R, T, din8, 0, wv, lane);
+  if (nck > 1) proj_stage(g_qa1, g_qb1, phi_t, x, row0, tok0, R, T, din8, 1, wv, lane);
+  // chunk ck: this wave's copies of it are in (those of chunk ck + 1 may
+  // still be on their way), then every wave's; the buffer of chunk ck + 2
+  // was last read for chunk ck - 1, which every wave has finished
+  static_assert(kQCopies < 16, "vmcnt field");
+#define PROJ_STEP(CK, LA, LB, NA, NB)                                                do {                                                                                 if ((CK) + 1 < nck)                                                                  __builtin_amdgcn_s_waitcnt(0x0F70 | kQCopies);                                   else                                                                                 __builtin_amdgcn_s_waitcnt(0x0F70);                                              proj_barrier();                                                                    if ((CK) + 2 < nck)                                                                  proj_stage(NA, NB, phi_t, x, row0, tok0, R, T, din8, (CK) + 2, wv, lane);        proj_chunk(LA, LB, wv, m, kg, acc);                                              } while (0)
+  for (int ck = 0; ck < nck; ck += kQStages) {
+    PROJ_STEP(ck, g_qa0, g_qb0, g_qa2, g_qb2);
+    if (ck + 1 < nck) PROJ_STEP(ck + 1, g_qa1, g_qb1, g_qa0, g_qb0);
+    if (ck + 2 < nck) PROJ_STEP(ck + 2, g_qa2, g_qb2, g_qa1, g_qb1);
   }
+#undef PROJ_STEP
   // lane (m, kg) of block (t, b) holds rows 4 kg .. + 3 of the 16-row block
   // for token 16 b + m
 #pragma unroll
@@ -712,7 +743,7 @@ int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, i
   if (routed) *routed = false;
   if (x_f32 && ((T >= 16 && din % 32 == 0) || din8 > kPMaxU * kWave || ((uintptr_t)x & 15u)))
     return fail(BITSMOE_EINVAL, "float32 x needs T < 16 or din %% 32 != 0, din <= 4096, 16-byte x");
-  if (T >= 64 && din % kQK == 0 && !x_f32) {
+  if (T >= 64 && din % kQK == 0 && !x_f32) {  // (x_f32 is refused above for T >= 16)
     const int nzp = (R + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
     RouteJob rj{};
     const bool fuse = route && route->E <= kRouteFuseMaxE;
