@@ -323,6 +323,24 @@ int bitsmoe_workspace_init(void* ws, size_t ws_bytes, bitsmoe_stream_t stream);
 uint32_t bitsmoe_debug_set_wait_limit(uint32_t spins);
 
 /*
+ * bitsmoe_wait_timeouts: the number of waits of the one-launch gate/up
+ * kernels (bitsmoe_moe_gateup at T <= 4) that gave up since the workspace
+ * was zero-filled, cumulative over calls.  Those kernels need every
+ * work-group resident at once (the groups wait for each other's z); when
+ * another kernel or process holds compute units, a wait can run out its
+ * bound, and the rows it covers are written as NaN while the call itself
+ * still returns BITSMOE_OK.  A count that grew across a call says that this
+ * happened.  ws / ws_bytes: the workspace the calls used (device memory);
+ * ws = NULL reads the current device's static workspace of
+ * bitsmoe_moe_gateup_noalloc.  count: host pointer, receives the count.
+ * Synchronises `stream` (the count includes every call queued on it).
+ * Returns BITSMOE_EINVAL for a null count or a workspace smaller than its
+ * sync words, BITSMOE_EHIP when the copy fails.
+ */
+int bitsmoe_wait_timeouts(const void* ws, size_t ws_bytes, uint32_t* count,
+                          bitsmoe_stream_t stream);
+
+/*
  * Codes of expert e as one of the device decoders produces them, in k order
  * ("execution": the width-grouped plane layout read back), for bit-exact
  * tests of the decode each kernel actually runs.  codes: device buffer of

@@ -60,6 +60,7 @@ _SIGS = {
     "bitsmoe_workspace_init": ([_vp, _sz, _vp], _i),
     "bitsmoe_dump_codes": ([_vp, _sz, _i, _i, _i, _i, _i, _vp, _vp], _i),
     "bitsmoe_debug_set_wait_limit": ([ctypes.c_uint32], ctypes.c_uint32),
+    "bitsmoe_wait_timeouts": ([_vp, _sz, ctypes.POINTER(ctypes.c_uint32), _vp], _i),
     "bitsmoe_pack_device_workspace_size": ([_i, _i, _i, _vp, _psz], _i),
     "bitsmoe_pack_device": ([_i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp], _i),
     "bitsmoe_fqcm_distortion": ([_vp, _i, _i, _i, _vp, _vp], _i),
@@ -208,6 +209,19 @@ def debug_set_wait_limit(spins):
     """Sets the bound on the one-launch gate/up kernel's waits for z (0: give
     up at once, every row NaN); returns the previous bound.  Test hook."""
     return int(_lib.bitsmoe_debug_set_wait_limit(int(spins)))
+
+
+def wait_timeouts(ws=None, stream=None):
+    """Waits of the one-launch gate/up kernels that gave up (rows written as
+    NaN) since the workspace was zero-filled; ws=None reads the static
+    workspace of moe_gateup_noalloc.  Synchronises the stream."""
+    n = ctypes.c_uint32(0)
+    if ws is None:
+        _check(_lib.bitsmoe_wait_timeouts(None, 0, ctypes.byref(n), _stream(stream)))
+    else:
+        _check(_lib.bitsmoe_wait_timeouts(_ptr(ws), _nbytes(ws), ctypes.byref(n),
+                                          _stream(stream)))
+    return int(n.value)
 
 
 DUMP_I8, DUMP_F16, DUMP_LANE = 0, 1, 2

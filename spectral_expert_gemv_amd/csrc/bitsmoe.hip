@@ -974,6 +974,7 @@ int bitsmoe_moe_gateup(const void* packed_gate, size_t gate_bytes, const void* p
     fa.bw = fa.cw + (size_t)kZRing * k * 2 * kOneSlots;
     fa.epoch = (uint32_t*)(wsb + plan.sync_off);
     fa.hint = fa.epoch + 32;
+    fa.timeouts = fa.epoch + 1;
     fa.grid = fgrid;
     fa.spin = g_wait_limit.load(std::memory_order_relaxed);
     if (one)
@@ -1088,6 +1089,29 @@ int bitsmoe_moe_gateup_noalloc(const void* packed_gate, size_t gate_bytes, const
 
 uint32_t bitsmoe_debug_set_wait_limit(uint32_t spins) {
   return g_wait_limit.exchange(spins);
+}
+
+int bitsmoe_wait_timeouts(const void* ws, size_t ws_bytes, uint32_t* count,
+                          bitsmoe_stream_t stream) {
+  if (!count) return fail(BITSMOE_EINVAL, "count is null");
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t* w = (const uint8_t*)ws;
+  if (!w) {
+    void* p = nullptr;
+    const int st = scratch_for_current_device(s, &p);
+    if (st) return st;
+    w = (const uint8_t*)p;
+  } else if (ws_bytes < kSyncBytes) {
+    return fail(BITSMOE_EINVAL, "ws_bytes=%zu below the %zu bytes of the sync words", ws_bytes,
+                kSyncBytes);
+  }
+  // word 1 of the sync line (the epoch is word 0, the hint counters follow)
+  hipError_t e = hipMemcpyAsync(count, w + sizeof(uint32_t), sizeof(uint32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(BITSMOE_EHIP, "reading the time-out count: %s",
+                                   hipGetErrorString(e));
+  return BITSMOE_OK;
 }
 
 int bitsmoe_dump_codes(const void* packed, size_t packed_bytes, int E, int dout, int r, int e,

@@ -227,11 +227,12 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
     }
     if (t != zt_cached) {
       // one wave polls the hint counters (the first time only), the rest wait
-      if (zt_cached < 0 && wv == 0) wait_hint(s.hint, tag * (uint32_t)nzw, s.spin);
+      if (zt_cached < 0 && wv == 0) (void)wait_hint(s.hint, tag * (uint32_t)nzw, s.spin);
       lds_sync();
       float zmx;
       zok = stage_z<kFThreads, kFZPer>(zt + (size_t)t * R, R, tag, &L.Z[0], s.spin, zmx);
       zok = __all(zok);
+      count_timeout(s, !zok, lane);
       if (lane == 0) L.zok[wv] = zok;  // every wave's words: combined in the epilogue
       lds_sync();                  // L.Z complete
       zt_cached = t;
@@ -452,7 +453,7 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
   // (Waited for with the default bound also when a test lowered the
   // launch's bound.)
   if (blockIdx.x == 0 && wv == 0) {
-    wait_hint(s.hint, tag * (uint32_t)nzw, max(s.spin, kSpinDefault));
+    count_timeout(s, !wait_hint(s.hint, tag * (uint32_t)nzw, max(s.spin, kSpinDefault)), lane);
     if (lane == 0) __hip_atomic_store(s.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

@@ -60,6 +60,7 @@ struct FusedArgs {
   uint32_t* hint;      // 64 counters, 32 words apart: producing waves done, cumulative over launches
   int grid;            // multiple of 8, all work-groups resident
   uint32_t spin;       // bound on the z exchange waits (0: give up at once, rows NaN)
+  uint32_t* timeouts;  // waits that gave up, cumulative over launches (word 1 of the sync line)
   // one-token kernel: kZRing launch buffers (the tag picks one) of tagged
   // coefficient words, pairs x 2 x kOneSlots (slot order), and of tagged
   // row-independent partial sums, pairs x 2 x r

@@ -699,6 +699,7 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
       ++spins;
     }
     const bool zok = spins < s.spin;
+    count_timeout(s, !zok, lane);
 
     // ---- digit rows; the width-8 correction and the partial sums ----
     float corr = 0.f;  // sum of rint(c 2^S) over width-8 slots (those enter as code - 128)
@@ -804,7 +805,8 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
   // itself (waited for with the default bound also when a test lowered the
   // launch's bound).
   if (blockIdx.x == 0 && wv == 0) {
-    wait_hint(s.hint, tag * (uint32_t)(s.grid * kOHint), max(s.spin, kSpinDefault));
+    count_timeout(s, !wait_hint(s.hint, tag * (uint32_t)(s.grid * kOHint), max(s.spin, kSpinDefault)),
+                  lane);
     if (lane == 0) __hip_atomic_store(s.epoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

@@ -170,17 +170,26 @@ __device__ __forceinline__ void hint_add(const FusedArgs& s, int pw, int lane) {
 // with tag g their sum is g times the number of producing waves (modulo
 // 2^32).  Lane i reads counter i; 64 counters on separate lines keep the
 // producers' increments from contending.  Only a hint: the tags decide.  At
-// most spin / 64 polls.
-__device__ __forceinline__ void wait_hint(const uint32_t* hint, uint32_t target, uint32_t spin) {
+// most spin / 64 polls; false when the count was not reached.
+__device__ __forceinline__ bool wait_hint(const uint32_t* hint, uint32_t target, uint32_t spin) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t polls = 0;
   while (true) {
     const uint32_t c =
         __hip_atomic_load(hint + kHintStride * lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t tot = wave_sum_u32_dpp(c);  // modulo 2^32, like the target
-    if ((int32_t)(tot - target) >= 0 || ++polls >= spin / 64) break;
+    if ((int32_t)(tot - target) >= 0) return true;
+    if (++polls >= spin / 64) return false;
     __builtin_amdgcn_s_sleep(4);
   }
+}
+
+// One more wait of this launch gave up (uniform condition; lane 0 counts
+// it): the host reads the cumulative count, so a time-out that turned rows
+// into NaN is never silent.
+__device__ __forceinline__ void count_timeout(const FusedArgs& s, bool gave_up, int lane) {
+  if (gave_up && lane == 0)
+    __hip_atomic_fetch_add(s.timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The token's R tagged z words, copied into LDS as floats by the NT lanes of

@@ -197,6 +197,10 @@ def test_device_entry_points_validate_before_launch():
     assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 0, 3, FAKE, None) == bm.EINVAL
     assert L.bitsmoe_dump_codes(FAKE, 1 << 16, 4, 96, 64, 0, -1, FAKE, None) == bm.EINVAL
     assert L.bitsmoe_workspace_init(None, 16, None) == bm.EINVAL
+    n = ctypes.c_uint32(7)
+    assert L.bitsmoe_wait_timeouts(FAKE, 1 << 20, None, None) == bm.EINVAL
+    assert L.bitsmoe_wait_timeouts(FAKE, 64, ctypes.byref(n), None) == bm.EINVAL
+    assert n.value == 7
     assert bm._lib.bitsmoe_last_error_detail()
 
 

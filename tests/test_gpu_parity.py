@@ -420,14 +420,16 @@ def test_blob_expert_count_mismatch_gives_nan(bm, wl_name):
 @pytest.mark.parametrize("wl_name", ["tiny_t1", "wide_t2"])
 def test_wait_limit_zero_gives_nan_rows_then_recovers(bm, wl_name):
     """With the wait bound set to 0 by the host, every wait of the one-launch
-    kernels gives up at once: the launch completes and every row is NaN.
-    With the bound restored, the next calls on the same workspace are exact
-    again (the launch counter advanced normally)."""
+    kernels gives up at once: the launch completes, every row is NaN and the
+    workspace's time-out count grows.  With the bound restored, the next
+    calls on the same workspace are exact again (the launch counter advanced
+    normally) and add no time-out."""
     wl = synth.workload(wl_name)
     L, dev = device_layer(wl.layer.name)
     x, ids = synth.make_batch(wl, L)
     T, k = ids.shape
     ws = dev.workspace(T, k)
+    t0 = bm.wait_timeouts(ws)
     prev = bm.debug_set_wait_limit(0)
     try:
         h = dev.gateup(_cuda(x), _cuda(ids), ws=ws)
@@ -435,7 +437,10 @@ def test_wait_limit_zero_gives_nan_rows_then_recovers(bm, wl_name):
         assert torch.isnan(h).all()
     finally:
         assert bm.debug_set_wait_limit(prev) == 0
+    t1 = bm.wait_timeouts(ws)
+    assert t1 > t0
     for _ in range(2):
         got = dev.gateup(_cuda(x), _cuda(ids), ws=ws)
         torch.cuda.synchronize()
         _check_h(got.cpu().numpy(), pairs_ref(L, x, ids))
+    assert bm.wait_timeouts(ws) == t1
