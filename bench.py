@@ -30,12 +30,25 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_ONE_TOKEN = ("k_gateup_one (z, every routed expert's coefficients, expert apply and "
                     "SiLU*mul in one launch)")
 KERNEL_ONE_LAUNCH = "k_gateup_fused (z, expert apply and SiLU*mul in one launch)"
-KERNEL_TWO_LAUNCHES = "k_proj_rows + k_route_group + k_gateup_grouped (timed together)"
+
+
+def kernel_batched(T):
+    """The launches of one batched step, timed together (the route grouping
+    runs as one more work-group of the projection launch)."""
+    proj = "k_proj_gemm" if T >= 64 else "k_proj_mfma" if T >= 16 else "k_proj_rows"
+    return proj + " + k_group_coef + k_gateup_grouped (timed together)"
+
 # HBM bytes per launch from FETCH_SIZE + WRITE_SIZE counter runs, scaled by
 # the same counters on a plain copy of known size, with the hash of the
 # kernel sources they were taken on: reported only while the sources still
 # hash the same (None once a kernel has changed since).
-TRAFFIC = {"qwen3_30b_a3b_t1": (28510807, "c2fe9a3999e96651")}
+TRAFFIC = {
+    "qwen3_30b_a3b_t1": (28510438, "aaa0f36d0484f0f3"),
+    "qwen3_30b_a3b_t32": (111204529, "aaa0f36d0484f0f3"),
+    "mixtral_8x7b_t1": (149463399, "aaa0f36d0484f0f3"),
+    "mixtral_8x7b_t8": (352923675, "aaa0f36d0484f0f3"),
+    "deepseek_moe_16b_t512": (599263904, "aaa0f36d0484f0f3"),
+}
 
 
 def kernel_source_hash():
@@ -646,7 +659,7 @@ def main():
                      "expert_bytes_avg": round(sum(s[2] for s in sb) / len(sb)),
                      "launch_us_avg": round(kern_us, 3),
                      "kernel": (KERNEL_ONE_TOKEN if T == 1 and spec.r <= 2048 else
-                                KERNEL_ONE_LAUNCH if T <= 4 else KERNEL_TWO_LAUNCHES)},
+                                KERNEL_ONE_LAUNCH if T <= 4 else kernel_batched(T))},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(L, host_batches, args.cpu_seconds)

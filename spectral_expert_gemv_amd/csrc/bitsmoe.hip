@@ -300,18 +300,28 @@ __global__ __launch_bounds__(kQWaves * kWave) void k_proj_gemm(const uint4* __re
                                                               float* __restrict__ zpart, int T,
                                                               int din8, int R, int nzp,
                                                               RouteJob rj) {
-  const int nmb = (R + kQM - 1) / kQM;
-  if (rj.ids && (int)blockIdx.x == nmb) {
-    if (blockIdx.y == 0) {
+  // Work-group b runs on XCD b % 8.  The work-groups of XCD x take the row
+  // blocks x, x + 8, ..., each with all of its token tiles one after
+  // another, so a row block's Phi^T rows come from HBM into one L2 and its
+  // token tiles read them there (with the tiles on different XCDs every L2
+  // fetched all of Phi^T).  The work-group after them groups the routed
+  // pairs when a route job is given.
+  const int nmb = (R + kQM - 1) / kQM, ntb = (T + kQN - 1) / kQN;
+  const int nmain = 8 * ((nmb + 7) / 8) * ntb;
+  if ((int)blockIdx.x >= nmain) {
+    if (rj.ids) {
       uint32_t* cnt = reinterpret_cast<uint32_t*>(g_qa0);
       static_assert(sizeof(g_qa0) >= (2 * kRouteFuseMaxE + kQWaves * kWave) * 4, "route LDS");
       route_lists<kQWaves * kWave>(rj, cnt, cnt + 2 * kRouteFuseMaxE);
     }
     return;
   }
+  const int jx = (int)blockIdx.x >> 3;
+  const int mb = ((int)blockIdx.x & 7) + 8 * (jx / ntb), tb = jx % ntb;
+  if (mb >= nmb) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row0 = (int)blockIdx.x * kQM, tok0 = (int)blockIdx.y * kQN;
+  const int row0 = mb * kQM, tok0 = tb * kQN;
   const int m = lane & 15, kg = lane >> 4;
   const int nck = din8 / kQP;
   f4v acc[2][4];
@@ -748,9 +758,11 @@ int launch_proj(const void* phi, const void* x, float* z, float* zpart, int T, i
     RouteJob rj{};
     const bool fuse = route && route->E <= kRouteFuseMaxE;
     if (fuse) rj = *route;
-    hipLaunchKernelGGL(k_proj_gemm,
-                       dim3((unsigned)((R + kQM - 1) / kQM + (fuse ? 1 : 0)),
-                            (unsigned)((T + kQN - 1) / kQN)),
+    // (row blocks grouped by XCD, each with all of its token tiles; one
+    // more work-group for the route job)
+    const long long nmb = (R + kQM - 1) / kQM, ntb = (T + kQN - 1) / kQN;
+    const long long nmain = 8 * ((nmb + 7) / 8) * ntb;
+    hipLaunchKernelGGL(k_proj_gemm, dim3((unsigned)(nmain + (fuse ? 1 : 0))),
                        dim3(kQWaves * kWave), 0, s, (const uint4*)phi, (const uint4*)x, z, zpart,
                        T, din8, R, nzp, rj);
     if (routed) *routed = fuse;
