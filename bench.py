@@ -43,11 +43,11 @@ def kernel_batched(T):
 # kernel sources they were taken on: reported only while the sources still
 # hash the same (None once a kernel has changed since).
 TRAFFIC = {
-    "qwen3_30b_a3b_t1": (28510438, "aaa0f36d0484f0f3"),
-    "qwen3_30b_a3b_t32": (111204529, "aaa0f36d0484f0f3"),
-    "mixtral_8x7b_t1": (149463399, "aaa0f36d0484f0f3"),
-    "mixtral_8x7b_t8": (352923675, "aaa0f36d0484f0f3"),
-    "deepseek_moe_16b_t512": (599263904, "aaa0f36d0484f0f3"),
+    "qwen3_30b_a3b_t1": (28584882, "c00040917fd974e8"),
+    "qwen3_30b_a3b_t32": (111204225, "c00040917fd974e8"),
+    "mixtral_8x7b_t1": (149464833, "c00040917fd974e8"),
+    "mixtral_8x7b_t8": (352800568, "c00040917fd974e8"),
+    "deepseek_moe_16b_t512": (599338664, "c00040917fd974e8"),
 }
 
 

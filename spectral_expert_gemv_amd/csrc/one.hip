@@ -287,10 +287,34 @@ __device__ __forceinline__ void apply_group(const OneLds& L, int pj, const StepT
   constexpr bool kQ = G < kNumQGroups;
   constexpr uint32_t kW = G == 0 ? 1 : G == 1 ? 2 : G == 2 ? 3 : G == 3 ? 4 : G == 4 ? 6 : G == 5 ? 8 : 16;
   constexpr uint32_t kBps = kQ ? 2u * kBlkPerK : (uint32_t)kBlkPerK;  // blocks per step
+  constexpr uint32_t kWps = kBps * 4u * kW;                            // plane words per whole step
   const uint32_t o0 = tb.off[G], o1 = min(tb.off[G + 1], hi);
   const uint32_t gb0 = tb.gb[G], gb1 = tb.gb[G + 1], gw0 = tb.gw[G];
+  uint32_t i0 = max(o0, lo);
+  if constexpr (kQ) {
+    // Whole 64-slot steps whose planes are in the arena (a prefix of the
+    // group's steps): no half-step test and no global-memory path; the B
+    // rows are read by every lane and zeroed past the four digit rows.
+    const uint32_t ifull = o0 + (gb1 - gb0) / kBps;
+    const uint32_t istg = staged >= gw0 ? o0 + (staged - gw0) / kWps : o0;
+    const uint32_t ie = min(o1, min(ifull, istg));
+    const int n = lane & 15, q = lane >> 4;
+    const int8_t* brow = &L.Dg[pj][n & (kDigits - 1)][16 * q];
+    const uint32_t* rec = &L.W[pj][gw0 + (i0 - o0) * kWps];
 #pragma unroll 1
-  for (uint32_t i = max(o0, lo); i < o1; ++i) {
+    for (uint32_t i = i0; i < ie; ++i, rec += kWps) {
+      u32x4 x0, x1;
+      decode_w<(int)kW>(rec, false, lane, x0, x1);
+      const uint32_t b0 = gb0 + (i - o0) * kBps;
+      u32x4 b = *reinterpret_cast<const u32x4*>(brow + 4u * b0);
+      if (n >= kDigits) b = u32x4{0u, 0u, 0u, 0u};
+      apply_step(false, x0, x1, b, ai0, ai1, af0, af1);
+    }
+    i0 = max(i0, ie);
+  }
+  // the rest: half steps, and steps decoded from global memory
+#pragma unroll 1
+  for (uint32_t i = i0; i < o1; ++i) {
     const uint32_t b0 = gb0 + (i - o0) * kBps;
     const uint32_t nb = min(gb1 - b0, kBps);
     const uint32_t w0 = gw0 + (b0 - gb0) * 4u * kW, nw = nb * 4u * kW;
@@ -540,10 +564,10 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
     } else if ((wv & 3) == 1) {
       // the projection's K steps, one entry per step (slot0 | nslot << 16),
       // and their split over the projection's eight waves: contiguous
-      // ranges of about equal cost, a step costing (in halves) 6 for its
-      // loads, digit rows and product plus its width per 32 slots of
-      // decode (8 for a 16-bit step); steps past kOPW * kONSMax are left
-      // out (their records give NaN rows)
+      // ranges of about equal cost, a step of width w costing 4 + 4 w (its
+      // plane decode is about 16 w + 16 vector instructions whether the
+      // step is whole or half) and a 16-bit step 12; steps past
+      // kOPW * kONSMax are left out (their records give NaN rows)
       const StepTab tb = step_tab(SP);
       const uint32_t nst = SP.ok ? tb.off[kNumGroups] : 0u;
       const uint32_t ns = min(nst, (uint32_t)(kOPW * kONSMax));
@@ -554,7 +578,7 @@ __global__ __launch_bounds__(kOThreads) void k_gateup_one(FusedArgs s) {
         if (i < ns) {
           const StepInfo si = step_info(tb, i);
           ent[h] = si.slot0 | (si.nslot << 16);
-          c[h] = si.g == kNumGroups - 1 ? 8u : 6u + (uint32_t)group_width(si.g) * (si.nslot / 32u);
+          c[h] = si.g == kNumGroups - 1 ? 12u : 4u + 4u * (uint32_t)group_width(si.g);
         }
       }
       // inclusive prefix sums of the costs in step order
