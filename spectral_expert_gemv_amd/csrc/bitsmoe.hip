@@ -822,7 +822,7 @@ size_t group_coef_bytes(int tcap, int r) {
   const size_t rpad = (size_t)group_rpad(r), nck = rpad / 256;
   const size_t rows = (size_t)tcap * 2 * kTile;
   return 2 * align_up(rows * rpad * 2 + 512, 256) + align_up((size_t)tcap * 2 * nck * kTile * 4, 256) +
-         align_up((size_t)tcap * 2 * 4, 256);
+         align_up((size_t)tcap * 2 * 4, 256) + align_up(rows * 4, 256);
 }
 
 void group_coef_tables(GroupArgs& gs, uint8_t* base, int r) {
@@ -833,6 +833,7 @@ void group_coef_tables(GroupArgs& gs, uint8_t* base, int r) {
   gs.tlo = (_Float16*)(base + hb);
   gs.tbias = (float*)(base + 2 * hb);
   gs.tbad = (uint32_t*)(base + 2 * hb + align_up((size_t)gs.tcap * 2 * nck * kTile * 4, 256));
+  gs.tsh = (int*)((uint8_t*)gs.tbad + align_up((size_t)gs.tcap * 2 * 4, 256));
   gs.rpad = (int)rpad;
   gs.nck = (int)nck;
 }

@@ -63,6 +63,24 @@ constexpr int kGProj = 256;                 // lanes per projection
 constexpr int kGPW = kGWaves / 2;           // waves per projection
 constexpr int kGMaxW = 7168;                // plane words per projection per chunk
 constexpr int kGZP = 16;                    // lanes per token for the partial maxima
+constexpr int kGZPer = 16;                  // partial maxima a lane loads at once (r <= 4096)
+
+// Largest of zp[i], i = i0, i0 + kGZP, ... < i1 (all >= 0): the first kGZPer
+// loads are all issued before any is used, so they cost one round trip, not
+// one each.
+__device__ __forceinline__ float strided_max(const float* zp, int i0, int i1) {
+  float v[kGZPer];
+#pragma unroll
+  for (int u = 0; u < kGZPer; ++u) {
+    const int i = i0 + u * kGZP;
+    v[u] = i < i1 ? zp[i] : 0.f;
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int u = 0; u < kGZPer; ++u) m = fmaxf(m, v[u]);
+  for (int i = i0 + kGZPer * kGZP; i < i1; i += kGZP) m = fmaxf(m, zp[i]);
+  return m;
+}
 
 struct __align__(16) GroupLds {
   uint32_t W[2][kGMaxW + 64];
@@ -120,25 +138,36 @@ __global__ __launch_bounds__(256) void k_group_coef(GroupArgs s) {
       pr = s.rl.pairs[p0 + n];
       const int t = single ? pr : pr / a.ktop;
       const float* zp = s.zpart + (size_t)t * s.nzp;
-      for (int i = pz0 + j; i < pz1; i += kGZP) zm = fmaxf(zm, zp[i]);
+      zm = strided_max(zp, pz0 + j, pz1);
     }
 #pragma unroll
     for (int off = kGZP / 2; off > 0; off >>= 1) zm = fmaxf(zm, __shfl_xor(zm, off, kWave));
     if (j == 0 && n < nt) {
       S[n] = coef_shift(P.cmax, zm);
+      if (ck == 0) s.tsh[(ti * 2 + pj) * kTile + n] = S[n];  // for the grouped kernel
       zoff[n] = single ? pr * a.r : (pr / a.ktop) * (2 * a.r) + (pj ? a.r : 0);
     }
   }
   __syncthreads();
   const uint32_t sl = 256u * (uint32_t)ck + threadIdx.x;
   const bool live = sl < P.n_slot;
-  uint32_t k = live ? P.kidx[sl] : 0u;
+  const bool isq = sl < P.n_qslot;
+  // the slot's entries, all four loads issued before any is used
+  uint32_t k = 0u;
+  float av = 0.f;
+  uint16_t sraw = 0x3C00u, mraw = 0u;  // fp16 1 and 0
+  if (live) {
+    k = P.kidx[sl];
+    av = P.A[sl];
+    if (isq) {
+      sraw = P.S[sl];
+      mraw = P.M[sl];
+    }
+  }
   bool good = k < (uint32_t)a.r;
   k = good ? k : 0u;
-  const float av = live ? P.A[sl] : 0.f;
-  const bool isq = sl < P.n_qslot;
-  const float sv = (live && isq) ? __half2float(__ushort_as_half(P.S[sl])) : 1.f;
-  const float mv = (live && isq) ? __half2float(__ushort_as_half(P.M[sl])) : 0.f;
+  const float sv = __half2float(__ushort_as_half(sraw));
+  const float mv = __half2float(__ushort_as_half(mraw));
   const size_t row0 = (size_t)(ti * 2 + pj) * kTile;
   // the tile's z values of this slot, all loaded before any is used
   float zv[kTile];
@@ -210,6 +239,16 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   const SegProj P = uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
                                          load_rec_s(blob, e, a.E), load_hdr(blob), a.E, a.dout,
                                          a.r));
+  // the tiles' pairs (output rows) and coefficient scales (k_group_coef's),
+  // loaded before the staging copies are issued and stored in LDS after
+  int prv[kSuperTiles], shv[kSuperTiles];
+#pragma unroll
+  for (int t = 0; t < kSuperTiles; ++t) {
+    prv[t] = shv[t] = 0;
+    if (t < nb && threadIdx.x < (unsigned)ntb[t]) prv[t] = s.rl.pairs[p0[t] + threadIdx.x];
+    if (t < nb && lp < ntb[t])
+      shv[t] = s.tsh[((ti0 + t) * 2 + (single ? 0 : pj)) * kTile + lp];
+  }
   uint32_t b1 = chunk_end(P, 0, kGMaxW);
   stage_chunk(&L.W[pj][0], P, sg, 0, b1, lp, lane, kGProj);
 
@@ -226,30 +265,6 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
               8u * (uint32_t)(lane >> 4);
   }
 
-  // tokens of the tiles and their coefficient scales: lanes (n, j) of the
-  // projection take partial maxima j, j + 16, ... of token n
-  {
-    const int n = lp / kGZP, j = lp % kGZP;
-    const int pz0 = (pj && !single) ? a.r / kProjRowsPerBlock : 0;
-    const int pz1 = (pj || single) ? s.nzp : (a.r + kProjRowsPerBlock - 1) / kProjRowsPerBlock;
-#pragma unroll
-    for (int t = 0; t < kSuperTiles; ++t) {
-      if (t < nb) {
-        if (threadIdx.x < (unsigned)ntb[t])
-          L.pair[kTile * t + threadIdx.x] = s.rl.pairs[p0[t] + threadIdx.x];
-        float zm = 0.f;
-        if (n < ntb[t]) {
-          const int pr = s.rl.pairs[p0[t] + n];
-          const int tk = single ? pr : pr / a.ktop;  // z row: the pair's own (single) or its token's
-          const float* zp = s.zpart + (size_t)tk * s.nzp;
-          for (int i = pz0 + j; i < pz1; i += kGZP) zm = fmaxf(zm, zp[i]);
-        }
-#pragma unroll
-        for (int off = kGZP / 2; off > 0; off >>= 1) zm = fmaxf(zm, __shfl_xor(zm, off, kWave));
-        if (j == 0 && n < ntb[t]) L.S[pj][kTile * t + n] = coef_shift(P.cmax, zm);
-      }
-    }
-  }
   // Plane chunks of at most kGMaxW words per projection: the two
   // projections' counts may differ, the barriers are shared, so the
   // work-group runs the larger count and a half past its own count only
@@ -258,6 +273,11 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
     int nc = 0;
     for (uint32_t b = 0; b < P.n_blk; b = chunk_end(P, b, kGMaxW)) ++nc;
     if (threadIdx.x == (unsigned)(pj * kGProj)) L.nch[pj] = nc;
+  }
+#pragma unroll
+  for (int t = 0; t < kSuperTiles; ++t) {
+    if (t < nb && threadIdx.x < (unsigned)ntb[t]) L.pair[kTile * t + threadIdx.x] = prv[t];
+    if (t < nb && lp < ntb[t]) L.S[pj][kTile * t + lp] = shv[t];
   }
   // the first plane chunk's staged words have landed
   __builtin_amdgcn_s_waitcnt(0);

@@ -117,11 +117,13 @@ struct GroupArgs {
   // c 2^S of token column n and slot s at [((tile * 2 + proj) * kTile + n) *
   // rpad + s]; the row-independent sums per 256-slot chunk at
   // [((tile * 2 + proj) * nck + chunk) * kTile + n]; a flag per (tile, proj)
-  // set when a column index is out of range
+  // set when a column index is out of range; the scale S of token column n at
+  // [(tile * 2 + proj) * kTile + n]
   _Float16* thi;
   _Float16* tlo;
   float* tbias;
   uint32_t* tbad;
+  int* tsh;
   int rpad, nck;
 };
 // slots of a tile's coefficient rows: the largest slot count an expert can
