@@ -64,6 +64,7 @@ constexpr int kGPW = kGWaves / 2;           // waves per projection
 constexpr int kGMaxW = 7168;                // plane words per projection per chunk
 constexpr int kGZP = 16;                    // lanes per token for the partial maxima
 constexpr int kGZPer = 16;                  // partial maxima a lane loads at once (r <= 4096)
+constexpr int kGBPer = 9;                   // chunk sums a lane loads up front (r <= 2048)
 
 // Largest of zp[i], i = i0, i0 + kGZP, ... < i1 (all >= 0): the first kGZPer
 // loads are all issued before any is used, so they cost one round trip, not
@@ -239,15 +240,26 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   const SegProj P = uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
                                          load_rec_s(blob, e, a.E), load_hdr(blob), a.E, a.dout,
                                          a.r));
-  // the tiles' pairs (output rows) and coefficient scales (k_group_coef's),
-  // loaded before the staging copies are issued and stored in LDS after
+  // the tiles' pairs (output rows), coefficient scales and row-independent
+  // chunk sums (k_group_coef's) and column-index flags: every load issued
+  // before the staging copies, the values used after them
   int prv[kSuperTiles], shv[kSuperTiles];
+  uint32_t tbv[kSuperTiles];
+  float bpv[kSuperTiles][kGBPer];
 #pragma unroll
   for (int t = 0; t < kSuperTiles; ++t) {
     prv[t] = shv[t] = 0;
+    tbv[t] = 0u;
+    const int row = (ti0 + t) * 2 + (single ? 0 : pj);
     if (t < nb && threadIdx.x < (unsigned)ntb[t]) prv[t] = s.rl.pairs[p0[t] + threadIdx.x];
-    if (t < nb && lp < ntb[t])
-      shv[t] = s.tsh[((ti0 + t) * 2 + (single ? 0 : pj)) * kTile + lp];
+    if (t < nb && lp < ntb[t]) shv[t] = s.tsh[row * kTile + lp];
+    if (t < nb) tbv[t] = s.tbad[row];
+#pragma unroll
+    for (int c = 0; c < kGBPer; ++c) {
+      bpv[t][c] = 0.f;
+      if (t < nb && wp == 0 && lane < ntb[t] && c < s.nck)
+        bpv[t][c] = s.tbias[((size_t)row * s.nck + c) * kTile + lane];
+    }
   }
   uint32_t b1 = chunk_end(P, 0, kGMaxW);
   stage_chunk(&L.W[pj][0], P, sg, 0, b1, lp, lane, kGProj);
@@ -274,10 +286,18 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
     for (uint32_t b = 0; b < P.n_blk; b = chunk_end(P, b, kGMaxW)) ++nc;
     if (threadIdx.x == (unsigned)(pj * kGProj)) L.nch[pj] = nc;
   }
+  float bsum[kSuperTiles];  // (wave 0 of each half, lanes of the tile's tokens)
 #pragma unroll
   for (int t = 0; t < kSuperTiles; ++t) {
     if (t < nb && threadIdx.x < (unsigned)ntb[t]) L.pair[kTile * t + threadIdx.x] = prv[t];
     if (t < nb && lp < ntb[t]) L.S[pj][kTile * t + lp] = shv[t];
+    // the chunks' row-independent sums in chunk order
+    bsum[t] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kGBPer; ++c) bsum[t] += bpv[t][c];
+    if (t < nb && wp == 0 && lane < ntb[t])
+      for (int c = kGBPer; c < s.nck; ++c)
+        bsum[t] += s.tbias[((size_t)((ti0 + t) * 2 + (single ? 0 : pj)) * s.nck + c) * kTile + lane];
   }
   // the first plane chunk's staged words have landed
   __builtin_amdgcn_s_waitcnt(0);
@@ -312,7 +332,7 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
 #pragma unroll
   for (int t = 0; t < kSuperTiles; ++t) {
     if (t >= nb) continue;  // (uniform)
-    const int ti = ti0 + t, nt = ntb[t];
+    const int nt = ntb[t];
     __syncthreads();  // the previous tile's sums are read
     {
       const int n = lane & 15, kg = lane >> 4;
@@ -326,14 +346,11 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
       // the row-independent sums of the tile's chunks (wave 0 of each half),
       // the column-index check from the coefficient pass
       if (wp == 0 && lane < nt) {
-        const float* tb = s.tbias + (size_t)(ti * 2 + (single ? 0 : pj)) * s.nck * kTile + lane;
-        float bsum = 0.f;
-        for (int c = 0; c < s.nck; ++c) bsum += tb[(size_t)c * kTile];
-        L.pbias[pj][0][lane] = bsum;
+        L.pbias[pj][0][lane] = bsum[t];
       } else if (lane < nt) {
         L.pbias[pj][wp][lane] = 0.f;
       }
-      const bool wok = __all(good) && s.tbad[ti * 2 + (single ? 0 : pj)] == 0u;
+      const bool wok = __all(good) && tbv[t] == 0u;
       if (lane == 0) L.pok[pj][wp] = wok;
     }
     __syncthreads();
