@@ -215,25 +215,36 @@ __global__ __launch_bounds__(kGThreads) void k_gateup_grouped(GroupArgs s) {
   // a group share one L2 for its coefficient tables; blocks past the group
   // count exit at once.
   typedef __attribute__((address_space(4))) const int CI32;
-  const int ngr = *(CI32*)s.rl.nstiles;  // written by the route step before this launch
   const bool single = s.single != 0;
   const int nsu = single ? (a.n_seg + 1) / 2 : a.n_seg;  // segment units per group
   const int xcd = (int)blockIdx.x & 7, jx = (int)blockIdx.x >> 3;
   const int gi = xcd + 8 * (jx / nsu), su = jx % nsu;
-  if (ngr <= 0 || gi >= ngr) return;
+  // the group count and this group's record (both written by the route step
+  // before this launch) are read together; the record of a block past the
+  // count is read from a group inside the lists and not used
+  int grec[kGroupRec];
+  {
+    CI32* gr = (CI32*)(s.rl.stile + (size_t)kGroupRec * min(gi, s.tcap - 1));
+#pragma unroll
+    for (int u = 0; u < kGroupRec; ++u) grec[u] = gr[u];
+  }
+  const int ngr = *(CI32*)s.rl.nstiles;
+  // (a record of a live group has a tile count of at least 1: testing it here
+  // keeps its load ahead of this branch, beside the count's)
+  if ((ngr <= 0) | (gi >= ngr) | (grec[1] <= 0)) return;
   // single: this half's segment (a half past the last segment repeats it
   // and writes nothing)
   const int sg0 = single ? 2 * su : su;
   const int sgh = single ? sg0 + pj : sg0;
   const int sg = sgh < a.n_seg ? sgh : a.n_seg - 1;
-  const int ti0 = __builtin_amdgcn_readfirstlane(s.rl.stile[2 * gi]);
-  const int nb = min(max(__builtin_amdgcn_readfirstlane(s.rl.stile[2 * gi + 1]), 1), kSuperTiles);
-  const int e = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti0]);
+  const int ti0 = grec[0];
+  const int nb = min(max(grec[1], 1), kSuperTiles);
+  const int e = grec[2];
   int p0[kSuperTiles], ntb[kSuperTiles];  // each tile's first pair and pair count (uniform)
 #pragma unroll
   for (int t = 0; t < kSuperTiles; ++t) {
-    p0[t] = t < nb ? __builtin_amdgcn_readfirstlane(s.rl.tile[3 * (ti0 + t) + 1]) : 0;
-    ntb[t] = t < nb ? __builtin_amdgcn_readfirstlane(s.rl.tile[3 * (ti0 + t) + 2]) : 0;
+    p0[t] = t < nb ? grec[3 + 2 * t] : 0;
+    ntb[t] = t < nb ? grec[4 + 2 * t] : 0;
   }
 
   const uint8_t* blob = pj ? a.blob_u : a.blob_g;

@@ -89,12 +89,17 @@ struct RouteLists {
   int* tile;     // per tile: expert id, first pair index into pairs, pair count (3 ints)
   int* pairs;    // pair indices t * k + slot, grouped by expert
   int* nstiles;  // [1]
-  int* stile;    // per group of up to kSuperTiles consecutive tiles of one expert:
-                 // first tile, tile count (2 ints)
+  int* stile;    // per group of up to kSuperTiles consecutive tiles of one expert, one
+                 // 8-int record: first tile, tile count, expert id, then first pair
+                 // and pair count of each tile (0 past the count), 0
 };
 constexpr int kSuperTiles = 2;  // tiles of one expert a grouped work-group applies together
+constexpr int kGroupRec = 8;    // ints of a group record
+static_assert(3 + 2 * kSuperTiles <= kGroupRec, "group record");
 // ints of the route lists for tcap tiles and P pairs, and their places
-inline size_t route_ints(int tcap, size_t P) { return 2 + 5 * (size_t)tcap + P; }
+inline size_t route_ints(int tcap, size_t P) {
+  return 2 + (3 + (size_t)kGroupRec) * (size_t)tcap + P;
+}
 inline void route_lists_at(RouteLists& rl, int* rb, int tcap, size_t P) {
   rl.ntiles = rb;
   rl.tile = rb + 1;

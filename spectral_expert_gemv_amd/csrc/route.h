@@ -88,8 +88,17 @@ __device__ void route_lists(const RouteJob& j, uint32_t* cnt, uint32_t* buf) {
     }
     // groups of up to kSuperTiles consecutive tiles of this expert
     for (uint32_t q = t0; q < ti; q += kSuperTiles, ++si) {
-      j.rl.stile[2 * si] = (int)q;
-      j.rl.stile[2 * si + 1] = (int)min((uint32_t)kSuperTiles, ti - q);
+      const uint32_t nq = min((uint32_t)kSuperTiles, ti - q);
+      int* g = j.rl.stile + (size_t)kGroupRec * si;
+      g[0] = (int)q;
+      g[1] = (int)nq;
+      g[2] = e;
+      for (uint32_t u = 0; u < (uint32_t)kSuperTiles; ++u) {
+        const uint32_t i = (q - t0 + u) * kTile;  // the tile's first pair of this expert
+        g[3 + 2 * u] = u < nq ? (int)(off + i) : 0;
+        g[4 + 2 * u] = u < nq ? (int)min((uint32_t)kTile, c - i) : 0;
+      }
+      for (int u = 3 + 2 * kSuperTiles; u < kGroupRec; ++u) g[u] = 0;
     }
     off += c;
   }
