@@ -114,17 +114,37 @@ __device__ __forceinline__ void stage_chunk(uint32_t* arena, const SegProj& p, i
 __global__ __launch_bounds__(256) void k_group_coef(GroupArgs s) {
   const GateUpArgs& a = s.g;
   const int ck = (int)blockIdx.x, ti = (int)blockIdx.y, pj = (int)blockIdx.z;
-  if (ti >= s.rl.ntiles[0]) return;
+  // the tile count and this tile's entry (ti < tcap: inside the lists) are
+  // read together
+  typedef __attribute__((address_space(4))) const int CI32;
+  const int ntl = *(CI32*)s.rl.ntiles;
+  const int e = ((CI32*)s.rl.tile)[3 * ti];
+  const int p0 = ((CI32*)s.rl.tile)[3 * ti + 1];
+  const int nt = ((CI32*)s.rl.tile)[3 * ti + 2];
+  if ((ti >= ntl) | (nt <= 0)) return;
   const bool single = s.single != 0;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
-  const int e = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti]);
-  const int p0 = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti + 1]);
-  const int nt = __builtin_amdgcn_readfirstlane(s.rl.tile[3 * ti + 2]);
   const uint8_t* blob = pj ? a.blob_u : a.blob_g;
   const SegProj P = uniform_seg(make_seg(blob, pj ? a.bytes_u : a.bytes_g, e,
                                          load_rec_s(blob, e, a.E), load_hdr(blob), a.E, a.dout,
                                          a.r));
+  // this thread's slot: its entries loaded first (they do not depend on the
+  // tile's tokens), all four issued before any is used
+  const uint32_t sl = 256u * (uint32_t)ck + threadIdx.x;
+  const bool live = sl < P.n_slot;
+  const bool isq = sl < P.n_qslot;
+  uint32_t k = 0u;
+  float av = 0.f;
+  uint16_t sraw = 0x3C00u, mraw = 0u;  // fp16 1 and 0
+  if (live) {
+    k = P.kidx[sl];
+    av = P.A[sl];
+    if (isq) {
+      sraw = P.S[sl];
+      mraw = P.M[sl];
+    }
+  }
   __shared__ int S[kTile];
   __shared__ int zoff[kTile];
   __shared__ float bred[4][kTile];
@@ -150,21 +170,6 @@ __global__ __launch_bounds__(256) void k_group_coef(GroupArgs s) {
     }
   }
   __syncthreads();
-  const uint32_t sl = 256u * (uint32_t)ck + threadIdx.x;
-  const bool live = sl < P.n_slot;
-  const bool isq = sl < P.n_qslot;
-  // the slot's entries, all four loads issued before any is used
-  uint32_t k = 0u;
-  float av = 0.f;
-  uint16_t sraw = 0x3C00u, mraw = 0u;  // fp16 1 and 0
-  if (live) {
-    k = P.kidx[sl];
-    av = P.A[sl];
-    if (isq) {
-      sraw = P.S[sl];
-      mraw = P.M[sl];
-    }
-  }
   bool good = k < (uint32_t)a.r;
   k = good ? k : 0u;
   const float sv = __half2float(__ushort_as_half(sraw));
