@@ -43,11 +43,11 @@ def kernel_batched(T):
 # kernel sources they were taken on: reported only while the sources still
 # hash the same (None once a kernel has changed since).
 TRAFFIC = {
-    "qwen3_30b_a3b_t1": (28584882, "c00040917fd974e8"),
-    "qwen3_30b_a3b_t32": (111204225, "c00040917fd974e8"),
-    "mixtral_8x7b_t1": (149464833, "c00040917fd974e8"),
-    "mixtral_8x7b_t8": (352800568, "c00040917fd974e8"),
-    "deepseek_moe_16b_t512": (599338664, "c00040917fd974e8"),
+    "qwen3_30b_a3b_t1": (28583267, "26d79436ccd4397e"),
+    "qwen3_30b_a3b_t32": (111054406, "26d79436ccd4397e"),
+    "mixtral_8x7b_t1": (149481248, "26d79436ccd4397e"),
+    "mixtral_8x7b_t8": (352227346, "26d79436ccd4397e"),
+    "deepseek_moe_16b_t512": (602120552, "26d79436ccd4397e"),
 }
 
 
