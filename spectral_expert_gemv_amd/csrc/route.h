@@ -22,6 +22,7 @@
 namespace bitsmoe {
 
 constexpr int kRouteFuseMaxE = 1024;  // experts a fused route work-group handles
+constexpr int kRouteBatch = 16;       // ids a lane loads at once
 
 struct RouteJob {
   const int32_t* ids;  // null: no route work in this launch
@@ -32,23 +33,42 @@ struct RouteJob {
   int nzero;
 };
 
-// Exclusive block scan of one value per thread over NT threads; total gets
-// the sum.
+// Exclusive block scans of three values per thread over NT threads (NT a
+// multiple of 64, at most 1024); total gets each sum.  Each wave scans its
+// lanes with shuffles, publishes its totals in buf (3 NT / 64 words), and
+// every wave adds the totals of the waves before it: two barriers for all
+// three scans.
 template <int NT>
-__device__ __forceinline__ uint32_t route_scan(uint32_t v, uint32_t* buf, uint32_t& total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int d = 1; d < NT; d <<= 1) {
-    const uint32_t a = tid >= d ? buf[tid - d] : 0u;
-    __syncthreads();
-    buf[tid] += a;
-    __syncthreads();
+__device__ __forceinline__ void route_scan3(const uint32_t (&v)[3], uint32_t* buf,
+                                            uint32_t (&excl)[3], uint32_t (&total)[3]) {
+  constexpr int kW = 64, NW = NT / kW;
+  static_assert(NT % kW == 0 && NW <= 16, "route scan");
+  const int lane = threadIdx.x & (kW - 1), wv = threadIdx.x / kW;
+  uint32_t inc[3];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    inc[q] = v[q];
+#pragma unroll
+    for (int d = 1; d < kW; d <<= 1) {
+      const uint32_t t = __shfl_up(inc[q], d, kW);
+      if (lane >= d) inc[q] += t;
+    }
+    if (lane == kW - 1) buf[q * NW + wv] = inc[q];
   }
-  total = buf[NT - 1];
-  const uint32_t incl = buf[tid];
   __syncthreads();
-  return incl - v;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t t = buf[q * NW + w];
+      off += w < wv ? t : 0u;
+      tot += t;
+    }
+    excl[q] = off + inc[q] - v[q];
+    total[q] = tot;
+  }
+  __syncthreads();  // (buf is free again)
 }
 
 // cnt: 2 E words of LDS (counters, then cursors); buf: NT words of LDS.
@@ -59,9 +79,21 @@ __device__ void route_lists(const RouteJob& j, uint32_t* cnt, uint32_t* buf) {
   for (int i = tid; i < j.nzero; i += NT) j.zero[i] = 0u;
   for (int i = tid; i < j.E; i += NT) cnt[i] = 0;
   __syncthreads();
-  for (int p = tid; p < j.P; p += NT) {
-    const int e = j.ids[p];
+  // (with more pairs than lanes, the ids of a batch are all loaded before
+  // any is used: one round trip per kRouteBatch ids of a lane, not one each)
+  if (j.P <= NT) {
+    const int e = tid < j.P ? j.ids[tid] : -1;
     if (e >= 0 && e < j.E) atomicAdd(&cnt[e], 1u);
+  } else for (int p0 = 0; p0 < j.P; p0 += NT * kRouteBatch) {
+    int ev[kRouteBatch];
+#pragma unroll
+    for (int u = 0; u < kRouteBatch; ++u) {
+      const int p = p0 + tid + u * NT;
+      ev[u] = p < j.P ? j.ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kRouteBatch; ++u)
+      if (ev[u] >= 0 && ev[u] < j.E) atomicAdd(&cnt[ev[u]], 1u);
   }
   __syncthreads();
   // each thread owns a contiguous run of experts
@@ -74,10 +106,11 @@ __device__ void route_lists(const RouteJob& j, uint32_t* cnt, uint32_t* buf) {
     nt += te;
     ns += (te + kSuperTiles - 1) / kSuperTiles;
   }
-  uint32_t total_pairs, total_tiles, total_st;
-  uint32_t off = route_scan<NT>(sum, buf, total_pairs);
-  uint32_t ti = route_scan<NT>(nt, buf, total_tiles);
-  uint32_t si = route_scan<NT>(ns, buf, total_st);
+  const uint32_t sv[3] = {sum, nt, ns};
+  uint32_t ex[3], tot[3];
+  route_scan3<NT>(sv, buf, ex, tot);
+  uint32_t off = ex[0], ti = ex[1], si = ex[2];
+  const uint32_t total_tiles = tot[1], total_st = tot[2];
   for (int e = e0; e < e1; ++e) {
     const uint32_t c = cnt[e], t0 = ti;
     cur[e] = off;
@@ -107,12 +140,31 @@ __device__ void route_lists(const RouteJob& j, uint32_t* cnt, uint32_t* buf) {
     j.rl.nstiles[0] = (int)total_st;
   }
   __syncthreads();
-  for (int p = tid; p < j.P; p += NT) {
-    const int e = j.ids[p];
-    if (e >= 0 && e < j.E) {
-      j.rl.pairs[atomicAdd(&cur[e], 1u)] = p;
-    } else {
-      for (int i = 0; i < j.dout; ++i) j.h[(size_t)p * j.dout + i] = __builtin_nanf("");
+  if (j.P <= NT) {
+    const int e = tid < j.P ? j.ids[tid] : 0;
+    if (tid < j.P) {
+      if (e >= 0 && e < j.E) {
+        j.rl.pairs[atomicAdd(&cur[e], 1u)] = tid;
+      } else {
+        for (int i = 0; i < j.dout; ++i) j.h[(size_t)tid * j.dout + i] = __builtin_nanf("");
+      }
+    }
+  } else for (int p0 = 0; p0 < j.P; p0 += NT * kRouteBatch) {
+    int ev[kRouteBatch];
+#pragma unroll
+    for (int u = 0; u < kRouteBatch; ++u) {
+      const int p = p0 + tid + u * NT;
+      ev[u] = p < j.P ? j.ids[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kRouteBatch; ++u) {
+      const int p = p0 + tid + u * NT, e = ev[u];
+      if (p >= j.P) continue;
+      if (e >= 0 && e < j.E) {
+        j.rl.pairs[atomicAdd(&cur[e], 1u)] = p;
+      } else {
+        for (int i = 0; i < j.dout; ++i) j.h[(size_t)p * j.dout + i] = __builtin_nanf("");
+      }
     }
   }
 }
