@@ -43,11 +43,11 @@ def kernel_batched(T):
 # kernel sources they were taken on: reported only while the sources still
 # hash the same (None once a kernel has changed since).
 TRAFFIC = {
-    "qwen3_30b_a3b_t1": (28583267, "26d79436ccd4397e"),
-    "qwen3_30b_a3b_t32": (111054406, "26d79436ccd4397e"),
-    "mixtral_8x7b_t1": (149481248, "26d79436ccd4397e"),
-    "mixtral_8x7b_t8": (352227346, "26d79436ccd4397e"),
-    "deepseek_moe_16b_t512": (602120552, "26d79436ccd4397e"),
+    "qwen3_30b_a3b_t1": (28584014, "69051a87be0a5b30"),
+    "qwen3_30b_a3b_t32": (111021303, "69051a87be0a5b30"),
+    "mixtral_8x7b_t1": (149458272, "69051a87be0a5b30"),
+    "mixtral_8x7b_t8": (352218610, "69051a87be0a5b30"),
+    "deepseek_moe_16b_t512": (602325360, "69051a87be0a5b30"),
 }
 
 
