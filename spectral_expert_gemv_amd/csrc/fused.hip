@@ -131,9 +131,12 @@ __global__ __launch_bounds__(kFThreads) void k_gateup_fused(FusedArgs s) {
   int u = (int)blockIdx.x;
   bool have = u < U;
   if (pj == 0) {
-    PhiRegs phr;
-    phi_issue(s, n0, nrw, lane, phr);
-    z_finish(s, zt, n0, nrw, lane, tag, phr);
+    // (the r > 2048 instantiation keeps whole rows of up to 4096 inputs in
+    // registers; the other keeps its first 2048)
+    constexpr int kNU = kFSper > 9 ? 8 : 4;
+    PhiRegs<kNU> phr;
+    phi_issue<kNU>(s, n0, nrw, lane, phr);
+    z_finish<kNU>(s, zt, n0, nrw, lane, tag, phr);
     // (the hint may run ahead of the z stores: a reader that comes too early
     // finds old tags and re-reads those words)
     hint_add(s, (int)blockIdx.x * kFPW + wp, lane);

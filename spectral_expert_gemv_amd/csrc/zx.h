@@ -41,18 +41,20 @@ __device__ __forceinline__ float fdot8(uint4 a, uint4 b, float acc) {
   return acc;
 }
 
-// This lane's partial dot product of one Phi^T row (p: this lane's 4 16-byte
-// units of the first 2048 inputs) with token tt's x, over all din inputs.
-__device__ __forceinline__ float zpart(const FusedArgs& s, const uint4* prow, const uint4 (&p)[4],
-                                       const uint4 (&xv)[4], int tt, int lane) {
+// This lane's partial dot product of one Phi^T row (p: this lane's NU
+// 16-byte units of the first NU * 512 inputs) with token tt's x, over all din
+// inputs (units past NU * 512 are loaded here, a batch of 4 at a time).
+template <int NU>
+__device__ __forceinline__ float zpart(const FusedArgs& s, const uint4* prow, const uint4 (&p)[NU],
+                                       const uint4 (&xv)[NU], int tt, int lane) {
   const uint4* xt = s.x + (size_t)tt * s.din8;
   float acc = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < NU; ++u) {
     const int i = lane + u * kWave;
     if (i < s.din8) acc = fdot8(p[u], tt == 0 ? xv[u] : xt[i], acc);
   }
-  for (int i0 = 4 * kWave; i0 < s.din8; i0 += 4 * kWave) {  // din > 2048
+  for (int i0 = NU * kWave; i0 < s.din8; i0 += 4 * kWave) {
     uint4 q4[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -87,38 +89,52 @@ __device__ __forceinline__ void tstep(float (&v)[kPre], bool up) {
 }
 
 // A producing wave owns z rows [n0, n0 + nrw) of every token.  The loads of
-// the first kPre Phi^T rows and of x go out first, in straight-line code (so
-// that they stay together and ahead of anything that depends on a load);
-// z_finish then reduces the kPre partial sums together (2 transposing
-// exchanges leave row lane & 3 in every lane, 4 more finish the sum), lane i
-// publishes row i, and rows beyond the first kPre follow one at a time.
+// its first kPre Phi^T rows (NU 16-byte units a lane: the whole row for din
+// <= NU * 512) and of x go out first, in straight-line code (so that they
+// stay together and ahead of anything that depends on a load); z_finish then
+// reduces the kPre partial sums together (2 transposing exchanges leave row
+// lane & 3 in every lane, 4 more finish the sum) and lane i publishes row i.
+// Rows beyond the first kPre follow kPre at a time, each batch's loads all
+// issued before any is used.
+template <int NU>
 struct PhiRegs {
-  uint4 pv[kPre][4];
-  uint4 xv[4];
+  uint4 pv[kPre][NU];
+  uint4 xv[NU];
 };
 
-__device__ __forceinline__ void phi_issue(const FusedArgs& s, int n0, int nrw, int lane,
-                                          PhiRegs& q) {
+template <int NU>
+__device__ __forceinline__ void phi_rows(const FusedArgs& s, int n0, int nrw, int j0, int lane,
+                                         uint4 (&pv)[kPre][NU]) {
   const int R = 2 * s.g.r;
 #pragma unroll
   for (int j = 0; j < kPre; ++j) {
-    const int n = (j < nrw && n0 + j < R) ? n0 + j : 0;
+    const int n = (j0 + j < nrw && n0 + j0 + j < R) ? n0 + j0 + j : 0;
     const uint4* prow = s.phi_t + (size_t)n * s.din8;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int i = lane + u * kWave;
-      q.pv[j][u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
+      pv[j][u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
     }
   }
+}
+
+template <int NU>
+__device__ __forceinline__ void phi_issue(const FusedArgs& s, int n0, int nrw, int lane,
+                                          PhiRegs<NU>& q) {
+  phi_rows<NU>(s, n0, nrw, 0, lane, q.pv);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < NU; ++u) {
     const int i = lane + u * kWave;
     q.xv[u] = i < s.din8 ? s.x[i] : make_uint4(0, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void z_finish(const FusedArgs& s, uint64_t* zt, int n0, int nrw,
-                                         int lane, uint32_t tag, const PhiRegs& q) {
+// z of rows n0 + j0 .. + kPre - 1 (those below nrw and R) for every token,
+// from their loaded units pv, published by lanes 0 .. kPre - 1.
+template <int NU>
+__device__ __forceinline__ void z_batch(const FusedArgs& s, uint64_t* zt, int n0, int nrw, int j0,
+                                        int lane, uint32_t tag, const uint4 (&pv)[kPre][NU],
+                                        const uint4 (&xv)[NU]) {
   static_assert(kPre == 4, "the transposing reduction is written for 4 rows");
   const int R = 2 * s.g.r;
   // (T >= 1: a do-while leaves no path on which the x and Phi^T loads are
@@ -129,8 +145,8 @@ __device__ __forceinline__ void z_finish(const FusedArgs& s, uint64_t* zt, int n
     float v[kPre];
 #pragma unroll
     for (int j = 0; j < kPre; ++j) {
-      const int n = (j < nrw && n0 + j < R) ? n0 + j : 0;
-      v[j] = zpart(s, s.phi_t + (size_t)n * s.din8, q.pv[j], q.xv, tt, lane);
+      const int n = (j0 + j < nrw && n0 + j0 + j < R) ? n0 + j0 + j : 0;
+      v[j] = zpart<NU>(s, s.phi_t + (size_t)n * s.din8, pv[j], xv, tt, lane);
     }
     tstep<2>(v, (lane & 2) != 0);
     tstep<1>(v, (lane & 1) != 0);
@@ -138,21 +154,19 @@ __device__ __forceinline__ void z_finish(const FusedArgs& s, uint64_t* zt, int n
 #pragma unroll
     for (int off = 4; off < kWave; off <<= 1) z += __shfl_xor(z, off, kWave);
     const int j = lane & 3;
-    if (lane < kPre && j < nrw && n0 + j < R) publish_z(zt, s.g.r, tt, n0 + j, z, tag);
+    if (lane < kPre && j0 + j < nrw && n0 + j0 + j < R) publish_z(zt, s.g.r, tt, n0 + j0 + j, z, tag);
   } while (++tt < s.T);
-  for (int j = kPre; j < nrw && n0 + j < R; ++j) {  // rows beyond the first kPre
-    const int n = n0 + j;
-    const uint4* prow = s.phi_t + (size_t)n * s.din8;
-    uint4 p0[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + u * kWave;
-      p0[u] = i < s.din8 ? prow[i] : make_uint4(0, 0, 0, 0);
-    }
-    for (int tt = 0; tt < s.T; ++tt) {
-      const float z = wave_sum(zpart(s, prow, p0, q.xv, tt, lane));
-      if (lane == 0) publish_z(zt, s.g.r, tt, n, z, tag);
-    }
+}
+
+template <int NU>
+__device__ __forceinline__ void z_finish(const FusedArgs& s, uint64_t* zt, int n0, int nrw,
+                                         int lane, uint32_t tag, const PhiRegs<NU>& q) {
+  const int R = 2 * s.g.r;
+  z_batch<NU>(s, zt, n0, nrw, 0, lane, tag, q.pv, q.xv);
+  for (int j0 = kPre; j0 < nrw && n0 + j0 < R; j0 += kPre) {  // rows beyond the first kPre
+    uint4 pv[kPre][NU];
+    phi_rows<NU>(s, n0, nrw, j0, lane, pv);
+    z_batch<NU>(s, zt, n0, nrw, j0, lane, tag, pv, q.xv);
   }
 }
 
