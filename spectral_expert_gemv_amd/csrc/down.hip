@@ -53,11 +53,27 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y,
   const int t = (int)blockIdx.y;
   const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
   if (i >= din) return;
+  // the slots' ids, weights and y values loaded kCombineBatch at a time,
+  // all before any is used, then summed in slot order
+  constexpr int kCombineBatch = 16;
   float acc = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int e = ids[t * k + j];
-    if (e < 0 || e >= E) continue;
-    acc += g[t * k + j] * y[((size_t)t * k + j) * din + i];
+  for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+    int ev[kCombineBatch];
+    float gv[kCombineBatch], yv[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int j = j0 + u;
+      ev[u] = -1;
+      gv[u] = yv[u] = 0.f;
+      if (j < k) {
+        ev[u] = ids[t * k + j];
+        gv[u] = g[t * k + j];
+        yv[u] = y[((size_t)t * k + j) * din + i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)
+      if (ev[u] >= 0 && ev[u] < E) acc += gv[u] * yv[u];
   }
   out[(size_t)t * din + i] = acc;
 }
