@@ -43,11 +43,11 @@ def kernel_batched(T):
 # kernel sources they were taken on: reported only while the sources still
 # hash the same (None once a kernel has changed since).
 TRAFFIC = {
-    "qwen3_30b_a3b_t1": (28583783, "6946a2ac37f3f793"),
-    "qwen3_30b_a3b_t32": (111023746, "6946a2ac37f3f793"),
-    "mixtral_8x7b_t1": (149261961, "6946a2ac37f3f793"),
-    "mixtral_8x7b_t8": (352217169, "6946a2ac37f3f793"),
-    "deepseek_moe_16b_t512": (602299282, "6946a2ac37f3f793"),
+    "qwen3_30b_a3b_t1": (28583154, "476f46c709b5bff4"),
+    "qwen3_30b_a3b_t32": (111021641, "476f46c709b5bff4"),
+    "mixtral_8x7b_t1": (149256251, "476f46c709b5bff4"),
+    "mixtral_8x7b_t8": (352212659, "476f46c709b5bff4"),
+    "deepseek_moe_16b_t512": (602235068, "476f46c709b5bff4"),
 }
 
 
